@@ -1,0 +1,318 @@
+"""Reference critical-wave split planner, a slow direct event simulation.
+
+Test infrastructure only (see the package docstring). The library's C++ planner
+must produce the same integers (split counts, ranges, task order) and the same
+double-precision scores, bit for bit; this file is written independently from
+the pages, in their order and notation.
+
+What the pages fix (LiquidCP, section 5.2 "Critical-wave KV splitting"):
+
+* Time unit: per-CTA time of one history KV tile with all K compute CTAs busy.
+  With k attention CTAs active the per-tile time is tau(k) = max(rho, k / K)
+  (Equation 5); every running attention task advances at rate 1 / tau(k), and k
+  is updated whenever an attention task starts or finishes.
+* An attention task t carries c_attn(t) = n_t + delta_attn tile-equivalents
+  (n_t KV tiles plus a fixed per-task overhead).
+* A history reduction u costs c_red(u) = delta_red + gamma * v_u * s_u
+  (Equation 6): v_u output vectors (query token-head pairs), s_u contributing
+  splits per vector.
+* Attention tasks are dispatched in queue order to the first available CTA. A
+  CTA releases its warps to reduction after its last attention task. Each
+  reduction uses one warp and starts in queue order when its warp and its
+  inputs are available. The score is the latest completion over attention and
+  reduction; lower is better.
+* Plan selection: start from NoSplit; each iteration evaluates +1 split on every
+  sequence below its limit, plus a joint +1 for sequences whose tasks tie at the
+  attention tail; accept the best candidate only if it improves the score; stop
+  otherwise. Return the best of NoSplit, the search result and the reference
+  plan; adopt a split plan only if it is at least 10% below NoSplit.
+* Task ordering: split decode-only plans use longest-processing-time-first by
+  c_attn; unsplit and mixed plans keep FIFO order, chunk tasks before history
+  tasks ("Task ordering"; section 5.1 "Execution model").
+* Appendix A.2 "Split planning": decode requests (at most 16 query tokens) with
+  at least K local history tiles get a split limit of at least four; score ties
+  favour earlier attention completion, then fewer attention tasks, then fewer
+  total splits; reduction runs of output vectors are the largest run in
+  {1, h_q, 2h_q, 4h_q, min(8h_q, 32)} that leaves at least 0.8 x (warps) tasks.
+
+Readings where the pages are silent (each listed in the design notes):
+
+* Reference plan: the pages use FA3's native heuristic, which they do not give.
+  It is replaced by a work-proportional plan s_b = clamp(floor(K n_b / W + 1/2),
+  1, min(n_b, max_splits)) with n_b the tile count of request b and W the total
+  tile-work of the batch; callers may inject an explicit reference plan instead.
+* A split of n tiles into s parts gives the first (n mod s) parts ceil(n/s)
+  tiles and the rest floor(n/s) (Figure 8 splits 176 tiles as 59, 59, 58).
+* One attention task per (request, KV head, query token, split); the pages fix
+  one query tile per decoding region and size the tile by the rows it holds.
+* Events at equal times: completions first (in CTA order), then dispatches to
+  the free CTAs in CTA-index order. Warps are claimed earliest-available first,
+  ties by CTA then warp index. Candidate ties after the pages' keys: the earlier
+  candidate (single increments in request order, then the joint increment).
+* overlap_reduction = 0 (a separate merge launch): every warp becomes free at
+  the last attention completion. overlap_reduction = 1: each CTA's warps become
+  free when it finishes its last attention task (the fused engine of the pages).
+"""
+from __future__ import annotations
+
+import heapq
+import math
+from dataclasses import dataclass, field
+
+
+@dataclass
+class Params:
+    tile_tokens: int = 64
+    slots: int = 256            # K: concurrent attention workers
+    warps_per_slot: int = 4     # warps each worker hands to reduction
+    rho: float = 0.43
+    delta_attn: float = 32.0
+    delta_red: float = 2.5
+    gamma: float = 0.47
+    max_splits: int = 64
+    min_gain: float = 0.10
+    overlap_reduction: int = 0
+
+
+@dataclass
+class Problem:
+    seq_lens: list
+    q_lens: list
+    num_kv_heads: int = 1       # attention tasks per query token and split
+    rows_per_token: int = 1     # output vectors per query token (query heads)
+    n_ext: int = 0              # external states merged into every row
+    causal: bool = True
+
+
+@dataclass
+class Task:
+    b: int
+    g: int
+    qi: int
+    r: int
+    lo: int       # first token of the split
+    hi: int       # end token of the split (exclusive)
+    n_t: int      # KV tiles of the split visible to this query token
+    c: float      # c_attn
+
+
+@dataclass
+class Evaluation:
+    splits: tuple
+    score: float
+    t_attn: float
+    n_tasks: int
+    total_splits: int
+    tail: list = field(default_factory=list)   # requests whose attention ends at t_attn
+
+    def key(self):
+        return (self.score, self.t_attn, self.n_tasks, self.total_splits)
+
+
+def n_tiles(L: int, T: int) -> int:
+    return (L + T - 1) // T
+
+
+def split_tiles(n: int, s: int):
+    """Tile ranges of n tiles in s parts: the first n mod s parts are one tile longer."""
+    q, rem = divmod(n, s)
+    out, start = [], 0
+    for r in range(s):
+        size = q + (1 if r < rem else 0)
+        out.append((start, start + size))
+        start += size
+    return out
+
+
+def split_ranges(L: int, s: int, T: int):
+    """Token ranges [lo, hi) of the s splits of a history of L tokens."""
+    return [(a * T, min(e * T, L)) for a, e in split_tiles(n_tiles(L, T), s)]
+
+
+def is_decode(n: int) -> bool:
+    return n <= 16
+
+
+def build_tasks(pb: Problem, prm: Params, splits):
+    """Attention tasks of a plan in queue order."""
+    T = prm.tile_tokens
+    B = len(pb.seq_lens)
+    fifo = []
+    for b in range(B):
+        L, n = pb.seq_lens[b], pb.q_lens[b]
+        rng = split_ranges(L, splits[b], T)
+        for qi in range(n):
+            vis = L - n + qi + 1 if pb.causal else L
+            vis_t = n_tiles(vis, T)
+            for g in range(pb.num_kv_heads):
+                for r, (lo, hi) in enumerate(rng):
+                    lo_t, hi_t = lo // T, n_tiles(hi, T)
+                    n_t = max(0, min(hi_t, vis_t) - lo_t)
+                    fifo.append(Task(b, g, qi, r, lo, hi, n_t, n_t + prm.delta_attn))
+    decode_only = all(is_decode(n) for n in pb.q_lens)
+    if decode_only and any(s > 1 for s in splits):
+        # stable: equal costs keep FIFO order
+        return sorted(fifo, key=lambda t: -t.c)
+    if not decode_only:
+        chunk = [t for t in fifo if not is_decode(pb.q_lens[t.b])]
+        hist = [t for t in fifo if is_decode(pb.q_lens[t.b])]
+        return chunk + hist
+    return fifo
+
+
+def reduction_run(pb: Problem, prm: Params) -> int:
+    """Rows per reduction unit: the largest run in {1, h, 2h, 4h, min(8h, 32)}
+    that leaves at least 0.8 x (K x warps) units (h = rows per query token)."""
+    h = pb.rows_per_token
+    warps = prm.slots * prm.warps_per_slot
+    best = 1
+    for run in (1, h, 2 * h, 4 * h, min(8 * h, 32)):
+        units = sum(math.ceil(n * h / run) for n in pb.q_lens)
+        if units >= 0.8 * warps and run > best:
+            best = run
+    return best
+
+
+def reduction_units(pb: Problem, prm: Params, splits):
+    """(request, c_red) of every reduction unit in queue order."""
+    run = reduction_run(pb, prm)
+    units = []
+    for b, n in enumerate(pb.q_lens):
+        rows = n * pb.rows_per_token
+        s_u = splits[b] + pb.n_ext
+        start = 0
+        while start < rows:
+            v = min(run, rows - start)
+            units.append((b, prm.delta_red + prm.gamma * v * s_u))
+            start += v
+    return units
+
+
+def simulate(pb: Problem, prm: Params, splits) -> Evaluation:
+    """Critical-wave simulation of one plan."""
+    tasks = build_tasks(pb, prm, splits)
+    K = prm.slots
+    B = len(pb.seq_lens)
+    t = 0.0          # model time
+    vw = 0.0         # work done so far by any running task (integral of 1/tau)
+    running = []     # heap of (finish work, slot, task index)
+    free = list(range(K))
+    heapq.heapify(free)
+    done = [0.0] * B
+    release = [0.0] * K
+    nxt = 0
+    while free and nxt < len(tasks):
+        s = heapq.heappop(free)
+        heapq.heappush(running, (vw + tasks[nxt].c, s, nxt))
+        nxt += 1
+    while running:
+        tau = max(prm.rho, len(running) / K)
+        fw = running[0][0]
+        t = t + (fw - vw) * tau
+        vw = fw
+        freed = []
+        while running and running[0][0] == fw:
+            _, s, i = heapq.heappop(running)
+            b = tasks[i].b
+            if t > done[b]:
+                done[b] = t
+            freed.append(s)
+        for s in freed:
+            heapq.heappush(free, s)
+        while free and nxt < len(tasks):
+            s = heapq.heappop(free)
+            heapq.heappush(running, (vw + tasks[nxt].c, s, nxt))
+            nxt += 1
+        for s in freed:
+            release[s] = t          # overwritten if the slot is dispatched again later
+    t_attn = t
+    # a slot dispatched again is not idle: its release is its later completion,
+    # which the loop above records when that task finishes.
+    if prm.overlap_reduction:
+        warps = [(release[s], s, w) for s in range(K) for w in range(prm.warps_per_slot)]
+    else:
+        warps = [(t_attn, s, w) for s in range(K) for w in range(prm.warps_per_slot)]
+    heapq.heapify(warps)
+    score = t_attn
+    for b, c in reduction_units(pb, prm, splits):
+        avail, s, w = heapq.heappop(warps)
+        start = avail if avail > done[b] else done[b]
+        end = start + c
+        heapq.heappush(warps, (end, s, w))
+        if end > score:
+            score = end
+    tail = [b for b in range(B) if done[b] == t_attn]
+    return Evaluation(tuple(splits), score, t_attn, len(tasks), sum(splits), tail)
+
+
+def reference_plan(pb: Problem, prm: Params):
+    """Work-proportional stand-in for the pages' FA3-derived reference plan."""
+    T = prm.tile_tokens
+    nt = [n_tiles(L, T) for L in pb.seq_lens]
+    work = sum(nt[b] * pb.q_lens[b] * pb.num_kv_heads for b in range(len(nt)))
+    out = []
+    for b in range(len(nt)):
+        x = math.floor(prm.slots * nt[b] / work + 0.5) if work > 0 else 1
+        out.append(max(1, min(x, nt[b], prm.max_splits)))
+    return out
+
+
+def split_limits(pb: Problem, prm: Params, ref):
+    """Per-request search limits: the reference counts, raised to at least four
+    for decode requests with at least K tiles, capped by tiles and max_splits."""
+    T = prm.tile_tokens
+    out = []
+    for b, L in enumerate(pb.seq_lens):
+        nt = n_tiles(L, T)
+        u = ref[b]
+        if is_decode(pb.q_lens[b]) and nt >= prm.slots:
+            u = max(u, 4)
+        out.append(max(1, min(u, nt, prm.max_splits)))
+    return out
+
+
+def plan(pb: Problem, prm: Params, ref=None, trace=None):
+    """Greedy critical-wave search; returns the chosen Evaluation.
+
+    ``trace`` (a list) receives the accepted evaluations in search order.
+    """
+    B = len(pb.seq_lens)
+    ref = list(reference_plan(pb, prm) if ref is None else ref)
+    lim = split_limits(pb, prm, ref)
+    nosplit = simulate(pb, prm, [1] * B)
+    cur = nosplit
+    if trace is not None:
+        trace.append(cur)
+    while True:
+        cands = []
+        for b in range(B):
+            if cur.splits[b] < lim[b]:
+                s = list(cur.splits)
+                s[b] += 1
+                cands.append(s)
+        tied = [b for b in cur.tail if cur.splits[b] < lim[b]]
+        if len(tied) >= 2:
+            s = list(cur.splits)
+            for b in tied:
+                s[b] += 1
+            cands.append(s)
+        if not cands:
+            break
+        best = None
+        for s in cands:
+            ev = simulate(pb, prm, s)
+            if best is None or ev.key() < best.key():
+                best = ev
+        if best.score < cur.score:
+            cur = best
+            if trace is not None:
+                trace.append(cur)
+        else:
+            break
+    chosen = nosplit
+    for ev in (cur, simulate(pb, prm, ref)):
+        if ev.key() < chosen.key():
+            chosen = ev
+    if chosen is not nosplit and not chosen.score <= (1.0 - prm.min_gain) * nosplit.score:
+        chosen = nosplit
+    return chosen
