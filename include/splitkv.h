@@ -1,0 +1,221 @@
+/*
+ * splitkv.h - split-KV partial decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * Decode-time attention over a paged KV cache is split along each request's KV
+ * history into tasks. Every task emits a partial attention state: the output
+ * normalised over its own KV subset plus the log-sum-exp (natural log) of its
+ * scores (LiquidCP, section 2.1 "Preliminaries"). An exact LSE-weighted merge
+ * composes the states into full attention (LiquidCP, section 3, Equation 1;
+ * the Helix deep dive, attention step 3: rescale each partial by
+ * exp(lse_r - lse_global) and sum). Split counts come from a critical-wave
+ * planner (LiquidCP, section 5.2 and appendix A.2).
+ *
+ * Conventions for every entry point
+ * ---------------------------------
+ * - All functions are extern "C", return an skv_status, and never throw. On a
+ *   non-OK status, skv_last_error() returns a thread-local message.
+ * - Arguments are validated on the host before anything is enqueued. Device work
+ *   is enqueued asynchronously on `stream` (a hipStream_t; NULL = null stream);
+ *   no entry point except skv_read_error_flag synchronises.
+ * - "host" pointers are CPU memory, "device" pointers are GPU global memory on
+ *   the current device. Every device buffer is owned by the caller; the library
+ *   allocates no device memory and keeps no device state between calls.
+ *
+ * Storage formats (all device, row-major, no padding)
+ * ---------------------------------------------------
+ * T = float (SKV_F32) or bf16 (SKV_BF16). X = 16 / sizeof(T) (4 or 8).
+ * q          [total_q][H_q][D]            T; requests concatenated in batch order,
+ *                                         request b owning q_lens[b] tokens.
+ * GQA keys   [num_pages][H_kv][D/X][P][X] T; 16-byte chunks of X dimensions,
+ *                                         tokens of a page adjacent per chunk.
+ * GQA values [num_pages][H_kv][D_v][P]    T; per page and head, dimension-major.
+ * MLA rows   [num_pages][P][D]            bf16, D = 576 (512 latent + 64 rope).
+ *                                         The value of a token is the first
+ *                                         D_v = 512 entries of its own row, so
+ *                                         v_pages must equal k_pages (SPLASH,
+ *                                         section 2: KV bytes per token
+ *                                         L(d_c + d_r)b; section 3: rows
+ *                                         [N_r, H, d_c + d_r], returned width d_c).
+ * page_table [batch][max_pages_per_seq]   int32; token j of request b is in page
+ *                                         page_table[b][j / P], slot j % P.
+ *                                         Entries past ceil(L_b / P) are never read
+ *                                         for addressing; slots past L_b in the last
+ *                                         page are never consumed.
+ * seq_lens   [batch]                      int32; L_b = KV tokens of request b,
+ *                                         including its own q_lens[b] new tokens.
+ * Query token i of request b with n_b tokens sees KV positions
+ * [0, L_b - n_b + i] when causal (bottom-right aligned), [0, L_b) otherwise.
+ * KV head of query head h is h / (H_q / H_kv).
+ *
+ * Partial states (plan-defined CSR layout). Request b has s_b splits and
+ * rows_b = q_lens[b] * H_q output rows (row = token * H_q + head). State r of
+ * request b occupies rows state_row_offset[b] + r * rows_b .. + rows_b - 1 of
+ *   o_part   [state_rows][D_v] float32   output normalised over the split's KV
+ *   lse_part [state_rows]      float32   natural-log LSE of the split's scores
+ * An empty split (no visible KV, possible for causal chunk rows) stores
+ * o = 0 and lse = -inf.
+ */
+#ifndef SPLITKV_H
+#define SPLITKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t skv_status;
+#define SKV_OK                 0
+#define SKV_ERR_INVALID_ARG   -1   /* null pointer, bad size, inconsistent shapes   */
+#define SKV_ERR_UNSUPPORTED   -2   /* valid but not implemented (dtype, head dims)  */
+#define SKV_ERR_HIP           -3   /* a HIP runtime call or kernel launch failed    */
+#define SKV_ERR_NO_MEMORY     -4   /* host allocation failed, or workspace too small */
+#define SKV_ERR_PLAN_MISMATCH -5   /* plan built for a different problem description */
+
+typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
+
+/* Problem description, passed by value in host memory. */
+typedef struct skv_attn_desc {
+  int32_t batch;              /* B >= 1                                          */
+  int32_t num_q_heads;        /* H_q                                             */
+  int32_t num_kv_heads;       /* H_kv, divides H_q; MLA: 1                       */
+  int32_t head_dim_qk;        /* D: GQA 64 or 128; MLA 576                       */
+  int32_t head_dim_v;         /* D_v: GQA == D; MLA 512                          */
+  int32_t page_size;          /* P: 16, 32 or 64                                 */
+  int32_t max_pages_per_seq;  /* row stride of page_table                        */
+  int32_t num_pages;          /* pages in the pool; ids outside [0, num_pages)
+                                 are not dereferenced and raise the device flag */
+  int32_t mla;                /* 1: MLA rows (v_pages == k_pages)                 */
+  int32_t causal;             /* 1: bottom-right causal rows when q_len > 1      */
+  int32_t dtype;              /* skv_dtype of q and the KV pages                 */
+  float softmax_scale;        /* scores are softmax_scale * <q, k>               */
+} skv_attn_desc;
+
+/* Critical-wave model parameters (LiquidCP, section 5.2, Equations 5-6; the
+ * pages' H100 calibration is in their Table 2). Model time unit: one KV tile
+ * of tile_tokens tokens with all K attention slots busy. */
+typedef struct skv_plan_params {
+  int32_t tile_tokens;        /* KV tile and split granularity; must be 64       */
+  int32_t slots_per_cu;       /* K = num_cu * slots_per_cu; 0 = kernel default   */
+  int32_t warps_per_slot;     /* merge waves per slot; 0 = kernel default        */
+  int32_t max_splits;         /* upper bound on splits per request (<= 64)       */
+  int32_t overlap_reduction;  /* 0: merge runs after attention (this library's
+                                 executor); 1: fused engine of the pages         */
+  int32_t reserved;
+  double rho;                 /* per-tile time floor                             */
+  double delta_attn;          /* per attention task overhead, tile-equivalents   */
+  double delta_red;           /* per reduction overhead                          */
+  double gamma;               /* cost per merged partial vector                  */
+  double min_gain;            /* adopt a split plan only if >= this much faster  */
+  double tile_time_us;        /* informational: microseconds per model unit      */
+} skv_plan_params;
+
+typedef struct skv_plan skv_plan;  /* opaque, immutable, host memory */
+
+typedef struct skv_plan_info {
+  int32_t batch;
+  int32_t num_tasks;          /* attention work-groups launched                 */
+  int32_t total_splits;       /* sum of s_b                                      */
+  int32_t slots;              /* K used by the model                             */
+  int32_t warps_per_slot;
+  int32_t reduction_run;      /* output rows per merge unit                      */
+  int32_t num_units;          /* merge units (one wave each)                     */
+  int32_t split_adopted;      /* 0: NoSplit kept                                 */
+  int64_t state_rows;         /* rows of o_part / lse_part                       */
+  int64_t total_rows;         /* rows of the merged output = total_q * H_q       */
+  double score;               /* model completion time of the chosen plan        */
+  double t_attn;              /* model attention completion of the chosen plan   */
+  double nosplit_score;       /* model completion time of NoSplit                */
+} skv_plan_info;
+
+/* Fill p with the library defaults (the pages' Table 2 values for rho,
+ * delta_attn, delta_red, gamma; tile 64; max_splits 64; min_gain 0.10). */
+void skv_plan_params_default(skv_plan_params* p);
+
+/* Critical-wave split plan (LiquidCP, section 5.2 "Plan selection" and
+ * "Task ordering"; appendix A.2 "Split planning").
+ * desc        host; the problem the plan will be used with.
+ * seq_lens    host int32 [batch]; q_lens host int32 [batch] or NULL (all 1).
+ * num_cu      compute units of the device (256 on MI355X).
+ * n_ext       external states that the merge will add to every row (model cost).
+ * params      host or NULL (defaults). ref_splits host int32 [batch] or NULL:
+ *             the reference plan compared against (NULL: work-proportional).
+ * out         receives a new plan; release it with skv_plan_destroy.
+ * Split boundaries are multiples of tile_tokens; the last split ends at L_b. */
+skv_status skv_plan_splits(const skv_attn_desc* desc, const int32_t* seq_lens,
+                           const int32_t* q_lens, int32_t num_cu, int32_t n_ext,
+                           const skv_plan_params* params, const int32_t* ref_splits,
+                           skv_plan** out);
+
+/* Plan with explicit split counts (host int32 [batch], 1 <= s_b <= tiles of b). */
+skv_status skv_plan_from_counts(const skv_attn_desc* desc, const int32_t* seq_lens,
+                                const int32_t* q_lens, const int32_t* split_counts,
+                                int32_t num_cu, int32_t n_ext,
+                                const skv_plan_params* params, skv_plan** out);
+
+/* Fixed-chunk plan: request b is split into ceil(L_b / chunk_tokens) pieces
+ * [k*c, min((k+1)*c, L_b)); chunk_tokens must be a positive multiple of 64. */
+skv_status skv_plan_fixed_chunks(const skv_attn_desc* desc, const int32_t* seq_lens,
+                                 const int32_t* q_lens, int32_t chunk_tokens,
+                                 int32_t num_cu, skv_plan** out);
+
+skv_status skv_plan_get_info(const skv_plan* plan, skv_plan_info* info);
+
+/* Copy the plan out (host buffers; any may be NULL):
+ * split_counts [batch]; split_start / split_end [total_splits] token ranges in
+ * request-then-split order; state_row_offset [batch + 1];
+ * task_order [num_tasks][4] = (request, kv_head, query token, split) in the
+ * launch order of the attention work-groups. */
+skv_status skv_plan_export(const skv_plan* plan, int32_t* split_counts, int32_t* split_start,
+                           int32_t* split_end, int64_t* state_row_offset,
+                           int32_t* task_order);
+
+/* Bytes of device workspace the plan's descriptors need (a multiple of 256). */
+size_t skv_plan_workspace_bytes(const skv_plan* plan);
+
+/* Copy the plan's descriptors into dev_workspace (device, >= workspace bytes)
+ * with an asynchronous host-to-device copy on stream, and clear the device
+ * error flag it holds. The plan must stay alive until that copy has executed. */
+skv_status skv_plan_upload(const skv_plan* plan, void* dev_workspace, size_t bytes,
+                           void* stream);
+
+void skv_plan_destroy(skv_plan* plan);
+
+/* Partial attention states for every split of the plan (A2-A6 of the method:
+ * page-gathered KV streaming, QK^T, online softmax, PV, local normalisation).
+ * q, k_pages, v_pages, page_table, seq_lens: device, formats above; seq_lens
+ * must hold the values the plan was built from. workspace: device, uploaded
+ * from `plan`. o_part / lse_part: device float32, plan state rows.
+ * Kernel choice: GQA with G = H_q/H_kv >= 16 (bf16) uses matrix cores; GQA
+ * with G < 16 (fp32 or bf16) uses vector ALUs; MLA uses matrix cores. */
+skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q,
+                                   const void* k_pages, const void* v_pages,
+                                   const int32_t* page_table, const int32_t* seq_lens,
+                                   const skv_plan* plan, const void* workspace,
+                                   float* o_part, float* lse_part, void* stream);
+
+/* Exact LSE merge of each row's states (LiquidCP Equation 1): the plan's local
+ * splits plus n_ext external states per row (device float32, o_ext
+ * [n_ext][total_rows][D_v], lse_ext [n_ext][total_rows]; NULL when n_ext = 0).
+ * o_out: device [total_rows][D_v] of out_dtype (float32, or bf16 rounded to
+ * nearest even); lse_out: device float32 [total_rows] or NULL.
+ * Rows whose states are all empty produce o = 0, lse = -inf. */
+skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan,
+                            const void* workspace, const float* o_part,
+                            const float* lse_part, int32_t n_ext, const float* o_ext,
+                            const float* lse_ext, void* o_out, int32_t out_dtype,
+                            float* lse_out, void* stream);
+
+/* Synchronise stream and read the workspace's device error flag:
+ * 0 = none; bit 0 = a page id outside [0, num_pages) was met (that page was
+ * not read and the affected state holds NaN). */
+skv_status skv_read_error_flag(const void* workspace, int32_t* flag, void* stream);
+
+/* Thread-local message for the last non-OK status of this thread. */
+const char* skv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPLITKV_H */

@@ -1,0 +1,321 @@
+"""Split-KV partial decode attention for AMD MI355X (gfx950).
+
+Python face of ``libsplitkv.so``: argument marshalling only. Planning runs in
+the library's C++ planner and every step of the attention and merge runs in its
+HIP kernels; torch supplies device memory and streams. Importing this module
+without the built library raises ``ImportError`` (build it with
+``python -m split_kv_partial_amd.build``).
+
+    spec = AttnSpec(num_q_heads=128, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+                    page_size=16, dtype=torch.bfloat16)
+    plan = plan_splits(seq_lens, spec, num_cu=256)
+    o_part, lse_part = decode_attn_partial(q, k_pages, v_pages, page_table, seq_lens_dev,
+                                           plan, scale)
+    o, lse = merge_states(o_part, lse_part, plan)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsplitkv.so")
+
+SKV_F32, SKV_BF16 = 0, 1
+STATUS = {0: "SKV_OK", -1: "SKV_ERR_INVALID_ARG", -2: "SKV_ERR_UNSUPPORTED", -3: "SKV_ERR_HIP",
+          -4: "SKV_ERR_NO_MEMORY", -5: "SKV_ERR_PLAN_MISMATCH"}
+
+# Every symbol the public header declares.
+EXPORTED = (
+    "skv_plan_params_default", "skv_plan_splits", "skv_plan_from_counts", "skv_plan_fixed_chunks",
+    "skv_plan_get_info", "skv_plan_export", "skv_plan_workspace_bytes", "skv_plan_upload",
+    "skv_plan_destroy", "skv_decode_attn_partial", "skv_merge_states", "skv_read_error_flag",
+    "skv_last_error",
+)
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim_qk", ctypes.c_int32),
+                ("head_dim_v", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("max_pages_per_seq", ctypes.c_int32), ("num_pages", ctypes.c_int32),
+                ("mla", ctypes.c_int32), ("causal", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class PlanParams(ctypes.Structure):
+    _fields_ = [("tile_tokens", ctypes.c_int32), ("slots_per_cu", ctypes.c_int32),
+                ("warps_per_slot", ctypes.c_int32), ("max_splits", ctypes.c_int32),
+                ("overlap_reduction", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("rho", ctypes.c_double), ("delta_attn", ctypes.c_double),
+                ("delta_red", ctypes.c_double), ("gamma", ctypes.c_double),
+                ("min_gain", ctypes.c_double), ("tile_time_us", ctypes.c_double)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_tasks", ctypes.c_int32),
+                ("total_splits", ctypes.c_int32), ("slots", ctypes.c_int32),
+                ("warps_per_slot", ctypes.c_int32), ("reduction_run", ctypes.c_int32),
+                ("num_units", ctypes.c_int32), ("split_adopted", ctypes.c_int32),
+                ("state_rows", ctypes.c_int64), ("total_rows", ctypes.c_int64),
+                ("score", ctypes.c_double), ("t_attn", ctypes.c_double),
+                ("nosplit_score", ctypes.c_double)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m split_kv_partial_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    pi64 = ctypes.POINTER(ctypes.c_int64)
+    pdesc = ctypes.POINTER(AttnDesc)
+    pprm = ctypes.POINTER(PlanParams)
+    pplan = ctypes.POINTER(ctypes.c_void_p)
+    sig = {
+        "skv_plan_params_default": (None, [pprm]),
+        "skv_plan_splits": (I32, [pdesc, pi32, pi32, I32, I32, pprm, pi32, pplan]),
+        "skv_plan_from_counts": (I32, [pdesc, pi32, pi32, pi32, I32, I32, pprm, pplan]),
+        "skv_plan_fixed_chunks": (I32, [pdesc, pi32, pi32, I32, I32, pplan]),
+        "skv_plan_get_info": (I32, [P, ctypes.POINTER(PlanInfo)]),
+        "skv_plan_export": (I32, [P, pi32, pi32, pi32, pi64, pi32]),
+        "skv_plan_workspace_bytes": (SZ, [P]),
+        "skv_plan_upload": (I32, [P, P, SZ, P]),
+        "skv_plan_destroy": (None, [P]),
+        "skv_decode_attn_partial": (I32, [pdesc, P, P, P, P, P, P, P, P, P, P]),
+        "skv_merge_states": (I32, [pdesc, P, P, P, P, I32, P, P, P, I32, P, P]),
+        "skv_read_error_flag": (I32, [P, pi32, P]),
+        "skv_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+
+
+class SplitKVError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _lib.skv_last_error().decode()
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {msg}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise SplitKVError(status, where)
+
+
+def _i32(a):
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream_ptr(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+@dataclass
+class AttnSpec:
+    """Shape of an attention layer (everything but the batch's lengths)."""
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim_qk: int
+    head_dim_v: int
+    page_size: int
+    dtype: torch.dtype = torch.bfloat16
+    mla: bool = False
+    causal: bool = True
+
+    def desc(self, batch: int, max_pages: int = 1, num_pages: int = 1, scale: float = 1.0) -> AttnDesc:
+        return AttnDesc(batch, self.num_q_heads, self.num_kv_heads, self.head_dim_qk, self.head_dim_v,
+                        self.page_size, max_pages, num_pages, int(self.mla), int(self.causal),
+                        SKV_BF16 if self.dtype == torch.bfloat16 else SKV_F32, float(scale))
+
+
+def default_params() -> PlanParams:
+    p = PlanParams()
+    _lib.skv_plan_params_default(ctypes.byref(p))
+    return p
+
+
+class Plan:
+    """Owns a host plan; uploads its descriptors to a device workspace on demand."""
+
+    def __init__(self, handle: ctypes.c_void_p, spec: AttnSpec, seq_lens, q_lens):
+        self._h = handle
+        self.spec = spec
+        self.seq_lens = np.asarray(seq_lens, np.int64).copy()
+        self.q_lens = np.asarray(q_lens, np.int64).copy()
+        self.max_pages = int(((self.seq_lens + spec.page_size - 1) // spec.page_size).max())
+        self._ws = {}
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h and _lib is not None:
+            for ws, ev in self._ws.values():
+                ev.synchronize()     # the upload reads host memory the plan owns
+            _lib.skv_plan_destroy(h)
+            self._h = None
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self) -> PlanInfo:
+        inf = PlanInfo()
+        _check(_lib.skv_plan_get_info(self._h, ctypes.byref(inf)), "skv_plan_get_info")
+        return inf
+
+    def export(self) -> dict:
+        inf = self.info()
+        B = inf.batch
+        counts = np.zeros(B, np.int32)
+        start = np.zeros(max(1, inf.total_splits), np.int32)
+        end = np.zeros(max(1, inf.total_splits), np.int32)
+        off = np.zeros(B + 1, np.int64)
+        order = np.zeros((max(1, inf.num_tasks), 4), np.int32)
+        p32 = lambda a: a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        _check(_lib.skv_plan_export(self._h, p32(counts), p32(start), p32(end),
+                                    off.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), p32(order)),
+               "skv_plan_export")
+        return {"split_counts": counts, "split_start": start[: inf.total_splits],
+                "split_end": end[: inf.total_splits], "state_row_offset": off,
+                "task_order": order[: inf.num_tasks]}
+
+    def ranges(self):
+        """Per request, the list of (start, end) token ranges of its splits."""
+        e = self.export()
+        out, k = [], 0
+        for c in e["split_counts"]:
+            out.append(list(zip(e["split_start"][k:k + c].tolist(), e["split_end"][k:k + c].tolist())))
+            k += c
+        return out
+
+    def workspace_bytes(self) -> int:
+        return int(_lib.skv_plan_workspace_bytes(self._h))
+
+    def workspace(self, device=None) -> torch.Tensor:
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        key = dev.index
+        if key not in self._ws:
+            n = self.workspace_bytes()
+            ws = torch.empty(n, dtype=torch.uint8, device=dev)
+            with torch.cuda.device(dev):
+                _check(_lib.skv_plan_upload(self._h, ws.data_ptr(), n, _stream_ptr()), "skv_plan_upload")
+                ev = torch.cuda.Event()
+                ev.record()
+            self._ws[key] = (ws, ev)
+        return self._ws[key][0]
+
+    def read_error_flag(self, device=None) -> int:
+        ws = self.workspace(device)
+        flag = ctypes.c_int32(0)
+        _check(_lib.skv_read_error_flag(ws.data_ptr(), ctypes.byref(flag), _stream_ptr()),
+               "skv_read_error_flag")
+        return flag.value
+
+
+def _make_plan(fn_name, spec, seq_lens, q_lens, *extra):
+    L, Lp = _i32(seq_lens)
+    B = L.shape[0]
+    if q_lens is None:
+        q_lens = np.ones(B, np.int32)
+    n, npp = _i32(q_lens)
+    max_pages = int(((L.astype(np.int64) + spec.page_size - 1) // spec.page_size).max())
+    desc = spec.desc(B, max_pages=max_pages, num_pages=1)
+    h = ctypes.c_void_p()
+    _check(getattr(_lib, fn_name)(ctypes.byref(desc), Lp, npp, *extra, ctypes.byref(h)), fn_name)
+    return Plan(h, spec, L, n)
+
+
+def plan_splits(seq_lens, spec: AttnSpec, num_cu: int = 256, q_lens=None, n_ext: int = 0,
+                params: PlanParams | None = None, ref_splits=None) -> Plan:
+    """Critical-wave split plan for a batch (host planner, once per batch)."""
+    ref = None
+    if ref_splits is not None:
+        ref_arr, ref = _i32(ref_splits)
+    return _make_plan("skv_plan_splits", spec, seq_lens, q_lens, int(num_cu), int(n_ext),
+                      None if params is None else ctypes.byref(params), ref)
+
+
+def plan_from_counts(seq_lens, spec: AttnSpec, split_counts, num_cu: int = 256, q_lens=None,
+                     n_ext: int = 0, params: PlanParams | None = None) -> Plan:
+    cnt, cp = _i32(split_counts)
+    return _make_plan("skv_plan_from_counts", spec, seq_lens, q_lens, cp, int(num_cu), int(n_ext),
+                      None if params is None else ctypes.byref(params))
+
+
+def plan_fixed_chunks(seq_lens, spec: AttnSpec, chunk_tokens: int, num_cu: int = 256,
+                      q_lens=None) -> Plan:
+    return _make_plan("skv_plan_fixed_chunks", spec, seq_lens, q_lens, int(chunk_tokens), int(num_cu))
+
+
+def _desc_for(plan: Plan, page_table: torch.Tensor, k_pages: torch.Tensor, scale: float) -> AttnDesc:
+    return plan.spec.desc(len(plan.seq_lens), max_pages=page_table.shape[1],
+                          num_pages=k_pages.shape[0], scale=scale)
+
+
+def decode_attn_partial(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, scale: float,
+                        o_part=None, lse_part=None):
+    """Partial states (O_r normalised over split r, natural-log LSE_r) for every
+    split of ``plan``. Returns (o_part [state_rows][D_v], lse_part [state_rows])."""
+    inf = plan.info()
+    dev = q.device
+    if o_part is None:
+        o_part = torch.empty(inf.state_rows, plan.spec.head_dim_v, dtype=torch.float32, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty(inf.state_rows, dtype=torch.float32, device=dev)
+    for t, name in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (page_table, "page_table"),
+                    (seq_lens, "seq_lens"), (o_part, "o_part"), (lse_part, "lse_part")):
+        if not t.is_contiguous() or t.device != dev:
+            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    if q.dtype != plan.spec.dtype or k_pages.dtype != plan.spec.dtype:
+        raise ValueError("q and the KV pages must have the plan's dtype")
+    if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("page_table and seq_lens must be int32")
+    desc = _desc_for(plan, page_table, k_pages, scale)
+    ws = plan.workspace(dev)
+    _check(_lib.skv_decode_attn_partial(ctypes.byref(desc), q.data_ptr(), k_pages.data_ptr(),
+                                        v_pages.data_ptr(), page_table.data_ptr(), seq_lens.data_ptr(),
+                                        plan.handle, ws.data_ptr(), o_part.data_ptr(),
+                                        lse_part.data_ptr(), _stream_ptr()),
+           "skv_decode_attn_partial")
+    return o_part, lse_part
+
+
+def merge_states(o_part, lse_part, plan: Plan, o_ext=None, lse_ext=None,
+                 out_dtype=torch.float32, o_out=None, lse_out=None, want_lse: bool = True):
+    """Exact LSE merge of each row's local splits plus optional external states
+    (o_ext [n_ext][total_rows][D_v], lse_ext [n_ext][total_rows], float32).
+    Returns (O [total_rows][D_v], LSE [total_rows] or None)."""
+    inf = plan.info()
+    dev = o_part.device
+    n_ext = 0 if o_ext is None else int(o_ext.shape[0])
+    if o_out is None:
+        o_out = torch.empty(inf.total_rows, plan.spec.head_dim_v, dtype=out_dtype, device=dev)
+    if want_lse and lse_out is None:
+        lse_out = torch.empty(inf.total_rows, dtype=torch.float32, device=dev)
+    for t in (o_part, lse_part, o_ext, lse_ext, o_out, lse_out):
+        if t is not None and (not t.is_contiguous() or t.device != dev):
+            raise ValueError("merge operands must be contiguous tensors on one device")
+    desc = plan.spec.desc(len(plan.seq_lens), max_pages=plan.max_pages, num_pages=1)
+    ws = plan.workspace(dev)
+    _check(_lib.skv_merge_states(ctypes.byref(desc), plan.handle, ws.data_ptr(), o_part.data_ptr(),
+                                 lse_part.data_ptr(), n_ext, _ptr(o_ext), _ptr(lse_ext),
+                                 o_out.data_ptr(), SKV_BF16 if o_out.dtype == torch.bfloat16 else SKV_F32,
+                                 _ptr(lse_out), _stream_ptr()),
+           "skv_merge_states")
+    return o_out, lse_out

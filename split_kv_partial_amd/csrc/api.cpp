@@ -1,0 +1,508 @@
+// C ABI of the split-KV partial attention library: argument validation, plan
+// construction (critical-wave planner, explicit and fixed-chunk plans),
+// workspace images, kernel dispatch and error reporting.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "internal.hpp"
+#include "kernels/device_common.hpp"
+
+using namespace skv;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+skv_status fail(skv_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+bool is_pow2_page(int p) { return p == 16 || p == 32 || p == 64; }
+
+Variant pick_variant(const skv_attn_desc& d) {
+  if (d.mla) return Variant::MlaMfma;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  if (d.dtype == SKV_BF16 && G >= 16) return Variant::GqaMfma;
+  return Variant::GqaValu;
+}
+
+// Shape checks shared by planning and compute entry points.
+skv_status check_desc(const skv_attn_desc* d) {
+  if (!d) return fail(SKV_ERR_INVALID_ARG, "desc is NULL");
+  if (d->batch < 1) return fail(SKV_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", d->batch);
+  if (d->num_q_heads < 1 || d->num_kv_heads < 1 || d->num_q_heads % d->num_kv_heads)
+    return fail(SKV_ERR_INVALID_ARG, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)",
+                d->num_q_heads, d->num_kv_heads);
+  if (!is_pow2_page(d->page_size))
+    return fail(SKV_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64 (got %d)", d->page_size);
+  if (d->max_pages_per_seq < 1) return fail(SKV_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
+  if (d->num_pages < 1) return fail(SKV_ERR_INVALID_ARG, "num_pages must be >= 1");
+  if (d->dtype != SKV_F32 && d->dtype != SKV_BF16)
+    return fail(SKV_ERR_INVALID_ARG, "dtype must be SKV_F32 or SKV_BF16 (got %d)", d->dtype);
+  if (!std::isfinite(d->softmax_scale)) return fail(SKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (d->causal != 0 && d->causal != 1) return fail(SKV_ERR_INVALID_ARG, "causal must be 0 or 1");
+  if (d->mla) {
+    if (d->mla != 1) return fail(SKV_ERR_INVALID_ARG, "mla must be 0 or 1");
+    if (d->num_kv_heads != 1 || d->head_dim_qk != 576 || d->head_dim_v != 512 || d->dtype != SKV_BF16)
+      return fail(SKV_ERR_UNSUPPORTED,
+                  "MLA needs bf16, num_kv_heads 1, head_dim_qk 576, head_dim_v 512");
+    if (d->num_q_heads % 16 || d->num_q_heads > 128)
+      return fail(SKV_ERR_UNSUPPORTED, "MLA needs num_q_heads a multiple of 16, at most 128 (got %d)",
+                  d->num_q_heads);
+    return SKV_OK;
+  }
+  if ((d->head_dim_qk != 64 && d->head_dim_qk != 128) || d->head_dim_v != d->head_dim_qk)
+    return fail(SKV_ERR_UNSUPPORTED, "GQA needs head_dim_qk = head_dim_v in {64, 128} (got %d, %d)",
+                d->head_dim_qk, d->head_dim_v);
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (pick_variant(*d) == Variant::GqaMfma) {
+    if (G != 16)
+      return fail(SKV_ERR_UNSUPPORTED, "bf16 GQA groups of 16 or more query heads must be exactly 16 (got %d)", G);
+  } else if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) {
+    return fail(SKV_ERR_UNSUPPORTED, "GQA group size must be 1, 2, 4, 8 or 16 (got %d)", G);
+  }
+  return SKV_OK;
+}
+
+skv_status check_lengths(const skv_attn_desc& d, const int32_t* seq_lens, const int32_t* q_lens) {
+  if (!seq_lens) return fail(SKV_ERR_INVALID_ARG, "seq_lens is NULL");
+  for (int b = 0; b < d.batch; ++b) {
+    const int64_t L = seq_lens[b], n = q_lens ? q_lens[b] : 1;
+    if (n < 1) return fail(SKV_ERR_INVALID_ARG, "q_lens[%d] = %lld must be >= 1", b, (long long)n);
+    if (L < n)
+      return fail(SKV_ERR_INVALID_ARG, "seq_lens[%d] = %lld is smaller than q_lens[%d] = %lld", b,
+                  (long long)L, b, (long long)n);
+    if ((L + d.page_size - 1) / d.page_size > d.max_pages_per_seq)
+      return fail(SKV_ERR_INVALID_ARG, "seq_lens[%d] = %lld needs more than max_pages_per_seq = %d pages",
+                  b, (long long)L, d.max_pages_per_seq);
+  }
+  return SKV_OK;
+}
+
+ModelParams model_params(const skv_attn_desc& d, int num_cu, const skv_plan_params* p) {
+  skv_plan_params def;
+  skv_plan_params_default(&def);
+  if (!p) p = &def;
+  const VariantShape vs = variant_shape(pick_variant(d));
+  ModelParams m;
+  m.tile_tokens = p->tile_tokens;
+  const int spc = p->slots_per_cu > 0 ? p->slots_per_cu : vs.slots_per_cu;
+  m.slots = num_cu * spc;
+  m.warps_per_slot = p->warps_per_slot > 0 ? p->warps_per_slot
+                                           : std::max(1, vs.merge_waves_per_cu / spc);
+  m.max_splits = p->max_splits;
+  m.overlap_reduction = p->overlap_reduction;
+  m.rho = p->rho;
+  m.delta_attn = p->delta_attn;
+  m.delta_red = p->delta_red;
+  m.gamma = p->gamma;
+  m.min_gain = p->min_gain;
+  m.tile_time_us = p->tile_time_us;
+  return m;
+}
+
+skv_status check_params(const skv_plan_params* p) {
+  if (!p) return SKV_OK;
+  if (p->tile_tokens != kTileTokens) return fail(SKV_ERR_UNSUPPORTED, "tile_tokens must be 64");
+  if (p->max_splits < 1 || p->max_splits > 64) return fail(SKV_ERR_INVALID_ARG, "max_splits must be in [1, 64]");
+  if (p->slots_per_cu < 0 || p->warps_per_slot < 0) return fail(SKV_ERR_INVALID_ARG, "negative slot counts");
+  if (!(p->rho > 0) || !(p->delta_attn >= 0) || !(p->delta_red >= 0) || !(p->gamma >= 0) ||
+      !(p->min_gain >= 0 && p->min_gain < 1))
+    return fail(SKV_ERR_INVALID_ARG, "model parameters out of range");
+  return SKV_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct skv_plan {
+  skv_attn_desc desc;
+  Problem pb;
+  ModelParams prm;
+  std::vector<std::vector<std::pair<int64_t, int64_t>>> ranges;
+  std::vector<int64_t> state_row_offset;  // [B + 1]
+  std::vector<TaskDesc> tasks;            // launch order
+  std::vector<DevReq> reqs;
+  std::vector<DevUnit> units;
+  int run = 1;
+  double score = NAN, t_attn = NAN, nosplit_score = NAN;
+  int split_adopted = 0;
+  std::vector<uint8_t> image;
+  int64_t tasks_off = 0, reqs_off = 0, units_off = 0;
+};
+
+namespace {
+
+// Fill tasks, request table, merge units and the workspace image of a plan
+// whose ranges are set.
+void finish_plan(skv_plan* pl) {
+  const skv_attn_desc& d = pl->desc;
+  const int B = d.batch;
+  const int H = d.num_q_heads, G = d.num_q_heads / d.num_kv_heads;
+  pl->state_row_offset.assign(B + 1, 0);
+  for (int b = 0; b < B; ++b)
+    pl->state_row_offset[b + 1] =
+        pl->state_row_offset[b] + (int64_t)pl->ranges[b].size() * pl->pb.q_lens[b] * H;
+  build_tasks(pl->pb, pl->prm, pl->ranges, pl->tasks, nullptr);
+  std::vector<int64_t> qoff(B + 1, 0);
+  for (int b = 0; b < B; ++b) qoff[b + 1] = qoff[b] + pl->pb.q_lens[b];
+  std::vector<DevTask> dev(pl->tasks.size());
+  for (size_t i = 0; i < pl->tasks.size(); ++i) {
+    TaskDesc& t = pl->tasks[i];
+    const int64_t L = pl->pb.seq_lens[t.b], n = pl->pb.q_lens[t.b];
+    const int64_t rows = n * H;
+    t.out_row = (int32_t)(pl->state_row_offset[t.b] + (int64_t)t.r * rows + (int64_t)t.qi * H +
+                          (int64_t)t.g * G);
+    const int64_t vis = pl->pb.causal ? L - n + t.qi + 1 : L;
+    DevTask& dt = dev[i];
+    dt.b = t.b;
+    dt.kvh = t.g;
+    dt.lo = t.lo;
+    dt.end = (int32_t)std::min<int64_t>(t.hi, vis);
+    dt.q_row = t.q_row;
+    dt.out_row = t.out_row;
+    dt.pad0 = dt.pad1 = 0;
+  }
+  pl->reqs.resize(B);
+  for (int b = 0; b < B; ++b) {
+    pl->reqs[b].state_row = (int32_t)pl->state_row_offset[b];
+    pl->reqs[b].splits = (int32_t)pl->ranges[b].size();
+    pl->reqs[b].rows = (int32_t)(pl->pb.q_lens[b] * H);
+    pl->reqs[b].out_row = (int32_t)(qoff[b] * H);
+  }
+  pl->run = reduction_run(pl->pb, pl->prm);
+  pl->units.clear();
+  for (int b = 0; b < B; ++b) {
+    const int rows = pl->reqs[b].rows;
+    for (int r = 0; r < rows; r += pl->run) pl->units.push_back({b, r, std::min(pl->run, rows - r), 0});
+  }
+  pl->tasks_off = sizeof(WsHeader);
+  pl->reqs_off = align256(pl->tasks_off + dev.size() * sizeof(DevTask));
+  pl->units_off = align256(pl->reqs_off + pl->reqs.size() * sizeof(DevReq));
+  const size_t total = align256(pl->units_off + pl->units.size() * sizeof(DevUnit));
+  pl->image.assign(total, 0);
+  WsHeader hdr;
+  std::memset(&hdr, 0, sizeof hdr);
+  hdr.num_tasks = (int32_t)dev.size();
+  hdr.batch = B;
+  hdr.num_units = (int32_t)pl->units.size();
+  hdr.tasks_off = pl->tasks_off;
+  hdr.reqs_off = pl->reqs_off;
+  hdr.units_off = pl->units_off;
+  std::memcpy(pl->image.data(), &hdr, sizeof hdr);
+  if (!dev.empty()) std::memcpy(pl->image.data() + pl->tasks_off, dev.data(), dev.size() * sizeof(DevTask));
+  std::memcpy(pl->image.data() + pl->reqs_off, pl->reqs.data(), pl->reqs.size() * sizeof(DevReq));
+  if (!pl->units.empty())
+    std::memcpy(pl->image.data() + pl->units_off, pl->units.data(), pl->units.size() * sizeof(DevUnit));
+}
+
+skv_status new_plan(const skv_attn_desc* desc, const int32_t* seq_lens, const int32_t* q_lens,
+                    int32_t num_cu, int32_t n_ext, const skv_plan_params* params, skv_plan** out,
+                    skv_plan** pl_out) {
+  if (!out) return fail(SKV_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  skv_status st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_lengths(*desc, seq_lens, q_lens))) return st;
+  if ((st = check_params(params))) return st;
+  if (num_cu < 1) return fail(SKV_ERR_INVALID_ARG, "num_cu must be >= 1");
+  if (n_ext < 0 || n_ext > 64) return fail(SKV_ERR_INVALID_ARG, "n_ext must be in [0, 64]");
+  skv_plan* pl = new (std::nothrow) skv_plan();
+  if (!pl) return fail(SKV_ERR_NO_MEMORY, "plan allocation failed");
+  pl->desc = *desc;
+  pl->pb.seq_lens.resize(desc->batch);
+  pl->pb.q_lens.resize(desc->batch);
+  int64_t total_q = 0;
+  for (int b = 0; b < desc->batch; ++b) {
+    pl->pb.seq_lens[b] = seq_lens[b];
+    pl->pb.q_lens[b] = q_lens ? q_lens[b] : 1;
+    total_q += pl->pb.q_lens[b];
+  }
+  if (total_q * desc->num_q_heads * 64 >= ((int64_t)1 << 31)) {
+    delete pl;
+    return fail(SKV_ERR_UNSUPPORTED, "too many output rows for 32-bit row indices");
+  }
+  pl->pb.num_kv_heads = desc->num_kv_heads;
+  pl->pb.rows_per_token = desc->num_q_heads;
+  pl->pb.n_ext = n_ext;
+  pl->pb.causal = desc->causal != 0;
+  pl->prm = model_params(*desc, num_cu, params);
+  *pl_out = pl;
+  return SKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void skv_plan_params_default(skv_plan_params* p) {
+  if (!p) return;
+  std::memset(p, 0, sizeof *p);
+  p->tile_tokens = kTileTokens;
+  p->slots_per_cu = 0;
+  p->warps_per_slot = 0;
+  p->max_splits = 64;
+  p->overlap_reduction = 0;
+  p->rho = 0.43;
+  p->delta_attn = 32.0;
+  p->delta_red = 2.5;
+  p->gamma = 0.47;
+  p->min_gain = 0.10;
+  p->tile_time_us = 1.08;
+}
+
+skv_status skv_plan_splits(const skv_attn_desc* desc, const int32_t* seq_lens, const int32_t* q_lens,
+                           int32_t num_cu, int32_t n_ext, const skv_plan_params* params,
+                           const int32_t* ref_splits, skv_plan** out) {
+  skv_plan* pl = nullptr;
+  skv_status st = new_plan(desc, seq_lens, q_lens, num_cu, n_ext, params, out, &pl);
+  if (st) return st;
+  try {
+    const int B = desc->batch;
+    std::vector<int> ref;
+    if (ref_splits) {
+      ref.assign(ref_splits, ref_splits + B);
+      for (int b = 0; b < B; ++b) {
+        const int64_t nt = n_tiles(pl->pb.seq_lens[b], pl->prm.tile_tokens);
+        if (ref[b] < 1 || ref[b] > nt || ref[b] > pl->prm.max_splits) {
+          delete pl;
+          return fail(SKV_ERR_INVALID_ARG, "ref_splits[%d] = %d outside [1, min(tiles, max_splits)]", b, ref[b]);
+        }
+      }
+    } else {
+      ref = reference_plan(pl->pb, pl->prm);
+    }
+    Evaluation ns;
+    Evaluation ev = plan_search(pl->pb, pl->prm, ref, &ns);
+    pl->score = ev.score;
+    pl->t_attn = ev.t_attn;
+    pl->nosplit_score = ns.score;
+    pl->split_adopted = 0;
+    for (int s : ev.splits) pl->split_adopted |= s > 1;
+    pl->ranges.resize(B);
+    for (int b = 0; b < B; ++b)
+      pl->ranges[b] = split_ranges(pl->pb.seq_lens[b], ev.splits[b], pl->prm.tile_tokens);
+    finish_plan(pl);
+  } catch (const std::bad_alloc&) {
+    delete pl;
+    return fail(SKV_ERR_NO_MEMORY, "host allocation failed while planning");
+  }
+  *out = pl;
+  return SKV_OK;
+}
+
+skv_status skv_plan_from_counts(const skv_attn_desc* desc, const int32_t* seq_lens, const int32_t* q_lens,
+                                const int32_t* split_counts, int32_t num_cu, int32_t n_ext,
+                                const skv_plan_params* params, skv_plan** out) {
+  if (!split_counts) return fail(SKV_ERR_INVALID_ARG, "split_counts is NULL");
+  skv_plan* pl = nullptr;
+  skv_status st = new_plan(desc, seq_lens, q_lens, num_cu, n_ext, params, out, &pl);
+  if (st) return st;
+  try {
+    const int B = desc->batch;
+    std::vector<int> s(split_counts, split_counts + B);
+    for (int b = 0; b < B; ++b) {
+      const int64_t nt = n_tiles(pl->pb.seq_lens[b], pl->prm.tile_tokens);
+      if (s[b] < 1 || s[b] > nt || s[b] > 64) {
+        delete pl;
+        return fail(SKV_ERR_INVALID_ARG, "split_counts[%d] = %d outside [1, min(tiles, 64)]", b, s[b]);
+      }
+    }
+    Evaluation ev = simulate(pl->pb, pl->prm, s);
+    pl->score = ev.score;
+    pl->t_attn = ev.t_attn;
+    pl->nosplit_score = simulate(pl->pb, pl->prm, std::vector<int>(B, 1)).score;
+    pl->ranges.resize(B);
+    for (int b = 0; b < B; ++b) {
+      pl->ranges[b] = split_ranges(pl->pb.seq_lens[b], s[b], pl->prm.tile_tokens);
+      pl->split_adopted |= s[b] > 1;
+    }
+    finish_plan(pl);
+  } catch (const std::bad_alloc&) {
+    delete pl;
+    return fail(SKV_ERR_NO_MEMORY, "host allocation failed while planning");
+  }
+  *out = pl;
+  return SKV_OK;
+}
+
+skv_status skv_plan_fixed_chunks(const skv_attn_desc* desc, const int32_t* seq_lens, const int32_t* q_lens,
+                                 int32_t chunk_tokens, int32_t num_cu, skv_plan** out) {
+  if (chunk_tokens < kTileTokens || chunk_tokens % kTileTokens)
+    return fail(SKV_ERR_INVALID_ARG, "chunk_tokens must be a positive multiple of 64 (got %d)", chunk_tokens);
+  skv_plan* pl = nullptr;
+  skv_status st = new_plan(desc, seq_lens, q_lens, num_cu, 0, nullptr, out, &pl);
+  if (st) return st;
+  try {
+    const int B = desc->batch;
+    pl->ranges.resize(B);
+    for (int b = 0; b < B; ++b) {
+      const int64_t L = pl->pb.seq_lens[b];
+      for (int64_t a = 0; a < L; a += chunk_tokens) pl->ranges[b].emplace_back(a, std::min<int64_t>(L, a + chunk_tokens));
+      if (pl->ranges[b].size() > 64) {
+        delete pl;
+        return fail(SKV_ERR_UNSUPPORTED, "request %d would have %zu chunks (at most 64)", b, pl->ranges[b].size());
+      }
+      pl->split_adopted |= pl->ranges[b].size() > 1;
+    }
+    finish_plan(pl);
+  } catch (const std::bad_alloc&) {
+    delete pl;
+    return fail(SKV_ERR_NO_MEMORY, "host allocation failed while planning");
+  }
+  *out = pl;
+  return SKV_OK;
+}
+
+skv_status skv_plan_get_info(const skv_plan* pl, skv_plan_info* info) {
+  if (!pl || !info) return fail(SKV_ERR_INVALID_ARG, "plan or info is NULL");
+  info->batch = pl->desc.batch;
+  info->num_tasks = (int32_t)pl->tasks.size();
+  int64_t ts = 0;
+  for (auto& r : pl->ranges) ts += (int64_t)r.size();
+  info->total_splits = (int32_t)ts;
+  info->slots = pl->prm.slots;
+  info->warps_per_slot = pl->prm.warps_per_slot;
+  info->reduction_run = pl->run;
+  info->num_units = (int32_t)pl->units.size();
+  info->split_adopted = pl->split_adopted;
+  info->state_rows = pl->state_row_offset.back();
+  int64_t tq = 0;
+  for (int64_t n : pl->pb.q_lens) tq += n;
+  info->total_rows = tq * pl->desc.num_q_heads;
+  info->score = pl->score;
+  info->t_attn = pl->t_attn;
+  info->nosplit_score = pl->nosplit_score;
+  return SKV_OK;
+}
+
+skv_status skv_plan_export(const skv_plan* pl, int32_t* split_counts, int32_t* split_start,
+                           int32_t* split_end, int64_t* state_row_offset, int32_t* task_order) {
+  if (!pl) return fail(SKV_ERR_INVALID_ARG, "plan is NULL");
+  const int B = pl->desc.batch;
+  int64_t k = 0;
+  for (int b = 0; b < B; ++b) {
+    if (split_counts) split_counts[b] = (int32_t)pl->ranges[b].size();
+    for (auto& r : pl->ranges[b]) {
+      if (split_start) split_start[k] = (int32_t)r.first;
+      if (split_end) split_end[k] = (int32_t)r.second;
+      ++k;
+    }
+  }
+  if (state_row_offset)
+    for (int b = 0; b <= B; ++b) state_row_offset[b] = pl->state_row_offset[b];
+  if (task_order)
+    for (size_t i = 0; i < pl->tasks.size(); ++i) {
+      task_order[4 * i + 0] = pl->tasks[i].b;
+      task_order[4 * i + 1] = pl->tasks[i].g;
+      task_order[4 * i + 2] = pl->tasks[i].qi;
+      task_order[4 * i + 3] = pl->tasks[i].r;
+    }
+  return SKV_OK;
+}
+
+size_t skv_plan_workspace_bytes(const skv_plan* pl) { return pl ? pl->image.size() : 0; }
+
+skv_status skv_plan_upload(const skv_plan* pl, void* ws, size_t bytes, void* stream) {
+  if (!pl || !ws) return fail(SKV_ERR_INVALID_ARG, "plan or workspace is NULL");
+  if (bytes < pl->image.size())
+    return fail(SKV_ERR_NO_MEMORY, "workspace has %zu bytes, the plan needs %zu", bytes, pl->image.size());
+  hipError_t e = hipMemcpyAsync(ws, pl->image.data(), pl->image.size(), hipMemcpyHostToDevice,
+                                (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SKV_ERR_HIP, "hipMemcpyAsync: %s", hipGetErrorString(e));
+  return SKV_OK;
+}
+
+void skv_plan_destroy(skv_plan* pl) { delete pl; }
+
+static skv_status check_plan_matches(const skv_attn_desc* d, const skv_plan* pl) {
+  if (!pl) return fail(SKV_ERR_INVALID_ARG, "plan is NULL");
+  const skv_attn_desc& p = pl->desc;
+  if (d->batch != p.batch || d->num_q_heads != p.num_q_heads || d->num_kv_heads != p.num_kv_heads ||
+      d->head_dim_qk != p.head_dim_qk || d->head_dim_v != p.head_dim_v || d->mla != p.mla ||
+      d->causal != p.causal || d->page_size != p.page_size || d->dtype != p.dtype)
+    return fail(SKV_ERR_PLAN_MISMATCH, "plan was built for a different problem description");
+  for (int b = 0; b < d->batch; ++b)
+    if ((pl->pb.seq_lens[b] + d->page_size - 1) / d->page_size > d->max_pages_per_seq)
+      return fail(SKV_ERR_PLAN_MISMATCH, "plan's seq_lens[%d] exceeds max_pages_per_seq", b);
+  return SKV_OK;
+}
+
+skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                                   const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
+                                   const skv_plan* plan, const void* workspace, float* o_part,
+                                   float* lse_part, void* stream) {
+  skv_status st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_plan_matches(desc, plan))) return st;
+  if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !workspace || !o_part || !lse_part)
+    return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
+  if (desc->mla && v_pages != k_pages)
+    return fail(SKV_ERR_INVALID_ARG, "MLA reads values from the key rows: v_pages must equal k_pages");
+  AttnLaunch a{desc, q, k_pages, v_pages, page_table, seq_lens, workspace, o_part, lse_part,
+               (int)plan->tasks.size(), plan->tasks_off, (hipStream_t)stream};
+  hipError_t e;
+  switch (pick_variant(*desc)) {
+    case Variant::GqaValu: e = launch_gqa_valu(a); break;
+    case Variant::GqaMfma: e = launch_gqa_mfma(a); break;
+    default: e = launch_mla_mfma(a); break;
+  }
+  if (e != hipSuccess) return fail(SKV_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
+  return SKV_OK;
+}
+
+skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan, const void* workspace,
+                            const float* o_part, const float* lse_part, int32_t n_ext, const float* o_ext,
+                            const float* lse_ext, void* o_out, int32_t out_dtype, float* lse_out,
+                            void* stream) {
+  skv_status st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_plan_matches(desc, plan))) return st;
+  if (!workspace || !o_part || !lse_part || !o_out)
+    return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
+  if (n_ext < 0 || n_ext > 64) return fail(SKV_ERR_INVALID_ARG, "n_ext must be in [0, 64]");
+  if (n_ext > 0 && (!o_ext || !lse_ext)) return fail(SKV_ERR_INVALID_ARG, "external states are NULL");
+  if (out_dtype != SKV_F32 && out_dtype != SKV_BF16) return fail(SKV_ERR_INVALID_ARG, "bad out_dtype");
+  int64_t tq = 0;
+  for (int64_t n : plan->pb.q_lens) tq += n;
+  MergeLaunch m{workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out, out_dtype == SKV_BF16, lse_out,
+                desc->head_dim_v, tq * desc->num_q_heads, (int)plan->units.size(), plan->reqs_off,
+                plan->units_off, (hipStream_t)stream};
+  hipError_t e = launch_merge(m);
+  if (e != hipSuccess) return fail(SKV_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return SKV_OK;
+}
+
+skv_status skv_read_error_flag(const void* workspace, int32_t* flag, void* stream) {
+  if (!workspace || !flag) return fail(SKV_ERR_INVALID_ARG, "workspace or flag is NULL");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e == hipSuccess) e = hipMemcpy(flag, workspace, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SKV_ERR_HIP, "reading the error flag: %s", hipGetErrorString(e));
+  return SKV_OK;
+}
+
+const char* skv_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"
+
+namespace skv {
+VariantShape variant_shape(Variant v) {
+  switch (v) {
+    case Variant::GqaValu: return {2, 16};
+    case Variant::GqaMfma: return {2, 16};
+    default: return {1, 16};
+  }
+}
+}  // namespace skv

@@ -1,0 +1,133 @@
+// Internal definitions shared by the host library and the kernel launchers.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include <hip/hip_runtime.h>
+
+#include "splitkv.h"
+
+namespace skv {
+
+constexpr int kTileTokens = 64;
+
+// One attention work-group's job: request b, KV head g, query token qi, split r,
+// KV token range [lo, hi) of the split. q_row = global query-token index;
+// out_row = state row of query head g*G of token qi in split r.
+struct TaskDesc {
+  int32_t b, g, qi, r;
+  int32_t lo, hi, q_row, out_row;
+};
+static_assert(sizeof(TaskDesc) == 32, "task descriptor is 32 bytes");
+
+// Per-request data the merge needs.
+struct ReqDesc {
+  int32_t state_row;   // first state row of the request
+  int32_t splits;      // s_b
+  int32_t rows;        // rows_b = q_lens[b] * H_q
+  int32_t out_row;     // first merged-output row of the request
+};
+
+// One merge unit: `count` consecutive rows of request b starting at row `row`.
+struct UnitDesc {
+  int32_t b, row, count, pad;
+};
+
+// Device workspace image: [header 256 B][tasks][reqs][units], each 256-aligned.
+struct WsHeader {
+  int32_t error_flag;
+  int32_t num_tasks, batch, num_units;
+  int64_t tasks_off, reqs_off, units_off;
+  int32_t pad[54];
+};
+static_assert(sizeof(WsHeader) == 256, "workspace header is 256 bytes");
+
+// Model parameters as used by the planner (mirrors skv_plan_params).
+struct ModelParams {
+  int tile_tokens = kTileTokens;
+  int slots = 256;
+  int warps_per_slot = 4;
+  int max_splits = 64;
+  int overlap_reduction = 0;
+  double rho = 0.43, delta_attn = 32.0, delta_red = 2.5, gamma = 0.47;
+  double min_gain = 0.10, tile_time_us = 1.08;
+};
+
+struct Problem {
+  std::vector<int64_t> seq_lens, q_lens;
+  int num_kv_heads = 1;
+  int rows_per_token = 1;
+  int n_ext = 0;
+  bool causal = true;
+};
+
+struct Evaluation {
+  std::vector<int> splits;
+  double score = 0, t_attn = 0;
+  int64_t n_tasks = 0, total_splits = 0;
+  std::vector<int> tail;
+};
+
+// Planner entry points (planner.cpp).
+int64_t n_tiles(int64_t L, int T);
+std::vector<std::pair<int64_t, int64_t>> split_ranges(int64_t L, int s, int T);
+void build_tasks(const Problem& pb, const ModelParams& prm,
+                 const std::vector<std::vector<std::pair<int64_t, int64_t>>>& ranges,
+                 std::vector<TaskDesc>& out, std::vector<double>* costs);
+int reduction_run(const Problem& pb, const ModelParams& prm);
+Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits);
+std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm);
+std::vector<int> split_limits(const Problem& pb, const ModelParams& prm,
+                              const std::vector<int>& ref);
+Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vector<int>& ref,
+                       Evaluation* nosplit_out);
+
+// Kernel launchers (one per kernel file). Return hipSuccess or the launch error.
+struct AttnLaunch {
+  const skv_attn_desc* desc;
+  const void* q;
+  const void* k_pages;
+  const void* v_pages;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const void* workspace;
+  float* o_part;
+  float* lse_part;
+  int num_tasks;
+  int64_t tasks_off;   // byte offset of the task descriptors in the workspace
+  hipStream_t stream;
+};
+hipError_t launch_gqa_valu(const AttnLaunch& a);
+hipError_t launch_gqa_mfma(const AttnLaunch& a);
+hipError_t launch_mla_mfma(const AttnLaunch& a);
+
+struct MergeLaunch {
+  const void* workspace;
+  const float* o_part;
+  const float* lse_part;
+  int n_ext;
+  const float* o_ext;
+  const float* lse_ext;
+  void* o_out;
+  int out_bf16;
+  float* lse_out;
+  int head_dim_v;
+  int64_t total_rows;
+  int num_units;
+  int64_t reqs_off, units_off;   // byte offsets in the workspace
+  hipStream_t stream;
+};
+hipError_t launch_merge(const MergeLaunch& m);
+
+// Default executor shape of each attention kernel (used by the planner).
+enum class Variant { GqaValu, GqaMfma, MlaMfma };
+struct VariantShape {
+  int slots_per_cu;    // concurrent attention work-groups per CU
+  int merge_waves_per_cu;
+};
+VariantShape variant_shape(Variant v);
+
+}  // namespace skv

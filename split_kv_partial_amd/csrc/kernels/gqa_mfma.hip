@@ -1,0 +1,298 @@
+// Paged split-KV partial attention for GQA groups of 16 query heads per KV
+// head (bf16 storage, fp32 accumulation) on the matrix cores.
+//
+// One work-group (4 waves) runs one task: the 16 query heads of one KV head for
+// one query token, over the KV range [lo, end) of one split. The waves take the
+// split's 32-token steps round-robin; each keeps its own online-softmax state,
+// and the four states are merged through LDS into the split's partial state
+// (output normalised over the split plus natural-log LSE; LiquidCP section 2.1
+// and Equation 1).
+//
+// Per 32-token step a wave issues two products with v_mfma_f32_16x16x32_bf16:
+//   S^T[16 tokens x 16 heads]  = K[16 x D] * Q^T[D x 16]     (two token blocks)
+//   O^T[16 dims  x 16 heads]  += V^T[16 x 32 tokens] * P^T[32 tokens x 16 heads]
+// Every lane owns one head (lane % 16) in both outputs, so the softmax rescale
+// needs no data movement, and the S^T output registers are exactly the P^T
+// operand of the second product once packed to bf16 (as a hi + lo pair of bf16
+// terms, two products per step). The storage layouts make
+// every operand a direct, coalesced load from HBM into registers: keys as
+// [D/8][P][8] per page (16 consecutive tokens of one 16-byte chunk are 256
+// contiguous bytes), values dimension-major [D][P] per page (a lane's 4 tokens
+// of one dimension are 8 contiguous bytes). No LDS is used until the final
+// merge of the four waves.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace skv {
+
+struct MfmaArgs {
+  const uint16_t* q;
+  const uint8_t* k;
+  const uint16_t* v;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const DevTask* tasks;
+  int32_t* err_flag;
+  float* o_part;
+  float* lse_part;
+  int32_t H_q, H_kv, page_shift, max_pages, num_pages;
+  float scale_log2;
+};
+
+namespace {
+
+constexpr int kG = 16;       // query heads per KV head
+constexpr int kWaves = 4;
+constexpr int kStep = 32;    // tokens per wave step (two 16-token MFMA blocks)
+
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int D>
+struct StepRegs {
+  u32x4_t k[2][D / 32];   // A operand of S^T for token blocks 0 and 1
+  u32x2_t v[2][D / 16];   // 4 tokens x 1 dimension per block, per 16-dim group
+};
+
+template <int D>
+struct Ctx {
+  const MfmaArgs* a;
+  const int32_t* ptab;
+  int64_t kvh;
+  int end;
+  int lane, g, r16;  // g = lane / 16 (k-group), r16 = lane % 16
+};
+
+// Issue the loads of the 32-token step starting at t0 (t0 < end).
+template <int D>
+__device__ __forceinline__ void load_step(const Ctx<D>& c, int t0, StepRegs<D>& s) {
+  const MfmaArgs& a = *c.a;
+  const int P = 1 << a.page_shift;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int tb = t0 + 16 * blk;
+    int pid = -1;
+    if (tb < c.end) {
+      pid = c.ptab[tb >> a.page_shift];
+      if (pid < 0 || pid >= a.num_pages) {
+        raise_error(a.err_flag, 1);
+        pid = -1;
+      }
+    }
+    if (pid >= 0) {
+      const int slot = tb & (P - 1);
+      const int64_t ph = (int64_t)pid * a.H_kv + c.kvh;   // page-head block
+      const uint8_t* kp = a.k + (ph * (D / 8) * P + slot + c.r16) * 16;
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m)
+        s.k[blk][m] = *reinterpret_cast<const u32x4_t*>(kp + (int64_t)(4 * m + c.g) * P * 16);
+      const uint16_t* vp = a.v + (ph * D + c.r16) * P + slot + 4 * c.g;
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb)
+        s.v[blk][nb] = *reinterpret_cast<const u32x2_t*>(vp + (int64_t)16 * nb * P);
+    } else {
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) s.k[blk][m] = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) s.v[blk][nb] = u32x2_t{0, 0};
+    }
+  }
+}
+
+template <int D>
+struct State {
+  float m, l;
+  f32x4_t o[D / 16];
+};
+
+template <int D>
+__device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D>& s,
+                                             const u32x4_t (&qf)[D / 32], State<D>& st,
+                                             float scale_log2) {
+  // scores S^T for both token blocks
+  f32x4_t sc[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) acc = mfma16(s.k[blk][m], qf[m], acc);
+    sc[blk] = acc;
+  }
+  // mask, scale to log2 units, row (= head) maximum over the 32 tokens
+  const bool tail = t0 + kStep > c.end;
+  float sv[8];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int tok = t0 + 16 * blk + 4 * c.g + e;
+      const float x = sc[blk][e] * scale_log2;
+      sv[4 * blk + e] = (!tail || tok < c.end) ? x : -INFINITY;
+    }
+  float mt = sv[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mn = fmaxf(st.m, mt);
+  const float alpha = fast_exp2(st.m - mn);
+  st.m = mn;
+  float p[8], ps = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = fast_exp2(sv[i] - mn);
+    ps += p[i];
+  }
+  st.l = st.l * alpha + ps;
+  // P^T operand as two bf16 terms (hi + lo): the second product costs matrix
+  // throughput that this HBM-bound kernel has to spare, and keeps ~16 bits of
+  // each weight instead of 8.
+  uint32_t hb[8], lb[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) split_bf16(p[i], hb[i], lb[i]);
+  const u32x4_t pf_hi = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
+                         hb[6] | (hb[7] << 16)};
+  const u32x4_t pf_lo = {lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
+                         lb[6] | (lb[7] << 16)};
+  // values past `end` (the split's end, or poisoned slots of the last page)
+  // are zeroed so that 0 * NaN cannot reach the accumulator
+  if (tail) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int tok = t0 + 16 * blk + 4 * c.g;
+      const int nv = c.end - tok;  // valid tokens among this lane's 4
+      if (nv < 4) {
+        const uint32_t m0 = nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0x0000FFFFu : 0u);
+        const uint32_t m1 = nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0x0000FFFFu : 0u);
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) {
+          s.v[blk][nb][0] &= m0;
+          s.v[blk][nb][1] &= m1;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) {
+    st.o[nb] *= alpha;
+    const u32x4_t vf = {s.v[0][nb][0], s.v[0][nb][1], s.v[1][nb][0], s.v[1][nb][1]};
+    st.o[nb] = mfma16(vf, pf_hi, st.o[nb]);
+    st.o[nb] = mfma16(vf, pf_lo, st.o[nb]);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void gqa_mfma_kernel(MfmaArgs a) {
+  __shared__ float m_lds[kWaves][kG], l_lds[kWaves][kG];
+  __shared__ float o_lds[kWaves][kG][D + 4];
+
+  const DevTask t = a.tasks[blockIdx.x];
+  Ctx<D> c;
+  c.a = &a;
+  c.lane = threadIdx.x & 63;
+  c.g = c.lane >> 4;
+  c.r16 = c.lane & 15;
+  c.kvh = t.kvh;
+  c.end = min(t.end, a.seq_lens[t.b]);
+  c.ptab = a.page_table + (int64_t)t.b * a.max_pages;
+  const int wave = threadIdx.x >> 6;
+
+  // Q^T operand: lane owns head r16; its k-slots of product m are dims 8(4m+g)..+7
+  u32x4_t qf[D / 32];
+  {
+    const uint16_t* qp = a.q + ((int64_t)t.q_row * a.H_q + (int64_t)t.kvh * kG + c.r16) * D;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m)
+      qf[m] = *reinterpret_cast<const u32x4_t*>(qp + 8 * (4 * m + c.g));
+  }
+
+  State<D> st;
+  st.m = -INFINITY;
+  st.l = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) st.o[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Two register sets alternate so that one step's loads are in flight while
+  // the previous step is computed.
+  constexpr int kStride = kWaves * kStep;
+  int t0 = t.lo + wave * kStep;
+  StepRegs<D> ra, rb;
+  if (t0 < c.end) load_step(c, t0, ra);
+  while (t0 < c.end) {
+    const int t1 = t0 + kStride;
+    if (t1 < c.end) load_step(c, t1, rb);
+    compute_step(c, t0, ra, qf, st, a.scale_log2);
+    if (t1 >= c.end) break;
+    const int t2 = t1 + kStride;
+    if (t2 < c.end) load_step(c, t2, ra);
+    compute_step(c, t1, rb, qf, st, a.scale_log2);
+    t0 = t2;
+  }
+
+  // Merge the four waves' states: sum l over the 4 lanes of each head first.
+  float l = st.l;
+  l += __shfl_xor(l, 16, 64);
+  l += __shfl_xor(l, 32, 64);
+  if (c.g == 0) {
+    m_lds[wave][c.r16] = st.m;
+    l_lds[wave][c.r16] = l;
+  }
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o_lds[wave][c.r16][16 * nb + 4 * c.g + e] = st.o[nb][e];
+  __syncthreads();
+  for (int i = threadIdx.x; i < kG * D; i += 256) {
+    const int h = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_lds[w][h]);
+    float Z = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = fast_exp2(m_lds[w][h] - M);
+        Z += sc * l_lds[w][h];
+        acc += sc * o_lds[w][h][d];
+      }
+    }
+    const int64_t row = (int64_t)t.out_row + h;
+    a.o_part[row * D + d] = M == -INFINITY ? 0.f : acc / Z;
+    if (d == 0) a.lse_part[row] = M == -INFINITY ? -INFINITY : (M + fast_log2(Z)) * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gqa_mfma(const AttnLaunch& L) {
+  const skv_attn_desc& d = *L.desc;
+  if (d.num_q_heads / d.num_kv_heads != kG || d.dtype != SKV_BF16) return hipErrorInvalidValue;
+  if (L.num_tasks == 0) return hipSuccess;
+  MfmaArgs a;
+  a.q = static_cast<const uint16_t*>(L.q);
+  a.k = static_cast<const uint8_t*>(L.k_pages);
+  a.v = static_cast<const uint16_t*>(L.v_pages);
+  a.page_table = L.page_table;
+  a.seq_lens = L.seq_lens;
+  a.tasks = reinterpret_cast<const DevTask*>(static_cast<const uint8_t*>(L.workspace) + L.tasks_off);
+  a.err_flag = reinterpret_cast<int32_t*>(const_cast<void*>(L.workspace));
+  a.o_part = L.o_part;
+  a.lse_part = L.lse_part;
+  a.H_q = d.num_q_heads;
+  a.H_kv = d.num_kv_heads;
+  a.page_shift = __builtin_ctz((unsigned)d.page_size);
+  a.max_pages = d.max_pages_per_seq;
+  a.num_pages = d.num_pages;
+  a.scale_log2 = d.softmax_scale * kLog2e;
+  if (d.head_dim_qk == 128)
+    hipLaunchKernelGGL(gqa_mfma_kernel<128>, dim3(L.num_tasks), dim3(256), 0, L.stream, a);
+  else if (d.head_dim_qk == 64)
+    hipLaunchKernelGGL(gqa_mfma_kernel<64>, dim3(L.num_tasks), dim3(256), 0, L.stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace skv

@@ -1,0 +1,303 @@
+// Paged split-KV partial attention for GQA groups of fewer than 16 query heads
+// per KV head, on the vector ALUs (fp32 or bf16 storage, fp32 accumulation).
+//
+// One work-group (4 waves) runs one task: KV head g of one query token over
+// the KV range [lo, end) of one split. The waves take the split's 64-token
+// tiles round-robin, each keeping its own online-softmax state; the four
+// states are merged through LDS at the end and written as the split's partial
+// state (output normalised over the split, natural-log LSE; LiquidCP section
+// 2.1 and Equation 1).
+//
+// Per tile, a wave computes scores with one lane per token (the key row of
+// that token is one coalesced read of its 16-byte chunks, query values are
+// LDS broadcasts), reduces the tile maximum across lanes, and then
+// accumulates P*V with one lane per value dimension (values are stored
+// dimension-major per page, so a lane reads its dimension's tokens as one
+// contiguous run). bf16 products use the packed dot2 instruction; the softmax
+// weights enter it as a two-term bf16 pair (hi + lo) so that P*V keeps ~16
+// significant bits of each weight.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace skv {
+
+struct ValuArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const DevTask* tasks;
+  int32_t* err_flag;
+  float* o_part;
+  float* lse_part;
+  int32_t H_q, H_kv, page_shift, max_pages, num_pages;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int X = 4;  // elements per 16-byte chunk
+};
+template <>
+struct Elem<uint16_t> {
+  static constexpr int X = 8;
+};
+
+constexpr int kWaves = 4;
+constexpr int kTile = 64;
+
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
+  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr int X = Elem<T>::X;
+  constexpr int NC = D / X;          // 16-byte chunks per key row
+  constexpr int DL = D / 64;         // value dimensions per lane
+  constexpr int QW = kBf16 ? D / 2 : D;  // 32-bit words per query row in LDS
+
+  __shared__ uint32_t q_lds[G * QW];
+  // Softmax weights of the current tile, private to each wave: fp32, or bf16
+  // (the bf16 path feeds them to dot2 in token pairs).
+  __shared__ float p_lds[kWaves][G][kBf16 ? 1 : kTile];
+  __shared__ uint16_t p16_lds[kWaves][2][G][kBf16 ? kTile : 2];   // [hi, lo]
+  __shared__ float m_lds[kWaves][G], l_lds[kWaves][G];
+  __shared__ float o_lds[kWaves][G][D];
+
+  const DevTask t = a.tasks[blockIdx.x];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int P = 1 << a.page_shift;
+  const int L = a.seq_lens[t.b];
+  const int end = min(t.end, L);  // never read past the request's own KV
+
+  // Query rows of the G heads of this KV head into LDS (fp32 or packed bf16).
+  {
+    const uint32_t* qsrc = reinterpret_cast<const uint32_t*>(
+        static_cast<const T*>(a.q) + ((int64_t)t.q_row * a.H_q + (int64_t)t.kvh * G) * D);
+    for (int i = threadIdx.x; i < G * QW; i += 256) q_lds[i] = qsrc[i];
+  }
+  __syncthreads();
+
+  const int32_t* ptab = a.page_table + (int64_t)t.b * a.max_pages;
+  float m[G], l[G], o[G][DL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int k = 0; k < DL; ++k) o[h][k] = 0.f;
+  }
+
+  for (int tok0 = t.lo + wave * kTile; tok0 < end; tok0 += kWaves * kTile) {
+    // ---------------- scores: one lane per token ----------------
+    const int j = tok0 + lane;
+    float s[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) s[h] = 0.f;
+    bool valid = j < end;
+    if (valid) {
+      const int pid = ptab[j >> a.page_shift];
+      if (pid < 0 || pid >= a.num_pages) {
+        raise_error(a.err_flag, 1);
+        valid = false;
+      } else {
+        const uint8_t* kp = static_cast<const uint8_t*>(a.k) +
+                            (((int64_t)pid * a.H_kv + t.kvh) * NC * P + (j & (P - 1))) * 16;
+        u32x4_t kr[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          kr[c] = *reinterpret_cast<const u32x4_t*>(kp + (int64_t)c * P * 16);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(&q_lds[h * QW + c * 4]);
+            if constexpr (kBf16) {
+              s[h] = dot2_bf16(qv[0], kr[c][0], s[h]);
+              s[h] = dot2_bf16(qv[1], kr[c][1], s[h]);
+              s[h] = dot2_bf16(qv[2], kr[c][2], s[h]);
+              s[h] = dot2_bf16(qv[3], kr[c][3], s[h]);
+            } else {
+              s[h] = fmaf(__uint_as_float(qv[0]), __uint_as_float(kr[c][0]), s[h]);
+              s[h] = fmaf(__uint_as_float(qv[1]), __uint_as_float(kr[c][1]), s[h]);
+              s[h] = fmaf(__uint_as_float(qv[2]), __uint_as_float(kr[c][2]), s[h]);
+              s[h] = fmaf(__uint_as_float(qv[3]), __uint_as_float(kr[c][3]), s[h]);
+            }
+          }
+        }
+      }
+    }
+    // ---------------- online softmax (log2 domain) ----------------
+    float alpha[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float sv = valid ? s[h] * a.scale_log2 : -INFINITY;
+      const float mt = wave_max(sv);
+      const float mn = fmaxf(m[h], mt);
+      alpha[h] = fast_exp2(m[h] - mn);  // m = -inf on the first tile gives 0
+      m[h] = mn;
+      const float p = fast_exp2(sv - mn);
+      l[h] = l[h] * alpha[h] + p;
+      if constexpr (kBf16) {
+        uint32_t hi, lo;
+        split_bf16(p, hi, lo);
+        p16_lds[wave][0][h][lane] = (uint16_t)hi;
+        p16_lds[wave][1][h][lane] = (uint16_t)lo;
+      } else
+        p_lds[wave][h][lane] = p;
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int k = 0; k < DL; ++k) o[h][k] *= alpha[h];
+    // The weights are private to this wave: a wavefront-scope fence orders the
+    // LDS writes above before the broadcast reads below.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---------------- P*V: one lane per value dimension ----------------
+#pragma unroll
+    for (int c16 = 0; c16 < kTile; c16 += 16) {
+      const int tok = tok0 + c16;
+      if (tok >= end) break;
+      const int pid = ptab[tok >> a.page_shift];
+      if (pid < 0 || pid >= a.num_pages) continue;  // flagged in the score pass
+      const int slot = tok & (P - 1);
+      const int nvalid = min(16, end - tok);
+#pragma unroll
+      for (int k = 0; k < DL; ++k) {
+        const int d = lane + 64 * k;
+        const T* vp = static_cast<const T*>(a.v) + (((int64_t)pid * a.H_kv + t.kvh) * D + d) * P + slot;
+        if constexpr (kBf16) {
+          u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(vp);
+          u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(vp + 8);
+          uint32_t vw[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+          if (nvalid < 16) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t lo_ok = (2 * e < nvalid) ? 0x0000FFFFu : 0u;
+              const uint32_t hi_ok = (2 * e + 1 < nvalid) ? 0xFFFF0000u : 0u;
+              vw[e] &= (lo_ok | hi_ok);
+            }
+          }
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float acc = o[h][k];
+            const uint32_t* ph = reinterpret_cast<const uint32_t*>(&p16_lds[wave][0][h][c16]);
+            const uint32_t* pl = reinterpret_cast<const uint32_t*>(&p16_lds[wave][1][h][c16]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              acc = dot2_bf16(ph[e], vw[e], acc);
+              acc = dot2_bf16(pl[e], vw[e], acc);
+            }
+            o[h][k] = acc;
+          }
+        } else {
+          float vv[16];
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(vp + 4 * e4);
+            vv[4 * e4 + 0] = x[0];
+            vv[4 * e4 + 1] = x[1];
+            vv[4 * e4 + 2] = x[2];
+            vv[4 * e4 + 3] = x[3];
+          }
+          if (nvalid < 16) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) vv[e] = e < nvalid ? vv[e] : 0.f;
+          }
+#pragma unroll
+          for (int h = 0; h < G; ++h) {
+            float acc = o[h][k];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc = fmaf(p_lds[wave][h][c16 + e], vv[e], acc);
+            o[h][k] = acc;
+          }
+        }
+      }
+    }
+  }
+
+  // ---------------- merge the four waves' states through LDS ----------------
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const float ls = wave_sum(l[h]);
+    if (lane == 0) {
+      m_lds[wave][h] = m[h];
+      l_lds[wave][h] = ls;
+    }
+#pragma unroll
+    for (int k = 0; k < DL; ++k) o_lds[wave][h][lane + 64 * k] = o[h][k];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * D; i += 256) {
+    const int h = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, m_lds[w][h]);
+    float Z = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = fast_exp2(m_lds[w][h] - M);
+        Z += sc * l_lds[w][h];
+        acc += sc * o_lds[w][h][d];
+      }
+    }
+    const int64_t row = (int64_t)t.out_row + h;
+    a.o_part[row * D + d] = M == -INFINITY ? 0.f : acc / Z;
+    if (d == 0) a.lse_part[row] = M == -INFINITY ? -INFINITY : (M + fast_log2(Z)) * kLn2;
+  }
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_t(const AttnLaunch& L, const ValuArgs& args) {
+  hipLaunchKernelGGL((gqa_valu_kernel<T, D, G>), dim3(L.num_tasks), dim3(256), 0, L.stream, args);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_g(const AttnLaunch& L, const ValuArgs& args, int G) {
+  switch (G) {
+    case 1: return launch_t<T, D, 1>(L, args);
+    case 2: return launch_t<T, D, 2>(L, args);
+    case 4: return launch_t<T, D, 4>(L, args);
+    case 8: return launch_t<T, D, 8>(L, args);
+    case 16: return launch_t<T, D, 16>(L, args);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gqa_valu(const AttnLaunch& L) {
+  const skv_attn_desc& d = *L.desc;
+  ValuArgs args;
+  args.q = L.q;
+  args.k = L.k_pages;
+  args.v = L.v_pages;
+  args.page_table = L.page_table;
+  args.seq_lens = L.seq_lens;
+  args.tasks = reinterpret_cast<const DevTask*>(static_cast<const uint8_t*>(L.workspace) + L.tasks_off);
+  args.err_flag = reinterpret_cast<int32_t*>(const_cast<void*>(L.workspace));
+  args.o_part = L.o_part;
+  args.lse_part = L.lse_part;
+  args.H_q = d.num_q_heads;
+  args.H_kv = d.num_kv_heads;
+  args.page_shift = __builtin_ctz((unsigned)d.page_size);
+  args.max_pages = d.max_pages_per_seq;
+  args.num_pages = d.num_pages;
+  args.scale_log2 = d.softmax_scale * kLog2e;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  if (L.num_tasks == 0) return hipSuccess;
+  if (d.dtype == SKV_BF16) {
+    if (d.head_dim_qk == 64) return launch_g<uint16_t, 64>(L, args, G);
+    if (d.head_dim_qk == 128) return launch_g<uint16_t, 128>(L, args, G);
+  } else {
+    if (d.head_dim_qk == 64) return launch_g<float, 64>(L, args, G);
+    if (d.head_dim_qk == 128) return launch_g<float, 128>(L, args, G);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace skv

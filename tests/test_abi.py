@@ -1,0 +1,150 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+public header declares, and rejects bad arguments with the documented status
+codes before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import split_kv_partial_amd as skv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "splitkv.h")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(skv_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert len(names) >= 13
+    lib = ctypes.CDLL(skv.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(skv.EXPORTED) == names
+
+
+def test_defaults_are_the_papers_table2():
+    p = skv.default_params()
+    assert (p.rho, p.delta_attn, p.delta_red, p.gamma) == (0.43, 32.0, 2.5, 0.47)
+    assert p.tile_tokens == 64 and p.max_splits == 64 and abs(p.min_gain - 0.10) < 1e-15
+
+
+SPEC = skv.AttnSpec(num_q_heads=8, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16)
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def _plan_call(desc, seq, q=None, num_cu=4, n_ext=0, params=None, ref=None):
+    L, Lp = skv._i32(seq)
+    qp = None
+    if q is not None:
+        qa, qp = skv._i32(q)
+    h = ctypes.c_void_p()
+    refp = None
+    if ref is not None:
+        ra, refp = skv._i32(ref)
+    st = skv._lib.skv_plan_splits(None if desc is None else ctypes.byref(desc), Lp, qp, num_cu, n_ext,
+                                  None if params is None else ctypes.byref(params), refp, ctypes.byref(h))
+    if st == 0:
+        skv._lib.skv_plan_destroy(h)
+    return st
+
+
+def test_plan_argument_errors():
+    d = SPEC.desc(2, max_pages=8, num_pages=16)
+    assert _plan_call(d, [100, 50]) == 0
+    assert _plan_call(None, [100, 50]) == -1
+    bad = SPEC.desc(2, max_pages=8, num_pages=16)
+    bad.page_size = 8
+    assert _plan_call(bad, [100, 50]) == -2
+    assert "page_size" in skv._lib.skv_last_error().decode()
+    bad = SPEC.desc(2, max_pages=8, num_pages=16)
+    bad.num_q_heads = 7
+    assert _plan_call(bad, [100, 50]) == -1
+    bad = SPEC.desc(2, max_pages=8, num_pages=16)
+    bad.head_dim_qk = bad.head_dim_v = 96
+    assert _plan_call(bad, [100, 50]) == -2
+    assert _plan_call(d, [100, 200]) == -1                       # needs 13 pages > 8
+    assert _plan_call(d, [3, 50], q=[4, 1]) == -1                # L < q_len
+    assert _plan_call(d, [100, 50], num_cu=0) == -1
+    assert _plan_call(d, [100, 50], ref=[2, 1]) == 0
+    assert _plan_call(d, [100, 50], ref=[3, 1]) == -1            # more splits than tiles
+    p = skv.default_params()
+    p.tile_tokens = 32
+    assert _plan_call(d, [100, 50], params=p) == -2
+    p = skv.default_params()
+    p.max_splits = 65
+    assert _plan_call(d, [100, 50], params=p) == -1
+
+
+def test_unsupported_shapes():
+    mla = skv.AttnSpec(num_q_heads=128, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
+                       mla=True)
+    assert _plan_call(mla.desc(1, max_pages=4, num_pages=4), [200]) == 0
+    d = mla.desc(1, max_pages=4, num_pages=4)
+    d.dtype = skv.SKV_F32
+    assert _plan_call(d, [200]) == -2
+    d = mla.desc(1, max_pages=4, num_pages=4)
+    d.num_q_heads = 100
+    assert _plan_call(d, [200]) == -2
+    g32 = skv.AttnSpec(num_q_heads=64, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16)
+    assert _plan_call(g32.desc(1, max_pages=4, num_pages=4), [60]) == -2
+
+
+def test_compute_calls_validate_before_launch():
+    # Only invalid calls here: each must fail in host validation, never reach a launch.
+    plan = skv.plan_splits([100, 50], SPEC, num_cu=4)
+    d = SPEC.desc(2, max_pages=8, num_pages=16, scale=0.1)
+    fake = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    st = skv._lib.skv_decode_attn_partial(ctypes.byref(d), None, fake, fake, fake, fake, plan.handle,
+                                          fake, fake, fake, None)
+    assert st == -1
+    d2 = SPEC.desc(3, max_pages=8, num_pages=16)
+    st = skv._lib.skv_decode_attn_partial(ctypes.byref(d2), fake, fake, fake, fake, fake, plan.handle,
+                                          fake, fake, fake, None)
+    assert st == -5
+    d3 = SPEC.desc(2, max_pages=2, num_pages=16)             # plan needs 7 pages for L = 100
+    st = skv._lib.skv_decode_attn_partial(ctypes.byref(d3), fake, fake, fake, fake, fake, plan.handle,
+                                          fake, fake, fake, None)
+    assert st == -5
+    st = skv._lib.skv_merge_states(ctypes.byref(d), plan.handle, fake, fake, fake, 2, None, None, fake, 0,
+                                   None, None)
+    assert st == -1                                          # external states missing
+    st = skv._lib.skv_merge_states(ctypes.byref(d), plan.handle, fake, fake, fake, 0, None, None, fake, 7,
+                                   None, None)
+    assert st == -1                                          # bad output dtype
+    mla = skv.AttnSpec(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
+                       mla=True)
+    mp = skv.plan_splits([100], mla, num_cu=4)
+    dm = mla.desc(1, max_pages=4, num_pages=4)
+    st = skv._lib.skv_decode_attn_partial(ctypes.byref(dm), fake, fake, ctypes.c_void_p(512), fake, fake,
+                                          mp.handle, fake, fake, fake, None)
+    assert st == -1 and "v_pages" in skv._lib.skv_last_error().decode()
+
+
+def test_upload_rejects_small_workspace():
+    plan = skv.plan_splits([100, 50], SPEC, num_cu=4)
+    n = plan.workspace_bytes()
+    assert n % 256 == 0 and n >= 256
+    st = skv._lib.skv_plan_upload(plan.handle, ctypes.c_void_p(256), n - 1, None)
+    assert st == -4
+
+
+def test_plan_export_shapes():
+    plan = skv.plan_fixed_chunks([100, 257], skv.AttnSpec(4, 1, 64, 64, 16, dtype=torch.float32), 64)
+    e = plan.export()
+    assert e["split_counts"].tolist() == [2, 5]
+    assert list(zip(e["split_start"], e["split_end"])) == [(0, 64), (64, 100), (0, 64), (64, 128),
+                                                            (128, 192), (192, 256), (256, 257)]
+    inf = plan.info()
+    assert inf.total_splits == 7 and inf.state_rows == 7 * 4 and inf.total_rows == 8
+    assert e["state_row_offset"].tolist() == [0, 8, 28]
+    assert inf.num_tasks == 7

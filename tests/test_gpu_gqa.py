@@ -1,0 +1,155 @@
+"""GPU parity of the GQA paths and of the merge against the float64 oracle:
+the vector-ALU kernel (groups below 16 query heads per KV head, fp32 and bf16)
+and the matrix-core kernel (bf16 groups of 16)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import split_kv_partial_amd as skv
+import workloads as wl
+from gpu_common import DeviceInputs, check_all, compare, run_path, spec_of, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def small(dtype, H_q, H_kv, D, P, seq, q_lens=None, seed=5, q_scale=1.0, causal=True, n_ext=0):
+    return wl.build(f"small-{dtype}-{H_q}x{H_kv}-d{D}-p{P}", dtype=dtype, mla=False, seq_lens=seq,
+                    q_lens=q_lens, num_q_heads=H_q, num_kv_heads=H_kv, head_dim_qk=D, head_dim_v=D,
+                    page_size=P, scale=1.0 / math.sqrt(D), seed=seed, q_scale=q_scale, causal=causal,
+                    n_ext=n_ext, ext_lse_center=4.0)
+
+
+@pytest.mark.parametrize("sharp", [False, True])
+def test_tiny_fp32_fixed_chunks(sharp):
+    # batch 2, 4 q heads / 1 KV head, D 64, L = 100 and 257, page 16 permuted,
+    # explicit 64-token chunks: 2 + 5 = 7 partial states, then the merge.
+    w = wl.make(1, sharp=sharp)
+    plan = skv.plan_fixed_chunks(w.seq_lens, spec_of(w), 64)
+    assert plan.info().total_splits == 7
+    check_all(w, plan)
+
+
+def test_tiny_fp32_planner_and_explicit_plans():
+    w = wl.make(1)
+    d = DeviceInputs(w)
+    check_all(w, skv.plan_splits(w.seq_lens, spec_of(w), 256), d)
+    for counts in ([1, 1], [2, 5], [2, 3], [1, 4]):
+        check_all(w, skv.plan_from_counts(w.seq_lens, spec_of(w), counts), d)
+
+
+RAGGED = [1, 15, 16, 17, 63, 64, 65, 127, 129, 1000, 2049]
+
+
+@pytest.mark.parametrize("G,D,P", [(1, 64, 16), (2, 128, 32), (4, 64, 64), (8, 128, 16), (16, 64, 16)])
+def test_fp32_group_sizes(G, D, P):
+    w = small("f32", 2 * G, 2, D, P, RAGGED, seed=G + D + P, q_scale=2.0)
+    rng = np.random.default_rng(G)
+    counts = [int(rng.integers(1, (L + 63) // 64 + 1)) for L in RAGGED]
+    check_all(w, skv.plan_from_counts(w.seq_lens, spec_of(w), counts))
+
+
+@pytest.mark.parametrize("H_q,H_kv,D,P", [(64, 8, 128, 16), (8, 1, 64, 32), (16, 16, 128, 64),
+                                          (16, 4, 128, 16), (8, 4, 64, 64),
+                                          # matrix-core kernel (16 query heads per KV head)
+                                          (128, 8, 128, 16), (16, 1, 128, 32), (32, 2, 128, 64),
+                                          (16, 1, 64, 16), (64, 4, 64, 64)])
+def test_bf16_shapes(H_q, H_kv, D, P):
+    w = small("bf16", H_q, H_kv, D, P, RAGGED, seed=H_q + P, q_scale=3.0)
+    rng = np.random.default_rng(H_q)
+    counts = [int(rng.integers(1, (L + 63) // 64 + 1)) for L in RAGGED]
+    check_all(w, skv.plan_from_counts(w.seq_lens, spec_of(w), counts))
+    check_all(w, skv.plan_splits(w.seq_lens, spec_of(w), 256))
+
+
+@pytest.mark.parametrize("dtype,G", [("f32", 4), ("bf16", 4), ("bf16", 16)])
+def test_causal_chunk_rows(dtype, G):
+    # chunked-prefill rows: query token i of n sees L - n + i + 1 tokens
+    seq, q = [300, 70, 65, 900], [40, 1, 65, 17]
+    w = small(dtype, 2 * G, 2, 64, 16, seq, q_lens=q, seed=11, q_scale=2.0)
+    check_all(w, skv.plan_from_counts(w.seq_lens, spec_of(w), [5, 1, 2, 3], q_lens=q))
+    check_all(w, skv.plan_splits(w.seq_lens, spec_of(w), 256, q_lens=q), check_partials=False)
+
+
+@pytest.mark.parametrize("dtype,G", [("f32", 8), ("bf16", 8), ("bf16", 16)])
+def test_permuted_equals_identity_bitwise(dtype, G):
+    w = small(dtype, 2 * G, 2, 128, 16, RAGGED, seed=3)
+    wi = wl.identity_layout(w)
+    plan = skv.plan_from_counts(w.seq_lens, spec_of(w), [1, 1, 1, 1, 1, 1, 2, 2, 3, 7, 9])
+    a = run_path(w, plan)
+    b = run_path(wi, plan)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint64), y.view(np.uint64))
+
+
+def _probe_thresholds(ranges, L, Dv):
+    xs = set()
+    for a, e in ranges:
+        for x in (a - 1, a, a + 1, e - 1, e, e + 1):
+            if 0 <= x <= L:
+                xs.add(x)
+    xs = sorted(xs)[:Dv]
+    return xs + [L] * (Dv - len(xs))
+
+
+@pytest.mark.parametrize("dtype,G,P", [("f32", 4, 16), ("bf16", 4, 32), ("bf16", 16, 16),
+                                       ("bf16", 16, 64)])
+def test_coverage_probe_recovers_split_ranges(dtype, G, P):
+    # q = 0 makes every weight exactly 1: LSE_r = ln(count_r) and, with
+    # V[j, d] = 1 if j >= x_d else 0, count_r * O_r[d] = |S_r intersect [x_d, L)|.
+    seq = [1000, 2049, 65, 129, 4000]
+    w = small(dtype, 2 * G, 2, 64, P, seq, seed=9)
+    w.q[...] = 0
+    plan = skv.plan_from_counts(w.seq_lens, spec_of(w), [3, 7, 2, 1, 13])
+    ranges = plan.ranges()
+    for b, L in enumerate(seq):
+        xs = _probe_thresholds(ranges[b], L, w.head_dim_v)
+        j = np.arange(L)[:, None]
+        vals = (j >= np.array(xs)[None, :]).astype(np.float32)
+        vals = np.broadcast_to(vals[:, None, :], (L, w.num_kv_heads, w.head_dim_v))
+        if dtype == "bf16":
+            vals = wl.f32_to_bf16_bits(np.ascontiguousarray(vals))
+        wl.set_logical_values(w, b, vals)
+    o_part, lse_part, o, lse = run_path(w, plan)
+    e = plan.export()
+    H = w.num_q_heads
+    for b, L in enumerate(seq):
+        xs = np.array(_probe_thresholds(ranges[b], L, w.head_dim_v))
+        off = int(e["state_row_offset"][b])
+        for r, (a, en) in enumerate(ranges[b]):
+            rows = slice(off + r * H, off + (r + 1) * H)
+            count = en - a
+            assert np.all(np.rint(np.exp(lse_part[rows])) == count)
+            want = np.maximum(0, en - np.maximum(a, xs))
+            got = np.rint(count * o_part[rows])
+            assert np.array_equal(got, np.broadcast_to(want, got.shape)), (b, r)
+
+
+def test_merge_external_states():
+    w = small("f32", 8, 2, 64, 16, [300, 1000, 17], seed=4, n_ext=5)
+    check_all(w, skv.plan_from_counts(w.seq_lens, spec_of(w), [2, 4, 1], n_ext=5))
+    wb = small("bf16", 16, 2, 128, 32, [300, 1000, 17], seed=4, n_ext=3)
+    check_all(wb, skv.plan_splits(wb.seq_lens, spec_of(wb), 256, n_ext=3))
+
+
+def test_bf16_output_rounding():
+    w = small("bf16", 16, 2, 128, 16, [500, 77], seed=8)
+    plan = skv.plan_from_counts(w.seq_lens, spec_of(w), [3, 2])
+    d = DeviceInputs(w)
+    o32 = run_path(w, plan, d)[2]
+    o16 = run_path(w, plan, d, out_dtype=torch.bfloat16)[2]
+    want = wl.f32_to_bf16_bits(o32.astype(np.float32))
+    got = wl.f32_to_bf16_bits(o16.astype(np.float32))
+    assert np.array_equal(want, got)
+
+
+@pytest.mark.parametrize("G", [8, 16])
+def test_outputs_deterministic(G):
+    w = small("bf16", 8 * G, 8, 128, 16, RAGGED, seed=21)
+    plan = skv.plan_splits(w.seq_lens, spec_of(w), 256)
+    d = DeviceInputs(w)
+    a, b = run_path(w, plan, d), run_path(w, plan, d)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint64), y.view(np.uint64))
+    assert plan.read_error_flag() == 0

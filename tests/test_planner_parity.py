@@ -1,0 +1,118 @@
+"""The library's C++ planner against the reference planner, bit for bit (CPU).
+
+Split counts, split token ranges, the launch order of the attention tasks and
+the model scores (as IEEE doubles) must be identical. The LiquidCP Figure 8
+example (section 5.2) is also checked through the C ABI.
+"""
+import json
+import os
+import struct
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import split_kv_partial_amd as skv
+import workloads as wl
+from oracle import planner as PL
+
+
+def bits(x: float) -> int:
+    return struct.unpack("<Q", struct.pack("<d", x))[0]
+
+
+def reference_for(plan: skv.Plan, spec: skv.AttnSpec, seq, qlen, n_ext=0, params=None, ref=None):
+    inf = plan.info()
+    p = params or skv.default_params()
+    prm = PL.Params(tile_tokens=64, slots=inf.slots, warps_per_slot=inf.warps_per_slot, rho=p.rho,
+                    delta_attn=p.delta_attn, delta_red=p.delta_red, gamma=p.gamma,
+                    max_splits=p.max_splits, min_gain=p.min_gain,
+                    overlap_reduction=p.overlap_reduction)
+    pb = PL.Problem(seq_lens=[int(x) for x in seq], q_lens=[int(x) for x in qlen],
+                    num_kv_heads=spec.num_kv_heads, rows_per_token=spec.num_q_heads, n_ext=n_ext,
+                    causal=spec.causal)
+    return pb, prm, PL.plan(pb, prm, ref=ref), PL.simulate(pb, prm, [1] * len(seq))
+
+
+def assert_same(plan: skv.Plan, pb, prm, ev, ns):
+    inf = plan.info()
+    e = plan.export()
+    assert e["split_counts"].tolist() == list(ev.splits)
+    exp_ranges = [r for b, L in enumerate(pb.seq_lens) for r in PL.split_ranges(L, ev.splits[b], 64)]
+    assert list(zip(e["split_start"].tolist(), e["split_end"].tolist())) == exp_ranges
+    tasks = PL.build_tasks(pb, prm, list(ev.splits))
+    assert e["task_order"].tolist() == [[t.b, t.g, t.qi, t.r] for t in tasks]
+    assert bits(inf.score) == bits(ev.score)
+    assert bits(inf.t_attn) == bits(ev.t_attn)
+    assert bits(inf.nosplit_score) == bits(ns.score)
+    assert inf.reduction_run == PL.reduction_run(pb, prm)
+
+
+def test_fig8_through_the_abi():
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fig8_critical_wave.json")))
+    spec = skv.AttnSpec(1, 1, 64, 64, 16, dtype=torch.float32)
+    p = skv.default_params()
+    p.slots_per_cu, p.warps_per_slot = 1, 1
+    p.rho, p.delta_attn, p.delta_red, p.gamma = 0.75, 4.0, 4.0, 1.0
+    p.overlap_reduction = 1
+    seq = [t * 64 for t in g["histories_tiles"]]
+    plan = skv.plan_splits(seq, spec, num_cu=4, params=p, ref_splits=g["reference_plan"])
+    inf = plan.info()
+    assert plan.export()["split_counts"].tolist() == g["chosen"]
+    assert inf.score == g["printed"]["critical-wave (2,2,1)"]
+    assert inf.nosplit_score == g["printed"]["NoSplit (1,1,1)"]
+    fa3 = skv.plan_from_counts(seq, spec, g["reference_plan"], num_cu=4, params=p)
+    assert fa3.info().score == g["printed"]["FA3-derived (3,3,1)"]
+
+
+SPECS = [
+    skv.AttnSpec(128, 8, 128, 128, 16),
+    skv.AttnSpec(64, 8, 128, 128, 16),
+    skv.AttnSpec(4, 1, 64, 64, 16, dtype=torch.float32),
+    skv.AttnSpec(128, 1, 576, 512, 64, mla=True),
+]
+
+
+@pytest.mark.parametrize("seed", range(200))
+def test_random_batches_bit_exact(seed):
+    rng = np.random.default_rng(1000 + seed)
+    spec = SPECS[seed % len(SPECS)]
+    B = int(rng.integers(1, 20))
+    seq = rng.integers(1, 20000, size=B)
+    if seed % 5 == 0:
+        seq[0] = int(rng.integers(50000, 300000))
+    q = np.ones(B, np.int64)
+    if seed % 7 == 3:
+        q[-1] = min(int(seq[-1]), int(rng.integers(17, 40)))
+    num_cu = int(rng.choice([4, 16, 64, 256]))
+    n_ext = int(rng.integers(0, 3))
+    p = skv.default_params()
+    p.overlap_reduction = int(seed % 2)
+    if seed % 3 == 0:
+        p.rho, p.delta_attn, p.gamma = float(rng.uniform(0.2, 0.9)), float(rng.integers(0, 40)), 0.1
+    plan = skv.plan_splits(seq, spec, num_cu=num_cu, q_lens=q, n_ext=n_ext, params=p)
+    pb, prm, ev, ns = reference_for(plan, spec, seq, q, n_ext, p)
+    assert_same(plan, pb, prm, ev, ns)
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 5])
+def test_benchmark_workloads_bit_exact(cid):
+    L, n = wl.config_lengths(cid)
+    spec = {1: SPECS[2], 2: SPECS[0], 3: SPECS[3], 5: SPECS[3]}[cid]
+    n_ext = 16 if cid == 5 else 0
+    t0 = time.time()
+    plan = skv.plan_splits(L, spec, num_cu=256, q_lens=n, n_ext=n_ext)
+    pb, prm, ev, ns = reference_for(plan, spec, L, n, n_ext)
+    assert_same(plan, pb, prm, ev, ns)
+    assert time.time() - t0 < 120
+
+
+def test_skewed_workload_bit_exact():
+    L, n = wl.config_lengths(4)
+    order = np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence(wl.SEED_BASE + 4).spawn(8)[1])).permutation(len(L))
+    L, n = L[order], n[order]
+    plan = skv.plan_splits(L, SPECS[1], num_cu=256, q_lens=n)
+    pb, prm, ev, ns = reference_for(plan, SPECS[1], L, n)
+    assert_same(plan, pb, prm, ev, ns)
