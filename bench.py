@@ -1,0 +1,256 @@
+"""Benchmark: decode-attention KV GB/s (% of MI355X HBM peak) and tokens/s, 1 GPU.
+
+One step = one attention layer's pass over one batch: the paged partial
+attention over every split of the batch's plan, then the LSE merge of the
+partial states (and of external states, when the workload has them). The split
+plan is built on the host once per batch and reused by every layer; its own
+cost is measured separately and reported as ``plan_ms``. Inputs are resident
+in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps 60] [--warmup 40] [--workload 2]
+
+Prints one JSON line. ``value`` is KV bytes read by the attention (visible
+tokens x bytes per token) divided by the time of a step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, vendor figure
+METRIC = "decode attention KV GB/s (% of MI355X HBM peak) + tokens/s at 1 GPU"
+
+KERNEL_FILES = {
+    "gqa_mfma": "split_kv_partial_amd/csrc/kernels/gqa_mfma.hip",
+    "gqa_valu": "split_kv_partial_amd/csrc/kernels/gqa_valu.hip",
+    "mla_mfma": "split_kv_partial_amd/csrc/kernels/mla_mfma.hip",
+    "merge": "split_kv_partial_amd/csrc/kernels/merge.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=60)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", type=str, default="2",
+                    help="1-5, or 5d for the decode-only part of workload 5")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def kernel_of(w) -> str:
+    if w.mla:
+        return "mla_mfma"
+    return "gqa_mfma" if (w.dtype == "bf16" and w.group >= 16) else "gqa_valu"
+
+
+def source_hash(kernel: str) -> str:
+    files = [KERNEL_FILES[kernel], "split_kv_partial_amd/csrc/kernels/device_common.hpp"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(f"{kernel}:{workload}")
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_hash") != source_hash(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def visible_kv_tokens(w) -> int:
+    tot = 0
+    for L, n in zip(w.seq_lens.astype(np.int64), w.q_lens.astype(np.int64)):
+        if w.causal and n > 1:
+            tot += int(n * (L - n) + n * (n + 1) // 2)   # row i sees L - n + i + 1 tokens
+        else:
+            tot += int(L) * int(n)
+    return tot
+
+
+def attention_flops(w) -> float:
+    per_head_token = 2.0 * (w.head_dim_qk + w.head_dim_v)
+    return per_head_token * w.num_q_heads * visible_kv_tokens(w)
+
+
+def cpu_baseline(w, target_s: float) -> dict:
+    """The oracle, as it is, on requests of the same batch in order until about
+    target_s seconds of CPU work; BLAS limited to one thread."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as A
+    done_tokens, done_bytes, rows = 0, 0, 0
+    per_tok = w.kv_bytes_per_token() if not w.mla else w.head_dim_qk * 2
+    reqs = []
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for b in range(w.batch):
+            n = int(w.q_lens[b])
+            ids = list(range(n)) if n <= 4 else [0, n // 2, n - 1]
+            A.attention_rows(w, b, ids)
+            L = int(w.seq_lens[b])
+            for i in ids:
+                vis = A.visible_end(w, b, i)
+                done_tokens += vis
+                done_bytes += vis * per_tok
+            rows += len(ids) * w.num_q_heads
+            reqs.append(b)
+            if time.perf_counter() - t0 >= target_s:
+                break
+    dt = time.perf_counter() - t0
+    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": f"float64 oracle attention over {len(reqs)} of {w.batch} requests "
+                      f"({rows} output rows, {done_tokens} visible KV tokens) of the same "
+                      f"workload, numpy with one BLAS thread"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    import split_kv_partial_amd as skv
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    dev = torch.device("cuda:0")
+    wid = args.workload
+    cid = int(wid.rstrip("d"))
+    t_gen = time.perf_counter()
+    w = wl.make(cid, decode_only=wid.endswith("d"))
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] workload {w.name}: batch {w.batch}, generated in {t_gen:.1f}s", file=sys.stderr,
+          flush=True)
+
+    def to_dev(a, bf16):
+        if bf16:
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    bf16 = w.dtype == "bf16"
+    q = to_dev(w.q, bf16)
+    k = to_dev(w.k_pages, bf16)
+    v = k if w.mla else to_dev(w.v_pages, bf16)
+    pt = torch.from_numpy(w.page_table).to(dev)
+    sl = torch.from_numpy(w.seq_lens).to(dev)
+    o_ext = None if w.o_ext is None else torch.from_numpy(w.o_ext).to(dev)
+    lse_ext = None if w.lse_ext is None else torch.from_numpy(w.lse_ext).to(dev)
+    spec = skv.AttnSpec(w.num_q_heads, w.num_kv_heads, w.head_dim_qk, w.head_dim_v, w.page_size,
+                        dtype=torch.bfloat16 if bf16 else torch.float32, mla=w.mla, causal=w.causal)
+    num_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    # host planner, once per batch (timed on its own)
+    plan_times = []
+    for _ in range(5):
+        t = time.perf_counter()
+        if w.chunk_tokens:
+            plan = skv.plan_fixed_chunks(w.seq_lens, spec, w.chunk_tokens, num_cu, q_lens=w.q_lens)
+        else:
+            plan = skv.plan_splits(w.seq_lens, spec, num_cu, q_lens=w.q_lens, n_ext=w.n_ext)
+        plan_times.append(time.perf_counter() - t)
+    info = plan.info()
+    ws = plan.workspace(dev)
+    o_part = torch.empty(info.state_rows, w.head_dim_v, dtype=torch.float32, device=dev)
+    lse_part = torch.empty(info.state_rows, dtype=torch.float32, device=dev)
+    o_out = torch.empty(info.total_rows, w.head_dim_v, dtype=torch.float32, device=dev)
+    lse_out = torch.empty(info.total_rows, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        skv.decode_attn_partial(q, k, v, pt, sl, plan, w.scale, o_part=o_part, lse_part=lse_part)
+        skv.merge_states(o_part, lse_part, plan, o_ext, lse_ext, o_out=o_out, lse_out=lse_out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # per-launch events on the launch stream (torch's current stream)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        ev[i][0].record()
+        skv.decode_attn_partial(q, k, v, pt, sl, plan, w.scale, o_part=o_part, lse_part=lse_part)
+        ev[i][1].record()
+        skv.merge_states(o_part, lse_part, plan, o_ext, lse_ext, o_out=o_out, lse_out=lse_out)
+        ev[i][2].record()
+    stop.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    total_ms = start.elapsed_time(stop)
+    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    ms_per_step = total_ms / args.steps
+    flag = plan.read_error_flag(dev)
+
+    kv_tokens = visible_kv_tokens(w)
+    kv_bytes = kv_tokens * (w.kv_bytes_per_token() if not w.mla else w.head_dim_qk * 2)
+    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    tokens = int(w.q_lens.sum())
+    kern = kernel_of(w)
+    attn_avg = float(attn_ms.mean())
+    achieved = kv_bytes / (attn_avg * 1e-3) / 1e9
+    traffic = measured_traffic(kern, wid)
+    roofline = {"kernel": kern, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "launch_ms_avg": round(attn_avg, 4),
+                "algorithmic_bytes_per_launch": int(kv_bytes)}
+    if w.mla:
+        fl = attention_flops(w)
+        roofline["mfma_tflops"] = round(fl / (attn_avg * 1e-3) / 1e12, 1)
+        roofline["mfma_frac"] = round(fl / (attn_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+    out = {
+        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim_qk": w.head_dim_qk,
+                   "head_dim_v": w.head_dim_v, "page_size": w.page_size,
+                   "kv_tokens": int(kv_tokens), "query_tokens": tokens, "n_ext": w.n_ext,
+                   "splits": int(info.total_splits), "tasks": int(info.num_tasks)},
+        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
+        "attn_ms": round(attn_avg, 4), "merge_ms": round(float(merge_ms.mean()), 4),
+        "attn_ms_p95": round(float(np.percentile(attn_ms, 95)), 4),
+        "plan_ms": {"p50": round(1e3 * float(np.median(plan_times)), 3),
+                    "p95": round(1e3 * float(np.percentile(plan_times, 95)), 3)},
+        "ms_per_step_incl_plan": round(ms_per_step + 1e3 * float(np.median(plan_times)), 4),
+        "wall_s_timed": round(t_wall, 4), "device_error_flag": flag,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -102,6 +102,12 @@ typedef struct skv_plan_params {
   int32_t max_splits;         /* upper bound on splits per request (<= 64)       */
   int32_t overlap_reduction;  /* 0: merge runs after attention (this library's
                                  executor); 1: fused engine of the pages         */
+  int32_t use_calibration;    /* 1: take rho, delta_attn, delta_red and gamma from
+                                 the library's MI355X fit for the kernel the
+                                 problem selects (the fields below are ignored) */
+  int32_t ref_waves;          /* the stand-in reference plan (used when no
+                                 ref_splits are given) aims at ref_waves * K
+                                 tasks of equal work; its counts bound the search */
   int32_t reserved;
   double rho;                 /* per-tile time floor                             */
   double delta_attn;          /* per attention task overhead, tile-equivalents   */
@@ -127,10 +133,15 @@ typedef struct skv_plan_info {
   double score;               /* model completion time of the chosen plan        */
   double t_attn;              /* model attention completion of the chosen plan   */
   double nosplit_score;       /* model completion time of NoSplit                */
+  double rho, delta_attn, delta_red, gamma;  /* model parameters in effect        */
+  double tile_time_us;        /* microseconds per model unit (calibration)       */
+  int32_t ref_waves;
+  int32_t reserved;
 } skv_plan_info;
 
-/* Fill p with the library defaults (the pages' Table 2 values for rho,
- * delta_attn, delta_red, gamma; tile 64; max_splits 64; min_gain 0.10). */
+/* Fill p with the library defaults: use_calibration = 1, ref_waves = 4, tile 64,
+ * max_splits 64, min_gain 0.10, and the pages' Table 2 (H100) values in rho,
+ * delta_attn, delta_red and gamma, which apply when use_calibration is 0. */
 void skv_plan_params_default(skv_plan_params* p);
 
 /* Critical-wave split plan (LiquidCP, section 5.2 "Plan selection" and

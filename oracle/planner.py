@@ -38,9 +38,10 @@ What the pages fix (LiquidCP, section 5.2 "Critical-wave KV splitting"):
 Readings where the pages are silent (each listed in the design notes):
 
 * Reference plan: the pages use FA3's native heuristic, which they do not give.
-  It is replaced by a work-proportional plan s_b = clamp(floor(K n_b / W + 1/2),
-  1, min(n_b, max_splits)) with n_b the tile count of request b and W the total
-  tile-work of the batch; callers may inject an explicit reference plan instead.
+  It is replaced by a work-proportional plan s_b = clamp(floor(R K n_b / W + 1/2),
+  1, min(n_b, max_splits)) with n_b the tile count of request b, W the total
+  tile-work of the batch and R = ref_waves the number of waves of K tasks it aims
+  at; callers may inject an explicit reference plan instead.
 * A split of n tiles into s parts gives the first (n mod s) parts ceil(n/s)
   tiles and the rest floor(n/s) (Figure 8 splits 176 tiles as 59, 59, 58).
 * One attention task per (request, KV head, query token, split); the pages fix
@@ -72,6 +73,7 @@ class Params:
     max_splits: int = 64
     min_gain: float = 0.10
     overlap_reduction: int = 0
+    ref_waves: int = 1          # waves of K tasks the stand-in reference plan aims at
 
 
 @dataclass
@@ -167,7 +169,7 @@ def reduction_run(pb: Problem, prm: Params) -> int:
     warps = prm.slots * prm.warps_per_slot
     best = 1
     for run in (1, h, 2 * h, 4 * h, min(8 * h, 32)):
-        units = sum(math.ceil(n * h / run) for n in pb.q_lens)
+        units = sum((n * h + run - 1) // run for n in pb.q_lens)
         if units >= 0.8 * warps and run > best:
             best = run
     return best
@@ -252,7 +254,7 @@ def reference_plan(pb: Problem, prm: Params):
     work = sum(nt[b] * pb.q_lens[b] * pb.num_kv_heads for b in range(len(nt)))
     out = []
     for b in range(len(nt)):
-        x = math.floor(prm.slots * nt[b] / work + 0.5) if work > 0 else 1
+        x = math.floor(prm.ref_waves * prm.slots * nt[b] / work + 0.5) if work > 0 else 1
         out.append(max(1, min(x, nt[b], prm.max_splits)))
     return out
 

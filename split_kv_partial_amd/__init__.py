@@ -50,7 +50,8 @@ class AttnDesc(ctypes.Structure):
 class PlanParams(ctypes.Structure):
     _fields_ = [("tile_tokens", ctypes.c_int32), ("slots_per_cu", ctypes.c_int32),
                 ("warps_per_slot", ctypes.c_int32), ("max_splits", ctypes.c_int32),
-                ("overlap_reduction", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("overlap_reduction", ctypes.c_int32), ("use_calibration", ctypes.c_int32),
+                ("ref_waves", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("rho", ctypes.c_double), ("delta_attn", ctypes.c_double),
                 ("delta_red", ctypes.c_double), ("gamma", ctypes.c_double),
                 ("min_gain", ctypes.c_double), ("tile_time_us", ctypes.c_double)]
@@ -63,7 +64,10 @@ class PlanInfo(ctypes.Structure):
                 ("num_units", ctypes.c_int32), ("split_adopted", ctypes.c_int32),
                 ("state_rows", ctypes.c_int64), ("total_rows", ctypes.c_int64),
                 ("score", ctypes.c_double), ("t_attn", ctypes.c_double),
-                ("nosplit_score", ctypes.c_double)]
+                ("nosplit_score", ctypes.c_double), ("rho", ctypes.c_double),
+                ("delta_attn", ctypes.c_double), ("delta_red", ctypes.c_double),
+                ("gamma", ctypes.c_double), ("tile_time_us", ctypes.c_double),
+                ("ref_waves", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 def _load():

@@ -103,12 +103,22 @@ ModelParams model_params(const skv_attn_desc& d, int num_cu, const skv_plan_para
                                            : std::max(1, vs.merge_waves_per_cu / spc);
   m.max_splits = p->max_splits;
   m.overlap_reduction = p->overlap_reduction;
-  m.rho = p->rho;
-  m.delta_attn = p->delta_attn;
-  m.delta_red = p->delta_red;
-  m.gamma = p->gamma;
+  m.ref_waves = p->ref_waves;
   m.min_gain = p->min_gain;
-  m.tile_time_us = p->tile_time_us;
+  if (p->use_calibration) {
+    const Calibration c = calibration(pick_variant(d));
+    m.rho = c.rho;
+    m.delta_attn = c.delta_attn;
+    m.delta_red = c.delta_red;
+    m.gamma = c.gamma;
+    m.tile_time_us = c.tile_time_us;
+  } else {
+    m.rho = p->rho;
+    m.delta_attn = p->delta_attn;
+    m.delta_red = p->delta_red;
+    m.gamma = p->gamma;
+    m.tile_time_us = p->tile_time_us;
+  }
   return m;
 }
 
@@ -117,6 +127,11 @@ skv_status check_params(const skv_plan_params* p) {
   if (p->tile_tokens != kTileTokens) return fail(SKV_ERR_UNSUPPORTED, "tile_tokens must be 64");
   if (p->max_splits < 1 || p->max_splits > 64) return fail(SKV_ERR_INVALID_ARG, "max_splits must be in [1, 64]");
   if (p->slots_per_cu < 0 || p->warps_per_slot < 0) return fail(SKV_ERR_INVALID_ARG, "negative slot counts");
+  if (p->ref_waves < 1 || p->ref_waves > 64) return fail(SKV_ERR_INVALID_ARG, "ref_waves must be in [1, 64]");
+  if (p->use_calibration != 0 && p->use_calibration != 1)
+    return fail(SKV_ERR_INVALID_ARG, "use_calibration must be 0 or 1");
+  if (p->overlap_reduction != 0 && p->overlap_reduction != 1)
+    return fail(SKV_ERR_INVALID_ARG, "overlap_reduction must be 0 or 1");
   if (!(p->rho > 0) || !(p->delta_attn >= 0) || !(p->delta_red >= 0) || !(p->gamma >= 0) ||
       !(p->min_gain >= 0 && p->min_gain < 1))
     return fail(SKV_ERR_INVALID_ARG, "model parameters out of range");
@@ -255,6 +270,8 @@ void skv_plan_params_default(skv_plan_params* p) {
   p->warps_per_slot = 0;
   p->max_splits = 64;
   p->overlap_reduction = 0;
+  p->use_calibration = 1;
+  p->ref_waves = 4;
   p->rho = 0.43;
   p->delta_attn = 32.0;
   p->delta_red = 2.5;
@@ -385,6 +402,13 @@ skv_status skv_plan_get_info(const skv_plan* pl, skv_plan_info* info) {
   info->score = pl->score;
   info->t_attn = pl->t_attn;
   info->nosplit_score = pl->nosplit_score;
+  info->rho = pl->prm.rho;
+  info->delta_attn = pl->prm.delta_attn;
+  info->delta_red = pl->prm.delta_red;
+  info->gamma = pl->prm.gamma;
+  info->tile_time_us = pl->prm.tile_time_us;
+  info->ref_waves = pl->prm.ref_waves;
+  info->reserved = 0;
   return SKV_OK;
 }
 
@@ -503,6 +527,18 @@ VariantShape variant_shape(Variant v) {
     case Variant::GqaValu: return {2, 16};
     case Variant::GqaMfma: return {2, 16};
     default: return {1, 16};
+  }
+}
+
+// Critical-wave parameters fitted on MI355X for each kernel (least-squares fit
+// of the model's attention completion to measured kernel times over plans with
+// 1 to 16 splits per request, the procedure of the pages' appendix A.2 applied
+// to whole-kernel times; time unit = one 64-token tile per slot, all slots busy).
+Calibration calibration(Variant v) {
+  switch (v) {
+    case Variant::GqaMfma: return {0.50, 3.0, 1.0, 0.47, 2.66};
+    case Variant::GqaValu: return {0.50, 3.0, 1.0, 0.47, 2.66};
+    default: return {0.50, 3.0, 1.0, 0.47, 2.66};
   }
 }
 }  // namespace skv

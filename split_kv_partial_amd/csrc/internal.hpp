@@ -52,6 +52,7 @@ struct ModelParams {
   int warps_per_slot = 4;
   int max_splits = 64;
   int overlap_reduction = 0;
+  int ref_waves = 1;
   double rho = 0.43, delta_attn = 32.0, delta_red = 2.5, gamma = 0.47;
   double min_gain = 0.10, tile_time_us = 1.08;
 };
@@ -129,5 +130,9 @@ struct VariantShape {
   int merge_waves_per_cu;
 };
 VariantShape variant_shape(Variant v);
+struct Calibration {
+  double rho, delta_attn, delta_red, gamma, tile_time_us;
+};
+Calibration calibration(Variant v);
 
 }  // namespace skv

@@ -184,7 +184,7 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void gqa_mfma_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_mfma_kernel(MfmaArgs a) {
   __shared__ float m_lds[kWaves][kG], l_lds[kWaves][kG];
   __shared__ float o_lds[kWaves][kG][D + 4];
 

@@ -19,6 +19,7 @@
 #include <cstdint>
 #include <numeric>
 #include <queue>
+#include <thread>
 #include <tuple>
 #include <vector>
 
@@ -193,22 +194,42 @@ Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector
   }
   const double t_attn = t;
 
-  std::vector<Warp> wv;
-  wv.reserve((size_t)K * prm.warps_per_slot);
-  for (int s = 0; s < K; ++s)
-    for (int w = 0; w < prm.warps_per_slot; ++w)
-      wv.push_back({prm.overlap_reduction ? release[s] : t_attn, s, w});
-  MinHeap<Warp> warps(std::greater<Warp>(), std::move(wv));
-  double score = t_attn;
+  // Reduction phase. Warps are claimed earliest-available first (ties by slot,
+  // then warp). Without overlap every warp becomes free at t_attn, when every
+  // request's inputs are ready, so the first K*W units start exactly at t_attn
+  // on warps taken in (slot, warp) order; only later units need the heap.
   const int run = reduction_run(pb, prm);
+  const int64_t nwarps = (int64_t)K * prm.warps_per_slot;
+  double score = t_attn;
+  // The shortcut needs every claimed warp to end strictly after t_attn, so that
+  // no used warp can tie with an untouched one: the cheapest unit costs at least
+  // delta_red + gamma (v_u >= 1, s_u >= 1).
+  const bool fast = !prm.overlap_reduction && t_attn + (prm.delta_red + prm.gamma) > t_attn;
+  std::vector<Warp> wv;
+  int64_t claimed = 0;
+  MinHeap<Warp> warps;
+  if (!fast) {
+    wv.reserve((size_t)nwarps);
+    for (int s = 0; s < K; ++s)
+      for (int w = 0; w < prm.warps_per_slot; ++w)
+        wv.push_back({prm.overlap_reduction ? release[s] : t_attn, s, w});
+    warps = MinHeap<Warp>(std::greater<Warp>(), std::move(wv));
+  }
   for (int b = 0; b < B; ++b) {
     const int64_t rows = pb.q_lens[b] * (int64_t)pb.rows_per_token;
     const int64_t s_u = splits[b] + pb.n_ext;
     for (int64_t start = 0; start < rows;) {
       const int64_t v = std::min<int64_t>(run, rows - start);
       const double c = prm.delta_red + prm.gamma * (double)v * (double)s_u;
-      Warp w = warps.top();
-      warps.pop();
+      Warp w;
+      if (fast && claimed < nwarps) {
+        // still-untouched warp number `claimed`: available at t_attn
+        w = {t_attn, (int)(claimed / prm.warps_per_slot), (int)(claimed % prm.warps_per_slot)};
+        ++claimed;
+      } else {
+        w = warps.top();
+        warps.pop();
+      }
       const double st = w.avail > done[b] ? w.avail : done[b];
       const double end = st + c;
       warps.push({end, w.slot, w.w});
@@ -246,7 +267,7 @@ std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
   for (int b = 0; b < B; ++b) {
     int64_t x = 1;
     if (work > 0)
-      x = (int64_t)std::floor((double)((int64_t)prm.slots * nt[b]) / (double)work + 0.5);
+      x = (int64_t)std::floor((double)((int64_t)prm.ref_waves * prm.slots * nt[b]) / (double)work + 0.5);
     out[b] = (int)std::max<int64_t>(1, std::min<int64_t>({x, nt[b], (int64_t)prm.max_splits}));
   }
   return out;
@@ -289,10 +310,24 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
       cands.push_back(std::move(s));
     }
     if (cands.empty()) break;
+    // Candidates are independent simulations: evaluate them on worker threads,
+    // then pick in candidate order exactly as a sequential loop would.
+    std::vector<Evaluation> evs(cands.size());
+    const size_t nthreads =
+        std::min<size_t>(cands.size(), std::max(1u, std::min(16u, std::thread::hardware_concurrency())));
+    if (nthreads <= 1 || cands.size() < 4) {
+      for (size_t i = 0; i < cands.size(); ++i) evs[i] = simulate(pb, prm, cands[i]);
+    } else {
+      std::vector<std::thread> pool;
+      for (size_t t = 0; t < nthreads; ++t)
+        pool.emplace_back([&, t]() {
+          for (size_t i = t; i < cands.size(); i += nthreads) evs[i] = simulate(pb, prm, cands[i]);
+        });
+      for (auto& th : pool) th.join();
+    }
     bool have = false;
     Evaluation best;
-    for (auto& s : cands) {
-      Evaluation ev = simulate(pb, prm, s);
+    for (auto& ev : evs) {
       if (!have || key_less(ev, best)) {
         best = std::move(ev);
         have = true;

@@ -25,10 +25,10 @@ def bits(x: float) -> int:
 def reference_for(plan: skv.Plan, spec: skv.AttnSpec, seq, qlen, n_ext=0, params=None, ref=None):
     inf = plan.info()
     p = params or skv.default_params()
-    prm = PL.Params(tile_tokens=64, slots=inf.slots, warps_per_slot=inf.warps_per_slot, rho=p.rho,
-                    delta_attn=p.delta_attn, delta_red=p.delta_red, gamma=p.gamma,
-                    max_splits=p.max_splits, min_gain=p.min_gain,
-                    overlap_reduction=p.overlap_reduction)
+    prm = PL.Params(tile_tokens=64, slots=inf.slots, warps_per_slot=inf.warps_per_slot,
+                    rho=inf.rho, delta_attn=inf.delta_attn, delta_red=inf.delta_red,
+                    gamma=inf.gamma, max_splits=p.max_splits, min_gain=p.min_gain,
+                    overlap_reduction=p.overlap_reduction, ref_waves=inf.ref_waves)
     pb = PL.Problem(seq_lens=[int(x) for x in seq], q_lens=[int(x) for x in qlen],
                     num_kv_heads=spec.num_kv_heads, rows_per_token=spec.num_q_heads, n_ext=n_ext,
                     causal=spec.causal)
@@ -53,6 +53,7 @@ def test_fig8_through_the_abi():
     g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "fig8_critical_wave.json")))
     spec = skv.AttnSpec(1, 1, 64, 64, 16, dtype=torch.float32)
     p = skv.default_params()
+    p.use_calibration = 0
     p.slots_per_cu, p.warps_per_slot = 1, 1
     p.rho, p.delta_attn, p.delta_red, p.gamma = 0.75, 4.0, 4.0, 1.0
     p.overlap_reduction = 1
@@ -89,8 +90,13 @@ def test_random_batches_bit_exact(seed):
     n_ext = int(rng.integers(0, 3))
     p = skv.default_params()
     p.overlap_reduction = int(seed % 2)
+    p.ref_waves = int(rng.choice([1, 2, 4]))
     if seed % 3 == 0:
+        p.use_calibration = 0
         p.rho, p.delta_attn, p.gamma = float(rng.uniform(0.2, 0.9)), float(rng.integers(0, 40)), 0.1
+    if seed % 11 == 5:
+        p.use_calibration = 0
+        p.delta_red, p.gamma = 0.0, 0.0        # zero-cost reductions: ties between warps
     plan = skv.plan_splits(seq, spec, num_cu=num_cu, q_lens=q, n_ext=n_ext, params=p)
     pb, prm, ev, ns = reference_for(plan, spec, seq, q, n_ext, p)
     assert_same(plan, pb, prm, ev, ns)
