@@ -530,15 +530,18 @@ VariantShape variant_shape(Variant v) {
   }
 }
 
-// Critical-wave parameters fitted on MI355X for each kernel (least-squares fit
-// of the model's attention completion to measured kernel times over plans with
-// 1 to 16 splits per request, the procedure of the pages' appendix A.2 applied
-// to whole-kernel times; time unit = one 64-token tile per slot, all slots busy).
+// Critical-wave parameters for each kernel on MI355X. GQA: least-squares fit of
+// the model's attention completion to measured kernel times over plans with 1
+// to 16 splits per request (the procedure of the pages' appendix A.2, applied
+// to whole-kernel times; time unit = one 64-token tile per slot with all slots
+// busy). MLA: a work-group's tile rate is set by its own matrix and LDS work,
+// not by shared HBM, so a lone work-group is no faster than one in a full
+// wave (rho = 1), and the per-task overhead is small (Q load, epilogue).
 Calibration calibration(Variant v) {
   switch (v) {
     case Variant::GqaMfma: return {0.50, 3.0, 1.0, 0.47, 2.66};
     case Variant::GqaValu: return {0.50, 3.0, 1.0, 0.47, 2.66};
-    default: return {0.50, 3.0, 1.0, 0.47, 2.66};
+    default: return {1.00, 2.0, 1.0, 0.47, 7.4};
   }
 }
 }  // namespace skv

@@ -4,27 +4,31 @@
 //
 // Shapes follow SPLASH sections 2-3: KV bytes per token L(d_c + d_r)b with
 // d_c = 512 and d_r = 64; the attention at a request's owner computes rows
-// [N_r, H, d_c + d_r] and returns width d_c. One work-group (8 waves) runs one
-// task: all heads of one query token over the KV range [lo, end) of one split,
-// so each latent row is read from HBM once per task and shared by every head
-// (the reason MLA decode is matrix-core work: ~242 flop per KV byte).
+// [N_r, H, d_c + d_r] and returns width d_c. One work-group runs one task: all
+// heads of one query token over the KV range [lo, end) of one split, so each
+// latent row is read from HBM once per task and shared by every head (the
+// reason MLA decode is matrix-core work: ~242 flop per KV byte).
 //
-// Work split inside the work-group: wave w owns head group hg = w / 2 (32 heads)
-// and dimension half dh = w % 2. For a 32-token tile staged in LDS:
+// Work split: 8 waves (2 per SIMD); wave w owns head group hg = w / 2 (32
+// heads) and dimension half dh = w % 2. For a 32-token tile staged in LDS it
+// computes with v_mfma_f32_16x16x32_bf16
 //   S^T[32 tok x 32 heads] partial over its 288 of the 576 qk dims
-//       (v_mfma_f32_16x16x32_bf16; two token blocks x two 16-head blocks),
-//   the two halves of a head group add their partial scores through LDS, so
-//   both hold identical full scores and softmax state,
+//       (two token blocks x two 16-head blocks),
+// adds the partner wave's half through LDS (both then hold identical full
+// scores and softmax state), and
 //   O^T[256 dims x 32 heads] += V^T[256 x 32 tok] * P^T[32 tok x 32 heads]
-//       over its 256 of the 512 value dims.
-// Every output element has exactly one owner wave, so no merge between waves
-// is needed at the end. The V^T operand comes from the row-major latent tile
-// through the gfx950 transposing LDS read (ds_read_b64_tr_b16: within each 16
-// lanes, lane i addresses row i/4, columns 4(i%4)..+3 of a 4 x 16 block and lane
-// n receives column n of its four rows), so the tile is stored in LDS once.
-// Tiles are double-buffered in LDS; the next tile is fetched into registers
-// while the current one is computed. Softmax weights enter P*V as one bf16
-// term (max |error| <= 2^-9 |V|, within the bf16 tolerance for latent values).
+// over its 256 of the 512 value dims. Every output element has one owner wave.
+// Each lane owns one head per head block in both outputs, so the softmax needs
+// no data movement beyond two lane shuffles. The V^T operand comes from the
+// row-major latent tile through the gfx950 transposing LDS read
+// (ds_read_b64_tr_b16: within each 16 lanes, lane i addresses row i/4, columns
+// 4(i%4)..+3 of a 4 x 16 block and lane n receives column n of its four rows),
+// so the tile is stored in LDS once. Tiles stream HBM -> LDS with the gfx950
+// LDS DMA (global_load_lds_dwordx4: lane i's 16 bytes land at the wave's LDS
+// base + 16 i) into a ring of three buffers, two tiles in flight while one is
+// computed, without staging registers. Softmax weights enter P*V as one bf16
+// term (|error| <= 2^-9 max|V| per weight, within the bf16 tolerance for latent
+// values; this kernel is matrix-bound, unlike the GQA one).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -48,15 +52,30 @@ namespace {
 constexpr int kD = 576;          // qk width: 512 latent + 64 rope
 constexpr int kDv = 512;         // value width (the latent)
 constexpr int kT = 32;           // tokens per tile
-constexpr int kRS = kD + 8;      // LDS row stride in bf16 (16-byte pad)
-constexpr int kChunks = kD / 8;  // 16-byte chunks per row (72)
-constexpr int kThreads = 512;
-constexpr int kStage = (kT * kChunks + kThreads - 1) / kThreads;  // chunks per thread (5)
-constexpr int kKs = kD / 2 / 32;  // 32-wide k-steps per dimension half (9)
-constexpr int kNb = kDv / 2 / 16; // 16-dim output blocks per dimension half (16)
+// LDS tile layout, in 16-byte slots: rows of 74 slots (72 of data, 2 of pad)
+// in groups of 8 rows followed by one pad slot. With 32 four-byte banks, the
+// row stride of 296 dwords (8 mod 32) makes the transposing V reads (4 rows x 4
+// eight-byte column groups per 16 lanes) conflict-free, and the extra slot per
+// 8 rows keeps the K reads of rows t and t + 8 (same 8-lane pass) apart.
+constexpr int kSlots = 74;                       // slots per LDS row
+constexpr int kRS = kSlots * 8;                  // LDS row stride in bf16 (592)
+constexpr int kGroupSlots = 8 * kSlots + 1;      // 593 slots per group of 8 rows
+constexpr int kGS = kGroupSlots * 8;             // group stride in bf16
+constexpr int kTileSlots = (kT / 8) * kGroupSlots;  // 2372
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kDmaPerTile = (kTileSlots + 63) / 64;               // 38 wave-instructions
+constexpr int kDmaPerWave = (kDmaPerTile + kWaves - 1) / kWaves;  // 5 for waves 0-5, else 4
+constexpr int kKs = kD / 2 / 32;  // 32-wide k-steps per qk dimension half (9)
+constexpr int kNb = kDv / 2 / 16; // 16-dim output blocks per value dimension half (16)
 
 typedef short __attribute__((__vector_size__(4 * sizeof(short)))) s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+// Page-table reads go through the constant address space: the table is not
+// written while the kernel runs, so they become scalar loads, which are
+// counted apart from the LDS DMA and never make the tile loop wait for it.
+typedef const __attribute__((address_space(4))) int32_t const_i32_t;
 
 __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -68,69 +87,98 @@ __device__ __forceinline__ u32x2_t tr_read(const uint16_t* lds_ptr) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
-struct Stage {
-  u32x4_t r[kStage];
-};
-
-// Fetch the 32 x 576 tile at token t0 into registers (zeros past `end`).
-__device__ __forceinline__ void fetch(const MlaArgs& a, const int32_t* ptab, int end, int t0,
-                                      Stage& st) {
-  const int P = 1 << a.page_shift;
-#pragma unroll
-  for (int j = 0; j < kStage; ++j) {
-    const int c = threadIdx.x + kThreads * j;
-    u32x4_t v = {0, 0, 0, 0};
-    if (c < kT * kChunks) {
-      const int tok = t0 + c / kChunks;
-      if (tok < end) {
-        const int pid = ptab[tok >> a.page_shift];
-        if (pid >= 0 && pid < a.num_pages) {
-          v = *reinterpret_cast<const u32x4_t*>(
-              a.kv + (((int64_t)pid * P + (tok & (P - 1))) * kD + (c % kChunks) * 8) * 2);
-        } else {
-          raise_error(a.err_flag, 1);
-        }
-      }
-    }
-    st.r[j] = v;
-  }
+// One wave-wide LDS DMA: each active lane's 16 bytes at `src` land at
+// dst + 16 * lane. Issued as inline assembly so that the compiler does not
+// track it: its own wait insertion would otherwise drain every DMA in flight
+// before each read of a different ring buffer (it cannot tell the buffers
+// apart). The tile loop orders these writes itself with vmcnt waits, which
+// stay correct for the compiler's own loads because vector-memory counters
+// retire in order. M0 carries the LDS base; one wait state separates its write
+// from the DMA.
+__device__ __forceinline__ void lds_dma16(const uint8_t* src, uint16_t* dst) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t*)dst;
+  __asm__ __volatile__(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+      : "memory", "m0");
 }
 
-__device__ __forceinline__ void store(uint16_t* tile, const Stage& st) {
+// Issue this wave's share of the DMA of the 32-token tile at t0 into `tile`.
+// Every slot of the tile is fetched by exactly one lane, so each wave issues a
+// fixed number of DMA instructions per tile (5 for waves 0-5, 4 for 6-7),
+// which the vmcnt waits of the main loop rely on. Rows at or past `end`, pad
+// slots and rows of an out-of-range page read page 0 instead (always valid);
+// their scores are masked and their values zeroed where they are used. Page ids
+// are wave-uniform scalars: a tile starts at a multiple of 32 tokens, so it
+// spans one page (P >= 32) or two (P = 16).
+__device__ __forceinline__ void issue_tile(const MlaArgs& a, const_i32_t* ptab, int end, int t0,
+                                           uint16_t* tile, int wave, int lane) {
+  // Recompute the per-lane slot arithmetic at every call: hoisted out of the
+  // tile loop it would occupy registers the kernel does not have, and the
+  // reload of a spilled address would wait for the DMAs issued before it.
+  __asm__ __volatile__("" : "+v"(lane));
+  const int P = 1 << a.page_shift;
+  const int pid0 = ptab[t0 >> a.page_shift];
+  const bool two = P == 16 && t0 + 16 < end;
+  const int pid1 = two ? ptab[(t0 + 16) >> a.page_shift] : pid0;
+  const bool ok0 = pid0 >= 0 && pid0 < a.num_pages;
+  const bool ok1 = pid1 >= 0 && pid1 < a.num_pages;
+  if ((!ok0 || !ok1) && lane == 0) raise_error(a.err_flag, 1);
 #pragma unroll
-  for (int j = 0; j < kStage; ++j) {
-    const int c = threadIdx.x + kThreads * j;
-    if (c < kT * kChunks)
-      *reinterpret_cast<u32x4_t*>(tile + (c / kChunks) * kRS + (c % kChunks) * 8) = st.r[j];
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int inst = wave + kWaves * j;
+    if (inst >= kDmaPerTile) break;   // wave-uniform
+    const int s = 64 * inst + lane;
+    const int grp = s / kGroupSlots, rem = s - grp * kGroupSlots;
+    const int rig = rem / kSlots, ch = rem - rig * kSlots;   // rig = 8 for the group pad
+    const int row = 8 * grp + rig;
+    const int tok = t0 + row;
+    const bool hi = P == 16 && row >= 16;
+    const int pid = hi ? pid1 : pid0;
+    const bool ok = rig < 8 && ch < kD / 8 && tok < end && (hi ? ok1 : ok0);
+    const uint8_t* src = ok ? a.kv + (((int64_t)pid * P + (tok & (P - 1))) * kD + ch * 8) * 2 : a.kv;
+    if (s < kTileSlots)   // only the last instruction has lanes past the tile
+      lds_dma16(src, tile + 64 * 8 * inst);
   }
 }
 
 }  // namespace
 
+// Workgroup barrier without a memory fence: LDS writes are ordered by the
+// explicit counter waits before it (a fenced barrier would also drain the LDS
+// DMA of the tiles still in flight).
+__device__ __forceinline__ void bare_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mla_mfma_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][kT * kRS];
-  __shared__ __attribute__((aligned(16))) float xbuf[8][16][64];
+  __shared__ __attribute__((aligned(16))) uint16_t ring[3][kTileSlots * 8];
+  __shared__ __attribute__((aligned(16))) f32x4_t xbuf[kWaves][4][64];
 
   const DevTask t = a.tasks[blockIdx.x];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
   const int hg = wave >> 1, dh = wave & 1;
   const int end = min(t.end, a.seq_lens[t.b]);
-  const int32_t* ptab = a.page_table + (int64_t)t.b * a.max_pages;
-  // head blocks of this wave that exist (H_q may be below 128)
-  const bool hb_ok[2] = {32 * hg < a.H_q, 32 * hg + 16 < a.H_q};
+  const_i32_t* ptab = (const_i32_t*)(a.page_table + (int64_t)t.b * a.max_pages);
 
-  // Q^T operand: lane owns head 32hg + 16hb + n; k-slots of step ks are dims
+  // Q^T operand: lane owns head 32 hg + 16 hb + n (heads past H_q compute on a
+  // copy of the last head and are not written); k-slots of step ks are dims
   // 288 dh + 32 ks + 8 g .. +7.
   u32x4_t qf[2][kKs];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    const int head = 32 * hg + 16 * hb + n;
-    const uint16_t* qp = a.q + ((int64_t)t.q_row * a.H_q + min(head, a.H_q - 1)) * kD + 288 * dh + 8 * g;
+    const int head = min(32 * hg + 16 * hb + n, a.H_q - 1);
+    const uint16_t* qp = a.q + ((int64_t)t.q_row * a.H_q + head) * kD + 288 * dh + 8 * g;
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks)
-      qf[hb][ks] = hb_ok[hb] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0, 0, 0, 0};
+    for (int ks = 0; ks < kKs; ++ks) qf[hb][ks] = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks);
   }
 
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
@@ -138,21 +186,25 @@ void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
   for (int nb = 0; nb < kNb; ++nb) o[nb][0] = o[nb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  Stage st;
-  int t0 = t.lo;
-  if (t0 < end) {
-    fetch(a, ptab, end, t0, st);
-    store(tiles[0], st);
-    if (t0 + kT < end) fetch(a, ptab, end, t0 + kT, st);
-  }
-  int buf = 0;
-  for (; t0 < end; t0 += kT, buf ^= 1) {
-    __syncthreads();  // tiles[buf] written; everyone is done with tiles[buf ^ 1]
-    if (t0 + kT < end) {
-      store(tiles[buf ^ 1], st);
-      if (t0 + 2 * kT < end) fetch(a, ptab, end, t0 + 2 * kT, st);
-    }
-    const uint16_t* tile = tiles[buf];
+  // Q has landed before the first DMA: otherwise the compiler places its wait
+  // at the first use, inside the tile loop, where it would drain the DMA ring
+  __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
+  const int ntiles = end > t.lo ? (end - t.lo + kT - 1) / kT : 0;
+  if (ntiles > 0) issue_tile(a, ptab, end, t.lo, ring[0], wave, lane);
+  if (ntiles > 1) issue_tile(a, ptab, end, t.lo + kT, ring[1], wave, lane);
+  for (int i = 0; i < ntiles; ++i) {
+    const int t0 = t.lo + i * kT;
+    // Tile i has landed once at most one newer tile's DMAs are outstanding: a
+    // wave issues 4 or 5 per tile, so vmcnt(4) waits for all of tile i (and
+    // possibly one instruction of tile i + 1).
+    if (i + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(0x3f74);   // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
+    // every wave's DMA of tile i is visible; every wave is done with ring[(i+2)%3]
+    bare_barrier();
+    if (i + 2 < ntiles) issue_tile(a, ptab, end, t0 + 2 * kT, ring[(i + 2) % 3], wave, lane);
+    const uint16_t* tile = ring[i % 3];
 
     // ---- partial scores over this wave's 288 qk dims ----
     f32x4_t s[2][2];  // [token block][head block]
@@ -160,88 +212,103 @@ void mla_mfma_kernel(MlaArgs a) {
     for (int blk = 0; blk < 2; ++blk) s[blk][0] = s[blk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     // row i of token block blk is token 8(i/4) + 4 blk + i%4, so that a lane's
     // outputs (rows 4g..4g+3 of both blocks) are the 8 consecutive tokens 8g..8g+7
+    const uint16_t* krow0 = tile + (n >> 2) * kGS + (n & 3) * kRS + 288 * dh + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const int tok = 8 * (n >> 2) + 4 * blk + (n & 3);
-        const u32x4_t ka =
-            *reinterpret_cast<const u32x4_t*>(tile + tok * kRS + 288 * dh + 32 * ks + 8 * g);
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          if (hb_ok[hb]) s[blk][hb] = mfma16(ka, qf[hb][ks], s[blk][hb]);
+        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(krow0 + 4 * blk * kRS + 32 * ks);
+        s[blk][0] = mfma16(ka, qf[0][ks], s[blk][0]);
+        s[blk][1] = mfma16(ka, qf[1][ks], s[blk][1]);
       }
+      // bound how far the scheduler hoists operand reads (register pressure)
+      if (ks % 3 == 2) __builtin_amdgcn_sched_barrier(0);
     }
     // ---- add the partner wave's half of the scores ----
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) xbuf[wave][8 * blk + 4 * hb + e][lane] = s[blk][hb][e];
-    __syncthreads();
+      for (int hb = 0; hb < 2; ++hb) xbuf[wave][2 * blk + hb][lane] = s[blk][hb];
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+    bare_barrier();
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[blk][hb][e] += xbuf[wave ^ 1][8 * blk + 4 * hb + e][lane];
+      for (int hb = 0; hb < 2; ++hb) s[blk][hb] += xbuf[wave ^ 1][2 * blk + hb][lane];
 
     // ---- online softmax per head (log2 domain) ----
+    // The running reference m only moves when a tile's maximum exceeds it by
+    // more than 8 (a factor 256): weights exp2(s - m) then stay <= 256, the
+    // accumulators are rescaled only on those (rare) tiles, and the common
+    // path leaves them to the matrix cores. The result is the same softmax.
     const bool tail = t0 + kT > end;
     u32x4_t pf[2];
-    float alpha[2];
+    float alpha[2] = {1.f, 1.f};
+    bool bump = false;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      float sv[8];
+      // scale in place; masked tokens become -inf
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int tok = t0 + 8 * g + 4 * blk + e;
           const float x = s[blk][hb][e] * a.scale_log2;
-          sv[4 * blk + e] = (!tail || tok < end) ? x : -INFINITY;
+          s[blk][hb][e] = (!tail || t0 + 8 * g + 4 * blk + e < end) ? x : -INFINITY;
         }
-      float mt = sv[0];
-#pragma unroll
-      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
+      float mt = fmaxf(fmaxf(fmaxf(s[0][hb][0], s[0][hb][1]), fmaxf(s[0][hb][2], s[0][hb][3])),
+                       fmaxf(fmaxf(s[1][hb][0], s[1][hb][1]), fmaxf(s[1][hb][2], s[1][hb][3])));
       mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float mn = fmaxf(m[hb], mt);
-      alpha[hb] = fast_exp2(m[hb] - mn);
-      m[hb] = mn;
-      float p[8], ps = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        p[i] = fast_exp2(sv[i] - mn);
-        ps += p[i];
+      if (mt > m[hb] + 8.f) {   // also true on the first tile (m = -inf)
+        alpha[hb] = fast_exp2(m[hb] - mt);
+        l[hb] *= alpha[hb];
+        m[hb] = mt;
+        bump = true;
       }
-      l[hb] = l[hb] * alpha[hb] + ps;
-      pf[hb] = u32x4_t{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                       pack_bf16x2(p[6], p[7])};
+      float ps = 0.f;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[blk][hb][e] = fast_exp2(s[blk][hb][e] - m[hb]);
+          ps += s[blk][hb][e];
+        }
+      l[hb] += ps;
+      pf[hb] = u32x4_t{pack_bf16x2(s[0][hb][0], s[0][hb][1]), pack_bf16x2(s[0][hb][2], s[0][hb][3]),
+                       pack_bf16x2(s[1][hb][0], s[1][hb][1]), pack_bf16x2(s[1][hb][2], s[1][hb][3])};
     }
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+#pragma unroll
+      for (int nb = 0; nb < kNb; ++nb) {
+        o[nb][0] *= alpha[0];
+        o[nb][1] *= alpha[1];
+      }
+    }
+    // values of tokens past `end` (unfetched or stale rows) are zeroed
+    const int nvalid = tail ? end - (t0 + 8 * g) : 8;   // valid tokens among 8g..8g+7
 
     // ---- O^T over this wave's 256 value dims ----
     // transposing reads: lane (g, i) addresses token 8g + i/4 (+4), dims d0 + 4(i%4)
-    const uint16_t* vrow = tile + (8 * g + (n >> 2)) * kRS + 256 * dh + 4 * (n & 3);
+    const uint16_t* vrow = tile + g * kGS + (n >> 2) * kRS + 256 * dh + 4 * (n & 3);
 #pragma unroll
     for (int nb = 0; nb < kNb; ++nb) {
       const u32x2_t lo = tr_read(vrow + 16 * nb);
       const u32x2_t hi = tr_read(vrow + 4 * kRS + 16 * nb);
-      const u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
+      u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
+      if (tail) {
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        if (!hb_ok[hb]) continue;
-        o[nb][hb] *= alpha[hb];
-        o[nb][hb] = mfma16(va, pf[hb], o[nb][hb]);
+        for (int k = 0; k < 4; ++k)
+          va[k] &= (2 * k + 1 < nvalid ? 0xFFFF0000u : 0u) | (2 * k < nvalid ? 0x0000FFFFu : 0u);
       }
+      o[nb][0] = mfma16(va, pf[0], o[nb][0]);
+      o[nb][1] = mfma16(va, pf[1], o[nb][1]);
+      if (nb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
     }
   }
 
   // ---- epilogue: normalise and write this wave's (heads, dims) block ----
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    if (!hb_ok[hb]) continue;
     float lt = l[hb];
     lt += __shfl_xor(lt, 16, 64);
     lt += __shfl_xor(lt, 32, 64);
