@@ -49,6 +49,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="also run one 1 GiB device-to-device copy (a plain copy of known size "
+                         "that scales the FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --traffic-probe` into profiles/counters.json and exit")
     return ap.parse_args()
 
 
@@ -98,38 +104,84 @@ def attention_flops(w) -> float:
 
 
 def cpu_baseline(w, target_s: float) -> dict:
-    """The oracle, as it is, on requests of the same batch in order until about
-    target_s seconds of CPU work; BLAS limited to one thread."""
+    """The oracle, as it is, on requests of the same batch in order (passes over
+    the batch repeat) until about target_s seconds of CPU work; one BLAS thread."""
     from threadpoolctl import threadpool_limits
     from oracle import attention as A
-    done_tokens, done_bytes, rows = 0, 0, 0
-    per_tok = w.kv_bytes_per_token() if not w.mla else w.head_dim_qk * 2
-    reqs = []
+    done_tokens, done_bytes, rows, calls = 0, 0, 0, 0
+    per_tok = w.kv_bytes_per_token()
+    reqs = set()
     t0 = time.perf_counter()
     with threadpool_limits(limits=1):
-        for b in range(w.batch):
-            n = int(w.q_lens[b])
-            ids = list(range(n)) if n <= 4 else [0, n // 2, n - 1]
-            A.attention_rows(w, b, ids)
-            L = int(w.seq_lens[b])
-            for i in ids:
-                vis = A.visible_end(w, b, i)
-                done_tokens += vis
-                done_bytes += vis * per_tok
-            rows += len(ids) * w.num_q_heads
-            reqs.append(b)
-            if time.perf_counter() - t0 >= target_s:
-                break
+        while time.perf_counter() - t0 < target_s:
+            for b in range(w.batch):
+                n = int(w.q_lens[b])
+                ids = list(range(n)) if n <= 4 else [0, n // 2, n - 1]
+                A.attention_rows(w, b, ids)
+                for i in ids:
+                    vis = A.visible_end(w, b, i)
+                    done_tokens += vis
+                    done_bytes += vis * per_tok
+                rows += len(ids) * w.num_q_heads
+                reqs.add(b)
+                calls += 1
+                if time.perf_counter() - t0 >= target_s:
+                    break
     dt = time.perf_counter() - t0
     return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "seconds": round(dt, 2),
-            "sample": f"float64 oracle attention over {len(reqs)} of {w.batch} requests "
-                      f"({rows} output rows, {done_tokens} visible KV tokens) of the same "
-                      f"workload, numpy with one BLAS thread"}
+            "sample": f"float64 oracle attention, {calls} request evaluations over {len(reqs)} "
+                      f"of {w.batch} requests ({rows} output rows, {done_tokens} visible KV "
+                      f"tokens) of the same workload, numpy with one BLAS thread"}
+
+
+COPY_PROBE_BYTES = 1 << 30
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
+    """HBM bytes per launch of the attention kernel from a FETCH_SIZE pass and a
+    WRITE_SIZE pass, each scaled by what the same counter reads for the 1 GiB
+    runtime copy (__amd_rocclr_copyBuffer) of the same run."""
+    import csv
+    import glob
+
+    def per_kernel(d, counter):
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)[0]
+        vals = {}
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    copy = [k for k in fetch if "copyBuffer" in k]
+    attn = [k for k in fetch if "mla_mfma_kernel" in k or "gqa_mfma_kernel" in k or "gqa_valu_kernel" in k]
+    assert copy and attn, (list(fetch), "need the copy probe and an attention kernel")
+    kib = COPY_PROBE_BYTES / 1024.0
+    cf = max(fetch[copy[0]]) / kib        # the probe is the largest copy
+    cw = max(write[copy[0]]) / kib
+    k = attn[0]
+    f_kib = float(np.median(fetch[k]))
+    w_kib = float(np.median(write[k]))
+    kern = "mla_mfma" if "mla" in k else ("gqa_mfma" if "gqa_mfma" in k else "gqa_valu")
+    hbm = (f_kib / cf + w_kib / cw) * 1024.0
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    db = json.load(open(path)) if os.path.exists(path) else {}
+    db[f"{kern}:{workload}"] = {
+        "source_hash": source_hash(kern), "kernel": k, "fetch_kib_per_launch": f_kib,
+        "write_kib_per_launch": w_kib, "copy_fetch_factor": cf, "copy_write_factor": cw,
+        "hbm_bytes_per_launch": hbm, "launches": len(fetch[k])}
+    with open(path, "w") as fh:
+        json.dump(db, fh, indent=1, sort_keys=True)
+    print(json.dumps(db[f"{kern}:{workload}"]))
 
 
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -181,6 +233,12 @@ def main():
     o_out = torch.empty(info.total_rows, w.head_dim_v, dtype=torch.float32, device=dev)
     lse_out = torch.empty(info.total_rows, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
+    if args.traffic_probe:
+        src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step():
         skv.decode_attn_partial(q, k, v, pt, sl, plan, w.scale, o_part=o_part, lse_part=lse_part)

@@ -35,7 +35,7 @@ What the pages fix (LiquidCP, section 5.2 "Critical-wave KV splitting"):
   total splits; reduction runs of output vectors are the largest run in
   {1, h_q, 2h_q, 4h_q, min(8h_q, 32)} that leaves at least 0.8 x (warps) tasks.
 
-Readings where the pages are silent (each listed in the design notes):
+Readings where the pages are silent:
 
 * Reference plan: the pages use FA3's native heuristic, which they do not give.
   It is replaced by a work-proportional plan s_b = clamp(floor(R K n_b / W + 1/2),
