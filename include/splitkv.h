@@ -105,10 +105,7 @@ typedef struct skv_plan_params {
   int32_t use_calibration;    /* 1: take rho, delta_attn, delta_red and gamma from
                                  the library's MI355X fit for the kernel the
                                  problem selects (the fields below are ignored) */
-  int32_t ref_waves;          /* the stand-in reference plan (used when no
-                                 ref_splits are given) aims at ref_waves * K
-                                 tasks of equal work; its counts bound the search */
-  int32_t reserved;
+  int32_t reserved[2];
   double rho;                 /* per-tile time floor                             */
   double delta_attn;          /* per attention task overhead, tile-equivalents   */
   double delta_red;           /* per reduction overhead                          */
@@ -135,11 +132,10 @@ typedef struct skv_plan_info {
   double nosplit_score;       /* model completion time of NoSplit                */
   double rho, delta_attn, delta_red, gamma;  /* model parameters in effect        */
   double tile_time_us;        /* microseconds per model unit (calibration)       */
-  int32_t ref_waves;
-  int32_t reserved;
+  int32_t reserved, reserved2;
 } skv_plan_info;
 
-/* Fill p with the library defaults: use_calibration = 1, ref_waves = 4, tile 64,
+/* Fill p with the library defaults: use_calibration = 1, tile 64,
  * max_splits 64, min_gain 0.10, and the pages' Table 2 (H100) values in rho,
  * delta_attn, delta_red and gamma, which apply when use_calibration is 0. */
 void skv_plan_params_default(skv_plan_params* p);
@@ -151,7 +147,6 @@ void skv_plan_params_default(skv_plan_params* p);
  * num_cu      compute units of the device (256 on MI355X).
  * n_ext       external states that the merge will add to every row (model cost).
  * params      host or NULL (defaults). ref_splits host int32 [batch] or NULL:
- *             the reference plan compared against (NULL: work-proportional).
  * out         receives a new plan; release it with skv_plan_destroy.
  * Split boundaries are multiples of tile_tokens; the last split ends at L_b. */
 skv_status skv_plan_splits(const skv_attn_desc* desc, const int32_t* seq_lens,

@@ -38,10 +38,12 @@ What the pages fix (LiquidCP, section 5.2 "Critical-wave KV splitting"):
 Readings where the pages are silent:
 
 * Reference plan: the pages use FA3's native heuristic, which they do not give.
-  It is replaced by a work-proportional plan s_b = clamp(floor(R K n_b / W + 1/2),
-  1, min(n_b, max_splits)) with n_b the tile count of request b, W the total
-  tile-work of the batch and R = ref_waves the number of waves of K tasks it aims
-  at; callers may inject an explicit reference plan instead.
+  FA3 splits every sequence of a batch the same number of times (Figure 8's
+  FA3-derived plan (3, 3, 1) is one count, capped by the 2-tile request). The
+  stand-in is that form: one batch-wide count u, request b gets min(u, n_b,
+  max_splits) splits, and u in 1..max_splits is the one with the best model
+  score (ties: the pages' keys, then the smaller u). Callers may inject an
+  explicit reference plan instead.
 * A split of n tiles into s parts gives the first (n mod s) parts ceil(n/s)
   tiles and the rest floor(n/s) (Figure 8 splits 176 tiles as 59, 59, 58).
 * One attention task per (request, KV head, query token, split); the pages fix
@@ -73,7 +75,6 @@ class Params:
     max_splits: int = 64
     min_gain: float = 0.10
     overlap_reduction: int = 0
-    ref_waves: int = 1          # waves of K tasks the stand-in reference plan aims at
 
 
 @dataclass
@@ -247,16 +248,21 @@ def simulate(pb: Problem, prm: Params, splits) -> Evaluation:
     return Evaluation(tuple(splits), score, t_attn, len(tasks), sum(splits), tail)
 
 
-def reference_plan(pb: Problem, prm: Params):
-    """Work-proportional stand-in for the pages' FA3-derived reference plan."""
+def uniform_plan(pb: Problem, prm: Params, u: int):
+    """One batch-wide split count u, capped per request by its tiles and max_splits."""
     T = prm.tile_tokens
-    nt = [n_tiles(L, T) for L in pb.seq_lens]
-    work = sum(nt[b] * pb.q_lens[b] * pb.num_kv_heads for b in range(len(nt)))
-    out = []
-    for b in range(len(nt)):
-        x = math.floor(prm.ref_waves * prm.slots * nt[b] / work + 0.5) if work > 0 else 1
-        out.append(max(1, min(x, nt[b], prm.max_splits)))
-    return out
+    return [max(1, min(u, n_tiles(L, T), prm.max_splits)) for L in pb.seq_lens]
+
+
+def reference_plan(pb: Problem, prm: Params):
+    """Stand-in for the pages' FA3-derived reference plan: the batch-wide count
+    with the best model score."""
+    best, best_u = None, 1
+    for u in range(1, prm.max_splits + 1):
+        ev = simulate(pb, prm, uniform_plan(pb, prm, u))
+        if best is None or ev.key() < best.key():
+            best, best_u = ev, u
+    return uniform_plan(pb, prm, best_u)
 
 
 def split_limits(pb: Problem, prm: Params, ref):

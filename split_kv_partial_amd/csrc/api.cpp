@@ -103,7 +103,6 @@ ModelParams model_params(const skv_attn_desc& d, int num_cu, const skv_plan_para
                                            : std::max(1, vs.merge_waves_per_cu / spc);
   m.max_splits = p->max_splits;
   m.overlap_reduction = p->overlap_reduction;
-  m.ref_waves = p->ref_waves;
   m.min_gain = p->min_gain;
   if (p->use_calibration) {
     const Calibration c = calibration(pick_variant(d));
@@ -127,7 +126,6 @@ skv_status check_params(const skv_plan_params* p) {
   if (p->tile_tokens != kTileTokens) return fail(SKV_ERR_UNSUPPORTED, "tile_tokens must be 64");
   if (p->max_splits < 1 || p->max_splits > 64) return fail(SKV_ERR_INVALID_ARG, "max_splits must be in [1, 64]");
   if (p->slots_per_cu < 0 || p->warps_per_slot < 0) return fail(SKV_ERR_INVALID_ARG, "negative slot counts");
-  if (p->ref_waves < 1 || p->ref_waves > 64) return fail(SKV_ERR_INVALID_ARG, "ref_waves must be in [1, 64]");
   if (p->use_calibration != 0 && p->use_calibration != 1)
     return fail(SKV_ERR_INVALID_ARG, "use_calibration must be 0 or 1");
   if (p->overlap_reduction != 0 && p->overlap_reduction != 1)
@@ -271,7 +269,6 @@ void skv_plan_params_default(skv_plan_params* p) {
   p->max_splits = 64;
   p->overlap_reduction = 0;
   p->use_calibration = 1;
-  p->ref_waves = 4;
   p->rho = 0.43;
   p->delta_attn = 32.0;
   p->delta_red = 2.5;
@@ -407,8 +404,8 @@ skv_status skv_plan_get_info(const skv_plan* pl, skv_plan_info* info) {
   info->delta_red = pl->prm.delta_red;
   info->gamma = pl->prm.gamma;
   info->tile_time_us = pl->prm.tile_time_us;
-  info->ref_waves = pl->prm.ref_waves;
   info->reserved = 0;
+  info->reserved2 = 0;
   return SKV_OK;
 }
 

@@ -52,7 +52,6 @@ struct ModelParams {
   int warps_per_slot = 4;
   int max_splits = 64;
   int overlap_reduction = 0;
-  int ref_waves = 1;
   double rho = 0.43, delta_attn = 32.0, delta_red = 2.5, gamma = 0.47;
   double min_gain = 0.10, tile_time_us = 1.08;
 };

@@ -253,24 +253,35 @@ static bool key_less(const Evaluation& a, const Evaluation& b) {
          std::tie(b.score, b.t_attn, b.n_tasks, b.total_splits);
 }
 
-// Work-proportional stand-in for the pages' FA3-derived reference plan (the
-// pages do not give FA3's heuristic).
-std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
+static std::vector<int> uniform_plan(const Problem& pb, const ModelParams& prm, int u) {
   const int B = (int)pb.seq_lens.size();
-  std::vector<int64_t> nt(B);
-  int64_t work = 0;
-  for (int b = 0; b < B; ++b) {
-    nt[b] = n_tiles(pb.seq_lens[b], prm.tile_tokens);
-    work += nt[b] * pb.q_lens[b] * pb.num_kv_heads;
-  }
   std::vector<int> out(B);
-  for (int b = 0; b < B; ++b) {
-    int64_t x = 1;
-    if (work > 0)
-      x = (int64_t)std::floor((double)((int64_t)prm.ref_waves * prm.slots * nt[b]) / (double)work + 0.5);
-    out[b] = (int)std::max<int64_t>(1, std::min<int64_t>({x, nt[b], (int64_t)prm.max_splits}));
-  }
+  for (int b = 0; b < B; ++b)
+    out[b] = (int)std::max<int64_t>(
+        1, std::min<int64_t>({(int64_t)u, n_tiles(pb.seq_lens[b], prm.tile_tokens), (int64_t)prm.max_splits}));
   return out;
+}
+
+// Stand-in for the pages' FA3-derived reference plan (FA3's heuristic is not
+// given): one batch-wide split count, capped per request by its tiles, chosen
+// by the model among 1..max_splits (ties: the pages' keys, then the smaller
+// count). Counts are simulated on worker threads; the pick is sequential.
+std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
+  const int U = prm.max_splits;
+  std::vector<Evaluation> evs(U);
+  const unsigned nthreads = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
+  {
+    std::vector<std::thread> pool;
+    for (unsigned t = 0; t < nthreads; ++t)
+      pool.emplace_back([&, t]() {
+        for (int u = 1 + (int)t; u <= U; u += (int)nthreads) evs[u - 1] = simulate(pb, prm, uniform_plan(pb, prm, u));
+      });
+    for (auto& th : pool) th.join();
+  }
+  int best_u = 1;
+  for (int u = 2; u <= U; ++u)
+    if (key_less(evs[u - 1], evs[best_u - 1])) best_u = u;
+  return uniform_plan(pb, prm, best_u);
 }
 
 std::vector<int> split_limits(const Problem& pb, const ModelParams& prm,

@@ -33,7 +33,7 @@ def test_defaults_are_the_papers_table2():
     p = skv.default_params()
     assert (p.rho, p.delta_attn, p.delta_red, p.gamma) == (0.43, 32.0, 2.5, 0.47)
     assert p.tile_tokens == 64 and p.max_splits == 64 and abs(p.min_gain - 0.10) < 1e-15
-    assert p.use_calibration == 1 and p.ref_waves == 4
+    assert p.use_calibration == 1
 
 
 def test_calibration_switch():
@@ -43,7 +43,7 @@ def test_calibration_switch():
     inf = skv.plan_splits([5000, 7000], spec, 8, params=p).info()
     assert (inf.rho, inf.delta_attn, inf.delta_red, inf.gamma) == (0.43, 32.0, 2.5, 0.47)
     inf = skv.plan_splits([5000, 7000], spec, 8).info()
-    assert inf.rho > 0 and inf.delta_attn >= 0 and inf.ref_waves == 4
+    assert inf.rho > 0 and inf.delta_attn >= 0
 
 
 SPEC = skv.AttnSpec(num_q_heads=8, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16)
