@@ -521,23 +521,33 @@ const char* skv_last_error(void) { return g_last_error.c_str(); }
 namespace skv {
 VariantShape variant_shape(Variant v) {
   switch (v) {
-    case Variant::GqaValu: return {2, 16};
+    case Variant::GqaValu: return {4, 16};
     case Variant::GqaMfma: return {2, 16};
     default: return {1, 16};
   }
 }
 
-// Critical-wave parameters for each kernel on MI355X. GQA: least-squares fit of
-// the model's attention completion to measured kernel times over plans with 1
-// to 16 splits per request (the procedure of the pages' appendix A.2, applied
-// to whole-kernel times; time unit = one 64-token tile per slot with all slots
-// busy). MLA: a work-group's tile rate is set by its own matrix and LDS work,
-// not by shared HBM, so a lone work-group is no faster than one in a full
-// wave (rho = 1), and the per-task overhead is small (Q load, epilogue).
+// Critical-wave parameters for each kernel on MI355X (the pages' appendix A.2
+// fits them per platform; here they are fitted per kernel to whole-kernel
+// times of plans with 1 to 64 splits per request).
+//  - GQA matrix-core kernel: least-squares fit over the 32-request,
+//    4K-32K-token shape (time unit = one 64-token tile per slot with all
+//    slots busy).
+//  - GQA vector kernel: four work-groups share a CU (128 registers per lane
+//    for a group of 8 heads), so a CU holds four slots. A work-group alone on
+//    a CU is bound by its own load-then-compute chain and runs only about
+//    twice as fast as in a full wave; the fit over the skewed 256-request
+//    batch (8 requests of 262,144 tokens) cannot follow both the lone and the
+//    loaded regime with the model's single floor, so rho is taken from the
+//    loaded side (0.8), which places the long requests' split count where the
+//    measured kernel time is lowest.
+//  - MLA: a work-group's tile rate is set by its own matrix and LDS work, not
+//    by shared HBM, so a lone work-group is no faster than one in a full wave
+//    (rho = 1), and the per-task overhead is small (Q load, epilogue).
 Calibration calibration(Variant v) {
   switch (v) {
     case Variant::GqaMfma: return {0.50, 3.0, 1.0, 0.47, 2.66};
-    case Variant::GqaValu: return {0.50, 3.0, 1.0, 0.47, 2.66};
+    case Variant::GqaValu: return {0.80, 1.0, 1.0, 0.47, 4.8};
     default: return {1.00, 2.0, 1.0, 0.47, 7.4};
   }
 }

@@ -64,16 +64,62 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 // Butterfly reductions over the 64 lanes of a wave (every lane gets the result).
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-  return v;
+// Cross-lane reductions without LDS traffic. All 64 lanes must be active.
+// DPP steps combine lanes within a 16-lane row (swap neighbours, swap pairs,
+// mirror within 8, mirror within 16); the gfx950 lane-swap instructions then
+// exchange whole rows (lane i with lane i^16, and lane i with lane i^32). Each
+// step combines two values that every lane of the pair sees in the same
+// order up to commutation, so the result is bit-identical in all lanes.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
+constexpr int kDppSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppSwap2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- lane 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <- lane 15-i within 16
+
+struct LanePair {
+  float a, b;  // the lane's own value and its partner's, in lane-independent order
+};
+__device__ __forceinline__ LanePair pair16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
+__device__ __forceinline__ LanePair pair32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return {__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const LanePair p = pair16(v);
+  return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const LanePair p = pair32(v);
+  return fmaxf(p.a, p.b);
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const LanePair p = pair16(v);
+  return p.a + p.b;
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const LanePair p = pair32(v);
+  return p.a + p.b;
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<kDppSwap1>(v));
+  v = fmaxf(v, dpp_f<kDppSwap2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  return fmaxf(v, dpp_f<kDppMirror>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<kDppSwap1>(v);
+  v += dpp_f<kDppSwap2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  return v + dpp_f<kDppMirror>(v);
+}
+__device__ __forceinline__ float wave_max(float v) { return max_xor32(max_xor16(row_max16(v))); }
+__device__ __forceinline__ float wave_sum(float v) { return sum_xor32(sum_xor16(row_sum16(v))); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }

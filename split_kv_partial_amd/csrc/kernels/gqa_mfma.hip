@@ -134,8 +134,7 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
   float mt = sv[0];
 #pragma unroll
   for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
-  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  mt = max_xor32(max_xor16(mt));
   const float mn = fmaxf(st.m, mt);
   const float alpha = fast_exp2(st.m - mn);
   st.m = mn;
@@ -233,8 +232,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // Merge the four waves' states: sum l over the 4 lanes of each head first.
   float l = st.l;
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = sum_xor32(sum_xor16(l));
   if (c.g == 0) {
     m_lds[wave][c.r16] = st.m;
     l_lds[wave][c.r16] = l;

@@ -166,53 +166,56 @@ __global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
       if (pid < 0 || pid >= a.num_pages) continue;  // flagged in the score pass
       const int slot = tok & (P - 1);
       const int nvalid = min(16, end - tok);
+      // Value runs of all the lane's dimensions first, then heads outer and
+      // dimensions inner, so each head's weights are read from LDS once per run.
+      uint32_t vw[DL][kBf16 ? 8 : 16];
 #pragma unroll
       for (int k = 0; k < DL; ++k) {
         const int d = lane + 64 * k;
         const T* vp = static_cast<const T*>(a.v) + (((int64_t)pid * a.H_kv + t.kvh) * D + d) * P + slot;
-        if constexpr (kBf16) {
-          u32x4_t v0 = *reinterpret_cast<const u32x4_t*>(vp);
-          u32x4_t v1 = *reinterpret_cast<const u32x4_t*>(vp + 8);
-          uint32_t vw[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-          if (nvalid < 16) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t lo_ok = (2 * e < nvalid) ? 0x0000FFFFu : 0u;
-              const uint32_t hi_ok = (2 * e + 1 < nvalid) ? 0xFFFF0000u : 0u;
-              vw[e] &= (lo_ok | hi_ok);
-            }
+        for (int q4 = 0; q4 < (kBf16 ? 2 : 4); ++q4) {
+          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp + q4 * (16 / sizeof(T)));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vw[k][4 * q4 + e] = x[e];
+        }
+        if (nvalid < 16) {   // zero values past `end` (poisoned or foreign slots)
+          if constexpr (kBf16) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              vw[k][e] &= ((2 * e < nvalid) ? 0x0000FFFFu : 0u) | ((2 * e + 1 < nvalid) ? 0xFFFF0000u : 0u);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) vw[k][e] = e < nvalid ? vw[k][e] : 0u;
           }
+        }
+      }
 #pragma unroll
-          for (int h = 0; h < G; ++h) {
+      for (int h = 0; h < G; ++h) {
+        if constexpr (kBf16) {
+          const u32x4_t* ph = reinterpret_cast<const u32x4_t*>(&p16_lds[wave][0][h][c16]);
+          const u32x4_t* pl = reinterpret_cast<const u32x4_t*>(&p16_lds[wave][1][h][c16]);
+          const u32x4_t h0 = ph[0], h1 = ph[1], l0 = pl[0], l1 = pl[1];
+          const uint32_t hw[8] = {h0[0], h0[1], h0[2], h0[3], h1[0], h1[1], h1[2], h1[3]};
+          const uint32_t lw[8] = {l0[0], l0[1], l0[2], l0[3], l1[0], l1[1], l1[2], l1[3]};
+#pragma unroll
+          for (int k = 0; k < DL; ++k) {
             float acc = o[h][k];
-            const uint32_t* ph = reinterpret_cast<const uint32_t*>(&p16_lds[wave][0][h][c16]);
-            const uint32_t* pl = reinterpret_cast<const uint32_t*>(&p16_lds[wave][1][h][c16]);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              acc = dot2_bf16(ph[e], vw[e], acc);
-              acc = dot2_bf16(pl[e], vw[e], acc);
+              acc = dot2_bf16(hw[e], vw[k][e], acc);
+              acc = dot2_bf16(lw[e], vw[k][e], acc);
             }
             o[h][k] = acc;
           }
         } else {
-          float vv[16];
+          const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(&p_lds[wave][h][c16]);
+          const f32x4_t p4[4] = {pp[0], pp[1], pp[2], pp[3]};
 #pragma unroll
-          for (int e4 = 0; e4 < 4; ++e4) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(vp + 4 * e4);
-            vv[4 * e4 + 0] = x[0];
-            vv[4 * e4 + 1] = x[1];
-            vv[4 * e4 + 2] = x[2];
-            vv[4 * e4 + 3] = x[3];
-          }
-          if (nvalid < 16) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) vv[e] = e < nvalid ? vv[e] : 0.f;
-          }
-#pragma unroll
-          for (int h = 0; h < G; ++h) {
+          for (int k = 0; k < DL; ++k) {
             float acc = o[h][k];
 #pragma unroll
-            for (int e = 0; e < 16; ++e) acc = fmaf(p_lds[wave][h][c16 + e], vv[e], acc);
+            for (int e = 0; e < 16; ++e) acc = fmaf(p4[e >> 2][e & 3], __uint_as_float(vw[k][e]), acc);
             o[h][k] = acc;
           }
         }

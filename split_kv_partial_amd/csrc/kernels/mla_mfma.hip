@@ -257,8 +257,7 @@ void mla_mfma_kernel(MlaArgs a) {
         }
       float mt = fmaxf(fmaxf(fmaxf(s[0][hb][0], s[0][hb][1]), fmaxf(s[0][hb][2], s[0][hb][3])),
                        fmaxf(fmaxf(s[1][hb][0], s[1][hb][1]), fmaxf(s[1][hb][2], s[1][hb][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = max_xor32(max_xor16(mt));
       if (mt > m[hb] + 8.f) {   // also true on the first tile (m = -inf)
         alpha[hb] = fast_exp2(m[hb] - mt);
         l[hb] *= alpha[hb];
@@ -310,8 +309,7 @@ void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
     float lt = l[hb];
-    lt += __shfl_xor(lt, 16, 64);
-    lt += __shfl_xor(lt, 32, 64);
+    lt = sum_xor32(sum_xor16(lt));
     const int head = 32 * hg + 16 * hb + n;
     if (head >= a.H_q) continue;
     const bool empty = m[hb] == -INFINITY;
