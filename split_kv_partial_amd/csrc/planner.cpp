@@ -15,8 +15,13 @@
 // (this file is built without floating-point contraction) so the scores are
 // reproducible bit for bit.
 #include <algorithm>
+#include <atomic>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
 #include <cmath>
 #include <cstdint>
+#include <map>
 #include <numeric>
 #include <queue>
 #include <thread>
@@ -126,116 +131,184 @@ int reduction_run(const Problem& pb, const ModelParams& prm) {
 
 namespace {
 
-// Min-heap entries ordered exactly like the reference's tuples.
-struct Running {
-  double fw;
-  int slot;
-  int64_t idx;
-  bool operator>(const Running& o) const {
-    return std::tie(fw, slot, idx) > std::tie(o.fw, o.slot, o.idx);
-  }
+// Slots are identical and warps are identical, so the simulation tracks
+// multisets of times rather than which slot or warp holds what: which of several
+// equally early slots takes the next task changes no time in the model. Tasks
+// that start together with equal costs finish together and are kept as one
+// group. Every time is computed with the same double operations in the same
+// order as a per-task, per-slot event simulation, so the results are equal bit
+// for bit.
+struct Group {
+  double fw;     // work-clock value at which the group's tasks finish
+  int64_t n;     // tasks in the group
+  bool operator>(const Group& o) const { return fw > o.fw; }
 };
-struct Warp {
-  double avail;
-  int slot, w;
-  bool operator>(const Warp& o) const {
-    return std::tie(avail, slot, w) > std::tie(o.avail, o.slot, o.w);
-  }
+
+struct SimScratch {
+  std::vector<double> cost;       // attention task costs in queue order
+  std::vector<int32_t> req;       // request of each queued task
+  std::vector<double> fifo_cost;
+  std::vector<int32_t> fifo_req;
+  std::vector<uint32_t> order;
+  std::vector<double> done_fw, ev_fw, ev_t, done;
+  std::vector<Group> heap;
 };
-template <class T>
-using MinHeap = std::priority_queue<T, std::vector<T>, std::greater<T>>;
+
+// Queue of attention tasks (cost and request), in the order build_tasks gives.
+static void queue_costs(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits,
+                        SimScratch& sc) {
+  const int T = prm.tile_tokens;
+  const int B = (int)pb.seq_lens.size();
+  bool any_split = false, decode_only = true;
+  for (int b = 0; b < B; ++b) {
+    any_split |= splits[b] > 1;
+    decode_only &= is_decode(pb.q_lens[b]);
+  }
+  sc.fifo_cost.clear();
+  sc.fifo_req.clear();
+  for (int b = 0; b < B; ++b) {
+    const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
+    const int64_t total = n_tiles(L, T);
+    const int s = splits[b];
+    for (int64_t qi = 0; qi < n; ++qi) {
+      const int64_t vis = pb.causal ? L - n + qi + 1 : L;
+      const int64_t vis_t = n_tiles(vis, T);
+      for (int g = 0; g < pb.num_kv_heads; ++g) {
+        // the same tile split as split_ranges: the first total mod s parts
+        // are one tile longer
+        int64_t lo_t = 0;
+        for (int r = 0; r < s; ++r) {
+          const int64_t len = total / s + (r < total % s ? 1 : 0);
+          const int64_t hi_t = lo_t + len;
+          const int64_t nt = std::max<int64_t>(0, std::min(hi_t, vis_t) - lo_t);
+          sc.fifo_cost.push_back((double)nt + prm.delta_attn);
+          sc.fifo_req.push_back(b);
+          lo_t = hi_t;
+        }
+      }
+    }
+  }
+  const size_t N = sc.fifo_cost.size();
+  sc.order.resize(N);
+  std::iota(sc.order.begin(), sc.order.end(), 0u);
+  if (decode_only && any_split) {
+    const double* c = sc.fifo_cost.data();
+    std::stable_sort(sc.order.begin(), sc.order.end(), [c](uint32_t x, uint32_t y) { return c[x] > c[y]; });
+  } else if (!decode_only) {
+    const int32_t* r = sc.fifo_req.data();
+    std::stable_partition(sc.order.begin(), sc.order.end(),
+                          [&](uint32_t x) { return !is_decode(pb.q_lens[r[x]]); });
+  }
+  sc.cost.resize(N);
+  sc.req.resize(N);
+  for (size_t i = 0; i < N; ++i) {
+    sc.cost[i] = sc.fifo_cost[sc.order[i]];
+    sc.req[i] = sc.fifo_req[sc.order[i]];
+  }
+}
 
 }  // namespace
 
 Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits) {
+  thread_local SimScratch sc;
   const int B = (int)pb.seq_lens.size();
-  const int K = prm.slots;
-  std::vector<std::vector<std::pair<int64_t, int64_t>>> ranges(B);
-  for (int b = 0; b < B; ++b) ranges[b] = split_ranges(pb.seq_lens[b], splits[b], prm.tile_tokens);
-  std::vector<TaskDesc> tasks;
-  std::vector<double> cost;
-  build_tasks(pb, prm, ranges, tasks, &cost);
-  const int64_t nt = (int64_t)tasks.size();
+  const int64_t K = prm.slots;
+  queue_costs(pb, prm, splits, sc);
+  const int64_t nt = (int64_t)sc.cost.size();
+  const double* cost = sc.cost.data();
+  const int32_t* req = sc.req.data();
 
+  // ---- attention phase ----
+  sc.done_fw.assign(B, 0.0);
+  sc.ev_fw.clear();
+  sc.ev_t.clear();
+  sc.heap.clear();
+  std::map<double, int64_t> release;  // slot release times (for overlapped reductions)
+  auto heap_push = [&](double fw, int64_t n) {
+    sc.heap.push_back({fw, n});
+    std::push_heap(sc.heap.begin(), sc.heap.end(), std::greater<Group>());
+  };
   double t = 0.0, vw = 0.0;
-  MinHeap<Running> running;
-  MinHeap<int> free_slots;
-  for (int s = 0; s < K; ++s) free_slots.push(s);
-  std::vector<double> done(B, 0.0), release(K, 0.0);
-  int64_t nxt = 0;
-  while (!free_slots.empty() && nxt < nt) {
-    int s = free_slots.top();
-    free_slots.pop();
-    running.push({vw + cost[nxt], s, nxt});
-    ++nxt;
-  }
-  std::vector<int> freed;
-  while (!running.empty()) {
-    const double tau = std::max(prm.rho, (double)running.size() / (double)K);
-    const double fw = running.top().fw;
+  int64_t running = 0, nxt = 0;
+  // start up to `free_slots` queued tasks at work clock vw; returns how many started
+  auto start_tasks = [&](int64_t free_slots) {
+    int64_t started = 0;
+    while (started < free_slots && nxt < nt) {
+      const double c = cost[nxt];
+      int64_t j = nxt + 1;
+      const int64_t lim = nxt + (free_slots - started);
+      while (j < lim && j < nt && cost[j] == c) ++j;
+      const double fw = vw + c;
+      for (int64_t i = nxt; i < j; ++i)
+        if (fw > sc.done_fw[req[i]]) sc.done_fw[req[i]] = fw;
+      heap_push(fw, j - nxt);
+      started += j - nxt;
+      nxt = j;
+    }
+    running += started;
+    return started;
+  };
+  start_tasks(K);
+  if (K > nt) release[0.0] += (K - nt) * prm.warps_per_slot;
+  while (!sc.heap.empty()) {
+    const double tau = std::max(prm.rho, (double)running / (double)K);
+    const double fw = sc.heap.front().fw;
     t = t + (fw - vw) * tau;
     vw = fw;
-    freed.clear();
-    while (!running.empty() && running.top().fw == fw) {
-      Running r = running.top();
-      running.pop();
-      const int b = tasks[r.idx].b;
-      if (t > done[b]) done[b] = t;
-      freed.push_back(r.slot);
+    int64_t m = 0;
+    while (!sc.heap.empty() && sc.heap.front().fw == fw) {
+      m += sc.heap.front().n;
+      std::pop_heap(sc.heap.begin(), sc.heap.end(), std::greater<Group>());
+      sc.heap.pop_back();
     }
-    for (int s : freed) free_slots.push(s);
-    while (!free_slots.empty() && nxt < nt) {
-      int s = free_slots.top();
-      free_slots.pop();
-      running.push({vw + cost[nxt], s, nxt});
-      ++nxt;
-    }
-    for (int s : freed) release[s] = t;
+    running -= m;
+    sc.ev_fw.push_back(fw);
+    sc.ev_t.push_back(t);
+    const int64_t started = start_tasks(m);
+    if (m > started) release[t] += (m - started) * prm.warps_per_slot;
   }
   const double t_attn = t;
-
-  // Reduction phase. Warps are claimed earliest-available first (ties by slot,
-  // then warp). Without overlap every warp becomes free at t_attn, when every
-  // request's inputs are ready, so the first K*W units start exactly at t_attn
-  // on warps taken in (slot, warp) order; only later units need the heap.
-  const int run = reduction_run(pb, prm);
-  const int64_t nwarps = (int64_t)K * prm.warps_per_slot;
-  double score = t_attn;
-  // The shortcut needs every claimed warp to end strictly after t_attn, so that
-  // no used warp can tie with an untouched one: the cheapest unit costs at least
-  // delta_red + gamma (v_u >= 1, s_u >= 1).
-  const bool fast = !prm.overlap_reduction && t_attn + (prm.delta_red + prm.gamma) > t_attn;
-  std::vector<Warp> wv;
-  int64_t claimed = 0;
-  MinHeap<Warp> warps;
-  if (!fast) {
-    wv.reserve((size_t)nwarps);
-    for (int s = 0; s < K; ++s)
-      for (int w = 0; w < prm.warps_per_slot; ++w)
-        wv.push_back({prm.overlap_reduction ? release[s] : t_attn, s, w});
-    warps = MinHeap<Warp>(std::greater<Warp>(), std::move(wv));
+  // a request's attention ends at the event of its latest-finishing task
+  sc.done.assign(B, 0.0);
+  for (int b = 0; b < B; ++b) {
+    const double f = sc.done_fw[b];
+    if (f == 0.0) continue;  // no task started (cannot happen: every request has one)
+    const auto it = std::lower_bound(sc.ev_fw.begin(), sc.ev_fw.end(), f);
+    sc.done[b] = sc.ev_t[it - sc.ev_fw.begin()];
   }
+
+  // ---- reduction phase: units in request order, each on the earliest-free warp ----
+  const int run = reduction_run(pb, prm);
+  const int64_t nwarps = K * prm.warps_per_slot;
+  std::map<double, int64_t> warps;
+  if (prm.overlap_reduction)
+    warps = std::move(release);
+  else
+    warps[t_attn] = nwarps;
+  double score = t_attn;
+  auto assign = [&](int64_t k, double c, double d) {
+    while (k > 0) {
+      auto it = warps.begin();
+      const double a = it->first;
+      const int64_t avail = it->second;
+      const double st = a > d ? a : d;
+      const double end = st + c;
+      const int64_t j = std::min(k, avail);
+      if (j == avail)
+        warps.erase(it);
+      else
+        it->second -= j;
+      warps[end] += j;
+      if (end > score) score = end;
+      k -= j;
+    }
+  };
   for (int b = 0; b < B; ++b) {
     const int64_t rows = pb.q_lens[b] * (int64_t)pb.rows_per_token;
     const int64_t s_u = splits[b] + pb.n_ext;
-    for (int64_t start = 0; start < rows;) {
-      const int64_t v = std::min<int64_t>(run, rows - start);
-      const double c = prm.delta_red + prm.gamma * (double)v * (double)s_u;
-      Warp w;
-      if (fast && claimed < nwarps) {
-        // still-untouched warp number `claimed`: available at t_attn
-        w = {t_attn, (int)(claimed / prm.warps_per_slot), (int)(claimed % prm.warps_per_slot)};
-        ++claimed;
-      } else {
-        w = warps.top();
-        warps.pop();
-      }
-      const double st = w.avail > done[b] ? w.avail : done[b];
-      const double end = st + c;
-      warps.push({end, w.slot, w.w});
-      if (end > score) score = end;
-      start += v;
-    }
+    const int64_t full = rows / run, rem = rows % run;
+    if (full > 0) assign(full, prm.delta_red + prm.gamma * (double)run * (double)s_u, sc.done[b]);
+    if (rem > 0) assign(1, prm.delta_red + prm.gamma * (double)rem * (double)s_u, sc.done[b]);
   }
   Evaluation ev;
   ev.splits = splits;
@@ -244,7 +317,7 @@ Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector
   ev.n_tasks = nt;
   ev.total_splits = std::accumulate(splits.begin(), splits.end(), (int64_t)0);
   for (int b = 0; b < B; ++b)
-    if (done[b] == t_attn) ev.tail.push_back(b);
+    if (sc.done[b] == t_attn) ev.tail.push_back(b);
   return ev;
 }
 
@@ -262,6 +335,83 @@ static std::vector<int> uniform_plan(const Problem& pb, const ModelParams& prm, 
   return out;
 }
 
+// Worker threads for independent simulations. The caller takes part; each
+// index is run exactly once and results are written by index, so the outcome
+// does not depend on which thread ran what.
+class SimPool {
+ public:
+  SimPool() {
+    const unsigned hw = std::thread::hardware_concurrency();
+    const unsigned n = std::max(1u, std::min(16u, hw));
+    for (unsigned i = 1; i < n; ++i) workers_.emplace_back([this] { loop(); });
+  }
+  ~SimPool() {
+    {
+      std::lock_guard<std::mutex> g(mu_);
+      stop_ = true;
+    }
+    cv_.notify_all();
+    for (auto& w : workers_) w.join();
+  }
+  size_t threads() const { return workers_.size() + 1; }
+  void run(size_t count, const std::function<void(size_t)>& fn) {
+    if (count == 0) return;
+    if (workers_.empty() || count < 4) {
+      for (size_t i = 0; i < count; ++i) fn(i);
+      return;
+    }
+    {
+      std::lock_guard<std::mutex> g(mu_);
+      fn_ = &fn;
+      count_ = count;
+      next_.store(0);
+      pending_ = count;
+      ++gen_;
+    }
+    cv_.notify_all();
+    work();
+    std::unique_lock<std::mutex> g(mu_);
+    done_cv_.wait(g, [this] { return pending_ == 0; });
+    fn_ = nullptr;
+  }
+
+ private:
+  void work() {
+    size_t finished = 0;
+    for (;;) {
+      const size_t i = next_.fetch_add(1);
+      if (i >= count_) break;
+      (*fn_)(i);
+      ++finished;
+    }
+    if (finished) {
+      std::lock_guard<std::mutex> g(mu_);
+      pending_ -= finished;
+      if (pending_ == 0) done_cv_.notify_all();
+    }
+  }
+  void loop() {
+    uint64_t seen = 0;
+    for (;;) {
+      {
+        std::unique_lock<std::mutex> g(mu_);
+        cv_.wait(g, [&] { return stop_ || gen_ != seen; });
+        if (stop_) return;
+        seen = gen_;
+      }
+      work();
+    }
+  }
+  std::vector<std::thread> workers_;
+  std::mutex mu_;
+  std::condition_variable cv_, done_cv_;
+  const std::function<void(size_t)>* fn_ = nullptr;
+  size_t count_ = 0, pending_ = 0;
+  std::atomic<size_t> next_{0};
+  uint64_t gen_ = 0;
+  bool stop_ = false;
+};
+
 // Stand-in for the pages' FA3-derived reference plan (FA3's heuristic is not
 // given): one batch-wide split count, capped per request by its tiles, chosen
 // by the model among 1..max_splits (ties: the pages' keys, then the smaller
@@ -269,15 +419,8 @@ static std::vector<int> uniform_plan(const Problem& pb, const ModelParams& prm, 
 std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
   const int U = prm.max_splits;
   std::vector<Evaluation> evs(U);
-  const unsigned nthreads = std::max(1u, std::min(16u, std::thread::hardware_concurrency()));
-  {
-    std::vector<std::thread> pool;
-    for (unsigned t = 0; t < nthreads; ++t)
-      pool.emplace_back([&, t]() {
-        for (int u = 1 + (int)t; u <= U; u += (int)nthreads) evs[u - 1] = simulate(pb, prm, uniform_plan(pb, prm, u));
-      });
-    for (auto& th : pool) th.join();
-  }
+  SimPool pool;
+  pool.run((size_t)U, [&](size_t i) { evs[i] = simulate(pb, prm, uniform_plan(pb, prm, (int)i + 1)); });
   int best_u = 1;
   for (int u = 2; u <= U; ++u)
     if (key_less(evs[u - 1], evs[best_u - 1])) best_u = u;
@@ -303,6 +446,7 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
   const std::vector<int> lim = split_limits(pb, prm, ref);
   const Evaluation nosplit = simulate(pb, prm, std::vector<int>(B, 1));
   Evaluation cur = nosplit;
+  SimPool pool;
   for (;;) {
     std::vector<std::vector<int>> cands;
     for (int b = 0; b < B; ++b) {
@@ -324,18 +468,7 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
     // Candidates are independent simulations: evaluate them on worker threads,
     // then pick in candidate order exactly as a sequential loop would.
     std::vector<Evaluation> evs(cands.size());
-    const size_t nthreads =
-        std::min<size_t>(cands.size(), std::max(1u, std::min(16u, std::thread::hardware_concurrency())));
-    if (nthreads <= 1 || cands.size() < 4) {
-      for (size_t i = 0; i < cands.size(); ++i) evs[i] = simulate(pb, prm, cands[i]);
-    } else {
-      std::vector<std::thread> pool;
-      for (size_t t = 0; t < nthreads; ++t)
-        pool.emplace_back([&, t]() {
-          for (size_t i = t; i < cands.size(); i += nthreads) evs[i] = simulate(pb, prm, cands[i]);
-        });
-      for (auto& th : pool) th.join();
-    }
+    pool.run(cands.size(), [&](size_t i) { evs[i] = simulate(pb, prm, cands[i]); });
     bool have = false;
     Evaluation best;
     for (auto& ev : evs) {
