@@ -40,14 +40,14 @@ __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u 
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // float -> bf16 bits, round to nearest even (inputs here are finite or +-inf).
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16 with round-to-nearest-even (the gfx950 packed conversion
+// instruction; NaN stays NaN).
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+typedef float f32x2v_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2v_t{lo, hi}), bf16x2v_t));
 }
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) { return pack_bf16x2(f, 0.f) & 0xFFFFu; }
 
 // Two-term bf16 representation of a softmax weight: p = hi + lo with hi the
 // nearest bf16 and lo the nearest bf16 to the (exact) remainder, so hi + lo
@@ -57,13 +57,17 @@ __device__ __forceinline__ void split_bf16(float p, uint32_t& hi, uint32_t& lo) 
   hi = f32_to_bf16_bits(p);
   lo = f32_to_bf16_bits(p - __uint_as_float(hi << 16));
 }
+// The same split for a pair of weights, packed as two bf16x2 words.
+__device__ __forceinline__ void split_bf16x2(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(p0, p1);
+  lo = pack_bf16x2(p0 - __uint_as_float(hi << 16), p1 - __uint_as_float(hi & 0xFFFF0000u));
+}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// Butterfly reductions over the 64 lanes of a wave (every lane gets the result).
 // Cross-lane reductions without LDS traffic. All 64 lanes must be active.
 // DPP steps combine lanes within a 16-lane row (swap neighbours, swap pairs,
 // mirror within 8, mirror within 16); the gfx950 lane-swap instructions then

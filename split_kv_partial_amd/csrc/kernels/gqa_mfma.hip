@@ -148,13 +148,11 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
   // P^T operand as two bf16 terms (hi + lo): the second product costs matrix
   // throughput that this HBM-bound kernel has to spare, and keeps ~16 bits of
   // each weight instead of 8.
-  uint32_t hb[8], lb[8];
+  uint32_t ph[4], pl[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) split_bf16(p[i], hb[i], lb[i]);
-  const u32x4_t pf_hi = {hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16), hb[4] | (hb[5] << 16),
-                         hb[6] | (hb[7] << 16)};
-  const u32x4_t pf_lo = {lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16), lb[4] | (lb[5] << 16),
-                         lb[6] | (lb[7] << 16)};
+  for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
+  const u32x4_t pf_hi = {ph[0], ph[1], ph[2], ph[3]};
+  const u32x4_t pf_lo = {pl[0], pl[1], pl[2], pl[3]};
   // values past `end` (the split's end, or poisoned slots of the last page)
   // are zeroed so that 0 * NaN cannot reach the accumulator
   if (tail) {

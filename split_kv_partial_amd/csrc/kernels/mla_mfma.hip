@@ -245,19 +245,22 @@ void mla_mfma_kernel(MlaArgs a) {
     u32x4_t pf[2];
     float alpha[2] = {1.f, 1.f};
     bool bump = false;
+    if (tail) {   // tokens at or past `end` take no part: score -inf, weight 0
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (t0 + 8 * g + 4 * blk + e >= end) s[blk][hb][e] = -INFINITY;
+    }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
-      // scale in place; masked tokens become -inf
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x = s[blk][hb][e] * a.scale_log2;
-          s[blk][hb][e] = (!tail || t0 + 8 * g + 4 * blk + e < end) ? x : -INFINITY;
-        }
+      // the maximum of the raw scores, scaled (scaling by a positive factor
+      // and rounding are monotone, so this is the maximum of the scaled scores)
       float mt = fmaxf(fmaxf(fmaxf(s[0][hb][0], s[0][hb][1]), fmaxf(s[0][hb][2], s[0][hb][3])),
                        fmaxf(fmaxf(s[1][hb][0], s[1][hb][1]), fmaxf(s[1][hb][2], s[1][hb][3])));
-      mt = max_xor32(max_xor16(mt));
+      mt = max_xor32(max_xor16(mt)) * a.scale_log2;
       if (mt > m[hb] + 8.f) {   // also true on the first tile (m = -inf)
         alpha[hb] = fast_exp2(m[hb] - mt);
         l[hb] *= alpha[hb];
@@ -269,7 +272,7 @@ void mla_mfma_kernel(MlaArgs a) {
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s[blk][hb][e] = fast_exp2(s[blk][hb][e] - m[hb]);
+          s[blk][hb][e] = fast_exp2(fmaf(s[blk][hb][e], a.scale_log2, -m[hb]));
           ps += s[blk][hb][e];
         }
       l[hb] += ps;
