@@ -23,7 +23,7 @@ RAGGED = [1, 31, 32, 33, 63, 64, 65, 200, 1000, 2049]
 
 
 @pytest.mark.parametrize("sharp", [False, True])
-@pytest.mark.parametrize("P", [64, 16])
+@pytest.mark.parametrize("P", [64, 32, 16])
 def test_mla_ragged(sharp, P):
     w = mla(RAGGED, P=P, q_scale=wl.SHARP_MLA if sharp else 1.0, seed=P + sharp)
     rng = np.random.default_rng(P)
