@@ -213,16 +213,24 @@ void mla_mfma_kernel(MlaArgs a) {
     // row i of token block blk is token 8(i/4) + 4 blk + i%4, so that a lane's
     // outputs (rows 4g..4g+3 of both blocks) are the 8 consecutive tokens 8g..8g+7
     const uint16_t* krow0 = tile + (n >> 2) * kGS + (n & 3) * kRS + 288 * dh + 8 * g;
+    // Operand reads run one k-step ahead of the matrix instructions that use
+    // them (a two-stage register ring), so LDS latency overlaps the MFMAs.
+    u32x4_t kb[2][2];
+    auto kread = [&](int ks, u32x4_t (&dst)[2]) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+        dst[blk] = *reinterpret_cast<const u32x4_t*>(krow0 + 4 * blk * kRS + 32 * ks);
+    };
+    kread(0, kb[0]);
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
+      if (ks + 1 < kKs) kread(ks + 1, kb[(ks + 1) % 2]);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
-        const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(krow0 + 4 * blk * kRS + 32 * ks);
-        s[blk][0] = mfma16(ka, qf[0][ks], s[blk][0]);
-        s[blk][1] = mfma16(ka, qf[1][ks], s[blk][1]);
+        s[blk][0] = mfma16(kb[ks % 2][blk], qf[0][ks], s[blk][0]);
+        s[blk][1] = mfma16(kb[ks % 2][blk], qf[1][ks], s[blk][1]);
       }
-      // bound how far the scheduler hoists operand reads (register pressure)
-      if (ks % 3 == 2) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     }
     // ---- add the partner wave's half of the scores ----
 #pragma unroll
