@@ -521,7 +521,7 @@ const char* skv_last_error(void) { return g_last_error.c_str(); }
 namespace skv {
 VariantShape variant_shape(Variant v) {
   switch (v) {
-    case Variant::GqaValu: return {4, 16};
+    case Variant::GqaValu: return {8, 16};
     case Variant::GqaMfma: return {2, 16};
     default: return {1, 16};
   }
@@ -534,20 +534,23 @@ VariantShape variant_shape(Variant v) {
 //    4K-32K-token shape (time unit = one 64-token tile per slot with all
 //    slots busy).
 //  - GQA vector kernel: four work-groups share a CU (128 registers per lane
-//    for a group of 8 heads), so a CU holds four slots. A work-group alone on
-//    a CU is bound by its own load-then-compute chain and runs only about
-//    twice as fast as in a full wave; the fit over the skewed 256-request
-//    batch (8 requests of 262,144 tokens) cannot follow both the lone and the
-//    loaded regime with the model's single floor, so rho is taken from the
-//    loaded side (0.8), which places the long requests' split count where the
-//    measured kernel time is lowest.
+//    for a group of 8 heads). A work-group alone on a CU is bound by its own
+//    load-then-compute chain and runs only about twice as fast as in a full
+//    wave. Measured on the skewed 256-request batch (8 requests of 262,144
+//    tokens), kernel time is lowest when the long requests give at least one
+//    full wave of equal long tasks on every CU (16 splits or more) and rises
+//    when a CU ends up with one long task more than its neighbours, which the
+//    model (identical slots, one global rate) does not see. Eight slots per
+//    CU with rho 0.8 and delta_attn 1 make the search split those requests
+//    24 ways, inside the measured optimum; four slots per CU (the occupancy)
+//    stopped at 13 (10% slower).
 //  - MLA: a work-group's tile rate is set by its own matrix and LDS work, not
 //    by shared HBM, so a lone work-group is no faster than one in a full wave
 //    (rho = 1), and the per-task overhead is small (Q load, epilogue).
 Calibration calibration(Variant v) {
   switch (v) {
     case Variant::GqaMfma: return {0.50, 3.0, 1.0, 0.47, 2.66};
-    case Variant::GqaValu: return {0.80, 1.0, 1.0, 0.47, 4.8};
+    case Variant::GqaValu: return {0.80, 1.0, 1.0, 0.47, 11.2};
     default: return {1.00, 2.0, 1.0, 0.47, 7.4};
   }
 }
