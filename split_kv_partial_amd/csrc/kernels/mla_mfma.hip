@@ -106,6 +106,30 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* src, uint16_t* dst) {
       : "memory", "m0");
 }
 
+// The same with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
+// (the instruction's scalar-address form: no 64-bit vector arithmetic).
+__device__ __forceinline__ void lds_dma16_sbase(const uint8_t* base, uint32_t off, uint16_t* dst) {
+  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t*)dst;
+  __asm__ __volatile__(
+      "s_mov_b32 m0, %0\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2"
+      :
+      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
+      : "memory", "m0");
+}
+
+// Byte offset, within a run of 32 consecutive latent rows, of the 16 bytes
+// that slot 64 inst + lane of a tile holds (pad slots: offset 0, a harmless
+// valid read that lands in a slot nothing reads).
+__device__ __forceinline__ uint32_t slot_offset(int inst, int lane) {
+  const int s = 64 * inst + lane;
+  const int grp = s / kGroupSlots, rem = s - grp * kGroupSlots;
+  const int rig = rem / kSlots, ch = rem - rig * kSlots;   // rig = 8 for the group pad
+  const bool data = rig < 8 && ch < kD / 8;
+  return data ? (uint32_t)((8 * grp + rig) * kD * 2 + ch * 16) : 0u;
+}
+
 // Issue this wave's share of the DMA of the 32-token tile at t0 into `tile`.
 // Every slot of the tile is fetched by exactly one lane, so each wave issues a
 // fixed number of DMA instructions per tile (5 for waves 0-5, 4 for 6-7),
@@ -113,20 +137,49 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* src, uint16_t* dst) {
 // slots and rows of an out-of-range page read page 0 instead (always valid);
 // their scores are masked and their values zeroed where they are used. Page ids
 // are wave-uniform scalars: a tile starts at a multiple of 32 tokens, so it
-// spans one page (P >= 32) or two (P = 16).
-__device__ __forceinline__ void issue_tile(const MlaArgs& a, const_i32_t* ptab, int end, int t0,
+// spans one page (P >= 32) or two (P = 16). They are read from the page table
+// one tile ahead of their use (see TilePages), so that the scalar-load latency
+// is not paid at every tile.
+struct TilePages {
+  int pid0, pid1;
+};
+__device__ __forceinline__ TilePages load_pages(const MlaArgs& a, const_i32_t* ptab, int end, int t0) {
+  // the second index does not depend on the first load, so neither load
+  // makes the wave wait before the ids are used
+  const int last = (end - 1) >> a.page_shift;   // never index past the request's pages
+  const int i0 = min(t0 >> a.page_shift, last);
+  const int i1 = (a.page_shift == 4 && t0 + 16 < end) ? min((t0 + 16) >> 4, last) : i0;
+  return TilePages{ptab[i0], ptab[i1]};
+}
+__device__ __forceinline__ void issue_tile(const MlaArgs& a, TilePages pg, int end, int t0,
                                            uint16_t* tile, int wave, int lane) {
   // Recompute the per-lane slot arithmetic at every call: hoisted out of the
   // tile loop it would occupy registers the kernel does not have, and the
   // reload of a spilled address would wait for the DMAs issued before it.
   __asm__ __volatile__("" : "+v"(lane));
   const int P = 1 << a.page_shift;
-  const int pid0 = ptab[t0 >> a.page_shift];
-  const bool two = P == 16 && t0 + 16 < end;
-  const int pid1 = two ? ptab[(t0 + 16) >> a.page_shift] : pid0;
+  const int pid0 = pg.pid0, pid1 = pg.pid1;
   const bool ok0 = pid0 >= 0 && pid0 < a.num_pages;
   const bool ok1 = pid1 >= 0 && pid1 < a.num_pages;
   if ((!ok0 || !ok1) && lane == 0) raise_error(a.err_flag, 1);
+  if (P >= 32) {
+    // The tile is 32 consecutive rows of one page: a scalar base plus the
+    // lane's fixed offset. Rows past `end` are read from the same (valid)
+    // page and masked where they are used.
+    const uint8_t* base = a.kv + (ok0 ? ((int64_t)pid0 * P + (t0 & (P - 1))) * (kD * 2) : 0);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const int inst = wave + kWaves * j;
+      if (inst >= kDmaPerTile) break;   // wave-uniform
+      const uint32_t off = slot_offset(inst, lane);
+      if (inst == kDmaPerTile - 1) {   // the only instruction with lanes past the tile
+        if (64 * inst + lane < kTileSlots) lds_dma16_sbase(base, off, tile + 64 * 8 * inst);
+      } else {
+        lds_dma16_sbase(base, off, tile + 64 * 8 * inst);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
     const int inst = wave + kWaves * j;
@@ -190,8 +243,9 @@ void mla_mfma_kernel(MlaArgs a) {
   // at the first use, inside the tile loop, where it would drain the DMA ring
   __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
   const int ntiles = end > t.lo ? (end - t.lo + kT - 1) / kT : 0;
-  if (ntiles > 0) issue_tile(a, ptab, end, t.lo, ring[0], wave, lane);
-  if (ntiles > 1) issue_tile(a, ptab, end, t.lo + kT, ring[1], wave, lane);
+  if (ntiles > 0) issue_tile(a, load_pages(a, ptab, end, t.lo), end, t.lo, ring[0], wave, lane);
+  if (ntiles > 1) issue_tile(a, load_pages(a, ptab, end, t.lo + kT), end, t.lo + kT, ring[1], wave, lane);
+  TilePages pg_next = load_pages(a, ptab, end, t.lo + 2 * kT);   // pages of tile i + 2
   for (int i = 0; i < ntiles; ++i) {
     const int t0 = t.lo + i * kT;
     // Tile i has landed once at most one newer tile's DMAs are outstanding: a
@@ -203,7 +257,7 @@ void mla_mfma_kernel(MlaArgs a) {
       __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
     // every wave's DMA of tile i is visible; every wave is done with ring[(i+2)%3]
     bare_barrier();
-    if (i + 2 < ntiles) issue_tile(a, ptab, end, t0 + 2 * kT, ring[(i + 2) % 3], wave, lane);
+    if (i + 2 < ntiles) issue_tile(a, pg_next, end, t0 + 2 * kT, ring[(i + 2) % 3], wave, lane);
     const uint16_t* tile = ring[i % 3];
 
     // ---- partial scores over this wave's 288 qk dims ----
@@ -243,6 +297,11 @@ void mla_mfma_kernel(MlaArgs a) {
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) s[blk][hb] += xbuf[wave ^ 1][2 * blk + hb][lane];
+    // page ids for the next iteration's DMA: the scalar loads complete during
+    // the softmax, before the next wait on LDS reads
+    __builtin_amdgcn_sched_barrier(0);   // after the adds have consumed the LDS reads
+    pg_next = load_pages(a, ptab, end, t0 + 3 * kT);   // clamped: always a valid entry
+    __builtin_amdgcn_sched_barrier(0);
 
     // ---- online softmax per head (log2 domain) ----
     // The running reference m only moves when a tile's maximum exceeds it by
