@@ -152,7 +152,7 @@ __device__ __forceinline__ TilePages load_pages(const MlaArgs& a, const_i32_t* p
   return TilePages{ptab[i0], ptab[i1]};
 }
 __device__ __forceinline__ void issue_tile(const MlaArgs& a, TilePages pg, int end, int t0,
-                                           uint16_t* tile, int wave, int lane) {
+                                           uint16_t* tile, int wave, int lane, const uint32_t* soff) {
   // Recompute the per-lane slot arithmetic at every call: hoisted out of the
   // tile loop it would occupy registers the kernel does not have, and the
   // reload of a spilled address would wait for the DMAs issued before it.
@@ -171,7 +171,7 @@ __device__ __forceinline__ void issue_tile(const MlaArgs& a, TilePages pg, int e
     for (int j = 0; j < kDmaPerWave; ++j) {
       const int inst = wave + kWaves * j;
       if (inst >= kDmaPerTile) break;   // wave-uniform
-      const uint32_t off = slot_offset(inst, lane);
+      const uint32_t off = soff[64 * j + lane];
       if (inst == kDmaPerTile - 1) {   // the only instruction with lanes past the tile
         if (64 * inst + lane < kTileSlots) lds_dma16_sbase(base, off, tile + 64 * 8 * inst);
       } else {
@@ -213,6 +213,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2))
 void mla_mfma_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ring[3][kTileSlots * 8];
   __shared__ __attribute__((aligned(16))) f32x4_t xbuf[kWaves][4][64];
+  __shared__ uint32_t soff_lds[kWaves][kDmaPerWave * 64];
 
   const DevTask t = a.tasks[blockIdx.x];
   const int lane = threadIdx.x & 63;
@@ -243,8 +244,13 @@ void mla_mfma_kernel(MlaArgs a) {
   // at the first use, inside the tile loop, where it would drain the DMA ring
   __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
   const int ntiles = end > t.lo ? (end - t.lo + kT - 1) / kT : 0;
-  if (ntiles > 0) issue_tile(a, load_pages(a, ptab, end, t.lo), end, t.lo, ring[0], wave, lane);
-  if (ntiles > 1) issue_tile(a, load_pages(a, ptab, end, t.lo + kT), end, t.lo + kT, ring[1], wave, lane);
+  // the lanes' fixed DMA offsets (used when a page holds 32 or more tokens),
+  // kept in LDS: registers are fully used; each wave reads only its own
+  uint32_t* soff = soff_lds[wave];
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) soff[64 * j + lane] = slot_offset(wave + kWaves * j, lane);
+  if (ntiles > 0) issue_tile(a, load_pages(a, ptab, end, t.lo), end, t.lo, ring[0], wave, lane, soff);
+  if (ntiles > 1) issue_tile(a, load_pages(a, ptab, end, t.lo + kT), end, t.lo + kT, ring[1], wave, lane, soff);
   TilePages pg_next = load_pages(a, ptab, end, t.lo + 2 * kT);   // pages of tile i + 2
   for (int i = 0; i < ntiles; ++i) {
     const int t0 = t.lo + i * kT;
@@ -257,7 +263,7 @@ void mla_mfma_kernel(MlaArgs a) {
       __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
     // every wave's DMA of tile i is visible; every wave is done with ring[(i+2)%3]
     bare_barrier();
-    if (i + 2 < ntiles) issue_tile(a, pg_next, end, t0 + 2 * kT, ring[(i + 2) % 3], wave, lane);
+    if (i + 2 < ntiles) issue_tile(a, pg_next, end, t0 + 2 * kT, ring[(i + 2) % 3], wave, lane, soff);
     const uint16_t* tile = ring[i % 3];
 
     // ---- partial scores over this wave's 288 qk dims ----
