@@ -76,6 +76,19 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       if (k < rq.splits) return a.lse_part[(int64_t)rq.state_row + (int64_t)k * rq.rows + r];
       return a.lse_ext[(int64_t)(k - rq.splits) * a.total_rows + out_row];
     };
+    auto src_of = [&](int k) -> const float* {
+      return k < rq.splits ? a.o_part + ((int64_t)rq.state_row + (int64_t)k * rq.rows + r) * DV
+                           : a.o_ext + ((int64_t)(k - rq.splits) * a.total_rows + out_row) * DV;
+    };
+    // Few states (the common decode case): fetch every state vector together
+    // with the LSEs, so the row costs one memory round trip instead of two.
+    constexpr int kFew = 8;
+    float vf[kFew][N];
+    if (S <= kFew) {
+#pragma unroll
+      for (int k = 0; k < kFew; ++k)
+        if (k < S) VecIO<DV>::load(src_of(k), lane, vf[k]);
+    }
     const float l0 = lane < S ? lse_of(lane) : -INFINITY;
     const float l1 = lane + 64 < S ? lse_of(lane + 64) : -INFINITY;
     const float M = wave_max(fmaxf(l0, l1));
@@ -87,18 +100,26 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
       const float w0 = fast_exp2((l0 - M) * kLog2e);
       const float w1 = fast_exp2((l1 - M) * kLog2e);
       const float Z = wave_sum(w0 + w1);
-      for (int k = 0; k < S; ++k) {
-        const float wk = __int_as_float(
-            __builtin_amdgcn_readlane(__float_as_int(k < 64 ? w0 : w1), k & 63));
-        if (wk == 0.f) continue;  // empty state, or negligible beyond fp32 range
-        const float* src =
-            k < rq.splits
-                ? a.o_part + ((int64_t)rq.state_row + (int64_t)k * rq.rows + r) * DV
-                : a.o_ext + ((int64_t)(k - rq.splits) * a.total_rows + out_row) * DV;
-        float v[N];
-        VecIO<DV>::load(src, lane, v);
+      if (S <= kFew) {
 #pragma unroll
-        for (int i = 0; i < N; ++i) acc[i] = fmaf(wk, v[i], acc[i]);
+        for (int k = 0; k < kFew; ++k) {
+          if (k >= S) break;
+          const float wk = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w0), k));
+          // an empty state, or one negligible beyond fp32 range, takes no part
+          // (its vector may hold anything, e.g. an external state's NaN)
+#pragma unroll
+          for (int i = 0; i < N; ++i) acc[i] = wk != 0.f ? fmaf(wk, vf[k][i], acc[i]) : acc[i];
+        }
+      } else {
+        for (int k = 0; k < S; ++k) {
+          const float wk = __int_as_float(
+              __builtin_amdgcn_readlane(__float_as_int(k < 64 ? w0 : w1), k & 63));
+          if (wk == 0.f) continue;  // empty state, or negligible beyond fp32 range
+          float v[N];
+          VecIO<DV>::load(src_of(k), lane, v);
+#pragma unroll
+          for (int i = 0; i < N; ++i) acc[i] = fmaf(wk, v[i], acc[i]);
+        }
       }
       const float inv = 1.f / Z;
 #pragma unroll
