@@ -247,24 +247,24 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # per-launch events on the launch stream (torch's current stream)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # per-launch events on the launch stream (torch's current stream): mark[j]
+    # precedes launch j (attention and merge alternate) and also ends launch
+    # j - 1, so a step carries two events and the first and last bracket the
+    # whole timed region
+    mark = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start.record()
     for i in range(args.steps):
-        ev[i][0].record()
+        mark[2 * i].record()
         skv.decode_attn_partial(q, k, v, pt, sl, plan, w.scale, o_part=o_part, lse_part=lse_part)
-        ev[i][1].record()
+        mark[2 * i + 1].record()
         skv.merge_states(o_part, lse_part, plan, o_ext, lse_ext, o_out=o_out, lse_out=lse_out)
-        ev[i][2].record()
-    stop.record()
+    mark[2 * args.steps].record()
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
-    total_ms = start.elapsed_time(stop)
-    attn_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    merge_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    total_ms = mark[0].elapsed_time(mark[2 * args.steps])
+    attn_ms = np.array([mark[2 * i].elapsed_time(mark[2 * i + 1]) for i in range(args.steps)])
+    merge_ms = np.array([mark[2 * i + 1].elapsed_time(mark[2 * i + 2]) for i in range(args.steps)])
     ms_per_step = total_ms / args.steps
     flag = plan.read_error_flag(dev)
 
