@@ -87,11 +87,11 @@ __device__ __forceinline__ void load_step(const Ctx<D>& c, int t0, StepRegs<D>& 
       const uint8_t* kp = a.k + (ph * (D / 8) * P + slot + c.r16) * 16;
 #pragma unroll
       for (int m = 0; m < D / 32; ++m)
-        s.k[blk][m] = *reinterpret_cast<const u32x4_t*>(kp + (int64_t)(4 * m + c.g) * P * 16);
+        s.k[blk][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + (int64_t)(4 * m + c.g) * P * 16));
       const uint16_t* vp = a.v + (ph * D + c.r16) * P + slot + 4 * c.g;
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb)
-        s.v[blk][nb] = *reinterpret_cast<const u32x2_t*>(vp + (int64_t)16 * nb * P);
+        s.v[blk][nb] = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(vp + (int64_t)16 * nb * P));
     } else {
 #pragma unroll
       for (int m = 0; m < D / 32; ++m) s.k[blk][m] = u32x4_t{0, 0, 0, 0};
