@@ -108,7 +108,7 @@ __global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
         u32x4_t kr[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-          kr[c] = *reinterpret_cast<const u32x4_t*>(kp + (int64_t)c * P * 16);
+          kr[c] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + (int64_t)c * P * 16));
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
@@ -175,7 +175,7 @@ __global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
         const T* vp = static_cast<const T*>(a.v) + (((int64_t)pid * a.H_kv + t.kvh) * D + d) * P + slot;
 #pragma unroll
         for (int q4 = 0; q4 < (kBf16 ? 2 : 4); ++q4) {
-          const u32x4_t x = *reinterpret_cast<const u32x4_t*>(vp + q4 * (16 / sizeof(T)));
+          const u32x4_t x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(vp + q4 * (16 / sizeof(T))));
 #pragma unroll
           for (int e = 0; e < 4; ++e) vw[k][4 * q4 + e] = x[e];
         }

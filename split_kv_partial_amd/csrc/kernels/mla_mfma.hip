@@ -100,7 +100,7 @@ __device__ __forceinline__ void lds_dma16(const uint8_t* src, uint16_t* dst) {
   __asm__ __volatile__(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off"
+      "global_load_lds_dwordx4 %1, off nt"
       :
       : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
       : "memory", "m0");
@@ -113,7 +113,7 @@ __device__ __forceinline__ void lds_dma16_sbase(const uint8_t* base, uint32_t of
   __asm__ __volatile__(
       "s_mov_b32 m0, %0\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2"
+      "global_load_lds_dwordx4 %1, %2 nt"
       :
       : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
       : "memory", "m0");
