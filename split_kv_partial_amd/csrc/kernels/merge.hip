@@ -30,23 +30,24 @@ struct VecIO;
 template <>
 struct VecIO<64> {  // one float per lane
   static constexpr int N = 1;
-  __device__ static void load(const float* p, int lane, float* v) { v[0] = p[lane]; }
+  __device__ static void load(const float* p, int lane, float* v) { v[0] = __builtin_nontemporal_load(p + lane); }
 };
 template <>
 struct VecIO<128> {  // two floats per lane
   static constexpr int N = 2;
   __device__ static void load(const float* p, int lane, float* v) {
-    const float2 x = reinterpret_cast<const float2*>(p)[lane];
-    v[0] = x.x;
-    v[1] = x.y;
+    typedef float f32x2v __attribute__((ext_vector_type(2)));
+    const f32x2v x = __builtin_nontemporal_load(reinterpret_cast<const f32x2v*>(p) + lane);
+    v[0] = x[0];
+    v[1] = x[1];
   }
 };
 template <>
 struct VecIO<512> {  // eight floats per lane: dims 4l..4l+3 and 256+4l..256+4l+3
   static constexpr int N = 8;
   __device__ static void load(const float* p, int lane, float* v) {
-    const f32x4_t a = reinterpret_cast<const f32x4_t*>(p)[lane];
-    const f32x4_t b = reinterpret_cast<const f32x4_t*>(p + 256)[lane];
+    const f32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p) + lane);
+    const f32x4_t b = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 256) + lane);
     v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
     v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
   }
