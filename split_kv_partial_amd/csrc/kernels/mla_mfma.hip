@@ -25,10 +25,12 @@
 // 4(i%4)..+3 of a 4 x 16 block and lane n receives column n of its four rows),
 // so the tile is stored in LDS once. Tiles stream HBM -> LDS with the gfx950
 // LDS DMA (global_load_lds_dwordx4: lane i's 16 bytes land at the wave's LDS
-// base + 16 i) into a ring of three buffers, two tiles in flight while one is
-// computed, without staging registers. Softmax weights enter P*V as one bf16
-// term (|error| <= 2^-9 max|V| per weight, within the bf16 tolerance for latent
-// values; this kernel is matrix-bound, unlike the GQA one).
+// base + 16 i) into a ring of three buffers, without staging registers.
+// Softmax weights enter P*V as one bf16 term (|error| <= 2^-9 max|V| per
+// weight, within the bf16 tolerance for latent values; this kernel is
+// matrix-bound, unlike the GQA one). Waves 0-3 and 4-7 (the two waves of each
+// SIMD) run the per-tile matrix and vector phases one barrier step apart, so
+// that the softmax of one overlaps the matrix work of the other.
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -249,76 +251,92 @@ void mla_mfma_kernel(MlaArgs a) {
   uint32_t* soff = soff_lds[wave];
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) soff[64 * j + lane] = slot_offset(wave + kWaves * j, lane);
+  // Schedule. A tile's work is a matrix phase M(k) = [P*V of tile k-1, partial
+  // scores of tile k] and a vector phase V(k) = [partner's half of the scores,
+  // online softmax of tile k]. Waves 0-3 run M(0) V(0) M(1) V(1) ... M(n), one
+  // phase per step; waves 4-7 (the other wave of each SIMD) run the same one
+  // step later, so on every SIMD one wave feeds the matrix core while the
+  // other works on the vector ALU. Steps are separated by work-group barriers
+  // (2n + 2 steps, every wave passes each). Tile k + 1 is fetched during steps
+  // 2k and 2k + 1 into the ring buffer that tile k - 2 left (its last reader,
+  // the second group's M(k - 1), ran in step 2k - 1); every wave drains its
+  // DMAs before the barrier of each even step.
+  const int grp = wave >> 2;
   if (ntiles > 0) issue_tile(a, load_pages(a, ptab, end, t.lo), end, t.lo, ring[0], wave, lane, soff);
-  if (ntiles > 1) issue_tile(a, load_pages(a, ptab, end, t.lo + kT), end, t.lo + kT, ring[1], wave, lane, soff);
-  TilePages pg_next = load_pages(a, ptab, end, t.lo + 2 * kT);   // pages of tile i + 2
-  for (int i = 0; i < ntiles; ++i) {
-    const int t0 = t.lo + i * kT;
-    // Tile i has landed once at most one newer tile's DMAs are outstanding: a
-    // wave issues 4 or 5 per tile, so vmcnt(4) waits for all of tile i (and
-    // possibly one instruction of tile i + 1).
-    if (i + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(0x3f74);   // vmcnt(4)
-    else
-      __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
-    // every wave's DMA of tile i is visible; every wave is done with ring[(i+2)%3]
-    bare_barrier();
-    if (i + 2 < ntiles) issue_tile(a, pg_next, end, t0 + 2 * kT, ring[(i + 2) % 3], wave, lane, soff);
-    const uint16_t* tile = ring[i % 3];
+  TilePages pg_next = load_pages(a, ptab, end, t.lo + kT);   // pages of the next tile to fetch
+  f32x4_t s[2][2];   // scores of the current tile: [token block][head block]
+  u32x4_t pf[2];     // softmax weights of the last tile, bf16 (P^T operand)
 
-    // ---- partial scores over this wave's 288 qk dims ----
-    f32x4_t s[2][2];  // [token block][head block]
+  auto matrix_phase = [&](const int k) {
+    if (k >= 1) {
+      // ---- O^T over this wave's 256 value dims, tile k - 1 ----
+      const int tp = t.lo + (k - 1) * kT;
+      const bool ptail = tp + kT > end;
+      const int nvalid = ptail ? end - (tp + 8 * g) : 8;   // valid tokens among 8g..8g+7
+      // transposing reads: lane (g, i) addresses token 8g + i/4 (+4), dims d0 + 4(i%4)
+      const uint16_t* vrow = ring[(k + 2) % 3] + g * kGS + (n >> 2) * kRS + 256 * dh + 4 * (n & 3);
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) s[blk][0] = s[blk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // row i of token block blk is token 8(i/4) + 4 blk + i%4, so that a lane's
-    // outputs (rows 4g..4g+3 of both blocks) are the 8 consecutive tokens 8g..8g+7
-    const uint16_t* krow0 = tile + (n >> 2) * kGS + (n & 3) * kRS + 288 * dh + 8 * g;
-    // Operand reads run one k-step ahead of the matrix instructions that use
-    // them (a two-stage register ring), so LDS latency overlaps the MFMAs.
-    u32x4_t kb[2][2];
-    auto kread = [&](int ks, u32x4_t (&dst)[2]) {
+      for (int nb = 0; nb < kNb; ++nb) {
+        const u32x2_t lo = tr_read(vrow + 16 * nb);
+        const u32x2_t hi = tr_read(vrow + 4 * kRS + 16 * nb);
+        u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
+        if (ptail) {   // values of tokens past `end` (unfetched or stale rows) are zeroed
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            va[e] &= (2 * e + 1 < nvalid ? 0xFFFF0000u : 0u) | (2 * e < nvalid ? 0x0000FFFFu : 0u);
+        }
+        o[nb][0] = mfma16(va, pf[0], o[nb][0]);
+        o[nb][1] = mfma16(va, pf[1], o[nb][1]);
+        if (nb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    if (k < ntiles) {
+      // ---- partial scores over this wave's 288 qk dims, tile k ----
+      const uint16_t* tile = ring[k % 3];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) s[blk][0] = s[blk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      // row i of token block blk is token 8(i/4) + 4 blk + i%4, so that a lane's
+      // outputs (rows 4g..4g+3 of both blocks) are the 8 consecutive tokens 8g..8g+7
+      const uint16_t* krow0 = tile + (n >> 2) * kGS + (n & 3) * kRS + 288 * dh + 8 * g;
+      // operand reads one k-step ahead of their MFMAs (two-stage register ring)
+      u32x4_t kb[2][2];
+      auto kread = [&](int ks, u32x4_t (&dst)[2]) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+          dst[blk] = *reinterpret_cast<const u32x4_t*>(krow0 + 4 * blk * kRS + 32 * ks);
+      };
+      kread(0, kb[0]);
+#pragma unroll
+      for (int ks = 0; ks < kKs; ++ks) {
+        if (ks + 1 < kKs) kread(ks + 1, kb[(ks + 1) % 2]);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          s[blk][0] = mfma16(kb[ks % 2][blk], qf[0][ks], s[blk][0]);
+          s[blk][1] = mfma16(kb[ks % 2][blk], qf[1][ks], s[blk][1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // publish this half for the partner wave (read after the next barrier)
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
-        dst[blk] = *reinterpret_cast<const u32x4_t*>(krow0 + 4 * blk * kRS + 32 * ks);
-    };
-    kread(0, kb[0]);
 #pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-      if (ks + 1 < kKs) kread(ks + 1, kb[(ks + 1) % 2]);
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        s[blk][0] = mfma16(kb[ks % 2][blk], qf[0][ks], s[blk][0]);
-        s[blk][1] = mfma16(kb[ks % 2][blk], qf[1][ks], s[blk][1]);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+        for (int hb = 0; hb < 2; ++hb) xbuf[wave][2 * blk + hb][lane] = s[blk][hb];
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the writes are done
     }
-    // ---- add the partner wave's half of the scores ----
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb) xbuf[wave][2 * blk + hb][lane] = s[blk][hb];
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
-    bare_barrier();
+  };
+
+  auto vector_phase = [&](const int k) {
+    const int t0 = t.lo + k * kT;
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) s[blk][hb] += xbuf[wave ^ 1][2 * blk + hb][lane];
-    // page ids for the next iteration's DMA: the scalar loads complete during
-    // the softmax, before the next wait on LDS reads
-    __builtin_amdgcn_sched_barrier(0);   // after the adds have consumed the LDS reads
-    pg_next = load_pages(a, ptab, end, t0 + 3 * kT);   // clamped: always a valid entry
-    __builtin_amdgcn_sched_barrier(0);
-
     // ---- online softmax per head (log2 domain) ----
     // The running reference m only moves when a tile's maximum exceeds it by
     // more than 8 (a factor 256): weights exp2(s - m) then stay <= 256, the
     // accumulators are rescaled only on those (rare) tiles, and the common
     // path leaves them to the matrix cores. The result is the same softmax.
-    const bool tail = t0 + kT > end;
-    u32x4_t pf[2];
-    float alpha[2] = {1.f, 1.f};
-    bool bump = false;
-    if (tail) {   // tokens at or past `end` take no part: score -inf, weight 0
+    if (t0 + kT > end) {   // tokens at or past `end` take no part: score -inf, weight 0
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
@@ -327,6 +345,8 @@ void mla_mfma_kernel(MlaArgs a) {
           for (int e = 0; e < 4; ++e)
             if (t0 + 8 * g + 4 * blk + e >= end) s[blk][hb][e] = -INFINITY;
     }
+    float alpha[2] = {1.f, 1.f};
+    bool bump = false;
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       // the maximum of the raw scores, scaled (scaling by a positive factor
@@ -352,6 +372,8 @@ void mla_mfma_kernel(MlaArgs a) {
       pf[hb] = u32x4_t{pack_bf16x2(s[0][hb][0], s[0][hb][1]), pack_bf16x2(s[0][hb][2], s[0][hb][3]),
                        pack_bf16x2(s[1][hb][0], s[1][hb][1]), pack_bf16x2(s[1][hb][2], s[1][hb][3])};
     }
+    // P*V of tile k runs in the next matrix phase, after the accumulators of
+    // tiles up to k - 1 are rescaled to the new reference
     if (__builtin_amdgcn_ballot_w64(bump) != 0) {
 #pragma unroll
       for (int nb = 0; nb < kNb; ++nb) {
@@ -359,25 +381,42 @@ void mla_mfma_kernel(MlaArgs a) {
         o[nb][1] *= alpha[1];
       }
     }
-    // values of tokens past `end` (unfetched or stale rows) are zeroed
-    const int nvalid = tail ? end - (t0 + 8 * g) : 8;   // valid tokens among 8g..8g+7
+  };
 
-    // ---- O^T over this wave's 256 value dims ----
-    // transposing reads: lane (g, i) addresses token 8g + i/4 (+4), dims d0 + 4(i%4)
-    const uint16_t* vrow = tile + g * kGS + (n >> 2) * kRS + 256 * dh + 4 * (n & 3);
-#pragma unroll
-    for (int nb = 0; nb < kNb; ++nb) {
-      const u32x2_t lo = tr_read(vrow + 16 * nb);
-      const u32x2_t hi = tr_read(vrow + 4 * kRS + 16 * nb);
-      u32x4_t va = {lo[0], lo[1], hi[0], hi[1]};
-      if (tail) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          va[k] &= (2 * k + 1 < nvalid ? 0xFFFF0000u : 0u) | (2 * k < nvalid ? 0x0000FFFFu : 0u);
+  // even steps: drain this wave's DMAs (tile step/2 has then landed for all),
+  // synchronise, start the next tile's DMA and read the page ids of the one after
+  auto even_barrier = [&](const int step) {
+    __builtin_amdgcn_s_waitcnt(0x3f70);   // vmcnt(0)
+    bare_barrier();
+    const int k1 = step / 2 + 1;
+    if (k1 < ntiles) {
+      issue_tile(a, pg_next, end, t.lo + k1 * kT, ring[k1 % 3], wave, lane, soff);
+      pg_next = load_pages(a, ptab, end, t.lo + (k1 + 1) * kT);   // clamped: always a valid entry
+    }
+  };
+  // Each group runs its own copy of the loop, so that only its own live state
+  // crosses the loop edge (the weights for group 0, the scores for group 1).
+  if (ntiles > 0) {
+    if (grp == 0) {
+      for (int k = 0; k < ntiles; ++k) {
+        even_barrier(2 * k);
+        matrix_phase(k);
+        bare_barrier();
+        vector_phase(k);
       }
-      o[nb][0] = mfma16(va, pf[0], o[nb][0]);
-      o[nb][1] = mfma16(va, pf[1], o[nb][1]);
-      if (nb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
+      even_barrier(2 * ntiles);
+      matrix_phase(ntiles);
+      bare_barrier();
+    } else {
+      even_barrier(0);
+      for (int k = 0; k < ntiles; ++k) {
+        bare_barrier();
+        matrix_phase(k);
+        even_barrier(2 * k + 2);
+        vector_phase(k);
+      }
+      bare_barrier();
+      matrix_phase(ntiles);
     }
   }
 
