@@ -23,7 +23,6 @@
 #include <cstdint>
 #include <map>
 #include <numeric>
-#include <queue>
 #include <thread>
 #include <tuple>
 #include <vector>
