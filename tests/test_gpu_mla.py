@@ -94,3 +94,26 @@ def test_mla_deterministic():
     for x, y in zip(run_path(w, plan, d), run_path(w, plan, d)):
         assert np.array_equal(x.view(np.uint64), y.view(np.uint64))
     assert plan.read_error_flag() == 0
+
+
+def _scale_rope(w, b, tokens, c):
+    """Multiply the 64 rope columns (key only, not the value) of the given
+    tokens of request b."""
+    for j in tokens:
+        pid, slot = wl.physical_slot(w, b, j)
+        rope = (w.k_pages[pid, slot, 512:].astype(np.uint32) << 16).view(np.float32)
+        w.k_pages[pid, slot, 512:] = wl.f32_to_bf16_bits(rope * np.float32(c))
+
+
+@pytest.mark.parametrize("P", [64, 16])
+def test_mla_rising_scores(P):
+    # a few late tokens with scaled-up rope keys: the maximum score of some
+    # heads rises by more than 64 (log2 units) above that of the first tile of
+    # their split, which makes the MLA kernel run the split a second time
+    w = mla([3000, 1500, 97], P=P, seed=31, q_scale=wl.SHARP_MLA)
+    _scale_rope(w, 0, [400, 401], 8.0)
+    _scale_rope(w, 0, [1500], 30.0)
+    _scale_rope(w, 0, [2900], 90.0)
+    _scale_rope(w, 1, [1400], 60.0)
+    _scale_rope(w, 2, [96], 60.0)
+    check_all(w, skv.plan_from_counts(w.seq_lens, spec_of(w), [2, 1, 1]))
