@@ -56,6 +56,7 @@ constexpr int kRowSlots = kD / 8;             // 16-byte slots per latent row (7
 constexpr int kRowBytes = kD * 2;             // 1152
 constexpr int kTileSlots = kT * kRowSlots;    // 2304
 constexpr int kTileElems = kTileSlots * 8;    // bf16 per LDS tile buffer
+constexpr int kTileBytes = kTileSlots * 16;   // 36,864
 constexpr int kBuf = 4;                       // LDS ring depth
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -68,15 +69,17 @@ constexpr int kKd = 4;           // K operand reads in flight, in k-steps
 constexpr int kVd = 8;           // V operand reads in flight, in output blocks
 
 // LDS tile layout: row r (token t0 + r) holds its 72 slots unpadded, chunk c
-// of the row at slot 72 r + (c ^ swz(r)). With 64 four-byte banks (16 slots
-// per 256 bytes), the K reads (a 16-lane pass of 16-byte reads: 16 rows at
-// one chunk) and the transposing V reads (a 32-lane pass of 8-byte reads: 8
-// rows at two adjacent chunks) then touch every bank once. Row parity already
-// separates the two halves of a bank line (72 r mod 16 = 8 (r % 2)); the XOR
-// of bits 1, 3 and 4 of r spreads the rows of one parity.
-__device__ __forceinline__ int swz(int r) {
-  return ((r >> 4) & 1) | (((r >> 1) & 1) << 1) | (((r >> 3) & 1) << 2);
-}
+// of the row at slot 72 r + (c ^ swz(r)). LDS bank structure of gfx950, as
+// measured with the bank-conflict counter: 64 four-byte banks (a 256-byte
+// line of 16 slots); a 16-byte read serves 16 lanes per cycle, lanes 8h..8h+7
+// of a 16-lane group g together with the other half of group g ^ 1 (lanes
+// 0-7 with 24-31, 8-15 with 16-23); an 8-byte transposing read serves 32
+// lanes per cycle. Row parity separates the two halves of a bank line
+// (72 r mod 16 = 8 (r % 2)) and the XOR of bits 1 and 3 of r spreads the rows
+// of one parity, so that the K reads (per cycle: 16 rows, chunks 4 ks + g and
+// 4 ks + (g ^ 1)) and the V reads (8 rows at two adjacent chunks) touch every
+// bank once.
+__device__ __forceinline__ int swz(int r) { return (r & 2) | ((r >> 1) & 4); }
 
 typedef short __attribute__((__vector_size__(4 * sizeof(short)))) s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -95,19 +98,30 @@ __device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
 // assembly: the compiler gives every MFMA result of a kernel the same register
 // kind, and the 256 output accumulators need all the accumulation registers,
 // so the scores are kept in vector registers this way. The compiler does not
-// see these as MFMAs when it inserts wait states, so the block starts with
-// three (an input written by a vector ALU instruction needs two), and
-// scores_ready() below covers the MFMA -> vector ALU distance. Consecutive
-// accumulations into the same registers need none.
+// see these as MFMAs when it inserts wait states: the operands here are only
+// written by LDS loads (the K fragments), by the global loads of Q before the
+// tile loop and by these MFMAs (chained accumulation needs no wait states),
+// the first step starts from zero accumulators instead of registers cleared
+// by a vector ALU instruction and begins with three wait states anyway, and
+// scores_ready() below covers the MFMA -> vector ALU distance.
+template <bool kFirst>
 __device__ __forceinline__ void qk_step(f32x4_t (&s)[2][2], const u32x4_t (&kf)[2], u32x4_t q0,
                                         u32x4_t q1) {
-  __asm__("s_nop 2\n\t"
-          "v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
-          "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
-          "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
-          "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3"
-          : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1])
-          : "v"(kf[0]), "v"(kf[1]), "v"(q0), "v"(q1));
+  if (kFirst)
+    __asm__("s_nop 2\n\t"
+            "v_mfma_f32_16x16x32_bf16 %0, %4, %6, 0\n\t"
+            "v_mfma_f32_16x16x32_bf16 %1, %4, %7, 0\n\t"
+            "v_mfma_f32_16x16x32_bf16 %2, %5, %6, 0\n\t"
+            "v_mfma_f32_16x16x32_bf16 %3, %5, %7, 0"
+            : "=&v"(s[0][0]), "=&v"(s[0][1]), "=&v"(s[1][0]), "=&v"(s[1][1])
+            : "v"(kf[0]), "v"(kf[1]), "v"(q0), "v"(q1));
+  else
+    __asm__("v_mfma_f32_16x16x32_bf16 %0, %4, %6, %0\n\t"
+            "v_mfma_f32_16x16x32_bf16 %1, %4, %7, %1\n\t"
+            "v_mfma_f32_16x16x32_bf16 %2, %5, %6, %2\n\t"
+            "v_mfma_f32_16x16x32_bf16 %3, %5, %7, %3"
+            : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1])
+            : "v"(kf[0]), "v"(kf[1]), "v"(q0), "v"(q1));
 }
 // Twenty wait states between the last score MFMA and the first vector ALU
 // read of the scores (more than an MFMA of this shape needs).
@@ -121,36 +135,42 @@ __device__ __forceinline__ u32x2_t tr_read(const uint8_t* lds_ptr) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
-// One wave-wide LDS DMA: each lane's 16 bytes at `src` land at dst + 16 *
-// lane. Issued as inline assembly so that the compiler does not track it: its
-// own wait insertion would otherwise drain every DMA in flight before each
-// read of a different ring buffer (it cannot tell the buffers apart). The tile
-// loop orders these writes itself with vmcnt waits, which stay correct for the
-// compiler's own loads because vector-memory counters retire in order. M0
-// carries the LDS base; one wait state separates its write from the DMA.
-__device__ __forceinline__ void lds_dma16(const uint8_t* src, uint16_t* dst) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t*)dst;
+// This wave's nine LDS DMAs of one tile: instruction j moves each lane's 16
+// bytes to LDS byte lds + 4096 j + 16 lane (the wave's 1 KB blocks wave,
+// wave + 4, ... of the tile). Inline assembly, so that the compiler does not
+// track them: its own wait insertion would otherwise drain every DMA in
+// flight before each read of a different ring buffer (it cannot tell the
+// buffers apart). The tile loop orders these writes itself with vmcnt waits,
+// which stay correct for the compiler's own loads because vector-memory
+// counters retire in order. M0 carries the LDS address; one wait state
+// separates its write from the DMA that reads it.
+#define SKV_DMA_STEP(J, SRC, ADDR) \
+  "s_add_u32 m0, %[l], " #J " * 4096\n\ts_nop 0\n\tglobal_load_lds_dwordx4 " SRC ", " ADDR " nt\n\t"
+// Scalar-address form: a wave-uniform 64-bit base plus each lane's 32-bit
+// byte offset.
+__device__ __forceinline__ void dma9_sbase(const uint8_t* base, const uint32_t (&o)[9], uint32_t lds) {
   __asm__ __volatile__(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off nt"
+      SKV_DMA_STEP(0, "%[o0]", "%[b]") SKV_DMA_STEP(1, "%[o1]", "%[b]") SKV_DMA_STEP(2, "%[o2]", "%[b]")
+      SKV_DMA_STEP(3, "%[o3]", "%[b]") SKV_DMA_STEP(4, "%[o4]", "%[b]") SKV_DMA_STEP(5, "%[o5]", "%[b]")
+      SKV_DMA_STEP(6, "%[o6]", "%[b]") SKV_DMA_STEP(7, "%[o7]", "%[b]") SKV_DMA_STEP(8, "%[o8]", "%[b]")
       :
-      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+      : [l] "s"(lds), [b] "s"(base), [o0] "v"(o[0]), [o1] "v"(o[1]), [o2] "v"(o[2]), [o3] "v"(o[3]),
+        [o4] "v"(o[4]), [o5] "v"(o[5]), [o6] "v"(o[6]), [o7] "v"(o[7]), [o8] "v"(o[8])
       : "memory", "m0");
 }
-
-// The same with a wave-uniform 64-bit base and a 32-bit per-lane byte offset
-// (the instruction's scalar-address form: no 64-bit vector arithmetic).
-__device__ __forceinline__ void lds_dma16_sbase(const uint8_t* base, uint32_t off, uint16_t* dst) {
-  const uint32_t lds = (uint32_t)(uintptr_t)(lds_void_t*)dst;
+// Vector-address form: each lane's 64-bit source address.
+__device__ __forceinline__ void dma9_vaddr(const uint8_t* const (&p)[9], uint32_t lds) {
   __asm__ __volatile__(
-      "s_mov_b32 m0, %0\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, %2 nt"
+      SKV_DMA_STEP(0, "%[p0]", "off") SKV_DMA_STEP(1, "%[p1]", "off") SKV_DMA_STEP(2, "%[p2]", "off")
+      SKV_DMA_STEP(3, "%[p3]", "off") SKV_DMA_STEP(4, "%[p4]", "off") SKV_DMA_STEP(5, "%[p5]", "off")
+      SKV_DMA_STEP(6, "%[p6]", "off") SKV_DMA_STEP(7, "%[p7]", "off") SKV_DMA_STEP(8, "%[p8]", "off")
       :
-      : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(off), "s"(base)
+      : [l] "s"(lds), [p0] "v"(p[0]), [p1] "v"(p[1]), [p2] "v"(p[2]), [p3] "v"(p[3]), [p4] "v"(p[4]),
+        [p5] "v"(p[5]), [p6] "v"(p[6]), [p7] "v"(p[7]), [p8] "v"(p[8])
       : "memory", "m0");
 }
+#undef SKV_DMA_STEP
+static_assert(kDmaPerWave == 9 && kWaves * 1024 == 4096, "the DMA blocks assume 9 per wave, 4 waves");
 
 // Byte offset, within a run of 32 consecutive latent rows, of the 16 bytes
 // that LDS slot 64 inst + lane of a tile holds (the inverse of the layout).
@@ -183,35 +203,32 @@ __device__ __forceinline__ TilePages load_pages(const MlaArgs& a, const_i32_t* p
 // Every slot of the tile is fetched by exactly one lane. Rows at or past `end`
 // are read from the same (valid) page and masked where they are used; an id
 // outside the page pool is reported and page 0 is read instead.
-__device__ __forceinline__ void issue_tile(const MlaArgs& a, TilePages pg, int t0, uint16_t* tile,
-                                           int wave, int lane, const uint32_t* soff) {
+__device__ __forceinline__ void issue_tile(const MlaArgs& a, TilePages pg, int t0, uint32_t lds,
+                                           int lane, const uint32_t* soff) {
   const int P = 1 << a.page_shift;
   const bool ok0 = pg.pid0 >= 0 && pg.pid0 < a.num_pages;
   const bool ok1 = pg.pid1 >= 0 && pg.pid1 < a.num_pages;
   if ((!ok0 || !ok1) && lane == 0) raise_error(a.err_flag, 1);
+  uint32_t off[kDmaPerWave];   // read together: the DMA block orders LDS accesses
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) off[j] = soff[64 * j + lane];
   if (P >= 32) {
     // the tile is 32 consecutive rows of one page: a scalar base plus the
     // lane's fixed offset
     const uint8_t* base = a.kv + (ok0 ? ((int64_t)pg.pid0 * P + (t0 & (P - 1))) * kRowBytes : 0);
-    uint32_t off[kDmaPerWave];   // read together: the DMA statements order LDS accesses
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) off[j] = soff[64 * j + lane];
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) lds_dma16_sbase(base, off[j], tile + 64 * 8 * (wave + kWaves * j));
+    dma9_sbase(base, off, lds);
     return;
   }
   // 16-token pages: rows 16..31 come from the second page
   const uint8_t* base0 = a.kv + (ok0 ? (int64_t)pg.pid0 * 16 * kRowBytes : 0);
   const uint8_t* base1 = a.kv + (ok1 ? (int64_t)pg.pid1 * 16 * kRowBytes : 0);
-  uint32_t off[kDmaPerWave];
-#pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j) off[j] = soff[64 * j + lane];
+  const uint8_t* src[kDmaPerWave];
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
     const bool hi = off[j] >= 16u * kRowBytes;
-    const uint8_t* src = hi ? base1 + (off[j] - 16u * kRowBytes) : base0 + off[j];
-    lds_dma16(src, tile + 64 * 8 * (wave + kWaves * j));
+    src[j] = hi ? base1 + (off[j] - 16u * kRowBytes) : base0 + off[j];
   }
+  dma9_vaddr(src, lds);
 }
 
 }  // namespace
@@ -266,6 +283,9 @@ void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) soff[64 * j + lane] = slot_offset(wave + kWaves * j, lane);
   if (threadIdx.x == 0) restart_pass = 0;
+  // LDS byte address of this wave's first DMA block in ring buffer 0
+  const uint32_t ring_lds =
+      __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&ring[0][0]) + 1024u * wave;
 
   // Per-lane byte offsets of the operand reads within a tile buffer.
   // K (A operand of the scores): lane (g, n) reads row 8(n/4) + 4 blk + n%4 of
@@ -319,7 +339,7 @@ void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
     for (int j = 0; j < kBuf - 1; ++j) {
       if (j < ntiles) {
-        issue_tile(a, pg, t.lo + j * kT, ring[j], wave, lane, soff);
+        issue_tile(a, pg, t.lo + j * kT, ring_lds + j * kTileBytes, lane, soff);
         pg = load_pages(a, ptab, end, t.lo + (j + 1) * kT);   // clamped: always a valid entry
       }
     }
@@ -332,7 +352,8 @@ void mla_mfma_kernel(MlaArgs a) {
       else __builtin_amdgcn_s_waitcnt(kWaitVm0);
       bare_barrier();
       if (k + kBuf - 1 < ntiles) {
-        issue_tile(a, pg, t.lo + (k + kBuf - 1) * kT, ring[(k + kBuf - 1) % kBuf], wave, lane, soff);
+        issue_tile(a, pg, t.lo + (k + kBuf - 1) * kT, ring_lds + ((k + kBuf - 1) % kBuf) * kTileBytes,
+                   lane, soff);
         pg = load_pages(a, ptab, end, t.lo + (k + kBuf) * kT);
       }
       uint16_t* tile = ring[k % kBuf];
@@ -351,8 +372,6 @@ void mla_mfma_kernel(MlaArgs a) {
 
       // ---- scores S^T of tile k over all 576 dims ----
       f32x4_t s[2][2];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) s[blk][0] = s[blk][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       {
         u32x4_t kb[kKd][2];
         auto kread = [&](int ks, u32x4_t (&dst)[2]) {
@@ -368,7 +387,8 @@ void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
         for (int ks = 0; ks < kKs; ++ks) {
           if (ks + kKd - 1 < kKs) kread(ks + kKd - 1, kb[(ks + kKd - 1) % kKd]);
-          qk_step(s, kb[ks % kKd], qf[0][ks], qf[1][ks]);
+          if (ks == 0) qk_step<true>(s, kb[0], qf[0][0], qf[1][0]);
+        else qk_step<false>(s, kb[ks % kKd], qf[0][ks], qf[1][ks]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
