@@ -29,6 +29,8 @@
 // tile issued three tiles ahead of its use, without staging registers.
 // Softmax weights enter P*V as one bf16 term (|error| <= 2^-9 max|V| per
 // weight, within the bf16 tolerance for latent values).
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -135,8 +137,8 @@ __device__ __forceinline__ u32x2_t tr_read(const uint8_t* lds_ptr) {
   return __builtin_bit_cast(u32x2_t, v);
 }
 
-// This wave's nine LDS DMAs of one tile: instruction j moves each lane's 16
-// bytes to LDS byte lds + 4096 j + 16 lane (the wave's 1 KB blocks wave,
+// One of this wave's nine LDS DMAs of a tile: instruction j moves each lane's
+// 16 bytes to LDS byte lds + 4096 j + 16 lane (the wave's 1 KB blocks wave,
 // wave + 4, ... of the tile). Inline assembly, so that the compiler does not
 // track them: its own wait insertion would otherwise drain every DMA in
 // flight before each read of a different ring buffer (it cannot tell the
@@ -144,33 +146,23 @@ __device__ __forceinline__ u32x2_t tr_read(const uint8_t* lds_ptr) {
 // which stay correct for the compiler's own loads because vector-memory
 // counters retire in order. M0 carries the LDS address; one wait state
 // separates its write from the DMA that reads it.
-#define SKV_DMA_STEP(J, SRC, ADDR) \
-  "s_add_u32 m0, %[l], " #J " * 4096\n\ts_nop 0\n\tglobal_load_lds_dwordx4 " SRC ", " ADDR " nt\n\t"
-// Scalar-address form: a wave-uniform 64-bit base plus each lane's 32-bit
-// byte offset.
-__device__ __forceinline__ void dma9_sbase(const uint8_t* base, const uint32_t (&o)[9], uint32_t lds) {
+template <int J>
+__device__ __forceinline__ void dma_sbase(const uint8_t* base, uint32_t off, uint32_t lds) {
   __asm__ __volatile__(
-      SKV_DMA_STEP(0, "%[o0]", "%[b]") SKV_DMA_STEP(1, "%[o1]", "%[b]") SKV_DMA_STEP(2, "%[o2]", "%[b]")
-      SKV_DMA_STEP(3, "%[o3]", "%[b]") SKV_DMA_STEP(4, "%[o4]", "%[b]") SKV_DMA_STEP(5, "%[o5]", "%[b]")
-      SKV_DMA_STEP(6, "%[o6]", "%[b]") SKV_DMA_STEP(7, "%[o7]", "%[b]") SKV_DMA_STEP(8, "%[o8]", "%[b]")
+      "s_add_u32 m0, %[l], %[o4k]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[o], %[b] nt"
       :
-      : [l] "s"(lds), [b] "s"(base), [o0] "v"(o[0]), [o1] "v"(o[1]), [o2] "v"(o[2]), [o3] "v"(o[3]),
-        [o4] "v"(o[4]), [o5] "v"(o[5]), [o6] "v"(o[6]), [o7] "v"(o[7]), [o8] "v"(o[8])
+      : [l] "s"(lds), [o4k] "i"(J * 4096), [b] "s"(base), [o] "v"(off)
       : "memory", "m0");
 }
-// Vector-address form: each lane's 64-bit source address.
-__device__ __forceinline__ void dma9_vaddr(const uint8_t* const (&p)[9], uint32_t lds) {
+template <int J>
+__device__ __forceinline__ void dma_vaddr(const uint8_t* src, uint32_t lds) {
   __asm__ __volatile__(
-      SKV_DMA_STEP(0, "%[p0]", "off") SKV_DMA_STEP(1, "%[p1]", "off") SKV_DMA_STEP(2, "%[p2]", "off")
-      SKV_DMA_STEP(3, "%[p3]", "off") SKV_DMA_STEP(4, "%[p4]", "off") SKV_DMA_STEP(5, "%[p5]", "off")
-      SKV_DMA_STEP(6, "%[p6]", "off") SKV_DMA_STEP(7, "%[p7]", "off") SKV_DMA_STEP(8, "%[p8]", "off")
+      "s_add_u32 m0, %[l], %[o4k]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[p], off nt"
       :
-      : [l] "s"(lds), [p0] "v"(p[0]), [p1] "v"(p[1]), [p2] "v"(p[2]), [p3] "v"(p[3]), [p4] "v"(p[4]),
-        [p5] "v"(p[5]), [p6] "v"(p[6]), [p7] "v"(p[7]), [p8] "v"(p[8])
+      : [l] "s"(lds), [o4k] "i"(J * 4096), [p] "v"(src)
       : "memory", "m0");
 }
-#undef SKV_DMA_STEP
-static_assert(kDmaPerWave == 9 && kWaves * 1024 == 4096, "the DMA blocks assume 9 per wave, 4 waves");
+static_assert(kDmaPerWave == 9 && kWaves * 1024 == 4096, "the DMA helpers assume 9 per wave, 4 waves");
 
 // Byte offset, within a run of 32 consecutive latent rows, of the 16 bytes
 // that LDS slot 64 inst + lane of a tile holds (the inverse of the layout).
@@ -198,38 +190,50 @@ __device__ __forceinline__ TilePages load_pages(const MlaArgs& a, const_i32_t* p
   return TilePages{ptab[i0], ptab[i1]};
 }
 
-// Issue this wave's share (9 instructions, a fixed count the vmcnt waits of
-// the tile loop rely on) of the DMA of the 32-token tile at t0 into `tile`.
-// Every slot of the tile is fetched by exactly one lane. Rows at or past `end`
-// are read from the same (valid) page and masked where they are used; an id
-// outside the page pool is reported and page 0 is read instead.
-__device__ __forceinline__ void issue_tile(const MlaArgs& a, TilePages pg, int t0, uint32_t lds,
-                                           int lane, const uint32_t* soff) {
-  const int P = 1 << a.page_shift;
-  const bool ok0 = pg.pid0 >= 0 && pg.pid0 < a.num_pages;
-  const bool ok1 = pg.pid1 >= 0 && pg.pid1 < a.num_pages;
-  if ((!ok0 || !ok1) && lane == 0) raise_error(a.err_flag, 1);
-  uint32_t off[kDmaPerWave];   // read together: the DMA block orders LDS accesses
+// This wave's share (9 instructions, a fixed count the vmcnt waits of the
+// tile loop rely on) of the DMA of the 32-token tile at t0: prepare() takes
+// the page bases and reads the lanes' offsets, issue<J>() sends instruction
+// J. Every slot of the tile is fetched by exactly one lane. Rows at or past
+// `end` are read from the same (valid) page and masked where they are used;
+// an id outside the page pool is reported and page 0 is read instead.
+template <bool kSinglePage>   // P >= 32: the tile is 32 consecutive rows of one page
+struct TileDma {
+  const uint8_t* base0;   // the tile's first row (P >= 32) or first page (P = 16)
+  const uint8_t* base1;   // P = 16: the second page
+  uint32_t off[kDmaPerWave];
+  uint32_t lds;
+
+  __device__ __forceinline__ void prepare(const MlaArgs& a, TilePages pg, int t0, uint32_t lds_addr,
+                                          int lane, const uint32_t* soff) {
+    const int P = 1 << a.page_shift;
+    const bool ok0 = pg.pid0 >= 0 && pg.pid0 < a.num_pages;
+    const bool ok1 = pg.pid1 >= 0 && pg.pid1 < a.num_pages;
+    if ((!ok0 || !ok1) && lane == 0) raise_error(a.err_flag, 1);
 #pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j) off[j] = soff[64 * j + lane];
-  if (P >= 32) {
-    // the tile is 32 consecutive rows of one page: a scalar base plus the
-    // lane's fixed offset
-    const uint8_t* base = a.kv + (ok0 ? ((int64_t)pg.pid0 * P + (t0 & (P - 1))) * kRowBytes : 0);
-    dma9_sbase(base, off, lds);
-    return;
+    for (int j = 0; j < kDmaPerWave; ++j) off[j] = soff[64 * j + lane];
+    lds = __builtin_amdgcn_readfirstlane(lds_addr);
+    if (kSinglePage) {
+      base0 = a.kv + (ok0 ? ((int64_t)pg.pid0 * P + (t0 & (P - 1))) * kRowBytes : 0);
+      base1 = base0;
+    } else {
+      base0 = a.kv + (ok0 ? (int64_t)pg.pid0 * 16 * kRowBytes : 0);
+      base1 = a.kv + (ok1 ? (int64_t)pg.pid1 * 16 * kRowBytes : 0);
+    }
   }
-  // 16-token pages: rows 16..31 come from the second page
-  const uint8_t* base0 = a.kv + (ok0 ? (int64_t)pg.pid0 * 16 * kRowBytes : 0);
-  const uint8_t* base1 = a.kv + (ok1 ? (int64_t)pg.pid1 * 16 * kRowBytes : 0);
-  const uint8_t* src[kDmaPerWave];
-#pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j) {
-    const bool hi = off[j] >= 16u * kRowBytes;
-    src[j] = hi ? base1 + (off[j] - 16u * kRowBytes) : base0 + off[j];
+  template <int J>
+  __device__ __forceinline__ void issue() const {
+    if (kSinglePage) {
+      dma_sbase<J>(base0, off[J], lds);
+    } else {   // 16-token pages: rows 16..31 come from the second page
+      const bool hi = off[J] >= 16u * kRowBytes;
+      dma_vaddr<J>(hi ? base1 + (off[J] - 16u * kRowBytes) : base0 + off[J], lds);
+    }
   }
-  dma9_vaddr(src, lds);
-}
+  __device__ __forceinline__ void issue_all() const {
+    issue<0>(); issue<1>(); issue<2>(); issue<3>(); issue<4>();
+    issue<5>(); issue<6>(); issue<7>(); issue<8>();
+  }
+};
 
 }  // namespace
 
@@ -249,6 +253,7 @@ constexpr int kWaitVm9 = 0x3f70 | 9;
 constexpr int kWaitVm18 = 0x3f70 | (18 & 15) | ((18 >> 4) << 14);
 static_assert(2 * kDmaPerWave == 18 && kBuf == 4, "vmcnt immediates assume 9 DMAs per tile, 4 buffers");
 
+template <bool kSinglePage>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_mfma_kernel(MlaArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t ring[kBuf][kTileElems];
@@ -339,7 +344,9 @@ void mla_mfma_kernel(MlaArgs a) {
 #pragma unroll
     for (int j = 0; j < kBuf - 1; ++j) {
       if (j < ntiles) {
-        issue_tile(a, pg, t.lo + j * kT, ring_lds + j * kTileBytes, lane, soff);
+        TileDma<kSinglePage> d;
+        d.prepare(a, pg, t.lo + j * kT, ring_lds + j * kTileBytes, lane, soff);
+        d.issue_all();
         pg = load_pages(a, ptab, end, t.lo + (j + 1) * kT);   // clamped: always a valid entry
       }
     }
@@ -351,11 +358,13 @@ void mla_mfma_kernel(MlaArgs a) {
       else if (ahead == 1) __builtin_amdgcn_s_waitcnt(kWaitVm9);
       else __builtin_amdgcn_s_waitcnt(kWaitVm0);
       bare_barrier();
-      if (k + kBuf - 1 < ntiles) {
-        issue_tile(a, pg, t.lo + (k + kBuf - 1) * kT, ring_lds + ((k + kBuf - 1) % kBuf) * kTileBytes,
-                   lane, soff);
-        pg = load_pages(a, ptab, end, t.lo + (k + kBuf) * kT);
-      }
+      // the DMA of tile k + 3, spread over the score MFMAs below (issued back
+      // to back, the nine instructions stall the wave)
+      const bool fetch = k + kBuf - 1 < ntiles;
+      TileDma<kSinglePage> d;   // prepared always (the page ids are clamped), issued if fetch
+      d.prepare(a, pg, t.lo + (k + kBuf - 1) * kT, ring_lds + ((k + kBuf - 1) % kBuf) * kTileBytes,
+                lane, soff);
+      if (fetch) pg = load_pages(a, ptab, end, t.lo + (k + kBuf) * kT);
       uint16_t* tile = ring[k % kBuf];
       const uint8_t* lb = reinterpret_cast<const uint8_t*>(tile);
       const int t0 = t.lo + k * kT;
@@ -372,7 +381,8 @@ void mla_mfma_kernel(MlaArgs a) {
 
       // ---- scores S^T of tile k over all 576 dims ----
       f32x4_t s[2][2];
-      {
+      auto qk = [&](auto fetch_tag) {
+        constexpr bool kFetch = decltype(fetch_tag)::value;
         u32x4_t kb[kKd][2];
         auto kread = [&](int ks, u32x4_t (&dst)[2]) {
 #pragma unroll
@@ -388,10 +398,25 @@ void mla_mfma_kernel(MlaArgs a) {
         for (int ks = 0; ks < kKs; ++ks) {
           if (ks + kKd - 1 < kKs) kread(ks + kKd - 1, kb[(ks + kKd - 1) % kKd]);
           if (ks == 0) qk_step<true>(s, kb[0], qf[0][0], qf[1][0]);
-        else qk_step<false>(s, kb[ks % kKd], qf[0][ks], qf[1][ks]);
+          else qk_step<false>(s, kb[ks % kKd], qf[0][ks], qf[1][ks]);
+          if (kFetch && ks % 2 == 1) {
+            switch (ks / 2) {
+              case 0: d.template issue<0>(); break;
+              case 1: d.template issue<1>(); break;
+              case 2: d.template issue<2>(); break;
+              case 3: d.template issue<3>(); break;
+              case 4: d.template issue<4>(); break;
+              case 5: d.template issue<5>(); break;
+              case 6: d.template issue<6>(); break;
+              case 7: d.template issue<7>(); break;
+              default: d.template issue<8>(); break;
+            }
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
-      }
+      };
+      if (fetch) qk(std::true_type{});
+      else qk(std::false_type{});
       scores_ready(s);
 
       // ---- softmax weights (log2 domain) ----
@@ -499,7 +524,10 @@ hipError_t launch_mla_mfma(const AttnLaunch& L) {
   a.max_pages = d.max_pages_per_seq;
   a.num_pages = d.num_pages;
   a.scale_log2 = d.softmax_scale * kLog2e;
-  hipLaunchKernelGGL(mla_mfma_kernel, dim3(L.num_tasks), dim3(kThreads), 0, L.stream, a);
+  if (d.page_size >= 32)
+    hipLaunchKernelGGL(mla_mfma_kernel<true>, dim3(L.num_tasks), dim3(kThreads), 0, L.stream, a);
+  else
+    hipLaunchKernelGGL(mla_mfma_kernel<false>, dim3(L.num_tasks), dim3(kThreads), 0, L.stream, a);
   return hipGetLastError();
 }
 
