@@ -332,6 +332,7 @@ void mla_mfma_kernel(MlaArgs a) {
   float l[2];
   f32x4_t o[kNb][2];
   for (int pass = 1;; ++pass) {
+    bool over = false;   // some head of this wave overflowed in this pass
     l[0] = l[1] = 0.f;
 #pragma unroll
     for (int nb = 0; nb < kNb; ++nb) o[nb][0] = o[nb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -429,7 +430,6 @@ void mla_mfma_kernel(MlaArgs a) {
             for (int e = 0; e < 4; ++e)
               if (t0 + 8 * g + 4 * blk + e >= end) s[blk][hb][e] = -INFINITY;
       }
-      bool over = false;
       u32x4_t pf[2];   // weights of tile k, bf16 (P^T operand)
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
@@ -439,10 +439,9 @@ void mla_mfma_kernel(MlaArgs a) {
                          fmaxf(fmaxf(s[1][hb][0], s[1][hb][1]), fmaxf(s[1][hb][2], s[1][hb][3])));
         mt = max_xor32(max_xor16(mt)) * a.scale_log2;
         if (m[hb] == -INFINITY) m[hb] = mt;   // the first tile of the first pass
-        if (mt > m[hb] + 64.f) {
-          over = true;
-          m[hb] = mt;   // the reference of the next pass
-        }
+        const bool up = mt > m[hb] + 64.f;
+        over = over || up;
+        m[hb] = up ? mt : m[hb];   // the reference of the next pass
         float ps = 0.f;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
@@ -455,7 +454,6 @@ void mla_mfma_kernel(MlaArgs a) {
         pf[hb] = u32x4_t{pack_bf16x2(s[0][hb][0], s[0][hb][1]), pack_bf16x2(s[0][hb][2], s[0][hb][3]),
                          pack_bf16x2(s[1][hb][0], s[1][hb][1]), pack_bf16x2(s[1][hb][2], s[1][hb][3])};
       }
-      if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) restart_pass = pass;
 
       // ---- O^T += V^T P^T over all 512 value dims, tile k ----
       {
@@ -482,6 +480,7 @@ void mla_mfma_kernel(MlaArgs a) {
     }
     // every wave has finished the pass (and its DMAs) before the decision;
     // the flag is only written by this pass, so it needs no reset
+    if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) restart_pass = pass;
     __builtin_amdgcn_s_waitcnt(kWaitVm0 & 0xc07f);   // vmcnt(0) lgkmcnt(0)
     bare_barrier();
     if (restart_pass != pass) break;
