@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--workload", type=str, default="2",
                     help="1-5, or 5d for the decode-only part of workload 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plan-param", action="append", default=[], metavar="NAME=VALUE",
+                    help="override one field of the planner parameters (repeatable)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -217,6 +219,14 @@ def main():
                         dtype=torch.bfloat16 if bf16 else torch.float32, mla=w.mla, causal=w.causal)
     num_cu = torch.cuda.get_device_properties(dev).multi_processor_count
 
+    plan_params = None
+    if args.plan_param:
+        plan_params = skv.default_params()
+        for item in args.plan_param:
+            name, _, val = item.partition("=")
+            cur = getattr(plan_params, name)   # unknown names raise AttributeError
+            setattr(plan_params, name, type(cur)(float(val)) if isinstance(cur, int) else float(val))
+
     # host planner, once per batch (timed on its own)
     plan_times = []
     for _ in range(5):
@@ -224,7 +234,8 @@ def main():
         if w.chunk_tokens:
             plan = skv.plan_fixed_chunks(w.seq_lens, spec, w.chunk_tokens, num_cu, q_lens=w.q_lens)
         else:
-            plan = skv.plan_splits(w.seq_lens, spec, num_cu, q_lens=w.q_lens, n_ext=w.n_ext)
+            plan = skv.plan_splits(w.seq_lens, spec, num_cu, q_lens=w.q_lens, n_ext=w.n_ext,
+                                   params=plan_params)
         plan_times.append(time.perf_counter() - t)
     info = plan.info()
     ws = plan.workspace(dev)

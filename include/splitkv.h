@@ -105,7 +105,15 @@ typedef struct skv_plan_params {
   int32_t use_calibration;    /* 1: take rho, delta_attn, delta_red and gamma from
                                  the library's MI355X fit for the kernel the
                                  problem selects (the fields below are ignored) */
-  int32_t reserved[2];
+  int32_t balanced_candidates; /* 1: the final choice also weighs the
+                                 proportional plans whose tasks fit 1-4 waves of
+                                 K slots (an addition to the pages' candidates:
+                                 NoSplit, the search result, the reference
+                                 plan); 0: the pages' candidates only;
+                                 -1 (default): the choice measured for the
+                                 kernel the problem selects (on for MLA, off
+                                 for GQA)                                      */
+  int32_t reserved;
   double rho;                 /* per-tile time floor                             */
   double delta_attn;          /* per attention task overhead, tile-equivalents   */
   double delta_red;           /* per reduction overhead                          */
@@ -132,11 +140,13 @@ typedef struct skv_plan_info {
   double nosplit_score;       /* model completion time of NoSplit                */
   double rho, delta_attn, delta_red, gamma;  /* model parameters in effect        */
   double tile_time_us;        /* microseconds per model unit (calibration)       */
-  int32_t reserved, reserved2;
+  int32_t balanced_candidates; /* 0 or 1: candidate set in effect               */
+  int32_t reserved;
 } skv_plan_info;
 
-/* Fill p with the library defaults: use_calibration = 1, tile 64,
- * max_splits 64, min_gain 0.10, and the pages' Table 2 (H100) values in rho,
+/* Fill p with the library defaults: use_calibration = 1,
+ * balanced_candidates = -1, tile 64, max_splits 64, min_gain 0.10, and the
+ * pages' Table 2 (H100) values in rho,
  * delta_attn, delta_red and gamma, which apply when use_calibration is 0. */
 void skv_plan_params_default(skv_plan_params* p);
 

@@ -55,6 +55,16 @@ Readings where the pages are silent:
 * overlap_reduction = 0 (a separate merge launch): every warp becomes free at
   the last attention completion. overlap_reduction = 1: each CTA's warps become
   free when it finishes its last attention task (the fused engine of the pages).
+
+Addition to the pages' candidate set (balanced_candidates = 1, the library's
+default; 0 gives the pages' set exactly): the final choice also weighs four
+proportional "balanced" plans, for m = 1..4 the plan with the smallest
+per-split tile budget t whose attention tasks fit m waves of K slots (request
+b gets min(ceil(n_b / t), n_b, max_splits) splits). The greedy +1 search cannot
+reach such a plan when several requests' tasks must all shrink together; the
+pages' reference plan plays this role for them, and the uniform stand-in above
+does not. The candidates are scored by the same model and keys, so they change
+the choice only when the model ranks one of them best.
 """
 from __future__ import annotations
 
@@ -75,6 +85,7 @@ class Params:
     max_splits: int = 64
     min_gain: float = 0.10
     overlap_reduction: int = 0
+    balanced_candidates: int = 1
 
 
 @dataclass
@@ -265,6 +276,33 @@ def reference_plan(pb: Problem, prm: Params):
     return uniform_plan(pb, prm, best_u)
 
 
+def balanced_plan(pb: Problem, prm: Params, wave_tasks: int):
+    """Proportional plan: the smallest per-split tile budget t whose plan has at
+    most wave_tasks attention tasks, request b getting min(ceil(n_b / t), n_b,
+    max_splits) splits (at least one); None if even NoSplit has more tasks."""
+    T = prm.tile_tokens
+    nt = [n_tiles(L, T) for L in pb.seq_lens]
+    per_split = [n * pb.num_kv_heads for n in pb.q_lens]   # tasks of one split
+
+    def counts(t):
+        return [max(1, min(-(-n // t), n, prm.max_splits)) for n in nt]
+
+    def tasks(c):
+        return sum(s * m for s, m in zip(c, per_split))
+
+    hi = max(max(nt), 1)
+    if tasks(counts(hi)) > wave_tasks:
+        return None
+    lo = 1
+    while lo < hi:   # tasks(counts(t)) does not increase with t
+        mid = (lo + hi) // 2
+        if tasks(counts(mid)) <= wave_tasks:
+            hi = mid
+        else:
+            lo = mid + 1
+    return counts(lo)
+
+
 def split_limits(pb: Problem, prm: Params, ref):
     """Per-request search limits: the reference counts, raised to at least four
     for decode requests with at least K tiles, capped by tiles and max_splits."""
@@ -317,8 +355,14 @@ def plan(pb: Problem, prm: Params, ref=None, trace=None):
                 trace.append(cur)
         else:
             break
+    cands = [cur, simulate(pb, prm, ref)]
+    if prm.balanced_candidates:
+        for m in (1, 2, 3, 4):
+            c = balanced_plan(pb, prm, m * prm.slots)
+            if c is not None:
+                cands.append(simulate(pb, prm, c))
     chosen = nosplit
-    for ev in (cur, simulate(pb, prm, ref)):
+    for ev in cands:
         if ev.key() < chosen.key():
             chosen = ev
     if chosen is not nosplit and not chosen.score <= (1.0 - prm.min_gain) * nosplit.score:

@@ -103,6 +103,8 @@ ModelParams model_params(const skv_attn_desc& d, int num_cu, const skv_plan_para
                                            : std::max(1, vs.merge_waves_per_cu / spc);
   m.max_splits = p->max_splits;
   m.overlap_reduction = p->overlap_reduction;
+  m.balanced_candidates = p->balanced_candidates >= 0 ? p->balanced_candidates
+                                                      : calibration(pick_variant(d)).balanced;
   m.min_gain = p->min_gain;
   if (p->use_calibration) {
     const Calibration c = calibration(pick_variant(d));
@@ -128,6 +130,8 @@ skv_status check_params(const skv_plan_params* p) {
   if (p->slots_per_cu < 0 || p->warps_per_slot < 0) return fail(SKV_ERR_INVALID_ARG, "negative slot counts");
   if (p->use_calibration != 0 && p->use_calibration != 1)
     return fail(SKV_ERR_INVALID_ARG, "use_calibration must be 0 or 1");
+  if (p->balanced_candidates < -1 || p->balanced_candidates > 1)
+    return fail(SKV_ERR_INVALID_ARG, "balanced_candidates must be -1, 0 or 1");
   if (p->overlap_reduction != 0 && p->overlap_reduction != 1)
     return fail(SKV_ERR_INVALID_ARG, "overlap_reduction must be 0 or 1");
   if (!(p->rho > 0) || !(p->delta_attn >= 0) || !(p->delta_red >= 0) || !(p->gamma >= 0) ||
@@ -269,6 +273,7 @@ void skv_plan_params_default(skv_plan_params* p) {
   p->max_splits = 64;
   p->overlap_reduction = 0;
   p->use_calibration = 1;
+  p->balanced_candidates = -1;
   p->rho = 0.43;
   p->delta_attn = 32.0;
   p->delta_red = 2.5;
@@ -404,8 +409,8 @@ skv_status skv_plan_get_info(const skv_plan* pl, skv_plan_info* info) {
   info->delta_red = pl->prm.delta_red;
   info->gamma = pl->prm.gamma;
   info->tile_time_us = pl->prm.tile_time_us;
+  info->balanced_candidates = pl->prm.balanced_candidates;
   info->reserved = 0;
-  info->reserved2 = 0;
   return SKV_OK;
 }
 
@@ -547,11 +552,17 @@ VariantShape variant_shape(Variant v) {
 //  - MLA: a work-group's tile rate is set by its own matrix and LDS work, not
 //    by shared HBM, so a lone work-group is no faster than one in a full wave
 //    (rho = 1), and the per-task overhead is small (Q load, epilogue).
+// The last field turns on the proportional candidates by default. On the MLA
+// 64-request DeepSeek shape the one-task-per-slot proportional plan the model
+// prefers ran 0.6-3.6% faster than the search result in alternating runs
+// (within the spread of separate runs); on the GQA 32-request
+// shape the model's one-wave proportional plan (512 tasks) ran 1% slower than
+// the two-wave search result, so GQA keeps the pages' candidates.
 Calibration calibration(Variant v) {
   switch (v) {
-    case Variant::GqaMfma: return {0.50, 3.0, 1.0, 0.47, 2.66};
-    case Variant::GqaValu: return {0.80, 1.0, 1.0, 0.47, 11.2};
-    default: return {1.00, 2.0, 1.0, 0.47, 7.4};
+    case Variant::GqaMfma: return {0.50, 3.0, 1.0, 0.47, 2.66, 0};
+    case Variant::GqaValu: return {0.80, 1.0, 1.0, 0.47, 11.2, 0};
+    default: return {1.00, 2.0, 1.0, 0.47, 7.4, 1};
   }
 }
 }  // namespace skv

@@ -52,6 +52,7 @@ struct ModelParams {
   int warps_per_slot = 4;
   int max_splits = 64;
   int overlap_reduction = 0;
+  int balanced_candidates = 1;
   double rho = 0.43, delta_attn = 32.0, delta_red = 2.5, gamma = 0.47;
   double min_gain = 0.10, tile_time_us = 1.08;
 };
@@ -79,6 +80,7 @@ void build_tasks(const Problem& pb, const ModelParams& prm,
                  std::vector<TaskDesc>& out, std::vector<double>* costs);
 int reduction_run(const Problem& pb, const ModelParams& prm);
 Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits);
+std::vector<int> balanced_plan(const Problem& pb, const ModelParams& prm, int64_t wave_tasks);
 std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm);
 std::vector<int> split_limits(const Problem& pb, const ModelParams& prm,
                               const std::vector<int>& ref);
@@ -131,6 +133,7 @@ struct VariantShape {
 VariantShape variant_shape(Variant v);
 struct Calibration {
   double rho, delta_attn, delta_red, gamma, tile_time_us;
+  int balanced;   // whether proportional plans join the final choice by default
 };
 Calibration calibration(Variant v);
 

@@ -426,6 +426,41 @@ std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
   return uniform_plan(pb, prm, best_u);
 }
 
+// Proportional plan whose attention tasks fit wave_tasks (an addition to the
+// pages' candidates): the smallest per-split tile budget t such that request b
+// with min(ceil(n_b / t), n_b, max_splits) splits (at least one) gives at most
+// wave_tasks tasks in all; empty if even NoSplit has more. The task count does
+// not increase with t, so t is found by bisection.
+std::vector<int> balanced_plan(const Problem& pb, const ModelParams& prm, int64_t wave_tasks) {
+  const int B = (int)pb.seq_lens.size();
+  std::vector<int64_t> nt(B), per_split(B);
+  int64_t hi = 1;
+  for (int b = 0; b < B; ++b) {
+    nt[b] = n_tiles(pb.seq_lens[b], prm.tile_tokens);
+    per_split[b] = pb.q_lens[b] * (int64_t)pb.num_kv_heads;
+    hi = std::max(hi, nt[b]);
+  }
+  std::vector<int> c(B);
+  auto tasks_at = [&](int64_t t) {
+    int64_t tasks = 0;
+    for (int b = 0; b < B; ++b) {
+      const int64_t s = std::max<int64_t>(1, std::min<int64_t>({(nt[b] + t - 1) / t, nt[b], (int64_t)prm.max_splits}));
+      c[b] = (int)s;
+      tasks += s * per_split[b];
+    }
+    return tasks;
+  };
+  if (tasks_at(hi) > wave_tasks) return {};
+  int64_t lo = 1;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) / 2;
+    if (tasks_at(mid) <= wave_tasks) hi = mid;
+    else lo = mid + 1;
+  }
+  tasks_at(lo);
+  return c;
+}
+
 std::vector<int> split_limits(const Problem& pb, const ModelParams& prm,
                               const std::vector<int>& ref) {
   const int B = (int)pb.seq_lens.size();
@@ -481,10 +516,24 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
     else
       break;
   }
+  // final candidates in order: the search result, the reference plan, then
+  // the proportional plans fitting 1..4 waves (when enabled); first best wins
+  std::vector<std::vector<int>> finals;
+  finals.push_back(ref);
+  if (prm.balanced_candidates)
+    for (int m = 1; m <= 4; ++m) {
+      std::vector<int> c = balanced_plan(pb, prm, (int64_t)m * prm.slots);
+      if (!c.empty()) finals.push_back(std::move(c));
+    }
+  std::vector<Evaluation> fevs(finals.size());
+  pool.run(finals.size(), [&](size_t i) { fevs[i] = simulate(pb, prm, finals[i]); });
   Evaluation chosen = nosplit;
   bool chose_nosplit = true;
-  for (int k = 0; k < 2; ++k) {
-    Evaluation ev = k == 0 ? cur : simulate(pb, prm, ref);
+  if (key_less(cur, chosen)) {
+    chosen = cur;
+    chose_nosplit = false;
+  }
+  for (auto& ev : fevs) {
     if (key_less(ev, chosen)) {
       chosen = std::move(ev);
       chose_nosplit = false;

@@ -28,7 +28,8 @@ def reference_for(plan: skv.Plan, spec: skv.AttnSpec, seq, qlen, n_ext=0, params
     prm = PL.Params(tile_tokens=64, slots=inf.slots, warps_per_slot=inf.warps_per_slot,
                     rho=inf.rho, delta_attn=inf.delta_attn, delta_red=inf.delta_red,
                     gamma=inf.gamma, max_splits=p.max_splits, min_gain=p.min_gain,
-                    overlap_reduction=p.overlap_reduction)
+                    overlap_reduction=p.overlap_reduction,
+                    balanced_candidates=inf.balanced_candidates)
     pb = PL.Problem(seq_lens=[int(x) for x in seq], q_lens=[int(x) for x in qlen],
                     num_kv_heads=spec.num_kv_heads, rows_per_token=spec.num_q_heads, n_ext=n_ext,
                     causal=spec.causal)
@@ -54,6 +55,7 @@ def test_fig8_through_the_abi():
     spec = skv.AttnSpec(1, 1, 64, 64, 16, dtype=torch.float32)
     p = skv.default_params()
     p.use_calibration = 0
+    p.balanced_candidates = 0   # the pages' candidate set, as in their example
     p.slots_per_cu, p.warps_per_slot = 1, 1
     p.rho, p.delta_attn, p.delta_red, p.gamma = 0.75, 4.0, 4.0, 1.0
     p.overlap_reduction = 1
@@ -97,7 +99,11 @@ def test_random_batches_bit_exact(seed):
     if seed % 11 == 5:
         p.use_calibration = 0
         p.delta_red, p.gamma = 0.0, 0.0        # zero-cost reductions: ties between warps
+    if seed % 8 in (1, 7):
+        p.balanced_candidates = 1 if seed % 8 == 1 else 0   # against the kernel's default
     plan = skv.plan_splits(seq, spec, num_cu=num_cu, q_lens=q, n_ext=n_ext, params=p)
+    assert plan.info().balanced_candidates == (
+        p.balanced_candidates if p.balanced_candidates >= 0 else int(spec.mla))
     pb, prm, ev, ns = reference_for(plan, spec, seq, q, n_ext, p)
     assert_same(plan, pb, prm, ev, ns)
 

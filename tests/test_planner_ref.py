@@ -147,3 +147,56 @@ def test_task_order_rules():
     assert [t.b for t in tasks][:20] == [1] * 20 and [t.b for t in tasks][20:] == [0, 0]
     # causal chunk rows see L - n + i + 1 tokens: tiles grow with i
     assert tasks[0].n_t == math.ceil(181 / 64) and tasks[19].n_t == math.ceil(200 / 64)
+
+
+def test_balanced_plan_hand_examples():
+    # tiles [10, 3, 1], one task per split: t = 1 gives 14 tasks, t = 2 gives [5, 2, 1] = 8
+    T = 64
+    pb = PL.Problem(seq_lens=[10 * T, 3 * T, 1], q_lens=[1, 1, 1])
+    prm = PL.Params(tile_tokens=T, slots=4, max_splits=64)
+    assert PL.balanced_plan(pb, prm, 14) == [10, 3, 1]
+    assert PL.balanced_plan(pb, prm, 8) == [5, 2, 1]
+    assert PL.balanced_plan(pb, prm, 7) == [4, 1, 1]      # t = 3: 4 + 1 + 1 = 6
+    assert PL.balanced_plan(pb, prm, 3) == [1, 1, 1]
+    assert PL.balanced_plan(pb, prm, 2) is None           # NoSplit already has 3 tasks
+    prm.max_splits = 3
+    assert PL.balanced_plan(pb, prm, 100) == [3, 3, 1]
+    # two KV heads and a 2-token request: each split of request 1 is 4 tasks
+    pb = PL.Problem(seq_lens=[10 * T, 3 * T], q_lens=[1, 2], num_kv_heads=2, rows_per_token=2)
+    prm = PL.Params(tile_tokens=T, slots=4)
+    assert PL.balanced_plan(pb, prm, 12) == [4, 1]   # t = 3: 4*2 + 1*4; t = 2 gives 18
+    # Figure 8's histories: one wave of 4 CTAs gives (2,1,1), two waves (4,3,1)
+    g, pb, prm = fig8()
+    assert PL.balanced_plan(pb, prm, 4) == [2, 1, 1]
+    assert PL.balanced_plan(pb, prm, 8) == [4, 3, 1]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_balanced_plan_is_smallest_budget(seed):
+    # the bisection over the tile budget equals a linear scan from t = 1
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 10))
+    L = rng.integers(1, 9000, size=B).tolist()
+    n = [int(rng.integers(1, 3)) if rng.random() < 0.3 else 1 for _ in range(B)]
+    n = [min(a, b) for a, b in zip(n, L)]
+    pb = PL.Problem(seq_lens=L, q_lens=n, num_kv_heads=int(rng.integers(1, 4)),
+                    rows_per_token=2)
+    prm = PL.Params(slots=int(rng.integers(2, 40)), max_splits=int(rng.integers(2, 80)))
+    nt = [PL.n_tiles(x, prm.tile_tokens) for x in L]
+    per = [q * pb.num_kv_heads for q in n]
+    for wave in (prm.slots, 2 * prm.slots, 4 * prm.slots, 1):
+        want = None
+        for t in range(1, max(nt) + 1):
+            c = [max(1, min(math.ceil(a / t), a, prm.max_splits)) for a in nt]
+            if sum(s * m for s, m in zip(c, per)) <= wave:
+                want = c
+                break
+        assert PL.balanced_plan(pb, prm, wave) == want
+
+
+def test_fig8_choice_with_and_without_balanced_candidates():
+    # the balanced candidates of Figure 8 ((2,1,1), (4,3,1), ...) all score above 104
+    g, pb, prm = fig8()
+    for bc in (0, 1):
+        prm.balanced_candidates = bc
+        assert list(PL.plan(pb, prm, ref=g["reference_plan"]).splits) == g["chosen"]
