@@ -16,6 +16,7 @@
 // reproducible bit for bit.
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <condition_variable>
 #include <functional>
 #include <mutex>
@@ -26,6 +27,8 @@
 #include <thread>
 #include <tuple>
 #include <vector>
+
+#include <unistd.h>
 
 #include "internal.hpp"
 
@@ -143,112 +146,252 @@ struct Group {
   bool operator>(const Group& o) const { return fw > o.fw; }
 };
 
-struct SimScratch {
-  std::vector<double> cost;       // attention task costs in queue order
-  std::vector<int32_t> req;       // request of each queued task
-  std::vector<double> fifo_cost;
-  std::vector<int32_t> fifo_req;
-  std::vector<uint32_t> order;
-  std::vector<double> done_fw, ev_fw, ev_t, done;
-  std::vector<Group> heap;
+// A run of consecutive queued tasks of one request with equal cost. Such tasks
+// are interchangeable in the model (same cost, same request), so the queue is
+// kept as runs rather than single tasks.
+struct QEntry {
+  double cost;
+  int32_t req;
+  int64_t count;
 };
 
-// Queue of attention tasks (cost and request), in the order build_tasks gives.
-static void queue_costs(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits,
-                        SimScratch& sc) {
+// A queue is a sequence of segments of runs (one segment per request for the
+// FIFO orders, one merged segment for the longest-first order).
+struct Seg {
+  const QEntry* p;
+  size_t n;
+};
+
+// Request b's tasks with s splits in FIFO order (query token, KV head, split),
+// consecutive equal costs merged.
+void request_fifo(const Problem& pb, const ModelParams& prm, int b, int s, std::vector<QEntry>& out) {
+  out.clear();
   const int T = prm.tile_tokens;
-  const int B = (int)pb.seq_lens.size();
-  bool any_split = false, decode_only = true;
-  for (int b = 0; b < B; ++b) {
-    any_split |= splits[b] > 1;
-    decode_only &= is_decode(pb.q_lens[b]);
-  }
-  sc.fifo_cost.clear();
-  sc.fifo_req.clear();
-  for (int b = 0; b < B; ++b) {
-    const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
-    const int64_t total = n_tiles(L, T);
-    const int s = splits[b];
-    for (int64_t qi = 0; qi < n; ++qi) {
-      const int64_t vis = pb.causal ? L - n + qi + 1 : L;
-      const int64_t vis_t = n_tiles(vis, T);
-      for (int g = 0; g < pb.num_kv_heads; ++g) {
-        // the same tile split as split_ranges: the first total mod s parts
-        // are one tile longer
-        int64_t lo_t = 0;
-        for (int r = 0; r < s; ++r) {
-          const int64_t len = total / s + (r < total % s ? 1 : 0);
-          const int64_t hi_t = lo_t + len;
-          const int64_t nt = std::max<int64_t>(0, std::min(hi_t, vis_t) - lo_t);
-          sc.fifo_cost.push_back((double)nt + prm.delta_attn);
-          sc.fifo_req.push_back(b);
-          lo_t = hi_t;
-        }
+  const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
+  const int64_t total = n_tiles(L, T);
+  for (int64_t qi = 0; qi < n; ++qi) {
+    const int64_t vis = pb.causal ? L - n + qi + 1 : L;
+    const int64_t vis_t = n_tiles(vis, T);
+    for (int g = 0; g < pb.num_kv_heads; ++g) {
+      // the same tile split as split_ranges: the first total mod s parts are
+      // one tile longer
+      int64_t lo_t = 0;
+      for (int r = 0; r < s; ++r) {
+        const int64_t len = total / s + (r < total % s ? 1 : 0);
+        const int64_t hi_t = lo_t + len;
+        const int64_t nt = std::max<int64_t>(0, std::min(hi_t, vis_t) - lo_t);
+        const double c = (double)nt + prm.delta_attn;
+        if (!out.empty() && out.back().cost == c)
+          ++out.back().count;
+        else
+          out.push_back({c, b, 1});
+        lo_t = hi_t;
       }
     }
   }
-  const size_t N = sc.fifo_cost.size();
-  sc.order.resize(N);
-  std::iota(sc.order.begin(), sc.order.end(), 0u);
-  if (decode_only && any_split) {
-    const double* c = sc.fifo_cost.data();
-    std::stable_sort(sc.order.begin(), sc.order.end(), [c](uint32_t x, uint32_t y) { return c[x] > c[y]; });
-  } else if (!decode_only) {
-    const int32_t* r = sc.fifo_req.data();
-    std::stable_partition(sc.order.begin(), sc.order.end(),
-                          [&](uint32_t x) { return !is_decode(pb.q_lens[r[x]]); });
-  }
-  sc.cost.resize(N);
-  sc.req.resize(N);
-  for (size_t i = 0; i < N; ++i) {
-    sc.cost[i] = sc.fifo_cost[sc.order[i]];
-    sc.req[i] = sc.fifo_req[sc.order[i]];
-  }
 }
 
-}  // namespace
+// The same tasks longest first: one run per distinct cost, costs descending.
+void request_sorted(const std::vector<QEntry>& fifo, std::vector<QEntry>& out) {
+  out.assign(fifo.begin(), fifo.end());
+  std::sort(out.begin(), out.end(), [](const QEntry& x, const QEntry& y) { return x.cost > y.cost; });
+  size_t w = 0;
+  for (size_t i = 0; i < out.size(); ++i) {
+    if (w > 0 && out[w - 1].cost == out[i].cost)
+      out[w - 1].count += out[i].count;
+    else
+      out[w++] = out[i];
+  }
+  out.resize(w);
+}
 
-Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits) {
-  thread_local SimScratch sc;
+// Longest-first queue order of the whole batch: costs descending, and among
+// equal costs the earlier request first (a stable sort of the FIFO queue).
+bool lpt_before(const QEntry& x, const QEntry& y) {
+  return x.cost > y.cost || (x.cost == y.cost && x.req < y.req);
+}
+
+// Which order build_tasks uses for this plan.
+enum class QOrder { Fifo, Lpt, ChunkFirst };
+QOrder queue_order(const Problem& pb, const std::vector<int>& splits) {
+  bool any_split = false, decode_only = true;
+  for (size_t b = 0; b < splits.size(); ++b) {
+    any_split |= splits[b] > 1;
+    decode_only &= is_decode(pb.q_lens[b]);
+  }
+  if (decode_only && any_split) return QOrder::Lpt;
+  return decode_only ? QOrder::Fifo : QOrder::ChunkFirst;
+}
+
+struct SimScratch {
+  std::vector<double> done_fw, ev_fw, ev_t, done;
+  std::vector<Group> heap;
+  std::vector<std::pair<double, int64_t>> warps;   // min-heap of (free time, warps)
+  std::vector<QEntry> tmp;
+  std::vector<std::vector<QEntry>> per_req;
+  std::vector<Seg> segs;
+};
+
+struct SimResult {
+  double score = 0, t_attn = 0;
+  int64_t n_tasks = 0;
+};
+
+bool warp_later(const std::pair<double, int64_t>& x, const std::pair<double, int64_t>& y) {
+  return x.first > y.first;
+}
+
+// State of a run just before one of its task-start steps, from which a run
+// over a queue that agrees with it up to the entries that step reads can
+// continue (the steps before it cannot tell the two queues apart).
+struct Snapshot {
+  double t = 0, vw = 0;
+  int64_t running = 0, started = 0;   // tasks running / started before the step
+  int64_t free_slots = 0;             // slots the step fills
+  size_t si = 0, ei = 0;              // queue position (segment, run)
+  int64_t off = 0;                    // tasks of that run already started
+  size_t n_ev = 0;                    // events before the step, its own included
+  std::vector<Group> heap;
+  std::vector<double> done_fw;
+};
+
+// A recording run: its events, and for each resume threshold (a global run
+// index, ascending) the state before the first step that reads that run.
+struct Recording {
+  std::vector<int64_t> thresholds;
+  std::vector<size_t> snap_of;        // per threshold, index into snaps
+  std::vector<Snapshot> snaps;
+  std::vector<double> ev_fw, ev_t;
+};
+
+// The model run over a queue given as segments of runs. tail (optional)
+// receives the requests whose attention ends at the attention completion.
+// With `from`, the run continues from a snapshot of the recording `base`; with
+// `rec` (non-overlapped model only), it records snapshots for rec->thresholds.
+SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits,
+                         const Seg* segs, size_t nseg, SimScratch& sc, std::vector<int>* tail,
+                         const Snapshot* from = nullptr, const Recording* base = nullptr,
+                         Recording* rec = nullptr, int run_hint = 0) {
   const int B = (int)pb.seq_lens.size();
   const int64_t K = prm.slots;
-  queue_costs(pb, prm, splits, sc);
-  const int64_t nt = (int64_t)sc.cost.size();
-  const double* cost = sc.cost.data();
-  const int32_t* req = sc.req.data();
+  int64_t nt = 0;
+  for (size_t i = 0; i < nseg; ++i)
+    for (size_t j = 0; j < segs[i].n; ++j) nt += segs[i].p[j].count;
 
   // ---- attention phase ----
-  sc.done_fw.assign(B, 0.0);
   sc.ev_fw.clear();
   sc.ev_t.clear();
-  sc.heap.clear();
-  std::map<double, int64_t> release;  // slot release times (for overlapped reductions)
+  std::map<double, int64_t> release;  // slot release times (overlapped reductions only)
   auto heap_push = [&](double fw, int64_t n) {
     sc.heap.push_back({fw, n});
     std::push_heap(sc.heap.begin(), sc.heap.end(), std::greater<Group>());
   };
   double t = 0.0, vw = 0.0;
-  int64_t running = 0, nxt = 0;
-  // start up to `free_slots` queued tasks at work clock vw; returns how many started
+  int64_t running = 0, started_total = 0;
+  size_t si = 0, ei = 0;   // queue position: segment, run
+  int64_t off = 0;         // tasks of the current run already started
+  size_t n_prefix = 0;     // events taken from `base`
+  if (from) {
+    sc.done_fw.assign(from->done_fw.begin(), from->done_fw.end());
+    sc.heap.assign(from->heap.begin(), from->heap.end());
+    t = from->t;
+    vw = from->vw;
+    running = from->running;
+    started_total = from->started;
+    si = from->si;
+    ei = from->ei;
+    off = from->off;
+    n_prefix = from->n_ev;
+  } else {
+    sc.done_fw.assign(B, 0.0);
+    sc.heap.clear();
+  }
+  std::vector<size_t> seg_start;
+  if (rec) {
+    seg_start.resize(nseg + 1, 0);
+    for (size_t i = 0; i < nseg; ++i) seg_start[i + 1] = seg_start[i] + segs[i].n;
+    rec->snap_of.assign(rec->thresholds.size(), 0);
+    rec->snaps.clear();
+  }
+  size_t next_thr = 0;
+  int64_t max_read = -1;
+  auto skip_empty = [&] {
+    while (si < nseg && ei >= segs[si].n) {
+      ++si;
+      ei = 0;
+    }
+  };
+  skip_empty();
+  auto entry = [&]() -> const QEntry& {
+    if (rec) max_read = std::max<int64_t>(max_read, (int64_t)(seg_start[si] + ei));
+    return segs[si].p[ei];
+  };
+  // start up to free_slots queued tasks at work clock vw, one group per maximal
+  // stretch of equal cost; returns how many started
   auto start_tasks = [&](int64_t free_slots) {
     int64_t started = 0;
-    while (started < free_slots && nxt < nt) {
-      const double c = cost[nxt];
-      int64_t j = nxt + 1;
-      const int64_t lim = nxt + (free_slots - started);
-      while (j < lim && j < nt && cost[j] == c) ++j;
+    while (started < free_slots && started_total < nt) {
+      const double c = entry().cost;
       const double fw = vw + c;
-      for (int64_t i = nxt; i < j; ++i)
-        if (fw > sc.done_fw[req[i]]) sc.done_fw[req[i]] = fw;
-      heap_push(fw, j - nxt);
-      started += j - nxt;
-      nxt = j;
+      const int64_t lim = free_slots - started;
+      int64_t taken = 0;
+      while (taken < lim && si < nseg && entry().cost == c) {
+        const QEntry& e = segs[si].p[ei];
+        const int64_t k = std::min(e.count - off, lim - taken);
+        if (fw > sc.done_fw[e.req]) sc.done_fw[e.req] = fw;
+        taken += k;
+        off += k;
+        if (off == e.count) {
+          off = 0;
+          ++ei;
+          skip_empty();
+        }
+      }
+      heap_push(fw, taken);
+      started += taken;
+      started_total += taken;
     }
     running += started;
     return started;
   };
-  start_tasks(K);
-  if (K > nt) release[0.0] += (K - nt) * prm.warps_per_slot;
+  // a task-start step, recorded when a pending threshold is within its reach
+  // (a step filling m slots reads at most m + 1 runs)
+  auto step = [&](int64_t free_slots) {
+    if (!rec || next_thr >= rec->thresholds.size()) return start_tasks(free_slots);
+    const int64_t pos = si < nseg ? (int64_t)(seg_start[si] + ei) : (int64_t)seg_start[nseg];
+    const bool reach = rec->thresholds[next_thr] <= pos + free_slots;
+    if (reach) {
+      Snapshot sn;
+      sn.t = t;
+      sn.vw = vw;
+      sn.running = running;
+      sn.started = started_total;
+      sn.free_slots = free_slots;
+      sn.si = si;
+      sn.ei = ei;
+      sn.off = off;
+      sn.n_ev = sc.ev_fw.size();
+      sn.heap = sc.heap;
+      sn.done_fw = sc.done_fw;
+      rec->snaps.push_back(std::move(sn));
+    }
+    const int64_t r = start_tasks(free_slots);
+    if (reach) {
+      bool used = false;
+      while (next_thr < rec->thresholds.size() && rec->thresholds[next_thr] <= max_read) {
+        rec->snap_of[next_thr++] = rec->snaps.size() - 1;
+        used = true;
+      }
+      if (!used) rec->snaps.pop_back();
+    }
+    return r;
+  };
+  if (from) {
+    step(from->free_slots);
+  } else {
+    step(K);
+    if (prm.overlap_reduction && K > nt) release[0.0] += (K - nt) * prm.warps_per_slot;
+  }
   while (!sc.heap.empty()) {
     const double tau = std::max(prm.rho, (double)running / (double)K);
     const double fw = sc.heap.front().fw;
@@ -263,41 +406,59 @@ Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector
     running -= m;
     sc.ev_fw.push_back(fw);
     sc.ev_t.push_back(t);
-    const int64_t started = start_tasks(m);
-    if (m > started) release[t] += (m - started) * prm.warps_per_slot;
+    const int64_t started = step(m);
+    if (prm.overlap_reduction && m > started) release[t] += (m - started) * prm.warps_per_slot;
   }
   const double t_attn = t;
-  // a request's attention ends at the event of its latest-finishing task
+  // a request's attention ends at the event of its latest-finishing task (the
+  // events are the recording's first n_prefix, then this run's own)
   sc.done.assign(B, 0.0);
+  const double* pfw = base ? base->ev_fw.data() : nullptr;
+  const double* pt = base ? base->ev_t.data() : nullptr;
   for (int b = 0; b < B; ++b) {
     const double f = sc.done_fw[b];
     if (f == 0.0) continue;  // no task started (cannot happen: every request has one)
-    const auto it = std::lower_bound(sc.ev_fw.begin(), sc.ev_fw.end(), f);
-    sc.done[b] = sc.ev_t[it - sc.ev_fw.begin()];
+    if (n_prefix > 0 && f <= pfw[n_prefix - 1]) {
+      sc.done[b] = pt[std::lower_bound(pfw, pfw + n_prefix, f) - pfw];
+    } else {
+      const auto it = std::lower_bound(sc.ev_fw.begin(), sc.ev_fw.end(), f);
+      sc.done[b] = sc.ev_t[it - sc.ev_fw.begin()];
+    }
+  }
+  if (rec) {
+    rec->ev_fw.assign(sc.ev_fw.begin(), sc.ev_fw.end());
+    rec->ev_t.assign(sc.ev_t.begin(), sc.ev_t.end());
   }
 
   // ---- reduction phase: units in request order, each on the earliest-free warp ----
-  const int run = reduction_run(pb, prm);
+  // (a heap of (free time, count) groups; equal times need not be merged, since
+  // every unit still starts at the earliest free time)
+  const int run = run_hint > 0 ? run_hint : reduction_run(pb, prm);
   const int64_t nwarps = K * prm.warps_per_slot;
-  std::map<double, int64_t> warps;
-  if (prm.overlap_reduction)
-    warps = std::move(release);
-  else
-    warps[t_attn] = nwarps;
+  auto& wh = sc.warps;
+  wh.clear();
+  if (prm.overlap_reduction) {
+    for (const auto& kv : release) wh.push_back(kv);
+    std::make_heap(wh.begin(), wh.end(), warp_later);
+  } else {
+    wh.push_back({t_attn, nwarps});
+  }
   double score = t_attn;
   auto assign = [&](int64_t k, double c, double d) {
     while (k > 0) {
-      auto it = warps.begin();
-      const double a = it->first;
-      const int64_t avail = it->second;
+      const double a = wh.front().first;
+      const int64_t avail = wh.front().second;
       const double st = a > d ? a : d;
       const double end = st + c;
       const int64_t j = std::min(k, avail);
-      if (j == avail)
-        warps.erase(it);
-      else
-        it->second -= j;
-      warps[end] += j;
+      if (j == avail) {
+        std::pop_heap(wh.begin(), wh.end(), warp_later);
+        wh.pop_back();
+      } else {
+        wh.front().second -= j;
+      }
+      wh.push_back({end, j});
+      std::push_heap(wh.begin(), wh.end(), warp_later);
       if (end > score) score = end;
       k -= j;
     }
@@ -309,15 +470,60 @@ Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector
     if (full > 0) assign(full, prm.delta_red + prm.gamma * (double)run * (double)s_u, sc.done[b]);
     if (rem > 0) assign(1, prm.delta_red + prm.gamma * (double)rem * (double)s_u, sc.done[b]);
   }
+  if (tail) {
+    tail->clear();
+    for (int b = 0; b < B; ++b)
+      if (sc.done[b] == t_attn) tail->push_back(b);
+  }
+  return {score, t_attn, nt};
+}
+
+// Segments of a plan's queue built from scratch.
+void build_queue(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits,
+                 SimScratch& sc) {
+  const int B = (int)pb.seq_lens.size();
+  const QOrder ord = queue_order(pb, splits);
+  sc.per_req.resize(B);
+  for (int b = 0; b < B; ++b) request_fifo(pb, prm, b, splits[b], sc.per_req[b]);
+  sc.segs.clear();
+  if (ord == QOrder::Lpt) {
+    sc.tmp.clear();
+    std::vector<QEntry> srt;
+    for (int b = 0; b < B; ++b) {
+      request_sorted(sc.per_req[b], srt);
+      sc.tmp.insert(sc.tmp.end(), srt.begin(), srt.end());
+    }
+    std::stable_sort(sc.tmp.begin(), sc.tmp.end(), lpt_before);
+    sc.segs.push_back({sc.tmp.data(), sc.tmp.size()});
+    return;
+  }
+  if (ord == QOrder::ChunkFirst)
+    for (int b = 0; b < B; ++b)
+      if (!is_decode(pb.q_lens[b])) sc.segs.push_back({sc.per_req[b].data(), sc.per_req[b].size()});
+  for (int b = 0; b < B; ++b)
+    if (ord == QOrder::Fifo || is_decode(pb.q_lens[b]))
+      sc.segs.push_back({sc.per_req[b].data(), sc.per_req[b].size()});
+}
+
+Evaluation to_eval(const std::vector<int>& splits, const SimResult& r, std::vector<int>&& tail) {
   Evaluation ev;
   ev.splits = splits;
-  ev.score = score;
-  ev.t_attn = t_attn;
-  ev.n_tasks = nt;
+  ev.score = r.score;
+  ev.t_attn = r.t_attn;
+  ev.n_tasks = r.n_tasks;
   ev.total_splits = std::accumulate(splits.begin(), splits.end(), (int64_t)0);
-  for (int b = 0; b < B; ++b)
-    if (sc.done[b] == t_attn) ev.tail.push_back(b);
+  ev.tail = std::move(tail);
   return ev;
+}
+
+}  // namespace
+
+Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits) {
+  thread_local SimScratch sc;
+  build_queue(pb, prm, splits, sc);
+  std::vector<int> tail;
+  const SimResult r = simulate_queue(pb, prm, splits, sc.segs.data(), sc.segs.size(), sc, &tail);
+  return to_eval(splits, r, std::move(tail));
 }
 
 static bool key_less(const Evaluation& a, const Evaluation& b) {
@@ -334,9 +540,11 @@ static std::vector<int> uniform_plan(const Problem& pb, const ModelParams& prm, 
   return out;
 }
 
-// Worker threads for independent simulations. The caller takes part; each
-// index is run exactly once and results are written by index, so the outcome
-// does not depend on which thread ran what.
+// Worker threads for independent simulations, shared by every planner call in
+// the process. The caller takes part; each index is run exactly once and
+// results are written by index, so the outcome does not depend on which thread
+// ran what. A call made while another thread is using the pool runs its items
+// on the calling thread.
 class SimPool {
  public:
   SimPool() {
@@ -344,10 +552,11 @@ class SimPool {
     const unsigned n = std::max(1u, std::min(16u, hw));
     for (unsigned i = 1; i < n; ++i) workers_.emplace_back([this] { loop(); });
   }
+  // (a process forked from this one has no workers: it runs batches itself)
   ~SimPool() {
     {
       std::lock_guard<std::mutex> g(mu_);
-      stop_ = true;
+      stop_.store(true);
     }
     cv_.notify_all();
     for (auto& w : workers_) w.join();
@@ -355,74 +564,144 @@ class SimPool {
   size_t threads() const { return workers_.size() + 1; }
   void run(size_t count, const std::function<void(size_t)>& fn) {
     if (count == 0) return;
-    if (workers_.empty() || count < 4) {
+    std::unique_lock<std::mutex> busy(busy_, std::try_to_lock);
+    if (workers_.empty() || count < 4 || !busy.owns_lock() || getpid() != pid_) {
       for (size_t i = 0; i < count; ++i) fn(i);
       return;
     }
+    pending_.store(count);
+    fn_.store(&fn);
+    count_.store(count);
+    next_.store(0);
     {
       std::lock_guard<std::mutex> g(mu_);
-      fn_ = &fn;
-      count_ = count;
-      next_.store(0);
-      pending_ = count;
-      ++gen_;
+      gen_.fetch_add(1);
+      if (sleepers_ > 0) cv_.notify_all();
     }
-    cv_.notify_all();
     work();
-    std::unique_lock<std::mutex> g(mu_);
-    done_cv_.wait(g, [this] { return pending_ == 0; });
-    fn_ = nullptr;
+    // the search issues many short batches: wait briefly by polling first
+    if (!spin_until([this] { return pending_.load() == 0; })) {
+      std::unique_lock<std::mutex> g(mu_);
+      done_cv_.wait(g, [this] { return pending_.load() == 0; });
+    }
   }
 
  private:
+  template <class Pred>
+  static bool spin_until(Pred p) {
+    const auto t0 = std::chrono::steady_clock::now();
+    for (unsigned i = 1;; ++i) {
+      if (p()) return true;
+      if ((i & 63) == 0 && std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(200))
+        return false;
+    }
+  }
   void work() {
-    size_t finished = 0;
     for (;;) {
       const size_t i = next_.fetch_add(1);
-      if (i >= count_) break;
-      (*fn_)(i);
-      ++finished;
-    }
-    if (finished) {
-      std::lock_guard<std::mutex> g(mu_);
-      pending_ -= finished;
-      if (pending_ == 0) done_cv_.notify_all();
+      if (i >= count_.load()) break;
+      (*fn_.load())(i);
+      if (pending_.fetch_sub(1) == 1) {
+        std::lock_guard<std::mutex> g(mu_);
+        done_cv_.notify_all();
+      }
     }
   }
   void loop() {
     uint64_t seen = 0;
     for (;;) {
-      {
+      if (!spin_until([&] { return stop_.load() || gen_.load() != seen; })) {
         std::unique_lock<std::mutex> g(mu_);
-        cv_.wait(g, [&] { return stop_ || gen_ != seen; });
-        if (stop_) return;
-        seen = gen_;
+        ++sleepers_;
+        cv_.wait(g, [&] { return stop_.load() || gen_.load() != seen; });
+        --sleepers_;
       }
+      if (stop_.load()) return;
+      seen = gen_.load();
       work();
     }
   }
   std::vector<std::thread> workers_;
-  std::mutex mu_;
+  std::mutex busy_, mu_;
   std::condition_variable cv_, done_cv_;
-  const std::function<void(size_t)>* fn_ = nullptr;
-  size_t count_ = 0, pending_ = 0;
-  std::atomic<size_t> next_{0};
-  uint64_t gen_ = 0;
-  bool stop_ = false;
+  std::atomic<const std::function<void(size_t)>*> fn_{nullptr};
+  std::atomic<size_t> count_{0}, next_{0}, pending_{0};
+  std::atomic<uint64_t> gen_{0};
+  std::atomic<bool> stop_{false};
+  int sleepers_ = 0;
+  const pid_t pid_ = getpid();
 };
+
+static SimPool& sim_pool() {
+  static SimPool pool;
+  return pool;
+}
+
+// A lower bound on a plan's score in the non-overlapped model. However many
+// slots run, attention advances by at most K tile units per time unit
+// (k / tau(k) <= K), so the attention completion is at least the summed task
+// cost over K; every reduction starts after it, on K x W warps. A query
+// token's splits cover its visible tiles once, so the task cost sums to
+// heads x visible tiles + delta_attn per task.
+static double score_lower_bound(const Problem& pb, const ModelParams& prm,
+                                const std::vector<int>& splits) {
+  const int T = prm.tile_tokens;
+  const int run = reduction_run(pb, prm);
+  double w = 0, r = 0;
+  for (size_t b = 0; b < splits.size(); ++b) {
+    const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
+    int64_t vis_tiles = 0;
+    for (int64_t qi = 0; qi < n; ++qi) vis_tiles += n_tiles(pb.causal ? L - n + qi + 1 : L, T);
+    w += (double)pb.num_kv_heads * ((double)vis_tiles + prm.delta_attn * (double)n * (double)splits[b]);
+    const int64_t rows = n * (int64_t)pb.rows_per_token;
+    const double s_u = (double)(splits[b] + pb.n_ext);
+    const int64_t full = rows / run, rem = rows % run;
+    r += (double)full * (prm.delta_red + prm.gamma * (double)run * s_u);
+    if (rem > 0) r += prm.delta_red + prm.gamma * (double)rem * s_u;
+  }
+  return w / (double)prm.slots + r / ((double)prm.slots * (double)prm.warps_per_slot);
+}
 
 // Stand-in for the pages' FA3-derived reference plan (FA3's heuristic is not
 // given): one batch-wide split count, capped per request by its tiles, chosen
 // by the model among 1..max_splits (ties: the pages' keys, then the smaller
-// count). Counts are simulated on worker threads; the pick is sequential.
+// count). Counts are simulated on worker threads, lowest score bound first;
+// a count whose bound exceeds the best score found so far cannot win and is
+// not simulated (non-overlapped model; the margin covers rounding in the
+// bound). The pick among simulated counts is sequential.
 std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
   const int U = prm.max_splits;
   std::vector<Evaluation> evs(U);
-  SimPool pool;
-  pool.run((size_t)U, [&](size_t i) { evs[i] = simulate(pb, prm, uniform_plan(pb, prm, (int)i + 1)); });
-  int best_u = 1;
-  for (int u = 2; u <= U; ++u)
-    if (key_less(evs[u - 1], evs[best_u - 1])) best_u = u;
+  std::vector<char> done(U, 0);
+  SimPool& pool = sim_pool();
+  if (prm.overlap_reduction) {
+    pool.run((size_t)U, [&](size_t i) { evs[i] = simulate(pb, prm, uniform_plan(pb, prm, (int)i + 1)); });
+    std::fill(done.begin(), done.end(), 1);
+  } else {
+    std::vector<double> lb(U);
+    std::vector<int> order(U);
+    for (int u = 1; u <= U; ++u) {
+      lb[u - 1] = score_lower_bound(pb, prm, uniform_plan(pb, prm, u));
+      order[u - 1] = u - 1;
+    }
+    std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return lb[x] < lb[y]; });
+    // items are claimed in bound order; one whose bound exceeds the best score
+    // found so far cannot win whenever it is skipped
+    std::atomic<double> best{INFINITY};
+    pool.run((size_t)U, [&](size_t i) {
+      const int u = order[i] + 1;
+      const double bst = best.load();
+      if (lb[u - 1] > bst + 1e-9 * std::fabs(bst)) return;
+      evs[u - 1] = simulate(pb, prm, uniform_plan(pb, prm, u));
+      done[u - 1] = 1;
+      double cur = best.load();
+      while (evs[u - 1].score < cur && !best.compare_exchange_weak(cur, evs[u - 1].score)) {
+      }
+    });
+  }
+  int best_u = 0;
+  for (int u = 1; u <= U; ++u)
+    if (done[u - 1] && (best_u == 0 || key_less(evs[u - 1], evs[best_u - 1]))) best_u = u;
   return uniform_plan(pb, prm, best_u);
 }
 
@@ -474,47 +753,197 @@ std::vector<int> split_limits(const Problem& pb, const ModelParams& prm,
   return out;
 }
 
+namespace {
+
+// Per-request queue runs for the request's current split count and the next
+// one, so a search candidate's queue is assembled without rebuilding every
+// request's tasks.
+struct ReqRuns {
+  int s = 0;                                  // split count of fifo[0], sorted[0]
+  std::vector<QEntry> fifo[2], sorted[2];     // [0]: s splits, [1]: s + 1
+};
+
+void fill_runs(const Problem& pb, const ModelParams& prm, int b, int s, ReqRuns& rr) {
+  rr.s = s;
+  for (int k = 0; k < 2; ++k) {
+    request_fifo(pb, prm, b, s + k, rr.fifo[k]);
+    request_sorted(rr.fifo[k], rr.sorted[k]);
+  }
+}
+
+// Longest-first queue of `base` (the current plan's, merged over requests) with
+// the requests marked in `changed` (listed in `clist`, ascending) replaced by
+// their runs for one more split.
+void merge_lpt(const std::vector<QEntry>& base, const std::vector<ReqRuns>& runs,
+               const std::vector<int>& clist, const std::vector<uint8_t>& changed,
+               std::vector<QEntry>& added, std::vector<QEntry>& out) {
+  added.clear();
+  for (int b : clist) added.insert(added.end(), runs[b].sorted[1].begin(), runs[b].sorted[1].end());
+  std::stable_sort(added.begin(), added.end(), lpt_before);
+  out.clear();
+  size_t j = 0;
+  for (const QEntry& e : base) {
+    if (changed[e.req]) continue;
+    while (j < added.size() && lpt_before(added[j], e)) out.push_back(added[j++]);
+    out.push_back(e);
+  }
+  while (j < added.size()) out.push_back(added[j++]);
+}
+
+struct CandScratch {
+  std::vector<uint8_t> changed;
+  std::vector<QEntry> added, lpt;
+  std::vector<Seg> segs;
+  std::vector<int> splits;
+  SimScratch sim;
+};
+
+}  // namespace
+
 Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vector<int>& ref,
                        Evaluation* nosplit_out) {
   const int B = (int)pb.seq_lens.size();
   const std::vector<int> lim = split_limits(pb, prm, ref);
   const Evaluation nosplit = simulate(pb, prm, std::vector<int>(B, 1));
   Evaluation cur = nosplit;
-  SimPool pool;
-  for (;;) {
-    std::vector<std::vector<int>> cands;
-    for (int b = 0; b < B; ++b) {
-      if (cur.splits[b] < lim[b]) {
-        std::vector<int> s = cur.splits;
-        s[b] += 1;
-        cands.push_back(std::move(s));
+  SimPool& pool = sim_pool();
+
+  std::vector<ReqRuns> runs(B);
+  for (int b = 0; b < B; ++b) fill_runs(pb, prm, b, 1, runs[b]);
+  bool decode_only = true;
+  for (int b = 0; b < B; ++b) decode_only &= is_decode(pb.q_lens[b]);
+  // Every candidate has a split, so candidates are queued longest first in
+  // decode-only batches and chunk requests first otherwise. `base` is the
+  // current plan's queue in that order (merged runs for longest first).
+  std::vector<QEntry> base;
+  if (decode_only) {
+    for (int b = 0; b < B; ++b) base.insert(base.end(), runs[b].sorted[0].begin(), runs[b].sorted[0].end());
+    std::stable_sort(base.begin(), base.end(), lpt_before);
+  }
+  auto fifo_segs = [&](const std::vector<uint8_t>* changed, std::vector<Seg>& segs) {
+    segs.clear();
+    auto seg = [&](int b) {
+      const std::vector<QEntry>& v = runs[b].fifo[changed && (*changed)[b] ? 1 : 0];
+      segs.push_back({v.data(), v.size()});
+    };
+    for (int b = 0; b < B; ++b)
+      if (!is_decode(pb.q_lens[b])) seg(b);
+    for (int b = 0; b < B; ++b)
+      if (is_decode(pb.q_lens[b])) seg(b);
+  };
+
+  // Resume points: a candidate's queue agrees with `base` up to the first run
+  // of a changed request (longest first: that request's first run in `base`,
+  // before which no new run sorts; chunk first: the start of its segment), so
+  // its run repeats the current plan's up to the first step that reads there.
+  // The overlapped model keeps slot-release state outside the snapshot and
+  // always runs in full.
+  const bool resume = !prm.overlap_reduction;
+  const int red_run = reduction_run(pb, prm);
+  std::vector<int64_t> first_run(B, 0);
+  Recording rec;
+  SimScratch rec_sc;
+  std::vector<Seg> base_segs;
+  auto record = [&](std::vector<int>* tail) {
+    if (decode_only) {
+      std::fill(first_run.begin(), first_run.end(), -1);
+      for (size_t i = 0; i < base.size(); ++i)
+        if (first_run[base[i].req] < 0) first_run[base[i].req] = (int64_t)i;
+      base_segs.assign(1, {base.data(), base.size()});
+    } else {
+      fifo_segs(nullptr, base_segs);
+      int64_t pos = 0;
+      for (const Seg& sg : base_segs) {
+        first_run[sg.p[0].req] = pos;
+        pos += (int64_t)sg.n;
       }
     }
+    rec.thresholds.clear();
+    for (int b = 0; b < B; ++b)
+      if (cur.splits[b] < lim[b]) rec.thresholds.push_back(first_run[b]);
+    std::sort(rec.thresholds.begin(), rec.thresholds.end());
+    rec.thresholds.erase(std::unique(rec.thresholds.begin(), rec.thresholds.end()), rec.thresholds.end());
+    return simulate_queue(pb, prm, cur.splits, base_segs.data(), base_segs.size(), rec_sc, tail,
+                          nullptr, nullptr, resume ? &rec : nullptr, red_run);
+  };
+  if (resume) record(nullptr);
+
+  // queue of cur with the requests in clist raised by one split; returns the
+  // first run index at which it can differ from `base`
+  auto build_cand = [&](const std::vector<int>& clist, CandScratch& cs) {
+    cs.changed.assign(B, 0);
+    cs.splits = cur.splits;
+    int64_t p = INT64_MAX;
+    for (int b : clist) {
+      cs.changed[b] = 1;
+      cs.splits[b] += 1;
+      p = std::min(p, first_run[b]);
+    }
+    if (decode_only) {
+      merge_lpt(base, runs, clist, cs.changed, cs.added, cs.lpt);
+      cs.segs.assign(1, {cs.lpt.data(), cs.lpt.size()});
+    } else {
+      fifo_segs(&cs.changed, cs.segs);
+    }
+    return p;
+  };
+  auto eval_cand = [&](const std::vector<int>& clist, CandScratch& cs, bool use_snapshot) {
+    const int64_t p = build_cand(clist, cs);
+    const Snapshot* from = nullptr;
+    if (use_snapshot) {
+      const size_t k = std::lower_bound(rec.thresholds.begin(), rec.thresholds.end(), p) -
+                       rec.thresholds.begin();
+      from = &rec.snaps[rec.snap_of[k]];
+    }
+    return simulate_queue(pb, prm, cs.splits, cs.segs.data(), cs.segs.size(), cs.sim, nullptr, from,
+                          from ? &rec : nullptr, nullptr, red_run);
+  };
+  CandScratch adopt;
+
+  for (;;) {
+    // candidates in the pages' order: one more split for each request below
+    // its limit, then the joint increment of the tied tail requests
+    std::vector<std::vector<int>> cands;
+    for (int b = 0; b < B; ++b)
+      if (cur.splits[b] < lim[b]) cands.push_back({b});
     std::vector<int> tied;
     for (int b : cur.tail)
       if (cur.splits[b] < lim[b]) tied.push_back(b);
-    if (tied.size() >= 2) {
-      std::vector<int> s = cur.splits;
-      for (int b : tied) s[b] += 1;
-      cands.push_back(std::move(s));
-    }
+    if (tied.size() >= 2) cands.push_back(tied);
     if (cands.empty()) break;
     // Candidates are independent simulations: evaluate them on worker threads,
     // then pick in candidate order exactly as a sequential loop would.
-    std::vector<Evaluation> evs(cands.size());
-    pool.run(cands.size(), [&](size_t i) { evs[i] = simulate(pb, prm, cands[i]); });
-    bool have = false;
-    Evaluation best;
-    for (auto& ev : evs) {
-      if (!have || key_less(ev, best)) {
-        best = std::move(ev);
-        have = true;
+    std::vector<SimResult> res(cands.size());
+    pool.run(cands.size(), [&](size_t i) {
+      thread_local CandScratch cs;
+      res[i] = eval_cand(cands[i], cs, resume);
+    });
+    const int64_t tot = cur.total_splits;
+    auto key = [&](size_t i) {
+      return std::make_tuple(res[i].score, res[i].t_attn, res[i].n_tasks,
+                             tot + (int64_t)cands[i].size());
+    };
+    size_t best = 0;
+    for (size_t i = 1; i < cands.size(); ++i)
+      if (key(i) < key(best)) best = i;
+    if (!(res[best].score < cur.score)) break;
+    // adopt the best candidate: its runs and queue, then record its run (which
+    // also gives its tail) for the next round's candidates
+    build_cand(cands[best], adopt);
+    if (decode_only) base.swap(adopt.lpt);
+    std::vector<int> tail;
+    cur.splits = adopt.splits;
+    for (int b : cands[best]) {
+      std::swap(runs[b].fifo[0], runs[b].fifo[1]);
+      std::swap(runs[b].sorted[0], runs[b].sorted[1]);
+      runs[b].s += 1;
+      if (runs[b].s < lim[b]) {
+        request_fifo(pb, prm, b, runs[b].s + 1, runs[b].fifo[1]);
+        request_sorted(runs[b].fifo[1], runs[b].sorted[1]);
       }
     }
-    if (best.score < cur.score)
-      cur = std::move(best);
-    else
-      break;
+    const SimResult r = record(&tail);
+    cur = to_eval(cur.splits, r, std::move(tail));
   }
   // final candidates in order: the search result, the reference plan, then
   // the proportional plans fitting 1..4 waves (when enabled); first best wins

@@ -135,3 +135,45 @@ def test_skewed_workload_bit_exact():
     plan = skv.plan_splits(L, SPECS[1], num_cu=256, q_lens=n, params=p)
     pb, prm, ev, ns = reference_for(plan, SPECS[1], L, n, params=p)
     assert_same(plan, pb, prm, ev, ns)
+
+
+def _plan_signature(cid):
+    L, n = wl.config_lengths(cid)
+    spec = {2: SPECS[0], 3: SPECS[3]}[cid]
+    p = skv.plan_splits(L, spec, num_cu=256, q_lens=n)
+    e = p.export()
+    return e["split_counts"].tolist(), e["task_order"].tolist(), bits(p.info().score)
+
+
+def test_concurrent_planners_agree():
+    # planners on several threads share one worker pool; a call that finds it
+    # busy runs its simulations itself, with the same result
+    import threading
+    want = {c: _plan_signature(c) for c in (2, 3)}
+    got, errs = [], []
+
+    def work(c):
+        try:
+            for _ in range(3):
+                got.append((c, _plan_signature(c)))
+        except Exception as e:   # pragma: no cover - reported below
+            errs.append(e)
+
+    th = [threading.Thread(target=work, args=(c,)) for c in (2, 3, 2, 3)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join(timeout=300)
+    assert not errs and len(got) == 12
+    for c, sig in got:
+        assert sig == want[c]
+
+
+def test_planner_in_forked_child():
+    # a forked child has no pool workers: it must plan on its own thread
+    import multiprocessing as mp
+    want = _plan_signature(2)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(1) as pool:
+        got = pool.apply_async(_plan_signature, (2,)).get(timeout=120)
+    assert got == want
