@@ -125,6 +125,15 @@ __device__ __forceinline__ void qk_step(f32x4_t (&s)[2][2], const u32x4_t (&kf)[
             : "+v"(s[0][0]), "+v"(s[0][1]), "+v"(s[1][0]), "+v"(s[1][1])
             : "v"(kf[0]), "v"(kf[1]), "v"(q0), "v"(q1));
 }
+// max(a, b, c) in one instruction. (The compiler's fmaxf would first quiet
+// each operand, since it cannot see that the scores are never signalling
+// NaNs.)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  __asm__("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // Twenty wait states between the last score MFMA and the first vector ALU
 // read of the scores (more than an MFMA of this shape needs).
 __device__ __forceinline__ void scores_ready(f32x4_t (&s)[2][2]) {
@@ -322,13 +331,23 @@ void mla_mfma_kernel(MlaArgs a) {
   // maximum of its first tile, and the weights exp2(s - m) of later tokens
   // may exceed 1: up to 2^64 they are exact in range for bf16 and the fp32
   // sums (a split holds at most 2^31 tokens of bounded values), and the
-  // normalisation at the end gives the same softmax. A tile whose maximum
-  // exceeds m + 64 raises m to that maximum and makes the whole work-group
-  // run the split again with the final references, which no tile exceeds by
-  // more than 64: at most one restart (ordinary attention scores never
-  // trigger one). The accumulators are thus never rewritten inside the tile
-  // loop, which keeps them in the accumulation registers.
-  float m[2] = {-INFINITY, -INFINITY};
+  // normalisation at the end gives the same softmax. After the first tile
+  // each lane only compares its own scores with the fixed reference (no
+  // cross-lane step per tile) and keeps its running maximum. A score above
+  // m + 64 makes the whole work-group run the split again, with references
+  // raised to the largest scores of the pass, which no score exceeds: at most
+  // one restart (ordinary attention scores never trigger one). The
+  // accumulators are thus never rewritten inside the tile loop, which keeps
+  // them in the accumulation registers.
+  float m[2] = {0.f, 0.f};             // references (log2 domain, scaled)
+  float thr[2] = {INFINITY, INFINITY};  // raw score above which m + 64 is exceeded
+  float mr[2] = {-INFINITY, -INFINITY}; // the lane's running raw maximum
+  // a head's reference: the maximum of its raw scores so far over the lanes
+  // holding it, scaled (a positive scale and rounding are monotone)
+  auto set_reference = [&](int hb) {
+    m[hb] = max_xor32(max_xor16(mr[hb])) * a.scale_log2;
+    thr[hb] = (m[hb] + 64.f) / a.scale_log2;
+  };
   float l[2];
   f32x4_t o[kNb][2];
   for (int pass = 1;; ++pass) {
@@ -431,17 +450,17 @@ void mla_mfma_kernel(MlaArgs a) {
               if (t0 + 8 * g + 4 * blk + e >= end) s[blk][hb][e] = -INFINITY;
       }
       u32x4_t pf[2];   // weights of tile k, bf16 (P^T operand)
+      const bool first = k == 0 && pass == 1;   // the tile that fixes the references
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        // the maximum of the raw scores, scaled (scaling by a positive factor
-        // and rounding are monotone, so this is the maximum of the scaled scores)
-        float mt = fmaxf(fmaxf(fmaxf(s[0][hb][0], s[0][hb][1]), fmaxf(s[0][hb][2], s[0][hb][3])),
-                         fmaxf(fmaxf(s[1][hb][0], s[1][hb][1]), fmaxf(s[1][hb][2], s[1][hb][3])));
-        mt = max_xor32(max_xor16(mt)) * a.scale_log2;
-        if (m[hb] == -INFINITY) m[hb] = mt;   // the first tile of the first pass
-        const bool up = mt > m[hb] + 64.f;
-        over = over || up;
-        m[hb] = up ? mt : m[hb];   // the reference of the next pass
+        // the lane's running maximum of its raw scores in this pass
+        mr[hb] = max3f(max3f(s[0][hb][0], s[0][hb][1], s[0][hb][2]),
+                       max3f(s[0][hb][3], s[1][hb][0], s[1][hb][1]),
+                       max3f(s[1][hb][2], s[1][hb][3], mr[hb]));
+        if (first) set_reference(hb);
+        over = over || mr[hb] > thr[hb];
+        // the row sums add the fp32 weights (their bf16 roundings would cost
+        // the exported log-sum-exp up to 2^-9)
         float ps = 0.f;
 #pragma unroll
         for (int blk = 0; blk < 2; ++blk)
@@ -484,6 +503,9 @@ void mla_mfma_kernel(MlaArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0 & 0xc07f);   // vmcnt(0) lgkmcnt(0)
     bare_barrier();
     if (restart_pass != pass) break;
+    // the next pass starts from the largest scores this one saw
+    set_reference(0);
+    set_reference(1);
   }
 
   // ---- epilogue: normalise and write this wave's 32 heads ----
