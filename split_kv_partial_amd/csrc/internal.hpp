@@ -121,6 +121,7 @@ struct MergeLaunch {
   int num_units;
   int64_t reqs_off, units_off;   // byte offsets in the workspace
   hipStream_t stream;
+  int max_states;                // largest states per row (splits + n_ext)
 };
 hipError_t launch_merge(const MergeLaunch& m);
 

@@ -61,15 +61,118 @@ __device__ __forceinline__ int dim_of(int lane, int i) {
   return (i < 4 ? 0 : 256) + 4 * lane + (i & 3);
 }
 
+constexpr int kFew = 8;   // states whose vectors are fetched together
+constexpr int R = 8;      // rows per step of the many-state path
+
+// Many states (external ones): R consecutive rows at a time, states in the
+// outer loop. For a fixed state the R rows' vectors are contiguous, so a wave
+// streams R x DV x 4 bytes from one or two states at a time instead of
+// touching every state's stream for every row; each row still accumulates
+// its states in state order, as the few-state path does. Measured on 263k
+// rows x 17 states of 512 floats (MI355X): one wave per unit taking rows one
+// at a time 1.98 ms -> R = 4: 1.79 -> R = 8 with two states in flight:
+// 1.65 ms. The latter needs 268 registers (one wave per SIMD); trimmed to
+// two waves per SIMD it ran slower (1.73 ms): fewer state streams at once
+// per CU read faster.
 template <int DV>
+__device__ __forceinline__ void merge_rows_many(const MergeArgs& a, const DevUnit& u, const DevReq& rq,
+                                                int S, int lane, int first, int stride) {
+  constexpr int N = VecIO<DV>::N;
+  constexpr int KB = 2;   // states per batch of loads: R x KB vectors in flight
+  for (int r0 = u.row + first; r0 < u.row + u.count; r0 += stride) {
+    const int nr = min(R, u.row + u.count - r0);
+    auto lse_of = [&](int k, int r) -> float {
+      if (k < rq.splits) return a.lse_part[(int64_t)rq.state_row + (int64_t)k * rq.rows + r];
+      return a.lse_ext[(int64_t)(k - rq.splits) * a.total_rows + rq.out_row + r];
+    };
+    auto src_of = [&](int k, int r) -> const float* {
+      return k < rq.splits ? a.o_part + ((int64_t)rq.state_row + (int64_t)k * rq.rows + r) * DV
+                           : a.o_ext + ((int64_t)(k - rq.splits) * a.total_rows + rq.out_row + r) * DV;
+    };
+    float w0[R], w1[R], Z[R], M[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      const float l0 = j < nr && lane < S ? lse_of(lane, r0 + j) : -INFINITY;
+      const float l1 = j < nr && lane + 64 < S ? lse_of(lane + 64, r0 + j) : -INFINITY;
+      M[j] = wave_max(fmaxf(l0, l1));
+      const bool live = M[j] != -INFINITY;
+      w0[j] = live ? fast_exp2((l0 - M[j]) * kLog2e) : 0.f;
+      w1[j] = live ? fast_exp2((l1 - M[j]) * kLog2e) : 0.f;
+      Z[j] = wave_sum(w0[j] + w1[j]);
+    }
+    float acc[R][N];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+      for (int i = 0; i < N; ++i) acc[j][i] = 0.f;
+    for (int k0 = 0; k0 < S; k0 += KB) {
+      float wk[KB][R], v[KB][R][N];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        const int k = k0 + kb;
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+          wk[kb][j] = k < S ? __int_as_float(__builtin_amdgcn_readlane(
+                                  __float_as_int(k < 64 ? w0[j] : w1[j]), k & 63))
+                            : 0.f;
+          // an empty state, or one negligible beyond fp32 range, is not read
+          // (its vector may hold anything, e.g. an external state's NaN)
+          if (wk[kb][j] != 0.f) VecIO<DV>::load(src_of(k, r0 + j), lane, v[kb][j]);
+        }
+      }
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+          for (int i = 0; i < N; ++i)
+            acc[j][i] = wk[kb][j] != 0.f ? fmaf(wk[kb][j], v[kb][j][i], acc[j][i]) : acc[j][i];
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (j >= nr) break;
+      const int64_t out_row = (int64_t)rq.out_row + r0 + j;
+      float lse = -INFINITY;
+      if (M[j] != -INFINITY) {
+        const float inv = 1.f / Z[j];
+#pragma unroll
+        for (int i = 0; i < N; ++i) acc[j][i] *= inv;
+        lse = M[j] + fast_log2(Z[j]) * kLn2;
+      }
+      if (a.out_bf16) {
+        uint16_t* o = static_cast<uint16_t*>(a.o_out) + out_row * DV;
+#pragma unroll
+        for (int i = 0; i < N; ++i) o[dim_of<DV>(lane, i)] = (uint16_t)f32_to_bf16_bits(acc[j][i]);
+      } else {
+        float* o = static_cast<float*>(a.o_out) + out_row * DV;
+#pragma unroll
+        for (int i = 0; i < N; ++i) o[dim_of<DV>(lane, i)] = acc[j][i];
+      }
+      if (a.lse_out && lane == 0) a.lse_out[out_row] = lse;
+    }
+  }
+}
+
+// kMany: one work-group per unit, its four waves taking R-row steps in turn
+// (finer pieces than a wave per unit, so the grid ends evenly); otherwise one
+// wave per unit.
+template <int DV, bool kMany>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int N = VecIO<DV>::N;
   const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int unit = kMany ? blockIdx.x : blockIdx.x * 4 + wave;
   if (unit >= a.num_units) return;
   const DevUnit u = a.units[unit];
   const DevReq rq = a.reqs[u.b];
   const int S = rq.splits + a.n_ext;  // <= 64 + n_ext, at most 128 (host-checked)
+  if (kMany) {
+    if (S > kFew) {
+      merge_rows_many<DV>(a, u, rq, S, lane, R * wave, 4 * R);
+      return;
+    }
+    if (wave != 0) return;   // a few-state unit: one wave, as below
+  }
 
   for (int r = u.row; r < u.row + u.count; ++r) {
     const int64_t out_row = (int64_t)rq.out_row + r;
@@ -83,7 +186,6 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     };
     // Few states (the common decode case): fetch every state vector together
     // with the LSEs, so the row costs one memory round trip instead of two.
-    constexpr int kFew = 8;
     float vf[kFew][N];
     if (S <= kFew) {
 #pragma unroll
@@ -156,11 +258,21 @@ hipError_t launch_merge(const MergeLaunch& m) {
   a.n_ext = m.n_ext;
   a.num_units = m.num_units;
   a.out_bf16 = m.out_bf16;
-  const dim3 grid((m.num_units + 3) / 4), block(256);
+  const bool many = m.max_states > kFew;
+  const dim3 grid(many ? m.num_units : (m.num_units + 3) / 4), block(256);
   switch (m.head_dim_v) {
-    case 64: hipLaunchKernelGGL(merge_kernel<64>, grid, block, 0, m.stream, a); break;
-    case 128: hipLaunchKernelGGL(merge_kernel<128>, grid, block, 0, m.stream, a); break;
-    case 512: hipLaunchKernelGGL(merge_kernel<512>, grid, block, 0, m.stream, a); break;
+    case 64:
+      if (many) hipLaunchKernelGGL((merge_kernel<64, true>), grid, block, 0, m.stream, a);
+      else hipLaunchKernelGGL((merge_kernel<64, false>), grid, block, 0, m.stream, a);
+      break;
+    case 128:
+      if (many) hipLaunchKernelGGL((merge_kernel<128, true>), grid, block, 0, m.stream, a);
+      else hipLaunchKernelGGL((merge_kernel<128, false>), grid, block, 0, m.stream, a);
+      break;
+    case 512:
+      if (many) hipLaunchKernelGGL((merge_kernel<512, true>), grid, block, 0, m.stream, a);
+      else hipLaunchKernelGGL((merge_kernel<512, false>), grid, block, 0, m.stream, a);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -133,6 +133,20 @@ def test_merge_external_states():
     check_all(wb, skv.plan_splits(wb.seq_lens, spec_of(wb), 256, n_ext=3))
 
 
+def test_merge_many_states_skip_empty():
+    # 12 external states (more than eight per row: the many-state merge path),
+    # 128-wide values, a 9-token request so that row runs are ragged; a fifth of
+    # the external states are empty (LSE -inf) with NaN vectors, which the merge
+    # must not read (the oracle takes an empty state's vector as zero)
+    w = small("bf16", 16, 2, 128, 32, [300, 1000, 40], q_lens=[1, 1, 9], seed=6, n_ext=12)
+    mask = np.random.default_rng(3).random(w.lse_ext.shape) < 0.2
+    w.lse_ext[mask] = -np.inf
+    w.o_ext[mask] = np.nan
+    d = DeviceInputs(w)
+    w.o_ext[mask] = 0.0
+    check_all(w, skv.plan_splits(w.seq_lens, spec_of(w), 256, q_lens=w.q_lens, n_ext=12), d)
+
+
 def test_bf16_output_rounding():
     w = small("bf16", 16, 2, 128, 16, [500, 77], seed=8)
     plan = skv.plan_from_counts(w.seq_lens, spec_of(w), [3, 2])

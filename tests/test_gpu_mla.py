@@ -87,6 +87,18 @@ def test_mla_external_states():
     check_all(w, skv.plan_splits(w.seq_lens, spec_of(w), 256, n_ext=16))
 
 
+def test_mla_external_states_empty_nan():
+    # empty external states (LSE -inf) carrying NaN vectors are not read by the
+    # many-state merge; a 3-token request makes the row runs ragged
+    w = mla([300, 1000], q_lens=[1, 3], seed=9, n_ext=16)
+    mask = np.random.default_rng(5).random(w.lse_ext.shape) < 0.25
+    w.lse_ext[mask] = -np.inf
+    w.o_ext[mask] = np.nan
+    d = DeviceInputs(w)
+    w.o_ext[mask] = 0.0
+    check_all(w, skv.plan_splits(w.seq_lens, spec_of(w), 256, q_lens=w.q_lens, n_ext=16), d)
+
+
 def test_mla_deterministic():
     w = mla(RAGGED, seed=21)
     plan = skv.plan_splits(w.seq_lens, spec_of(w), 256)
