@@ -63,7 +63,7 @@ def parse():
 def kernel_of(w) -> str:
     if w.mla:
         return "mla_mfma"
-    return "gqa_mfma" if (w.dtype == "bf16" and w.group >= 16) else "gqa_valu"
+    return "gqa_mfma" if (w.dtype == "bf16" and w.group >= 8) else "gqa_valu"
 
 
 def source_hash(kernel: str) -> str:

@@ -34,6 +34,7 @@ Variant pick_variant(const skv_attn_desc& d) {
   if (d.mla) return Variant::MlaMfma;
   const int G = d.num_q_heads / d.num_kv_heads;
   if (d.dtype == SKV_BF16 && G >= 16) return Variant::GqaMfma;
+  if (d.dtype == SKV_BF16 && G == 8) return Variant::GqaMfmaG8;
   return Variant::GqaValu;
 }
 
@@ -482,7 +483,8 @@ skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q, con
   hipError_t e;
   switch (pick_variant(*desc)) {
     case Variant::GqaValu: e = launch_gqa_valu(a); break;
-    case Variant::GqaMfma: e = launch_gqa_mfma(a); break;
+    case Variant::GqaMfma:
+    case Variant::GqaMfmaG8: e = launch_gqa_mfma(a); break;
     default: e = launch_mla_mfma(a); break;
   }
   if (e != hipSuccess) return fail(SKV_ERR_HIP, "attention kernel launch: %s", hipGetErrorString(e));
@@ -530,6 +532,7 @@ VariantShape variant_shape(Variant v) {
   switch (v) {
     case Variant::GqaValu: return {8, 16};
     case Variant::GqaMfma: return {2, 16};
+    case Variant::GqaMfmaG8: return {4, 16};
     default: return {1, 16};
   }
 }
@@ -554,6 +557,14 @@ VariantShape variant_shape(Variant v) {
 //  - MLA: a work-group's tile rate is set by its own matrix and LDS work, not
 //    by shared HBM, so a lone work-group is no faster than one in a full wave
 //    (rho = 1), and the per-task overhead is small (Q load, epilogue).
+//  - GQA matrix-core kernel on groups of 8 (the skewed 256-request batch: 8
+//    requests of 262,144 tokens among 248 of 512-2,048): with the fit above
+//    the search split the long requests too little (281 splits, 1.68 ms per
+//    step); four slots per CU, rho 0.5 and delta_attn 3 give 313 splits and
+//    1.47 ms, the best of the six parameter sets measured (the vector kernel's
+//    set gives 440 splits and 1.51 ms). On the 32-request group-16 shape the
+//    same four-slot set would cost 5%, so the two group sizes keep separate
+//    fits.
 // The last field turns on the proportional candidates by default. On the MLA
 // 64-request DeepSeek shape the one-task-per-slot proportional plan the model
 // prefers ran 0.6-3.6% faster than the search result in alternating runs
@@ -563,6 +574,7 @@ VariantShape variant_shape(Variant v) {
 Calibration calibration(Variant v) {
   switch (v) {
     case Variant::GqaMfma: return {0.50, 3.0, 1.0, 0.47, 2.66, 0};
+    case Variant::GqaMfmaG8: return {0.50, 3.0, 1.0, 0.47, 5.2, 0};
     case Variant::GqaValu: return {0.80, 1.0, 1.0, 0.47, 11.2, 0};
     default: return {1.00, 2.0, 1.0, 0.47, 7.4, 1};
   }

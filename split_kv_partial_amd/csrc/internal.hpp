@@ -126,7 +126,9 @@ struct MergeLaunch {
 hipError_t launch_merge(const MergeLaunch& m);
 
 // Default executor shape of each attention kernel (used by the planner).
-enum class Variant { GqaValu, GqaMfma, MlaMfma };
+// GqaMfmaG8: the matrix-core GQA kernel on groups of 8 (the same kernel, with
+// its own planner calibration)
+enum class Variant { GqaValu, GqaMfma, GqaMfmaG8, MlaMfma };
 struct VariantShape {
   int slots_per_cu;    // concurrent attention work-groups per CU
   int merge_waves_per_cu;

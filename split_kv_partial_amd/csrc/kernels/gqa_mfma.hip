@@ -1,5 +1,11 @@
-// Paged split-KV partial attention for GQA groups of 16 query heads per KV
-// head (bf16 storage, fp32 accumulation) on the matrix cores.
+// Paged split-KV partial attention for GQA groups of 16 (or 8) query heads per
+// KV head (bf16 storage, fp32 accumulation) on the matrix cores.
+//
+// A group of 8 fills the 16 head columns of the products with copies of its
+// heads (lane n takes head n mod 8) and writes 8 rows: the matrix cores stay a
+// small share of the time (the kernel streams KV bytes), and the stream runs
+// as fast as for 16 heads (8 heads on the vector-ALU kernel left it half
+// bound by its dot products).
 //
 // One work-group (4 waves) runs one task: the 16 query heads of one KV head for
 // one query token, over the KV range [lo, end) of one split. The waves take the
@@ -35,7 +41,7 @@ struct MfmaArgs {
   int32_t* err_flag;
   float* o_part;
   float* lse_part;
-  int32_t H_q, H_kv, page_shift, max_pages, num_pages;
+  int32_t H_q, H_kv, G, page_shift, max_pages, num_pages;
   float scale_log2;
 };
 
@@ -199,7 +205,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // Q^T operand: lane owns head r16; its k-slots of product m are dims 8(4m+g)..+7
   u32x4_t qf[D / 32];
   {
-    const uint16_t* qp = a.q + ((int64_t)t.q_row * a.H_q + (int64_t)t.kvh * kG + c.r16) * D;
+    // groups of G < 16 heads: lanes past G compute copies of the group's heads
+    const uint16_t* qp = a.q + ((int64_t)t.q_row * a.H_q + (int64_t)t.kvh * a.G + (c.r16 & (a.G - 1))) * D;
 #pragma unroll
     for (int m = 0; m < D / 32; ++m)
       qf[m] = *reinterpret_cast<const u32x4_t*>(qp + 8 * (4 * m + c.g));
@@ -240,7 +247,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
     for (int e = 0; e < 4; ++e) o_lds[wave][c.r16][16 * nb + 4 * c.g + e] = st.o[nb][e];
   __syncthreads();
-  for (int i = threadIdx.x; i < kG * D; i += 256) {
+  for (int i = threadIdx.x; i < a.G * D; i += 256) {
     const int h = i / D, d = i % D;
     float M = -INFINITY;
 #pragma unroll
@@ -264,7 +271,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
 hipError_t launch_gqa_mfma(const AttnLaunch& L) {
   const skv_attn_desc& d = *L.desc;
-  if (d.num_q_heads / d.num_kv_heads != kG || d.dtype != SKV_BF16) return hipErrorInvalidValue;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  if ((G != kG && G != kG / 2) || d.dtype != SKV_BF16) return hipErrorInvalidValue;
   if (L.num_tasks == 0) return hipSuccess;
   MfmaArgs a;
   a.q = static_cast<const uint16_t*>(L.q);
@@ -278,6 +286,7 @@ hipError_t launch_gqa_mfma(const AttnLaunch& L) {
   a.lse_part = L.lse_part;
   a.H_q = d.num_q_heads;
   a.H_kv = d.num_kv_heads;
+  a.G = G;
   a.page_shift = __builtin_ctz((unsigned)d.page_size);
   a.max_pages = d.max_pages_per_seq;
   a.num_pages = d.num_pages;
