@@ -509,7 +509,7 @@ skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan, con
   for (const auto& r : plan->ranges) max_splits = std::max(max_splits, (int)r.size());
   MergeLaunch m{workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out, out_dtype == SKV_BF16, lse_out,
                 desc->head_dim_v, tq * desc->num_q_heads, (int)plan->units.size(), plan->reqs_off,
-                plan->units_off, (hipStream_t)stream, max_splits + n_ext};
+                plan->units_off, (hipStream_t)stream, max_splits + n_ext, plan->run};
   hipError_t e = launch_merge(m);
   if (e != hipSuccess) return fail(SKV_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return SKV_OK;

@@ -122,6 +122,7 @@ struct MergeLaunch {
   int64_t reqs_off, units_off;   // byte offsets in the workspace
   hipStream_t stream;
   int max_states;                // largest states per row (splits + n_ext)
+  int run;                       // rows per merge unit (the planner's run)
 };
 hipError_t launch_merge(const MergeLaunch& m);
 

@@ -155,7 +155,8 @@ __device__ __forceinline__ void merge_rows_many(const MergeArgs& a, const DevUni
 
 // kMany: one work-group per unit, its four waves taking R-row steps in turn
 // (finer pieces than a wave per unit, so the grid ends evenly); otherwise one
-// wave per unit.
+// wave per unit, row by row (units of a few rows: decode merges of many
+// splits, where a work-group per unit would leave most waves idle).
 template <int DV, bool kMany>
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   constexpr int N = VecIO<DV>::N;
@@ -214,14 +215,23 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
           for (int i = 0; i < N; ++i) acc[i] = wk != 0.f ? fmaf(wk, vf[k][i], acc[i]) : acc[i];
         }
       } else {
-        for (int k = 0; k < S; ++k) {
-          const float wk = __int_as_float(
-              __builtin_amdgcn_readlane(__float_as_int(k < 64 ? w0 : w1), k & 63));
-          if (wk == 0.f) continue;  // empty state, or negligible beyond fp32 range
-          float v[N];
-          VecIO<DV>::load(src_of(k), lane, v);
+        // more states on a short unit: kFew vectors in flight per batch,
+        // accumulated in state order
+        for (int k0 = 0; k0 < S; k0 += kFew) {
+          float wb[kFew];
 #pragma unroll
-          for (int i = 0; i < N; ++i) acc[i] = fmaf(wk, v[i], acc[i]);
+          for (int j = 0; j < kFew; ++j) {
+            const int k = k0 + j;
+            wb[j] = k < S ? __int_as_float(
+                                __builtin_amdgcn_readlane(__float_as_int(k < 64 ? w0 : w1), k & 63))
+                          : 0.f;
+            // an empty state, or one negligible beyond fp32 range, is not read
+            if (wb[j] != 0.f) VecIO<DV>::load(src_of(k), lane, vf[j]);
+          }
+#pragma unroll
+          for (int j = 0; j < kFew; ++j)
+#pragma unroll
+            for (int i = 0; i < N; ++i) acc[i] = wb[j] != 0.f ? fmaf(wb[j], vf[j][i], acc[i]) : acc[i];
         }
       }
       const float inv = 1.f / Z;
@@ -258,7 +268,8 @@ hipError_t launch_merge(const MergeLaunch& m) {
   a.n_ext = m.n_ext;
   a.num_units = m.num_units;
   a.out_bf16 = m.out_bf16;
-  const bool many = m.max_states > kFew;
+  // the many-state shape needs units of at least R rows (each wave takes R)
+  const bool many = m.max_states > kFew && m.run >= R;
   const dim3 grid(many ? m.num_units : (m.num_units + 3) / 4), block(256);
   switch (m.head_dim_v) {
     case 64:
