@@ -99,6 +99,22 @@ def test_mla_external_states_empty_nan():
     check_all(w, skv.plan_splits(w.seq_lens, spec_of(w), 256, q_lens=w.q_lens, n_ext=16), d)
 
 
+@pytest.mark.parametrize("num_cu", [256, 4])
+def test_mla_merge_up_to_128_states(num_cu):
+    # 512-wide merge with 64 external states and a request in 40 splits (104
+    # states per row), single-row units (256 CUs) and multi-row units (4)
+    w = mla([2600, 300], q_lens=[1, 12], seed=15, n_ext=64)
+    mask = np.random.default_rng(9).random(w.lse_ext.shape) < 0.1
+    w.lse_ext[mask] = -np.inf
+    w.o_ext[mask] = np.nan
+    d = DeviceInputs(w)
+    w.o_ext[mask] = 0.0
+    plan = skv.plan_from_counts(w.seq_lens, spec_of(w), [40, 3], num_cu, q_lens=w.q_lens, n_ext=64)
+    if num_cu == 4:
+        assert plan.info().reduction_run >= 8
+    check_all(w, plan, d)
+
+
 def test_mla_deterministic():
     w = mla(RAGGED, seed=21)
     plan = skv.plan_splits(w.seq_lens, spec_of(w), 256)
