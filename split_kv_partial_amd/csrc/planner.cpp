@@ -900,6 +900,31 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
   };
   CandScratch adopt;
 
+  // Lower bound on a candidate's score in the non-overlapped model: a task of
+  // cost c takes at least rho c (tau >= rho), so attention ends no earlier
+  // than rho times the largest task cost (a request's first split, which its
+  // last query token sees whole: ceil(tiles / s) + delta_attn); every
+  // reduction unit starts after attention, so the score is at least that
+  // plus the largest unit cost.
+  const bool bound = !prm.overlap_reduction;
+  std::vector<int64_t> tiles_of(B);
+  for (int b = 0; b < B; ++b) tiles_of[b] = n_tiles(pb.seq_lens[b], prm.tile_tokens);
+  auto task_max = [&](int b, int s) { return (double)((tiles_of[b] + s - 1) / s) + prm.delta_attn; };
+  auto red_max = [&](int b, int s) {
+    const int64_t rows = pb.q_lens[b] * (int64_t)pb.rows_per_token;
+    const int64_t unit = rows >= red_run ? red_run : rows;
+    return prm.delta_red + prm.gamma * (double)unit * (double)(s + pb.n_ext);
+  };
+  auto cand_bound = [&](const std::vector<int>& clist) {
+    double tm = 0, rm = 0;
+    for (int b = 0; b < B; ++b) {
+      const int s = cur.splits[b] + (std::find(clist.begin(), clist.end(), b) != clist.end() ? 1 : 0);
+      tm = std::max(tm, task_max(b, s));
+      rm = std::max(rm, red_max(b, s));
+    }
+    return prm.rho * tm + rm;
+  };
+
   for (;;) {
     // candidates in the pages' order: one more split for each request below
     // its limit, then the joint increment of the tied tail requests
@@ -912,20 +937,48 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
     if (tied.size() >= 2) cands.push_back(tied);
     if (cands.empty()) break;
     // Candidates are independent simulations: evaluate them on worker threads,
-    // then pick in candidate order exactly as a sequential loop would.
-    std::vector<SimResult> res(cands.size());
-    pool.run(cands.size(), [&](size_t i) {
-      thread_local CandScratch cs;
-      res[i] = eval_cand(cands[i], cs, resume);
-    });
+    // then pick in candidate order exactly as a sequential loop would. In the
+    // non-overlapped model they are claimed in order of a lower bound on
+    // their score, and one whose bound exceeds the best score found so far is
+    // not simulated: it cannot be the pick (the key starts with the score).
+    const size_t nc = cands.size();
+    std::vector<SimResult> res(nc);
+    std::vector<char> done(nc, 1);
+    if (bound) {
+      std::vector<double> lb(nc);
+      std::vector<uint32_t> order(nc);
+      for (size_t i = 0; i < nc; ++i) {
+        lb[i] = cand_bound(cands[i]);
+        order[i] = (uint32_t)i;
+      }
+      std::stable_sort(order.begin(), order.end(), [&](uint32_t x, uint32_t y) { return lb[x] < lb[y]; });
+      std::fill(done.begin(), done.end(), 0);
+      std::atomic<double> best_score{INFINITY};
+      pool.run(nc, [&](size_t j) {
+        const uint32_t i = order[j];
+        const double bs = best_score.load();
+        if (lb[i] > bs + 1e-9 * std::fabs(bs)) return;
+        thread_local CandScratch cs;
+        res[i] = eval_cand(cands[i], cs, resume);
+        done[i] = 1;
+        double c = best_score.load();
+        while (res[i].score < c && !best_score.compare_exchange_weak(c, res[i].score)) {
+        }
+      });
+    } else {
+      pool.run(nc, [&](size_t i) {
+        thread_local CandScratch cs;
+        res[i] = eval_cand(cands[i], cs, resume);
+      });
+    }
     const int64_t tot = cur.total_splits;
     auto key = [&](size_t i) {
       return std::make_tuple(res[i].score, res[i].t_attn, res[i].n_tasks,
                              tot + (int64_t)cands[i].size());
     };
-    size_t best = 0;
-    for (size_t i = 1; i < cands.size(); ++i)
-      if (key(i) < key(best)) best = i;
+    size_t best = nc;
+    for (size_t i = 0; i < nc; ++i)
+      if (done[i] && (best == nc || key(i) < key(best))) best = i;
     if (!(res[best].score < cur.score)) break;
     // adopt the best candidate: its runs and queue, then record its run (which
     // also gives its tail) for the next round's candidates
