@@ -203,8 +203,9 @@ void skv_plan_destroy(skv_plan* plan);
  * q, k_pages, v_pages, page_table, seq_lens: device, formats above; seq_lens
  * must hold the values the plan was built from. workspace: device, uploaded
  * from `plan`. o_part / lse_part: device float32, plan state rows.
- * Kernel choice: GQA with G = H_q/H_kv >= 16 (bf16) uses matrix cores; GQA
- * with G < 16 (fp32 or bf16) uses vector ALUs; MLA uses matrix cores. */
+ * Kernel choice: bf16 GQA with G = H_q/H_kv of 16 or 8 uses matrix cores (a
+ * group of 8 fills the 16 head columns with copies); fp32 GQA and bf16 groups
+ * below 8 use vector ALUs; MLA uses matrix cores. */
 skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q,
                                    const void* k_pages, const void* v_pages,
                                    const int32_t* page_table, const int32_t* seq_lens,

@@ -1,6 +1,7 @@
 """GPU parity of the GQA paths and of the merge against the float64 oracle:
-the vector-ALU kernel (groups below 16 query heads per KV head, fp32 and bf16)
-and the matrix-core kernel (bf16 groups of 16)."""
+the vector-ALU kernel (fp32, and bf16 groups below 8 query heads per KV head)
+and the matrix-core kernel (bf16 groups of 16, and of 8 with the head columns
+filled by copies)."""
 import math
 
 import numpy as np
@@ -50,8 +51,10 @@ def test_fp32_group_sizes(G, D, P):
     check_all(w, skv.plan_from_counts(w.seq_lens, spec_of(w), counts))
 
 
-@pytest.mark.parametrize("H_q,H_kv,D,P", [(64, 8, 128, 16), (8, 1, 64, 32), (16, 16, 128, 64),
-                                          (16, 4, 128, 16), (8, 4, 64, 64),
+@pytest.mark.parametrize("H_q,H_kv,D,P", [# matrix-core kernel, groups of 8
+                                          (64, 8, 128, 16), (8, 1, 64, 32),
+                                          # vector-ALU kernel, groups of 1, 4 and 2
+                                          (16, 16, 128, 64), (16, 4, 128, 16), (8, 4, 64, 64),
                                           # matrix-core kernel (16 query heads per KV head)
                                           (128, 8, 128, 16), (16, 1, 128, 32), (32, 2, 128, 64),
                                           (16, 1, 64, 16), (64, 4, 64, 64)])
