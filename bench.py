@@ -60,6 +60,27 @@ def parse():
     return ap.parse_args()
 
 
+def plan_overrides(items):
+    """Planner parameters with NAME=VALUE overrides applied (None if there are
+    none); integer fields take integral values, unknown names raise."""
+    if not items:
+        return None
+    import split_kv_partial_amd as skv
+    p = skv.default_params()
+    for item in items:
+        name, sep, val = item.partition("=")
+        if not sep or name.startswith("_") or name not in dict(type(p)._fields_):
+            raise ValueError(f"bad --plan-param {item!r}")
+        cur = getattr(p, name)
+        if isinstance(cur, int):
+            if float(val) != int(float(val)):
+                raise ValueError(f"--plan-param {name} takes an integer, got {val!r}")
+            setattr(p, name, int(float(val)))
+        else:
+            setattr(p, name, float(val))
+    return p
+
+
 def kernel_of(w) -> str:
     if w.mla:
         return "mla_mfma"
@@ -219,13 +240,7 @@ def main():
                         dtype=torch.bfloat16 if bf16 else torch.float32, mla=w.mla, causal=w.causal)
     num_cu = torch.cuda.get_device_properties(dev).multi_processor_count
 
-    plan_params = None
-    if args.plan_param:
-        plan_params = skv.default_params()
-        for item in args.plan_param:
-            name, _, val = item.partition("=")
-            cur = getattr(plan_params, name)   # unknown names raise AttributeError
-            setattr(plan_params, name, type(cur)(float(val)) if isinstance(cur, int) else float(val))
+    plan_params = plan_overrides(args.plan_param)
 
     # host planner, once per batch (timed on its own, after one untimed call
     # that starts the planner's worker threads, a once-per-process cost)

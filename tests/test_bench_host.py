@@ -73,3 +73,13 @@ def test_counter_summary_scales_by_the_copy_probe(tmp_path, monkeypatch):
         fh.write("\n// edited\n")
     assert bench.measured_traffic("gqa_mfma", "2") is None
     assert bench.measured_traffic("gqa_valu", "4") is None
+
+
+def test_plan_param_overrides():
+    assert bench.plan_overrides([]) is None
+    p = bench.plan_overrides(["balanced_candidates=0", "rho=0.8", "slots_per_cu=4", "use_calibration=0"])
+    assert (p.balanced_candidates, p.slots_per_cu, p.use_calibration) == (0, 4, 0)
+    assert p.rho == 0.8
+    for bad in (["rho"], ["no_such=1"], ["slots_per_cu=2.5"], ["_fields_=1"]):
+        with pytest.raises(ValueError):
+            bench.plan_overrides(bad)
