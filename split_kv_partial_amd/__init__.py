@@ -4,7 +4,7 @@ Python face of ``libsplitkv.so``: argument marshalling only. Planning runs in
 the library's C++ planner and every step of the attention and merge runs in its
 HIP kernels; torch supplies device memory and streams. Importing this module
 without the built library raises ``ImportError`` (build it with
-``python -m split_kv_partial_amd.build``).
+``python split_kv_partial_amd/build.py``).
 
     spec = AttnSpec(num_q_heads=128, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
                     page_size=16, dtype=torch.bfloat16)
@@ -72,7 +72,7 @@ class PlanInfo(ctypes.Structure):
 
 def _load():
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m split_kv_partial_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python split_kv_partial_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     pi32 = ctypes.POINTER(ctypes.c_int32)

@@ -1,6 +1,8 @@
 """Build libsplitkv.so in-tree with hipcc for gfx950.
 
-Usage: python -m split_kv_partial_amd.build  (or call build()).
+Usage: python split_kv_partial_amd/build.py  (or load this file and call
+build(); importing it as a submodule of the package would first load the
+library it builds).
 Every source is compiled on each call; objects go to _build/ next to this file.
 """
 from __future__ import annotations

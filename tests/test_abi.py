@@ -4,6 +4,8 @@ codes before anything is enqueued."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -11,7 +13,8 @@ import torch
 
 import split_kv_partial_amd as skv
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "splitkv.h")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "splitkv.h")
 
 
 def declared_symbols():
@@ -159,3 +162,18 @@ def test_plan_export_shapes():
     assert inf.total_splits == 7 and inf.state_rows == 7 * 4 and inf.total_rows == 8
     assert e["state_row_offset"].tolist() == [0, 8, 28]
     assert inf.num_tasks == 7
+
+
+def test_build_script_loads_without_the_package():
+    # the build step must work on a tree with no library yet: loading the
+    # build script (as build() does) must not import the package, whose import
+    # loads the library
+    code = (
+        "import importlib.util, sys; "
+        f"spec = importlib.util.spec_from_file_location('b', {os.path.join(ROOT, 'split_kv_partial_amd', 'build.py')!r}); "
+        "m = importlib.util.module_from_spec(spec); spec.loader.exec_module(m); "
+        "assert callable(m.build); "
+        "assert 'split_kv_partial_amd' not in sys.modules; print('ok')"
+    )
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
