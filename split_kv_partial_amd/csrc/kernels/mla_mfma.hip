@@ -68,7 +68,7 @@ static_assert(kTileSlots % 64 == 0 && kDmaPerTile % kWaves == 0, "whole DMA inst
 constexpr int kKs = kD / 32;     // 32-wide k-steps of the scores (18)
 constexpr int kNb = kDv / 16;    // 16-dim output blocks (32)
 constexpr int kKd = 4;           // K operand reads in flight, in k-steps
-constexpr int kVd = 8;           // V operand reads in flight, in output blocks
+constexpr int kVd = 12;          // V operand reads in flight, in output blocks
 
 // LDS tile layout: row r (token t0 + r) holds its 72 slots unpadded, chunk c
 // of the row at slot 72 r + (c ^ swz(r)). LDS bank structure of gfx950, as
