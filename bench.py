@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--workload", type=str, default="2",
                     help="1-5, or 5d for the decode-only part of workload 5")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-hbm-probe", action="store_true",
+                    help="skip the streaming-read probe of the practical HBM read ceiling")
     ap.add_argument("--plan-param", action="append", default=[], metavar="NAME=VALUE",
                     help="override one field of the planner parameters (repeatable)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -58,6 +60,36 @@ def parse():
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --traffic-probe` into profiles/counters.json and exit")
     return ap.parse_args()
+
+
+def hbm_probe(dev, num_cu: int, gib: int = 4, reps: int = 10) -> dict:
+    """Practical HBM read ceiling: the library's streaming-read probe over a
+    `gib` GiB buffer (well past the 256 MB Infinity Cache), the best median
+    of `reps` timed launches over three grid sizes; HIP events on the launch
+    stream."""
+    import torch
+    import split_kv_partial_amd as skv
+    nbytes = gib << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    buf.fill_(0x5A5A5A5A)
+    best = None
+    for blocks in (4 * num_cu, 8 * num_cu, 16 * num_cu):
+        out = torch.empty(blocks, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            skv.hbm_read_probe(buf, blocks, out)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        for i in range(reps):
+            ev[i].record()
+            skv.hbm_read_probe(buf, blocks, out)
+        ev[reps].record()
+        torch.cuda.synchronize()
+        ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]))
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        if best is None or gbs > best["gbs"]:
+            best = {"gbs": round(gbs, 1), "bytes": nbytes, "blocks": blocks, "ms": round(ms, 4)}
+    del buf
+    torch.cuda.synchronize()
+    return best
 
 
 def plan_overrides(items):
@@ -332,6 +364,11 @@ def main():
         "wall_s_timed": round(t_wall, 4), "device_error_flag": flag,
         "roofline": roofline,
     }
+    if not args.no_hbm_probe:
+        pr = hbm_probe(dev, num_cu)
+        out["hbm_probe"] = pr
+        out["frac_of_probe"] = round(gbs / pr["gbs"], 4)
+        roofline["frac_of_probe"] = round(achieved / pr["gbs"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

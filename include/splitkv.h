@@ -229,6 +229,16 @@ skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan,
  * not read and the affected state holds NaN). */
 skv_status skv_read_error_flag(const void* workspace, int32_t* flag, void* stream);
 
+/* Measurement utility (not a step of the method): a streaming read of
+ * `bytes` bytes at device address `buf` (16-byte aligned, bytes a positive
+ * multiple of 16) with the non-temporal hint, over `blocks` work-groups of
+ * 256 threads (1..65536); out: device uint32[blocks], each the XOR of the
+ * 32-bit words its work-group read (so the XOR of all of them is the XOR of
+ * the buffer). Asynchronous on `stream`; the caller times it. Used to state
+ * the practical HBM read ceiling beside the attention kernels' KV streams. */
+skv_status skv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,
+                              void* stream);
+
 /* Thread-local message for the last non-OK status of this thread. */
 const char* skv_last_error(void);
 

@@ -34,7 +34,7 @@ EXPORTED = (
     "skv_plan_params_default", "skv_plan_splits", "skv_plan_from_counts", "skv_plan_fixed_chunks",
     "skv_plan_get_info", "skv_plan_export", "skv_plan_workspace_bytes", "skv_plan_upload",
     "skv_plan_destroy", "skv_decode_attn_partial", "skv_merge_states", "skv_read_error_flag",
-    "skv_last_error",
+    "skv_hbm_read_probe", "skv_last_error",
 )
 
 
@@ -93,6 +93,7 @@ def _load():
         "skv_decode_attn_partial": (I32, [pdesc, P, P, P, P, P, P, P, P, P, P]),
         "skv_merge_states": (I32, [pdesc, P, P, P, P, I32, P, P, P, I32, P, P]),
         "skv_read_error_flag": (I32, [P, pi32, P]),
+        "skv_hbm_read_probe": (I32, [P, I64, P, I32, P]),
         "skv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -323,3 +324,17 @@ def merge_states(o_part, lse_part, plan: Plan, o_ext=None, lse_ext=None,
                                  _ptr(lse_out), _stream_ptr()),
            "skv_merge_states")
     return o_out, lse_out
+
+
+def hbm_read_probe(buf: torch.Tensor, blocks: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Streaming read of the contiguous device tensor `buf` (a measurement
+    utility for the HBM read ceiling, not a step of the method); returns
+    out [blocks] uint32-valued int32, whose XOR is the XOR of buf's words."""
+    if not buf.is_contiguous() or buf.device.type != "cuda":
+        raise ValueError("buf must be a contiguous device tensor")
+    if out is None:
+        out = torch.empty(blocks, dtype=torch.int32, device=buf.device)
+    _check(_lib.skv_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(),
+                                   int(blocks), _stream_ptr()),
+           "skv_hbm_read_probe")
+    return out

@@ -26,6 +26,7 @@ SOURCES = [
     "kernels/gqa_mfma.hip",
     "kernels/mla_mfma.hip",
     "kernels/merge.hip",
+    "kernels/probe.hip",
 ]
 
 COMMON = [

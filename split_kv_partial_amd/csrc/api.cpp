@@ -515,6 +515,17 @@ skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan, con
   return SKV_OK;
 }
 
+skv_status skv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,
+                              void* stream) {
+  if (!buf || !out) return fail(SKV_ERR_INVALID_ARG, "buf or out is NULL");
+  if ((uintptr_t)buf % 16 != 0) return fail(SKV_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(SKV_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (blocks < 1 || blocks > 65536) return fail(SKV_ERR_INVALID_ARG, "blocks must be in [1, 65536]");
+  hipError_t e = launch_hbm_probe(buf, bytes, out, blocks, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SKV_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+  return SKV_OK;
+}
+
 skv_status skv_read_error_flag(const void* workspace, int32_t* flag, void* stream) {
   if (!workspace || !flag) return fail(SKV_ERR_INVALID_ARG, "workspace or flag is NULL");
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);

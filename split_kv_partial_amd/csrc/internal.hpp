@@ -125,6 +125,7 @@ struct MergeLaunch {
   int run;                       // rows per merge unit (the planner's run)
 };
 hipError_t launch_merge(const MergeLaunch& m);
+hipError_t launch_hbm_probe(const void* buf, int64_t bytes, uint32_t* out, int blocks, hipStream_t stream);
 
 // Default executor shape of each attention kernel (used by the planner).
 // GqaMfmaG8: the matrix-core GQA kernel on groups of 8 (the same kernel, with

@@ -177,3 +177,15 @@ def test_build_script_loads_without_the_package():
     )
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and r.stdout.strip() == "ok", r.stderr
+
+
+def test_hbm_probe_argument_errors():
+    # checked before any launch (no device memory is touched: these addresses
+    # are never dereferenced)
+    lib = skv._lib
+    out = ctypes.c_void_p(4096)
+    for buf, nbytes, blocks in [(None, 1024, 8), (4096 + 8, 1024, 8), (4096, 1000, 8), (4096, 0, 8),
+                                (4096, 1024, 0), (4096, 1024, 70000)]:
+        st = lib.skv_hbm_read_probe(buf, nbytes, out, blocks, None)
+        assert st == -1, (buf, nbytes, blocks, st)
+    assert lib.skv_hbm_read_probe(4096, 1024, None, 8, None) == -1

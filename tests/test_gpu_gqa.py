@@ -189,3 +189,13 @@ def test_outputs_deterministic(G):
     for x, y in zip(a, b):
         assert np.array_equal(x.view(np.uint64), y.view(np.uint64))
     assert plan.read_error_flag() == 0
+
+
+def test_hbm_read_probe_reads_every_word():
+    # the probe's per-block XORs combine to the XOR of the whole buffer
+    n = (64 << 20) // 4 + 4 * 37   # words; not a multiple of the grid stride
+    words = np.random.default_rng(1).integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    for blocks in (1, 7, 512):
+        out = skv.hbm_read_probe(buf, blocks).cpu().numpy().view(np.uint32)
+        assert np.bitwise_xor.reduce(out) == np.bitwise_xor.reduce(words)
