@@ -31,25 +31,27 @@ def _lengths(rng, batch, q_lens, cap):
 def _plan(rng, w):
     spec = spec_of(w)
     if rng.integers(0, 2) == 0:
-        return skv.plan_splits(w.seq_lens, spec, int(rng.choice([8, 64, 256])), q_lens=w.q_lens,
+        return skv.plan_splits(w.seq_lens, spec, int(rng.choice([4, 8, 64, 256])), q_lens=w.q_lens,
                                n_ext=w.n_ext)
     counts = [int(rng.integers(1, (L + 63) // 64 + 1)) for L in w.seq_lens]
     counts = [min(c, 64) for c in counts]
-    return skv.plan_from_counts(w.seq_lens, spec, counts, q_lens=w.q_lens, n_ext=w.n_ext)
+    # 4 CUs gives merge units of several rows (the work-group-per-unit merge)
+    return skv.plan_from_counts(w.seq_lens, spec, counts, int(rng.choice([4, 256])), q_lens=w.q_lens,
+                                n_ext=w.n_ext)
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_gqa(seed):
     rng = np.random.default_rng(1000 + seed)
     dtype = str(rng.choice(["f32", "bf16"]))
     D = int(rng.choice([64, 128]))
     P = int(rng.choice([16, 32, 64]))
-    G = int(rng.choice([1, 2, 4, 8, 16]))   # bf16 16 runs on the matrix cores
+    G = int(rng.choice([1, 2, 4, 8, 16]))   # bf16 8 and 16 run on the matrix cores
     H_kv = int(rng.choice([1, 2, 4]))
     batch = int(rng.integers(1, 6))
     q_lens = [int(rng.integers(2, 24)) if rng.random() < 0.2 else 1 for _ in range(batch)]
     seq = _lengths(rng, batch, q_lens, 2500)
-    n_ext = int(rng.choice([0, 0, 1, 3]))
+    n_ext = int(rng.choice([0, 0, 1, 3, 12, 64]))
     w = wl.build(f"rand-gqa-{seed}", dtype=dtype, mla=False, seq_lens=seq, q_lens=q_lens,
                  num_q_heads=G * H_kv, num_kv_heads=H_kv, head_dim_qk=D, head_dim_v=D, page_size=P,
                  scale=1.0 / math.sqrt(D), seed=seed, q_scale=float(rng.choice([1.0, 3.0])),
@@ -57,7 +59,7 @@ def test_random_gqa(seed):
     check_all(w, _plan(rng, w))
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(20))
 def test_random_mla(seed):
     rng = np.random.default_rng(2000 + seed)
     H = int(rng.choice([16, 32, 64, 96, 128]))
@@ -65,7 +67,7 @@ def test_random_mla(seed):
     batch = int(rng.integers(1, 5))
     q_lens = [int(rng.integers(2, 12)) if rng.random() < 0.2 else 1 for _ in range(batch)]
     seq = _lengths(rng, batch, q_lens, 2200)
-    n_ext = int(rng.choice([0, 0, 2]))
+    n_ext = int(rng.choice([0, 0, 2, 16, 64]))
     w = wl.build(f"rand-mla-{seed}", dtype="bf16", mla=True, seq_lens=seq, q_lens=q_lens,
                  num_q_heads=H, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=P,
                  scale=wl.MLA_SCALE, seed=seed, value_scale=0.1,
