@@ -151,19 +151,19 @@ def test_merge_many_states_skip_empty():
 
 
 @pytest.mark.parametrize("num_cu", [256, 4])
-def test_merge_up_to_128_states(num_cu):
-    # 64 external states and a request in 50 splits: 114 states per row, so
-    # the LSEs of states 64 and up sit in each lane's second slot. num_cu 256
+def test_merge_with_128_states(num_cu):
+    # 64 external states and a request in 64 splits: 128 states per row (the
+    # most a row can have), so both of each lane's LSE slots are full. num_cu 256
     # gives single-row merge units, 4 gives units of several rows (the
     # work-group-per-unit merge); some external states are empty with NaN
     # vectors (not read; the oracle takes an empty state's vector as zero)
-    w = small("bf16", 16, 2, 128, 16, [3300, 900, 70], q_lens=[1, 60, 1], seed=12, n_ext=64)
+    w = small("bf16", 16, 2, 128, 16, [4200, 900, 70], q_lens=[1, 60, 1], seed=12, n_ext=64)
     mask = np.random.default_rng(7).random(w.lse_ext.shape) < 0.1
     w.lse_ext[mask] = -np.inf
     w.o_ext[mask] = np.nan
     d = DeviceInputs(w)
     w.o_ext[mask] = 0.0
-    plan = skv.plan_from_counts(w.seq_lens, spec_of(w), [50, 14, 2], num_cu, q_lens=w.q_lens, n_ext=64)
+    plan = skv.plan_from_counts(w.seq_lens, spec_of(w), [64, 14, 2], num_cu, q_lens=w.q_lens, n_ext=64)
     if num_cu == 4:
         assert plan.info().reduction_run >= 8
     check_all(w, plan, d)
