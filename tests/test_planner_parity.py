@@ -177,3 +177,33 @@ def test_planner_in_forked_child():
     with ctx.Pool(1) as pool:
         got = pool.apply_async(_plan_signature, (2,)).get(timeout=120)
     assert got == want
+
+
+@pytest.mark.parametrize("B", [2048, 4096])
+def test_large_skewed_batches(B):
+    # thousands of requests with a few of 1M tokens: the C++ planner finishes
+    # in seconds and its plan keeps the invariants (the pure-Python reference
+    # is too slow for these sizes; the bit-exact tests cover smaller batches)
+    rng = np.random.default_rng(B)
+    L = rng.integers(1, 40000, size=B)
+    L[rng.choice(B, 16, replace=False)] = 1 << 20
+    for spec in (SPECS[0], SPECS[3]):
+        t0 = time.time()
+        plan = skv.plan_splits(L, spec, num_cu=256)
+        assert time.time() - t0 < 30
+        inf = plan.info()
+        e = plan.export()
+        counts = e["split_counts"]
+        tiles = (L + 63) // 64
+        assert np.all(counts >= 1) and np.all(counts <= np.minimum(tiles, 64))
+        starts, ends = e["split_start"], e["split_end"]
+        off = np.concatenate([[0], np.cumsum(counts)])
+        for b in range(B):
+            s, en = starts[off[b]:off[b + 1]], ends[off[b]:off[b + 1]]
+            assert s[0] == 0 and en[-1] == L[b] and np.all(s[1:] == en[:-1]) and np.all(s < en)
+        assert inf.total_splits == counts.sum()
+        assert inf.num_tasks == counts.sum() * spec.num_kv_heads
+        if inf.split_adopted:
+            assert inf.score <= 0.9 * inf.nosplit_score
+        else:
+            assert np.all(counts == 1)
