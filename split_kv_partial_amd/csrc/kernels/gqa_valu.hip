@@ -1,5 +1,6 @@
-// Paged split-KV partial attention for GQA groups of fewer than 16 query heads
-// per KV head, on the vector ALUs (fp32 or bf16 storage, fp32 accumulation).
+// Paged split-KV partial attention on the vector ALUs for fp32 GQA (any group
+// size up to 16) and bf16 groups of fewer than 8 query heads per KV head
+// (fp32 accumulation); bf16 groups of 8 and 16 run on the matrix cores.
 //
 // One work-group (4 waves) runs one task: KV head g of one query token over
 // the KV range [lo, end) of one split. The waves take the split's 64-token
