@@ -85,11 +85,14 @@ typedef struct skv_attn_desc {
   int32_t page_size;          /* P: 16, 32 or 64                                 */
   int32_t max_pages_per_seq;  /* row stride of page_table                        */
   int32_t num_pages;          /* pages in the pool; ids outside [0, num_pages)
-                                 are not dereferenced and raise the device flag */
+                                 are never dereferenced: they set bit 0 of the
+                                 device error flag and the task that met one
+                                 writes a NaN state (see skv_read_error_flag) */
   int32_t mla;                /* 1: MLA rows (v_pages == k_pages)                 */
   int32_t causal;             /* 1: bottom-right causal rows when q_len > 1      */
   int32_t dtype;              /* skv_dtype of q and the KV pages                 */
-  float softmax_scale;        /* scores are softmax_scale * <q, k>               */
+  float softmax_scale;        /* scores are softmax_scale * <q, k>; must be
+                                 positive and finite (SKV_ERR_INVALID_ARG)     */
 } skv_attn_desc;
 
 /* Critical-wave model parameters (LiquidCP, section 5.2, Equations 5-6; the
@@ -198,11 +201,13 @@ skv_status skv_plan_upload(const skv_plan* plan, void* dev_workspace, size_t byt
 
 void skv_plan_destroy(skv_plan* plan);
 
-/* Partial attention states for every split of the plan (A2-A6 of the method:
- * page-gathered KV streaming, QK^T, online softmax, PV, local normalisation).
+/* Partial attention states for every split of the plan (page-gathered KV
+ * streaming, QK^T, online softmax, PV, local normalisation).
  * q, k_pages, v_pages, page_table, seq_lens: device, formats above; seq_lens
- * must hold the values the plan was built from. workspace: device, uploaded
- * from `plan`. o_part / lse_part: device float32, plan state rows.
+ * must hold the values the plan was built from (a task whose request's device
+ * length differs reads no KV, writes a NaN state and sets bit 1 of the error
+ * flag). workspace: device, uploaded from `plan`. o_part / lse_part: device
+ * float32, plan state rows.
  * Kernel choice: bf16 GQA with G = H_q/H_kv of 16 or 8 uses matrix cores (a
  * group of 8 fills the 16 head columns with copies); fp32 GQA and bf16 groups
  * below 8 use vector ALUs; MLA uses matrix cores. */
@@ -217,16 +222,26 @@ skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q,
  * [n_ext][total_rows][D_v], lse_ext [n_ext][total_rows]; NULL when n_ext = 0).
  * o_out: device [total_rows][D_v] of out_dtype (float32, or bf16 rounded to
  * nearest even); lse_out: device float32 [total_rows] or NULL.
- * Rows whose states are all empty produce o = 0, lse = -inf. */
+ * Rows whose states are all empty produce o = 0, lse = -inf; a row with a
+ * NaN LSE among its states (a task that met a device error) produces NaN. */
 skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan,
                             const void* workspace, const float* o_part,
                             const float* lse_part, int32_t n_ext, const float* o_ext,
                             const float* lse_ext, void* o_out, int32_t out_dtype,
                             float* lse_out, void* stream);
 
-/* Synchronise stream and read the workspace's device error flag:
- * 0 = none; bit 0 = a page id outside [0, num_pages) was met (that page was
- * not read and the affected state holds NaN). */
+/* Synchronise stream and read the workspace's device error flag (bits OR-ed
+ * by every launch since the last skv_plan_upload of this workspace):
+ * 0 = none;
+ * bit 0 (1) = a page id outside [0, num_pages) was met: that id was not
+ *             dereferenced and every row of the affected task's partial state
+ *             (o_part and lse_part) is NaN, so the merged rows are NaN too;
+ * bit 1 (2) = a request's device seq_lens value differs from the plan's: its
+ *             tasks read no KV and write NaN states;
+ * bit 2 (4) = MLA only: scores whose scaled values fp32 cannot order within
+ *             the kernel's two passes (only with absurdly large scales): the
+ *             affected state is NaN.
+ * Rows of tasks that met no error are computed normally. */
 skv_status skv_read_error_flag(const void* workspace, int32_t* flag, void* stream);
 
 /* Measurement utility (not a step of the method): a streaming read of

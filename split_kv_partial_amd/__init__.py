@@ -23,7 +23,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsplitkv.so")
+# SKV_LIBRARY names another build of the same library (the host-sanitizer
+# build of the CPU tests); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("SKV_LIBRARY") or os.path.join(_HERE, "libsplitkv.so")
 
 SKV_F32, SKV_BF16 = 0, 1
 STATUS = {0: "SKV_OK", -1: "SKV_ERR_INVALID_ARG", -2: "SKV_ERR_UNSUPPORTED", -3: "SKV_ERR_HIP",
@@ -268,6 +270,22 @@ def plan_fixed_chunks(seq_lens, spec: AttnSpec, chunk_tokens: int, num_cu: int =
     return _make_plan("skv_plan_fixed_chunks", spec, seq_lens, q_lens, int(chunk_tokens), int(num_cu))
 
 
+def _check_tensor(t, name: str, dev, dtypes, numel=None, shape=None) -> None:
+    """Raise ValueError unless t is a contiguous tensor on dev with one of
+    dtypes and, when given, exactly `shape` or at least `numel` elements. The
+    C ABI takes bare device pointers, so buffer sizes are checked here."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if not t.is_contiguous() or t.device != dev:
+        raise ValueError(f"{name} must be a contiguous tensor on {dev}")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype {' or '.join(map(str, dtypes))}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, needs at least {numel}")
+
+
 def _desc_for(plan: Plan, page_table: torch.Tensor, k_pages: torch.Tensor, scale: float) -> AttnDesc:
     return plan.spec.desc(len(plan.seq_lens), max_pages=page_table.shape[1],
                           num_pages=k_pages.shape[0], scale=scale)
@@ -278,19 +296,37 @@ def decode_attn_partial(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, s
     """Partial states (O_r normalised over split r, natural-log LSE_r) for every
     split of ``plan``. Returns (o_part [state_rows][D_v], lse_part [state_rows])."""
     inf = plan.info()
+    sp = plan.spec
     dev = q.device
     if o_part is None:
-        o_part = torch.empty(inf.state_rows, plan.spec.head_dim_v, dtype=torch.float32, device=dev)
+        o_part = torch.empty(inf.state_rows, sp.head_dim_v, dtype=torch.float32, device=dev)
     if lse_part is None:
         lse_part = torch.empty(inf.state_rows, dtype=torch.float32, device=dev)
-    for t, name in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (page_table, "page_table"),
-                    (seq_lens, "seq_lens"), (o_part, "o_part"), (lse_part, "lse_part")):
-        if not t.is_contiguous() or t.device != dev:
-            raise ValueError(f"{name} must be a contiguous tensor on {dev}")
-    if q.dtype != plan.spec.dtype or k_pages.dtype != plan.spec.dtype:
-        raise ValueError("q and the KV pages must have the plan's dtype")
-    if page_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
-        raise ValueError("page_table and seq_lens must be int32")
+    B = len(plan.seq_lens)
+    _check_tensor(q, "q", dev, (sp.dtype,),
+                  shape=(int(plan.q_lens.sum()), sp.num_q_heads, sp.head_dim_qk))
+    _check_tensor(k_pages, "k_pages", dev, (sp.dtype,))
+    if k_pages.dim() < 1 or k_pages.shape[0] < 1:
+        raise ValueError("k_pages must hold at least one page")
+    n_pages = int(k_pages.shape[0])
+    if sp.mla:
+        if v_pages is not k_pages and v_pages.data_ptr() != k_pages.data_ptr():
+            raise ValueError("MLA reads values from the key rows: v_pages must be k_pages")
+        if k_pages.numel() != n_pages * sp.page_size * sp.head_dim_qk:
+            raise ValueError(f"MLA k_pages must be [num_pages][{sp.page_size}][{sp.head_dim_qk}]")
+    else:
+        per_page_k = sp.num_kv_heads * sp.head_dim_qk * sp.page_size
+        per_page_v = sp.num_kv_heads * sp.head_dim_v * sp.page_size
+        if k_pages.numel() != n_pages * per_page_k:
+            raise ValueError(f"k_pages must hold {per_page_k} elements per page")
+        _check_tensor(v_pages, "v_pages", dev, (sp.dtype,), numel=n_pages * per_page_v)
+    _check_tensor(page_table, "page_table", dev, (torch.int32,))
+    if page_table.dim() != 2 or page_table.shape[0] != B or page_table.shape[1] < plan.max_pages:
+        raise ValueError(f"page_table must be [{B}][>= {plan.max_pages}] int32, "
+                         f"got {tuple(page_table.shape)}")
+    _check_tensor(seq_lens, "seq_lens", dev, (torch.int32,), shape=(B,))
+    _check_tensor(o_part, "o_part", dev, (torch.float32,), numel=inf.state_rows * sp.head_dim_v)
+    _check_tensor(lse_part, "lse_part", dev, (torch.float32,), numel=inf.state_rows)
     desc = _desc_for(plan, page_table, k_pages, scale)
     ws = plan.workspace(dev)
     _check(_lib.skv_decode_attn_partial(ctypes.byref(desc), q.data_ptr(), k_pages.data_ptr(),
@@ -307,15 +343,25 @@ def merge_states(o_part, lse_part, plan: Plan, o_ext=None, lse_ext=None,
     (o_ext [n_ext][total_rows][D_v], lse_ext [n_ext][total_rows], float32).
     Returns (O [total_rows][D_v], LSE [total_rows] or None)."""
     inf = plan.info()
+    dv = plan.spec.head_dim_v
     dev = o_part.device
+    if (o_ext is None) != (lse_ext is None):
+        raise ValueError("o_ext and lse_ext go together")
     n_ext = 0 if o_ext is None else int(o_ext.shape[0])
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
     if o_out is None:
-        o_out = torch.empty(inf.total_rows, plan.spec.head_dim_v, dtype=out_dtype, device=dev)
+        o_out = torch.empty(inf.total_rows, dv, dtype=out_dtype, device=dev)
     if want_lse and lse_out is None:
         lse_out = torch.empty(inf.total_rows, dtype=torch.float32, device=dev)
-    for t in (o_part, lse_part, o_ext, lse_ext, o_out, lse_out):
-        if t is not None and (not t.is_contiguous() or t.device != dev):
-            raise ValueError("merge operands must be contiguous tensors on one device")
+    _check_tensor(o_part, "o_part", dev, (torch.float32,), numel=inf.state_rows * dv)
+    _check_tensor(lse_part, "lse_part", dev, (torch.float32,), numel=inf.state_rows)
+    if o_ext is not None:
+        _check_tensor(o_ext, "o_ext", dev, (torch.float32,), shape=(n_ext, inf.total_rows, dv))
+        _check_tensor(lse_ext, "lse_ext", dev, (torch.float32,), shape=(n_ext, inf.total_rows))
+    _check_tensor(o_out, "o_out", dev, (torch.float32, torch.bfloat16), numel=inf.total_rows * dv)
+    if lse_out is not None:
+        _check_tensor(lse_out, "lse_out", dev, (torch.float32,), numel=inf.total_rows)
     desc = plan.spec.desc(len(plan.seq_lens), max_pages=plan.max_pages, num_pages=1)
     ws = plan.workspace(dev)
     _check(_lib.skv_merge_states(ctypes.byref(desc), plan.handle, ws.data_ptr(), o_part.data_ptr(),

@@ -10,7 +10,6 @@
 #include <vector>
 
 #include "internal.hpp"
-#include "kernels/device_common.hpp"
 
 using namespace skv;
 
@@ -51,7 +50,10 @@ skv_status check_desc(const skv_attn_desc* d) {
   if (d->num_pages < 1) return fail(SKV_ERR_INVALID_ARG, "num_pages must be >= 1");
   if (d->dtype != SKV_F32 && d->dtype != SKV_BF16)
     return fail(SKV_ERR_INVALID_ARG, "dtype must be SKV_F32 or SKV_BF16 (got %d)", d->dtype);
-  if (!std::isfinite(d->softmax_scale)) return fail(SKV_ERR_INVALID_ARG, "softmax_scale is not finite");
+  // a positive finite scale (the MLA kernel's overflow threshold divides by it)
+  if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f))
+    return fail(SKV_ERR_INVALID_ARG, "softmax_scale must be positive and finite (got %g)",
+                (double)d->softmax_scale);
   if (d->causal != 0 && d->causal != 1) return fail(SKV_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (d->mla) {
     if (d->mla != 1) return fail(SKV_ERR_INVALID_ARG, "mla must be 0 or 1");
@@ -191,7 +193,8 @@ void finish_plan(skv_plan* pl) {
     dt.end = (int32_t)std::min<int64_t>(t.hi, vis);
     dt.q_row = t.q_row;
     dt.out_row = t.out_row;
-    dt.pad0 = dt.pad1 = 0;
+    dt.seq_len = (int32_t)L;
+    dt.pad = 0;
   }
   pl->reqs.resize(B);
   for (int b = 0; b < B; ++b) {

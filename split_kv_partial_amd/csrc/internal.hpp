@@ -6,7 +6,7 @@
 #include <string>
 #include <vector>
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include "splitkv.h"
 
@@ -23,8 +23,23 @@ struct TaskDesc {
 };
 static_assert(sizeof(TaskDesc) == 32, "task descriptor is 32 bytes");
 
+// Device-side descriptor of one attention work-group (built by the host,
+// uploaded in launch order).
+struct DevTask {
+  int32_t b;        // request
+  int32_t kvh;      // KV head
+  int32_t lo;       // first KV token of the split (multiple of 64)
+  int32_t end;      // one past the last KV token this task may read:
+                    // min(split end, visible end of its query token)
+  int32_t q_row;    // global query-token index
+  int32_t out_row;  // state row of the task's first query head
+  int32_t seq_len;  // L_b the plan was built with (checked against seq_lens)
+  int32_t pad;
+};
+static_assert(sizeof(DevTask) == 32, "device task descriptor is 32 bytes");
+
 // Per-request data the merge needs.
-struct ReqDesc {
+struct DevReq {
   int32_t state_row;   // first state row of the request
   int32_t splits;      // s_b
   int32_t rows;        // rows_b = q_lens[b] * H_q
@@ -32,7 +47,7 @@ struct ReqDesc {
 };
 
 // One merge unit: `count` consecutive rows of request b starting at row `row`.
-struct UnitDesc {
+struct DevUnit {
   int32_t b, row, count, pad;
 };
 

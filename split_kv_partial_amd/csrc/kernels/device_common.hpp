@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "internal.hpp"
+
 namespace skv {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
@@ -15,25 +17,6 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-
-// Device-side descriptor of one attention work-group (built by the host).
-struct DevTask {
-  int32_t b;        // request
-  int32_t kvh;      // KV head
-  int32_t lo;       // first KV token of the split (multiple of 64)
-  int32_t end;      // one past the last KV token this task may read:
-                    // min(split end, visible end of its query token)
-  int32_t q_row;    // global query-token index
-  int32_t out_row;  // state row of the task's first query head
-  int32_t pad0, pad1;
-};
-
-struct DevReq {
-  int32_t state_row, splits, rows, out_row;
-};
-struct DevUnit {
-  int32_t b, row, count, pad;
-};
 
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
@@ -128,9 +111,23 @@ __device__ __forceinline__ float wave_sum(float v) { return sum_xor32(sum_xor16(
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
-// Record a device error (vector atomic; bit 0 = page id outside the pool).
+// Bits of the workspace's device error flag.
+constexpr int32_t kErrPageId = 1;   // a page id outside [0, num_pages)
+constexpr int32_t kErrSeqLen = 2;   // device seq_lens differ from the plan's
+constexpr int32_t kErrRange = 4;    // scores beyond the range the softmax represents
+
+// Record a device error (a vector atomic OR into the flag word).
 __device__ __forceinline__ void raise_error(int32_t* flag, int32_t bit) {
   atomicOr(flag, bit);
+}
+
+// The state of a task that met an error: every thread of the work-group
+// writes its share of rows [row0, row0 + nrows) of o (dv floats each) and lse
+// as NaN, so that the merged rows of the task come out NaN as well.
+__device__ __forceinline__ void write_nan_state(float* o, float* lse, int64_t row0, int nrows, int dv) {
+  const float nan = __builtin_nanf("");
+  for (int i = threadIdx.x; i < nrows * dv; i += blockDim.x) o[row0 * dv + i] = nan;
+  for (int i = threadIdx.x; i < nrows; i += blockDim.x) lse[row0 + i] = nan;
 }
 
 }  // namespace skv

@@ -71,11 +71,14 @@ struct Ctx {
   int lane, g, r16;  // g = lane / 16 (k-group), r16 = lane % 16
 };
 
-// Issue the loads of the 32-token step starting at t0 (t0 < end).
+// Issue the loads of the 32-token step starting at t0 (t0 < end). Returns
+// true if a page id of the step is outside the pool: that page is not read
+// (zeros stand in for it) and the task's state is written as NaN.
 template <int D>
-__device__ __forceinline__ void load_step(const Ctx<D>& c, int t0, StepRegs<D>& s) {
+__device__ __forceinline__ bool load_step(const Ctx<D>& c, int t0, StepRegs<D>& s) {
   const MfmaArgs& a = *c.a;
   const int P = 1 << a.page_shift;
+  bool bad = false;
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int tb = t0 + 16 * blk;
@@ -83,7 +86,8 @@ __device__ __forceinline__ void load_step(const Ctx<D>& c, int t0, StepRegs<D>& 
     if (tb < c.end) {
       pid = c.ptab[tb >> a.page_shift];
       if (pid < 0 || pid >= a.num_pages) {
-        raise_error(a.err_flag, 1);
+        if (c.lane == 0) raise_error(a.err_flag, kErrPageId);
+        bad = true;
         pid = -1;
       }
     }
@@ -105,6 +109,7 @@ __device__ __forceinline__ void load_step(const Ctx<D>& c, int t0, StepRegs<D>& 
       for (int nb = 0; nb < D / 16; ++nb) s.v[blk][nb] = u32x2_t{0, 0};
     }
   }
+  return bad;
 }
 
 template <int D>
@@ -190,15 +195,23 @@ template <int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_mfma_kernel(MfmaArgs a) {
   __shared__ float m_lds[kWaves][kG], l_lds[kWaves][kG];
   __shared__ float o_lds[kWaves][kG][D + 4];
+  __shared__ int bad_lds[kWaves];
 
   const DevTask t = a.tasks[blockIdx.x];
+  if (a.seq_lens[t.b] != t.seq_len) {
+    // the device lengths are not the ones the plan was built from: no KV is
+    // read and the state is NaN (uniform over the work-group: one task)
+    if (threadIdx.x == 0) raise_error(a.err_flag, kErrSeqLen);
+    write_nan_state(a.o_part, a.lse_part, t.out_row, a.G, D);
+    return;
+  }
   Ctx<D> c;
   c.a = &a;
   c.lane = threadIdx.x & 63;
   c.g = c.lane >> 4;
   c.r16 = c.lane & 15;
   c.kvh = t.kvh;
-  c.end = min(t.end, a.seq_lens[t.b]);
+  c.end = t.end;
   c.ptab = a.page_table + (int64_t)t.b * a.max_pages;
   const int wave = threadIdx.x >> 6;
 
@@ -223,14 +236,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   constexpr int kStride = kWaves * kStep;
   int t0 = t.lo + wave * kStep;
   StepRegs<D> ra, rb;
-  if (t0 < c.end) load_step(c, t0, ra);
+  bool bad = false;   // wave-uniform: the page ids are per 16-token block
+  if (t0 < c.end) bad |= load_step(c, t0, ra);
   while (t0 < c.end) {
     const int t1 = t0 + kStride;
-    if (t1 < c.end) load_step(c, t1, rb);
+    if (t1 < c.end) bad |= load_step(c, t1, rb);
     compute_step(c, t0, ra, qf, st, a.scale_log2);
     if (t1 >= c.end) break;
     const int t2 = t1 + kStride;
-    if (t2 < c.end) load_step(c, t2, ra);
+    if (t2 < c.end) bad |= load_step(c, t2, ra);
     compute_step(c, t1, rb, qf, st, a.scale_log2);
     t0 = t2;
   }
@@ -242,11 +256,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     m_lds[wave][c.r16] = st.m;
     l_lds[wave][c.r16] = l;
   }
+  if (c.lane == 0) bad_lds[wave] = bad;
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb)
 #pragma unroll
     for (int e = 0; e < 4; ++e) o_lds[wave][c.r16][16 * nb + 4 * c.g + e] = st.o[nb][e];
   __syncthreads();
+  if (bad_lds[0] | bad_lds[1] | bad_lds[2] | bad_lds[3]) {
+    write_nan_state(a.o_part, a.lse_part, t.out_row, a.G, D);
+    return;
+  }
   for (int i = threadIdx.x; i < a.G * D; i += 256) {
     const int h = i / D, d = i % D;
     float M = -INFINITY;

@@ -65,13 +65,21 @@ __global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
   __shared__ uint16_t p16_lds[kWaves][2][G][kBf16 ? kTile : 2];   // [hi, lo]
   __shared__ float m_lds[kWaves][G], l_lds[kWaves][G];
   __shared__ float o_lds[kWaves][G][D];
+  __shared__ int bad_lds[kWaves];
 
   const DevTask t = a.tasks[blockIdx.x];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int P = 1 << a.page_shift;
-  const int L = a.seq_lens[t.b];
-  const int end = min(t.end, L);  // never read past the request's own KV
+  if (a.seq_lens[t.b] != t.seq_len) {
+    // the device lengths are not the ones the plan was built from: no KV is
+    // read and the state is NaN (uniform over the work-group: one task)
+    if (threadIdx.x == 0) raise_error(a.err_flag, kErrSeqLen);
+    write_nan_state(a.o_part, a.lse_part, t.out_row, G, D);
+    return;
+  }
+  const int end = t.end;
+  bool bad = false;   // this lane met a page id outside the pool
 
   // Query rows of the G heads of this KV head into LDS (fp32 or packed bf16).
   {
@@ -100,8 +108,9 @@ __global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
     bool valid = j < end;
     if (valid) {
       const int pid = ptab[j >> a.page_shift];
-      if (pid < 0 || pid >= a.num_pages) {
-        raise_error(a.err_flag, 1);
+      if (pid < 0 || pid >= a.num_pages) {   // not read; the state becomes NaN
+        raise_error(a.err_flag, kErrPageId);
+        bad = true;
         valid = false;
       } else {
         const uint8_t* kp = static_cast<const uint8_t*>(a.k) +
@@ -225,6 +234,7 @@ __global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
   }
 
   // ---------------- merge the four waves' states through LDS ----------------
+  if (lane == 0) bad_lds[wave] = __builtin_amdgcn_ballot_w64(bad) != 0;
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     const float ls = wave_sum(l[h]);
@@ -236,6 +246,10 @@ __global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
     for (int k = 0; k < DL; ++k) o_lds[wave][h][lane + 64 * k] = o[h][k];
   }
   __syncthreads();
+  if (bad_lds[0] | bad_lds[1] | bad_lds[2] | bad_lds[3]) {
+    write_nan_state(a.o_part, a.lse_part, t.out_row, G, D);
+    return;
+  }
   for (int i = threadIdx.x; i < G * D; i += 256) {
     const int h = i / D, d = i % D;
     float M = -INFINITY;

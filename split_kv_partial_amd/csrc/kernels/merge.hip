@@ -61,6 +61,15 @@ __device__ __forceinline__ int dim_of(int lane, int i) {
   return (i < 4 ? 0 : 256) + 4 * lane + (i & 3);
 }
 
+// The reference M = max of a row's state LSEs (lane k holds states k and
+// k + 64). A NaN LSE marks a state its attention task could not compute (see
+// the attention kernels' error flag): M is then NaN, so the whole merged row
+// comes out NaN instead of the NaN being dropped by the maximum.
+__device__ __forceinline__ float row_reference(float l0, float l1) {
+  const float M = wave_max(fmaxf(l0, l1));
+  return __builtin_amdgcn_ballot_w64(l0 != l0 || l1 != l1) != 0 ? __builtin_nanf("") : M;
+}
+
 constexpr int kFew = 8;   // states whose vectors are fetched together
 constexpr int R = 8;      // rows per step of the many-state path
 
@@ -94,7 +103,7 @@ __device__ __forceinline__ void merge_rows_many(const MergeArgs& a, const DevUni
     for (int j = 0; j < R; ++j) {
       const float l0 = j < nr && lane < S ? lse_of(lane, r0 + j) : -INFINITY;
       const float l1 = j < nr && lane + 64 < S ? lse_of(lane + 64, r0 + j) : -INFINITY;
-      M[j] = wave_max(fmaxf(l0, l1));
+      M[j] = row_reference(l0, l1);
       const bool live = M[j] != -INFINITY;
       w0[j] = live ? fast_exp2((l0 - M[j]) * kLog2e) : 0.f;
       w1[j] = live ? fast_exp2((l1 - M[j]) * kLog2e) : 0.f;
@@ -195,7 +204,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
     }
     const float l0 = lane < S ? lse_of(lane) : -INFINITY;
     const float l1 = lane + 64 < S ? lse_of(lane + 64) : -INFINITY;
-    const float M = wave_max(fmaxf(l0, l1));
+    const float M = row_reference(l0, l1);
     float acc[N];
 #pragma unroll
     for (int i = 0; i < N; ++i) acc[i] = 0.f;

@@ -203,8 +203,9 @@ __device__ __forceinline__ TilePages load_pages(const MlaArgs& a, const_i32_t* p
 // tile loop rely on) of the DMA of the 32-token tile at t0: prepare() takes
 // the page bases and reads the lanes' offsets, issue<J>() sends instruction
 // J. Every slot of the tile is fetched by exactly one lane. Rows at or past
-// `end` are read from the same (valid) page and masked where they are used;
-// an id outside the page pool is reported and page 0 is read instead.
+// `end` are read from the same (valid) page and masked where they are used.
+// An id outside the page pool is never dereferenced: it is reported, page 0
+// stands in for it, and the task's state is written as NaN.
 template <bool kSinglePage>   // P >= 32: the tile is 32 consecutive rows of one page
 struct TileDma {
   const uint8_t* base0;   // the tile's first row (P >= 32) or first page (P = 16)
@@ -212,12 +213,14 @@ struct TileDma {
   uint32_t off[kDmaPerWave];
   uint32_t lds;
 
-  __device__ __forceinline__ void prepare(const MlaArgs& a, TilePages pg, int t0, uint32_t lds_addr,
+  // Returns true if a page id of the tile is outside the pool (the same for
+  // every wave: the ids are wave-uniform scalars of the same tile).
+  __device__ __forceinline__ bool prepare(const MlaArgs& a, TilePages pg, int t0, uint32_t lds_addr,
                                           int lane, const uint32_t* soff) {
     const int P = 1 << a.page_shift;
     const bool ok0 = pg.pid0 >= 0 && pg.pid0 < a.num_pages;
     const bool ok1 = pg.pid1 >= 0 && pg.pid1 < a.num_pages;
-    if ((!ok0 || !ok1) && lane == 0) raise_error(a.err_flag, 1);
+    if ((!ok0 || !ok1) && lane == 0) raise_error(a.err_flag, kErrPageId);
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) off[j] = soff[64 * j + lane];
     lds = __builtin_amdgcn_readfirstlane(lds_addr);
@@ -228,6 +231,7 @@ struct TileDma {
       base0 = a.kv + (ok0 ? (int64_t)pg.pid0 * 16 * kRowBytes : 0);
       base1 = a.kv + (ok1 ? (int64_t)pg.pid1 * 16 * kRowBytes : 0);
     }
+    return !ok0 || !ok1;
   }
   template <int J>
   __device__ __forceinline__ void issue() const {
@@ -273,7 +277,14 @@ void mla_mfma_kernel(MlaArgs a) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
-  const int end = min(t.end, a.seq_lens[t.b]);
+  if (a.seq_lens[t.b] != t.seq_len) {
+    // the device lengths are not the ones the plan was built from: no KV is
+    // read and the state is NaN (uniform over the work-group: one task)
+    if (threadIdx.x == 0) raise_error(a.err_flag, kErrSeqLen);
+    write_nan_state(a.o_part, a.lse_part, t.out_row, a.H_q, kDv);
+    return;
+  }
+  const int end = t.end;
   const_i32_t* ptab = (const_i32_t*)(a.page_table + (int64_t)t.b * a.max_pages);
 
   // Q^T operand: lane owns head 32 wave + 16 hb + n (heads past H_q compute on
@@ -336,7 +347,10 @@ void mla_mfma_kernel(MlaArgs a) {
   // cross-lane step per tile) and keeps its running maximum. A score above
   // m + 64 makes the whole work-group run the split again, with references
   // raised to the largest scores of the pass, which no score exceeds: at most
-  // one restart (ordinary attention scores never trigger one). The
+  // one restart (ordinary attention scores never trigger one; the scale is
+  // positive, checked on the host). A second pass that still overflows can
+  // only come from rounding of absurdly scaled scores: it is reported and the
+  // state written as NaN instead of running a third pass. The
   // accumulators are thus never rewritten inside the tile loop, which keeps
   // them in the accumulation registers.
   float m[2] = {0.f, 0.f};             // references (log2 domain, scaled)
@@ -350,6 +364,8 @@ void mla_mfma_kernel(MlaArgs a) {
   };
   float l[2];
   f32x4_t o[kNb][2];
+  bool bad_page = false;    // some page id of the split is outside the pool
+  bool range_err = false;   // scores beyond what one restart can represent
   for (int pass = 1;; ++pass) {
     bool over = false;   // some head of this wave overflowed in this pass
     l[0] = l[1] = 0.f;
@@ -365,7 +381,7 @@ void mla_mfma_kernel(MlaArgs a) {
     for (int j = 0; j < kBuf - 1; ++j) {
       if (j < ntiles) {
         TileDma<kSinglePage> d;
-        d.prepare(a, pg, t.lo + j * kT, ring_lds + j * kTileBytes, lane, soff);
+        bad_page |= d.prepare(a, pg, t.lo + j * kT, ring_lds + j * kTileBytes, lane, soff);
         d.issue_all();
         pg = load_pages(a, ptab, end, t.lo + (j + 1) * kT);   // clamped: always a valid entry
       }
@@ -382,8 +398,8 @@ void mla_mfma_kernel(MlaArgs a) {
       // to back, the nine instructions stall the wave)
       const bool fetch = k + kBuf - 1 < ntiles;
       TileDma<kSinglePage> d;   // prepared always (the page ids are clamped), issued if fetch
-      d.prepare(a, pg, t.lo + (k + kBuf - 1) * kT, ring_lds + ((k + kBuf - 1) % kBuf) * kTileBytes,
-                lane, soff);
+      bad_page |= d.prepare(a, pg, t.lo + (k + kBuf - 1) * kT,
+                            ring_lds + ((k + kBuf - 1) % kBuf) * kTileBytes, lane, soff);
       if (fetch) pg = load_pages(a, ptab, end, t.lo + (k + kBuf) * kT);
       uint16_t* tile = ring[k % kBuf];
       const uint8_t* lb = reinterpret_cast<const uint8_t*>(tile);
@@ -503,9 +519,21 @@ void mla_mfma_kernel(MlaArgs a) {
     __builtin_amdgcn_s_waitcnt(kWaitVm0 & 0xc07f);   // vmcnt(0) lgkmcnt(0)
     bare_barrier();
     if (restart_pass != pass) break;
+    if (pass == 2) {
+      // the second pass starts from the first pass's maxima, which no score
+      // of the split exceeds: an overflow here means scores whose scaled
+      // values fp32 cannot separate (an absurd scale); report, do not loop
+      range_err = true;
+      if (threadIdx.x == 0) raise_error(a.err_flag, kErrRange);
+      break;
+    }
     // the next pass starts from the largest scores this one saw
     set_reference(0);
     set_reference(1);
+  }
+  if (bad_page || range_err) {   // uniform: every wave saw the same ids and flag
+    write_nan_state(a.o_part, a.lse_part, t.out_row, a.H_q, kDv);
+    return;
   }
 
   // ---- epilogue: normalise and write this wave's 32 heads ----

@@ -16,21 +16,15 @@
 // reproducible bit for bit.
 #include <algorithm>
 #include <atomic>
-#include <chrono>
-#include <condition_variable>
-#include <functional>
-#include <mutex>
 #include <cmath>
 #include <cstdint>
 #include <map>
 #include <numeric>
-#include <thread>
 #include <tuple>
 #include <vector>
 
-#include <unistd.h>
-
 #include "internal.hpp"
+#include "sim_pool.hpp"
 
 namespace skv {
 
@@ -539,98 +533,6 @@ static std::vector<int> uniform_plan(const Problem& pb, const ModelParams& prm, 
         1, std::min<int64_t>({(int64_t)u, n_tiles(pb.seq_lens[b], prm.tile_tokens), (int64_t)prm.max_splits}));
   return out;
 }
-
-// Worker threads for independent simulations, shared by every planner call in
-// the process. The caller takes part; each index is run exactly once and
-// results are written by index, so the outcome does not depend on which thread
-// ran what. A call made while another thread is using the pool runs its items
-// on the calling thread.
-class SimPool {
- public:
-  SimPool() {
-    const unsigned hw = std::thread::hardware_concurrency();
-    const unsigned n = std::max(1u, std::min(16u, hw));
-    for (unsigned i = 1; i < n; ++i) workers_.emplace_back([this] { loop(); });
-  }
-  // (a process forked from this one has no workers: it runs batches itself)
-  ~SimPool() {
-    {
-      std::lock_guard<std::mutex> g(mu_);
-      stop_.store(true);
-    }
-    cv_.notify_all();
-    for (auto& w : workers_) w.join();
-  }
-  size_t threads() const { return workers_.size() + 1; }
-  void run(size_t count, const std::function<void(size_t)>& fn) {
-    if (count == 0) return;
-    std::unique_lock<std::mutex> busy(busy_, std::try_to_lock);
-    if (workers_.empty() || count < 4 || !busy.owns_lock() || getpid() != pid_) {
-      for (size_t i = 0; i < count; ++i) fn(i);
-      return;
-    }
-    pending_.store(count);
-    fn_.store(&fn);
-    count_.store(count);
-    next_.store(0);
-    {
-      std::lock_guard<std::mutex> g(mu_);
-      gen_.fetch_add(1);
-      if (sleepers_ > 0) cv_.notify_all();
-    }
-    work();
-    // the search issues many short batches: wait briefly by polling first
-    if (!spin_until([this] { return pending_.load() == 0; })) {
-      std::unique_lock<std::mutex> g(mu_);
-      done_cv_.wait(g, [this] { return pending_.load() == 0; });
-    }
-  }
-
- private:
-  template <class Pred>
-  static bool spin_until(Pred p) {
-    const auto t0 = std::chrono::steady_clock::now();
-    for (unsigned i = 1;; ++i) {
-      if (p()) return true;
-      if ((i & 63) == 0 && std::chrono::steady_clock::now() - t0 > std::chrono::microseconds(200))
-        return false;
-    }
-  }
-  void work() {
-    for (;;) {
-      const size_t i = next_.fetch_add(1);
-      if (i >= count_.load()) break;
-      (*fn_.load())(i);
-      if (pending_.fetch_sub(1) == 1) {
-        std::lock_guard<std::mutex> g(mu_);
-        done_cv_.notify_all();
-      }
-    }
-  }
-  void loop() {
-    uint64_t seen = 0;
-    for (;;) {
-      if (!spin_until([&] { return stop_.load() || gen_.load() != seen; })) {
-        std::unique_lock<std::mutex> g(mu_);
-        ++sleepers_;
-        cv_.wait(g, [&] { return stop_.load() || gen_.load() != seen; });
-        --sleepers_;
-      }
-      if (stop_.load()) return;
-      seen = gen_.load();
-      work();
-    }
-  }
-  std::vector<std::thread> workers_;
-  std::mutex busy_, mu_;
-  std::condition_variable cv_, done_cv_;
-  std::atomic<const std::function<void(size_t)>*> fn_{nullptr};
-  std::atomic<size_t> count_{0}, next_{0}, pending_{0};
-  std::atomic<uint64_t> gen_{0};
-  std::atomic<bool> stop_{false};
-  int sleepers_ = 0;
-  const pid_t pid_ = getpid();
-};
 
 static SimPool& sim_pool() {
   static SimPool pool;

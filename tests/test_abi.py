@@ -189,3 +189,101 @@ def test_hbm_probe_argument_errors():
         st = lib.skv_hbm_read_probe(buf, nbytes, out, blocks, None)
         assert st == -1, (buf, nbytes, blocks, st)
     assert lib.skv_hbm_read_probe(4096, 1024, None, 8, None) == -1
+
+
+def test_softmax_scale_must_be_positive_and_finite():
+    # the MLA kernel's overflow threshold divides by the scale: zero, -0.0,
+    # negative and non-finite scales are refused before any launch, by the
+    # planner and by both compute calls
+    plan = skv.plan_splits([100, 50], SPEC, num_cu=4)
+    fake = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    mla = skv.AttnSpec(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
+                       mla=True)
+    mp = skv.plan_splits([100], mla, num_cu=4)
+    for scale in (0.0, -0.0, -0.125, float("inf"), float("-inf"), float("nan")):
+        d = SPEC.desc(2, max_pages=8, num_pages=16, scale=scale)
+        assert _plan_call(d, [100, 50]) == -1, scale
+        assert "softmax_scale" in skv._lib.skv_last_error().decode()
+        st = skv._lib.skv_decode_attn_partial(ctypes.byref(d), fake, fake, fake, fake, fake, plan.handle,
+                                              fake, fake, fake, None)
+        assert st == -1, scale
+        st = skv._lib.skv_merge_states(ctypes.byref(d), plan.handle, fake, fake, fake, 0, None, None,
+                                       fake, 0, None, None)
+        assert st == -1, scale
+        dm = mla.desc(1, max_pages=4, num_pages=4, scale=scale)
+        st = skv._lib.skv_decode_attn_partial(ctypes.byref(dm), fake, fake, fake, fake, fake, mp.handle,
+                                              fake, fake, fake, None)
+        assert st == -1, scale
+    d = SPEC.desc(2, max_pages=8, num_pages=16, scale=1e-30)
+    assert _plan_call(d, [100, 50]) == 0
+
+
+def _cpu_operands(spec, seq, n_pages=16):
+    """CPU tensors shaped as the Python face expects (host-side checks only:
+    every call below must raise before reaching the library)."""
+    B = len(seq)
+    dt = spec.dtype
+    q = torch.zeros(B, spec.num_q_heads, spec.head_dim_qk, dtype=dt)
+    if spec.mla:
+        k = torch.zeros(n_pages, spec.page_size, spec.head_dim_qk, dtype=dt)
+        v = k
+    else:
+        k = torch.zeros(n_pages, spec.num_kv_heads, spec.head_dim_qk, spec.page_size, dtype=dt)
+        v = torch.zeros(n_pages, spec.num_kv_heads, spec.head_dim_v, spec.page_size, dtype=dt)
+    pt = torch.zeros(B, 8, dtype=torch.int32)
+    sl = torch.tensor(seq, dtype=torch.int32)
+    return q, k, v, pt, sl
+
+
+def test_python_face_checks_buffers_before_any_call():
+    plan = skv.plan_splits([100, 50], SPEC, num_cu=4)
+    inf = plan.info()
+    q, k, v, pt, sl = _cpu_operands(SPEC, [100, 50])
+    o = torch.zeros(inf.state_rows, 128)
+    lse = torch.zeros(inf.state_rows)
+    ok = dict(o_part=o, lse_part=lse)
+
+    def bad(fn, *a, match, **kw):
+        with pytest.raises(ValueError, match=match):
+            fn(*a, **kw)
+
+    bad(skv.decode_attn_partial, q.float(), k, v, pt, sl, plan, 0.1, **ok, match="q must have dtype")
+    bad(skv.decode_attn_partial, q[:1], k, v, pt, sl, plan, 0.1, **ok, match="q must have shape")
+    bad(skv.decode_attn_partial, q, k[:, :1].contiguous(), v, pt, sl, plan, 0.1, **ok, match="k_pages must hold")
+    bad(skv.decode_attn_partial, q, k, v[:15], pt, sl, plan, 0.1, **ok, match="v_pages holds")
+    bad(skv.decode_attn_partial, q, k, v, pt.long(), sl, plan, 0.1, **ok, match="page_table must have")
+    bad(skv.decode_attn_partial, q, k, v, pt[:, :2], sl, plan, 0.1, **ok, match="page_table must be")
+    bad(skv.decode_attn_partial, q, k, v, pt, sl[:1], plan, 0.1, **ok, match="seq_lens must have shape")
+    bad(skv.decode_attn_partial, q, k, v, pt, sl, plan, 0.1, o_part=o[:-1], lse_part=lse,
+        match="o_part holds")
+    bad(skv.decode_attn_partial, q, k, v, pt, sl, plan, 0.1, o_part=o.double(), lse_part=lse,
+        match="o_part must have dtype")
+    bad(skv.decode_attn_partial, q, k, v, pt, sl, plan, 0.1, o_part=o, lse_part=lse[:-1],
+        match="lse_part holds")
+    rows = inf.total_rows
+    out = torch.zeros(rows, 128)
+    bad(skv.merge_states, o, lse, plan, o_out=out.half(), lse_out=torch.zeros(rows),
+        match="o_out must have dtype")
+    bad(skv.merge_states, o, lse, plan, o_out=out[:-1], lse_out=torch.zeros(rows), match="o_out holds")
+    bad(skv.merge_states, o, lse, plan, o_out=out, lse_out=torch.zeros(rows - 1), match="lse_out holds")
+    bad(skv.merge_states, o[:-1], lse, plan, o_out=out, lse_out=torch.zeros(rows), match="o_part holds")
+    bad(skv.merge_states, o, lse, plan, torch.zeros(2, rows, 128), None, o_out=out,
+        lse_out=torch.zeros(rows), match="go together")
+    bad(skv.merge_states, o, lse, plan, torch.zeros(2, rows, 128).bfloat16(), torch.zeros(2, rows),
+        o_out=out, lse_out=torch.zeros(rows), match="o_ext must have dtype")
+    bad(skv.merge_states, o, lse, plan, torch.zeros(2, rows - 1, 128), torch.zeros(2, rows - 1),
+        o_out=out, lse_out=torch.zeros(rows), match="o_ext must have shape")
+    bad(skv.merge_states, o, lse, plan, torch.zeros(2, rows, 128), torch.zeros(3, rows),
+        o_out=out, lse_out=torch.zeros(rows), match="lse_ext must have shape")
+    bad(skv.merge_states, o, lse, plan, out_dtype=torch.float16, match="out_dtype")
+    # MLA: values are the key rows
+    mla = skv.AttnSpec(num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
+                       mla=True)
+    mp = skv.plan_splits([100], mla, num_cu=4)
+    q, k, v, pt, sl = _cpu_operands(mla, [100], n_pages=4)
+    mi = mp.info()
+    mo, ml = torch.zeros(mi.state_rows, 512), torch.zeros(mi.state_rows)
+    bad(skv.decode_attn_partial, q, k, k.clone(), pt, sl, mp, 0.1, o_part=mo, lse_part=ml,
+        match="v_pages must be k_pages")
+    bad(skv.decode_attn_partial, q, k[:, :, :512].contiguous(), k[:, :, :512].contiguous(), pt, sl,
+        mp, 0.1, o_part=mo, lse_part=ml, match="v_pages must be k_pages")

@@ -207,3 +207,52 @@ def test_large_skewed_batches(B):
             assert inf.score <= 0.9 * inf.nosplit_score
         else:
             assert np.all(counts == 1)
+
+
+def _default_cap_case(cid: int) -> None:
+    """C++ = Python at the library's default parameters (split cap 64) on a
+    benchmark workload: the plans the bench and the full-size GPU tests use."""
+    L, n = wl.config_lengths(cid)
+    if cid == 4:   # the workload's own request order (a seeded shuffle)
+        order = np.random.Generator(np.random.PCG64(
+            np.random.SeedSequence(wl.SEED_BASE + 4).spawn(8)[1])).permutation(len(L))
+        L, n = L[order], n[order]
+    spec = {2: SPECS[0], 3: SPECS[3], 4: SPECS[1], 5: SPECS[3]}[cid]
+    n_ext = 16 if cid == 5 else 0
+    plan = skv.plan_splits(L, spec, num_cu=256, q_lens=n, n_ext=n_ext)
+    assert plan.info().balanced_candidates == int(spec.mla)
+    pb, prm, ev, ns = reference_for(plan, spec, L, n, n_ext)
+    assert prm.max_splits == 64
+    assert_same(plan, pb, prm, ev, ns)
+
+
+def test_default_cap_benchmark_workload_2_bit_exact():
+    _default_cap_case(2)
+
+
+@pytest.mark.slow
+def test_default_cap_large_workloads_bit_exact():
+    # the pure-Python reference takes 0.5-2 minutes per workload here, so the
+    # three run side by side in child processes
+    import subprocess
+    import sys
+    tests = os.path.dirname(os.path.abspath(__file__))
+    root = os.path.dirname(tests)
+    procs = {}
+    for cid in (3, 4, 5):
+        code = (f"import sys; sys.path[:0] = [{root!r}, {tests!r}]; "
+                f"import test_planner_parity as t; t._default_cap_case({cid}); print('ok')")
+        procs[cid] = subprocess.Popen([sys.executable, "-c", code], stdout=subprocess.PIPE,
+                                      stderr=subprocess.PIPE, text=True)
+    failed = []
+    for cid, p in procs.items():
+        try:
+            out, err = p.communicate(timeout=900)
+        except subprocess.TimeoutExpired:
+            p.kill()
+            out, err = p.communicate()
+            failed.append((cid, "timeout", err[-2000:]))
+            continue
+        if p.returncode != 0 or out.strip() != "ok":
+            failed.append((cid, p.returncode, err[-2000:]))
+    assert not failed, failed
