@@ -230,6 +230,25 @@ skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan,
                             const float* lse_ext, void* o_out, int32_t out_dtype,
                             float* lse_out, void* stream);
 
+/* Bytes of device scratch skv_decode_attn needs for `plan` (a multiple of
+ * 256): a 256-byte-aligned block of counters, then the plan's partial states
+ * (o_part, lse_part; layouts above). 0 if plan is NULL. */
+size_t skv_decode_attn_scratch_bytes(const skv_plan* plan);
+
+/* The whole path in one call: the partial attention state of every split of
+ * the plan (as skv_decode_attn_partial) into `scratch`, then their exact merge
+ * with n_ext external states into o_out / lse_out (as skv_merge_states).
+ * Arguments are those of the two calls; scratch: device, caller-owned, at
+ * least skv_decode_attn_scratch_bytes(plan) bytes (SKV_ERR_NO_MEMORY if
+ * scratch_bytes is smaller), not read before it is written; the same scratch
+ * must not be used by two calls that overlap in time. */
+skv_status skv_decode_attn(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
+                           const skv_plan* plan, const void* workspace, void* scratch,
+                           size_t scratch_bytes, int32_t n_ext, const float* o_ext,
+                           const float* lse_ext, void* o_out, int32_t out_dtype, float* lse_out,
+                           void* stream);
+
 /* Synchronise stream and read the workspace's device error flag (bits OR-ed
  * by every launch since the last skv_plan_upload of this workspace):
  * 0 = none;

@@ -36,7 +36,7 @@ EXPORTED = (
     "skv_plan_params_default", "skv_plan_splits", "skv_plan_from_counts", "skv_plan_fixed_chunks",
     "skv_plan_get_info", "skv_plan_export", "skv_plan_workspace_bytes", "skv_plan_upload",
     "skv_plan_destroy", "skv_decode_attn_partial", "skv_merge_states", "skv_read_error_flag",
-    "skv_hbm_read_probe", "skv_last_error",
+    "skv_hbm_read_probe", "skv_last_error", "skv_decode_attn_scratch_bytes", "skv_decode_attn",
 )
 
 
@@ -94,6 +94,8 @@ def _load():
         "skv_plan_destroy": (None, [P]),
         "skv_decode_attn_partial": (I32, [pdesc, P, P, P, P, P, P, P, P, P, P]),
         "skv_merge_states": (I32, [pdesc, P, P, P, P, I32, P, P, P, I32, P, P]),
+        "skv_decode_attn_scratch_bytes": (SZ, [P]),
+        "skv_decode_attn": (I32, [pdesc, P, P, P, P, P, P, P, P, SZ, I32, P, P, P, I32, P, P]),
         "skv_read_error_flag": (I32, [P, pi32, P]),
         "skv_hbm_read_probe": (I32, [P, I64, P, I32, P]),
         "skv_last_error": (ctypes.c_char_p, []),
@@ -291,17 +293,9 @@ def _desc_for(plan: Plan, page_table: torch.Tensor, k_pages: torch.Tensor, scale
                           num_pages=k_pages.shape[0], scale=scale)
 
 
-def decode_attn_partial(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, scale: float,
-                        o_part=None, lse_part=None):
-    """Partial states (O_r normalised over split r, natural-log LSE_r) for every
-    split of ``plan``. Returns (o_part [state_rows][D_v], lse_part [state_rows])."""
-    inf = plan.info()
+def _check_attention_inputs(q, k_pages, v_pages, page_table, seq_lens, plan: Plan) -> None:
     sp = plan.spec
     dev = q.device
-    if o_part is None:
-        o_part = torch.empty(inf.state_rows, sp.head_dim_v, dtype=torch.float32, device=dev)
-    if lse_part is None:
-        lse_part = torch.empty(inf.state_rows, dtype=torch.float32, device=dev)
     B = len(plan.seq_lens)
     _check_tensor(q, "q", dev, (sp.dtype,),
                   shape=(int(plan.q_lens.sum()), sp.num_q_heads, sp.head_dim_qk))
@@ -325,6 +319,46 @@ def decode_attn_partial(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, s
         raise ValueError(f"page_table must be [{B}][>= {plan.max_pages}] int32, "
                          f"got {tuple(page_table.shape)}")
     _check_tensor(seq_lens, "seq_lens", dev, (torch.int32,), shape=(B,))
+
+
+def _merge_outputs(plan: Plan, dev, o_ext, lse_ext, out_dtype, o_out, lse_out, want_lse):
+    """Checked (n_ext, o_out, lse_out) of a merge; outputs allocated when not given."""
+    inf = plan.info()
+    dv = plan.spec.head_dim_v
+    if (o_ext is None) != (lse_ext is None):
+        raise ValueError("o_ext and lse_ext go together")
+    n_ext = 0 if o_ext is None else int(o_ext.shape[0])
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+    if o_out is None:
+        o_out = torch.empty(inf.total_rows, dv, dtype=out_dtype, device=dev)
+    if want_lse and lse_out is None:
+        lse_out = torch.empty(inf.total_rows, dtype=torch.float32, device=dev)
+    if o_ext is not None:
+        _check_tensor(o_ext, "o_ext", dev, (torch.float32,), shape=(n_ext, inf.total_rows, dv))
+        _check_tensor(lse_ext, "lse_ext", dev, (torch.float32,), shape=(n_ext, inf.total_rows))
+    _check_tensor(o_out, "o_out", dev, (torch.float32, torch.bfloat16), numel=inf.total_rows * dv)
+    if lse_out is not None:
+        _check_tensor(lse_out, "lse_out", dev, (torch.float32,), numel=inf.total_rows)
+    return n_ext, o_out, lse_out
+
+
+def _out_dtype_code(o_out) -> int:
+    return SKV_BF16 if o_out.dtype == torch.bfloat16 else SKV_F32
+
+
+def decode_attn_partial(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, scale: float,
+                        o_part=None, lse_part=None):
+    """Partial states (O_r normalised over split r, natural-log LSE_r) for every
+    split of ``plan``. Returns (o_part [state_rows][D_v], lse_part [state_rows])."""
+    inf = plan.info()
+    sp = plan.spec
+    dev = q.device
+    if o_part is None:
+        o_part = torch.empty(inf.state_rows, sp.head_dim_v, dtype=torch.float32, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty(inf.state_rows, dtype=torch.float32, device=dev)
+    _check_attention_inputs(q, k_pages, v_pages, page_table, seq_lens, plan)
     _check_tensor(o_part, "o_part", dev, (torch.float32,), numel=inf.state_rows * sp.head_dim_v)
     _check_tensor(lse_part, "lse_part", dev, (torch.float32,), numel=inf.state_rows)
     desc = _desc_for(plan, page_table, k_pages, scale)
@@ -345,30 +379,44 @@ def merge_states(o_part, lse_part, plan: Plan, o_ext=None, lse_ext=None,
     inf = plan.info()
     dv = plan.spec.head_dim_v
     dev = o_part.device
-    if (o_ext is None) != (lse_ext is None):
-        raise ValueError("o_ext and lse_ext go together")
-    n_ext = 0 if o_ext is None else int(o_ext.shape[0])
-    if out_dtype not in (torch.float32, torch.bfloat16):
-        raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
-    if o_out is None:
-        o_out = torch.empty(inf.total_rows, dv, dtype=out_dtype, device=dev)
-    if want_lse and lse_out is None:
-        lse_out = torch.empty(inf.total_rows, dtype=torch.float32, device=dev)
+    n_ext, o_out, lse_out = _merge_outputs(plan, dev, o_ext, lse_ext, out_dtype, o_out, lse_out, want_lse)
     _check_tensor(o_part, "o_part", dev, (torch.float32,), numel=inf.state_rows * dv)
     _check_tensor(lse_part, "lse_part", dev, (torch.float32,), numel=inf.state_rows)
-    if o_ext is not None:
-        _check_tensor(o_ext, "o_ext", dev, (torch.float32,), shape=(n_ext, inf.total_rows, dv))
-        _check_tensor(lse_ext, "lse_ext", dev, (torch.float32,), shape=(n_ext, inf.total_rows))
-    _check_tensor(o_out, "o_out", dev, (torch.float32, torch.bfloat16), numel=inf.total_rows * dv)
-    if lse_out is not None:
-        _check_tensor(lse_out, "lse_out", dev, (torch.float32,), numel=inf.total_rows)
     desc = plan.spec.desc(len(plan.seq_lens), max_pages=plan.max_pages, num_pages=1)
     ws = plan.workspace(dev)
     _check(_lib.skv_merge_states(ctypes.byref(desc), plan.handle, ws.data_ptr(), o_part.data_ptr(),
                                  lse_part.data_ptr(), n_ext, _ptr(o_ext), _ptr(lse_ext),
-                                 o_out.data_ptr(), SKV_BF16 if o_out.dtype == torch.bfloat16 else SKV_F32,
-                                 _ptr(lse_out), _stream_ptr()),
+                                 o_out.data_ptr(), _out_dtype_code(o_out), _ptr(lse_out), _stream_ptr()),
            "skv_merge_states")
+    return o_out, lse_out
+
+
+def scratch_bytes(plan: Plan) -> int:
+    """Device scratch bytes decode_attn needs for ``plan``."""
+    return int(_lib.skv_decode_attn_scratch_bytes(plan.handle))
+
+
+def decode_attn(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, scale: float,
+                o_ext=None, lse_ext=None, out_dtype=torch.float32, o_out=None, lse_out=None,
+                want_lse: bool = True, scratch=None):
+    """The whole path in one library call: partial states of every split into
+    ``scratch`` (a uint8 device tensor of at least scratch_bytes(plan) bytes;
+    allocated when not given), then their merge with optional external states.
+    Returns (O [total_rows][D_v], LSE [total_rows] or None)."""
+    dev = q.device
+    _check_attention_inputs(q, k_pages, v_pages, page_table, seq_lens, plan)
+    n_ext, o_out, lse_out = _merge_outputs(plan, dev, o_ext, lse_ext, out_dtype, o_out, lse_out, want_lse)
+    need = scratch_bytes(plan)
+    if scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check_tensor(scratch, "scratch", dev, (torch.uint8,), numel=need)
+    desc = _desc_for(plan, page_table, k_pages, scale)
+    ws = plan.workspace(dev)
+    _check(_lib.skv_decode_attn(ctypes.byref(desc), q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                page_table.data_ptr(), seq_lens.data_ptr(), plan.handle, ws.data_ptr(),
+                                scratch.data_ptr(), scratch.numel(), n_ext, _ptr(o_ext), _ptr(lse_ext),
+                                o_out.data_ptr(), _out_dtype_code(o_out), _ptr(lse_out), _stream_ptr()),
+           "skv_decode_attn")
     return o_out, lse_out
 
 

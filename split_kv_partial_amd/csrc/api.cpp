@@ -14,9 +14,10 @@
 using namespace skv;
 
 namespace {
-
 thread_local std::string g_last_error;
+}  // namespace
 
+namespace skv {
 skv_status fail(skv_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -26,6 +27,9 @@ skv_status fail(skv_status st, const char* fmt, ...) {
   g_last_error = buf;
   return st;
 }
+}  // namespace skv
+
+namespace {
 
 bool is_pow2_page(int p) { return p == 16 || p == 32 || p == 64; }
 
@@ -470,17 +474,42 @@ static skv_status check_plan_matches(const skv_attn_desc* d, const skv_plan* pl)
   return SKV_OK;
 }
 
-skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q, const void* k_pages,
-                                   const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
-                                   const skv_plan* plan, const void* workspace, float* o_part,
-                                   float* lse_part, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of the attention launch (no launch).
+skv_status check_attention(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
+                           const skv_plan* plan, const void* workspace) {
   skv_status st = check_desc(desc);
   if (st) return st;
   if ((st = check_plan_matches(desc, plan))) return st;
-  if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !workspace || !o_part || !lse_part)
+  if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !workspace)
     return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
   if (desc->mla && v_pages != k_pages)
     return fail(SKV_ERR_INVALID_ARG, "MLA reads values from the key rows: v_pages must equal k_pages");
+  return SKV_OK;
+}
+
+// Argument checks of the merge launch (no launch).
+skv_status check_merge(const skv_attn_desc* desc, const skv_plan* plan, const void* workspace,
+                       int32_t n_ext, const float* o_ext, const float* lse_ext, const void* o_out,
+                       int32_t out_dtype) {
+  skv_status st = check_desc(desc);
+  if (st) return st;
+  if ((st = check_plan_matches(desc, plan))) return st;
+  if (!workspace || !o_out) return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
+  if (n_ext < 0 || n_ext > 64) return fail(SKV_ERR_INVALID_ARG, "n_ext must be in [0, 64]");
+  if (n_ext > 0 && (!o_ext || !lse_ext)) return fail(SKV_ERR_INVALID_ARG, "external states are NULL");
+  if (out_dtype != SKV_F32 && out_dtype != SKV_BF16) return fail(SKV_ERR_INVALID_ARG, "bad out_dtype");
+  return SKV_OK;
+}
+
+skv_status launch_attention(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
+                            const skv_plan* plan, const void* workspace, float* o_part, float* lse_part,
+                            void* stream) {
   AttnLaunch a{desc, q, k_pages, v_pages, page_table, seq_lens, workspace, o_part, lse_part,
                (int)plan->tasks.size(), plan->tasks_off, (hipStream_t)stream};
   hipError_t e;
@@ -494,18 +523,10 @@ skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q, con
   return SKV_OK;
 }
 
-skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan, const void* workspace,
+skv_status launch_merge_for(const skv_attn_desc* desc, const skv_plan* plan, const void* workspace,
                             const float* o_part, const float* lse_part, int32_t n_ext, const float* o_ext,
                             const float* lse_ext, void* o_out, int32_t out_dtype, float* lse_out,
                             void* stream) {
-  skv_status st = check_desc(desc);
-  if (st) return st;
-  if ((st = check_plan_matches(desc, plan))) return st;
-  if (!workspace || !o_part || !lse_part || !o_out)
-    return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
-  if (n_ext < 0 || n_ext > 64) return fail(SKV_ERR_INVALID_ARG, "n_ext must be in [0, 64]");
-  if (n_ext > 0 && (!o_ext || !lse_ext)) return fail(SKV_ERR_INVALID_ARG, "external states are NULL");
-  if (out_dtype != SKV_F32 && out_dtype != SKV_BF16) return fail(SKV_ERR_INVALID_ARG, "bad out_dtype");
   int64_t tq = 0;
   for (int64_t n : plan->pb.q_lens) tq += n;
   int max_splits = 1;
@@ -516,6 +537,81 @@ skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan, con
   hipError_t e = launch_merge(m);
   if (e != hipSuccess) return fail(SKV_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return SKV_OK;
+}
+
+}  // namespace
+
+namespace skv {
+
+ScratchLayout scratch_layout(const skv_plan* pl) {
+  ScratchLayout s;
+  const int64_t rows = pl->state_row_offset.back();
+  s.counters_off = 0;
+  s.o_off = align256(sizeof(int32_t) * (4 + (size_t)pl->desc.batch));
+  s.lse_off = s.o_off + align256((size_t)rows * pl->desc.head_dim_v * sizeof(float));
+  s.total = s.lse_off + align256((size_t)rows * sizeof(float));
+  return s;
+}
+
+skv_status decode_attn_impl(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
+                            const skv_plan* plan, const void* workspace, void* scratch,
+                            size_t scratch_bytes, int32_t n_ext, const float* o_ext, const float* lse_ext,
+                            void* o_out, int32_t out_dtype, float* lse_out, void* stream) {
+  skv_status st = check_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace);
+  if (st) return st;
+  if ((st = check_merge(desc, plan, workspace, n_ext, o_ext, lse_ext, o_out, out_dtype))) return st;
+  if (!scratch) return fail(SKV_ERR_INVALID_ARG, "scratch is NULL");
+  const ScratchLayout lay = scratch_layout(plan);
+  if (scratch_bytes < lay.total)
+    return fail(SKV_ERR_NO_MEMORY, "scratch holds %zu bytes, the plan needs %zu", scratch_bytes, lay.total);
+  uint8_t* base = static_cast<uint8_t*>(scratch);
+  float* o_part = reinterpret_cast<float*>(base + lay.o_off);
+  float* lse_part = reinterpret_cast<float*>(base + lay.lse_off);
+  if ((st = launch_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, o_part,
+                             lse_part, stream)))
+    return st;
+  return launch_merge_for(desc, plan, workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out, out_dtype,
+                          lse_out, stream);
+}
+
+}  // namespace skv
+
+extern "C" {
+
+skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                                   const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
+                                   const skv_plan* plan, const void* workspace, float* o_part,
+                                   float* lse_part, void* stream) {
+  skv_status st = check_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace);
+  if (st) return st;
+  if (!o_part || !lse_part) return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
+  return launch_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, o_part,
+                          lse_part, stream);
+}
+
+skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan, const void* workspace,
+                            const float* o_part, const float* lse_part, int32_t n_ext, const float* o_ext,
+                            const float* lse_ext, void* o_out, int32_t out_dtype, float* lse_out,
+                            void* stream) {
+  skv_status st = check_merge(desc, plan, workspace, n_ext, o_ext, lse_ext, o_out, out_dtype);
+  if (st) return st;
+  if (!o_part || !lse_part) return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
+  return launch_merge_for(desc, plan, workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out, out_dtype,
+                          lse_out, stream);
+}
+
+size_t skv_decode_attn_scratch_bytes(const skv_plan* plan) {
+  return plan ? scratch_layout(plan).total : 0;
+}
+
+skv_status skv_decode_attn(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                           const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
+                           const skv_plan* plan, const void* workspace, void* scratch,
+                           size_t scratch_bytes, int32_t n_ext, const float* o_ext, const float* lse_ext,
+                           void* o_out, int32_t out_dtype, float* lse_out, void* stream) {
+  return decode_attn_impl(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, scratch,
+                          scratch_bytes, n_ext, o_ext, lse_ext, o_out, out_dtype, lse_out, stream);
 }
 
 skv_status skv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,

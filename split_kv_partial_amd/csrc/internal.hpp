@@ -142,6 +142,26 @@ struct MergeLaunch {
 hipError_t launch_merge(const MergeLaunch& m);
 hipError_t launch_hbm_probe(const void* buf, int64_t bytes, uint32_t* out, int blocks, hipStream_t stream);
 
+// Error reporting shared by the entry points: sets the thread-local message
+// that skv_last_error returns and gives back st.
+skv_status fail(skv_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Scratch of the whole-path entry points (byte offsets, 256-aligned): counters
+// (4 + batch int32), then the partial states o_part [state_rows][D_v] and
+// lse_part [state_rows], float32.
+struct ScratchLayout {
+  size_t counters_off, o_off, lse_off, total;
+};
+ScratchLayout scratch_layout(const skv_plan* plan);
+
+// The whole path (partial attention of every split, then the merge) with the
+// partial states in `scratch`; validates every argument before any launch.
+skv_status decode_attn_impl(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                            const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
+                            const skv_plan* plan, const void* workspace, void* scratch,
+                            size_t scratch_bytes, int32_t n_ext, const float* o_ext, const float* lse_ext,
+                            void* o_out, int32_t out_dtype, float* lse_out, void* stream);
+
 // Default executor shape of each attention kernel (used by the planner).
 // GqaMfmaG8: the matrix-core GQA kernel on groups of 8 (the same kernel, with
 // its own planner calibration)

@@ -287,3 +287,26 @@ def test_python_face_checks_buffers_before_any_call():
         match="v_pages must be k_pages")
     bad(skv.decode_attn_partial, q, k[:, :, :512].contiguous(), k[:, :, :512].contiguous(), pt, sl,
         mp, 0.1, o_part=mo, lse_part=ml, match="v_pages must be k_pages")
+
+
+def test_whole_path_scratch_size_and_checks():
+    plan = skv.plan_splits([100, 50], SPEC, num_cu=4)
+    inf = plan.info()
+    need = skv.scratch_bytes(plan)
+    # counters block, then o_part and lse_part, each 256-aligned
+    up = lambda x: (x + 255) // 256 * 256
+    assert need == up(4 * (4 + 2)) + up(inf.state_rows * 128 * 4) + up(inf.state_rows * 4)
+    assert skv._lib.skv_decode_attn_scratch_bytes(None) == 0
+    d = SPEC.desc(2, max_pages=8, num_pages=16, scale=0.1)
+    fake = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    call = lambda scratch, nbytes, n_ext=0, ext=None: skv._lib.skv_decode_attn(
+        ctypes.byref(d), fake, fake, fake, fake, fake, plan.handle, fake, scratch, nbytes, n_ext, ext,
+        ext, fake, 0, None, None)
+    assert call(fake, need - 1) == -4 and "scratch" in skv._lib.skv_last_error().decode()
+    assert call(None, need) == -1
+    assert call(fake, need, n_ext=2) == -1                       # external states missing
+    st = skv._lib.skv_decode_attn(ctypes.byref(d), fake, fake, fake, fake, fake, plan.handle, fake, fake,
+                                  need, 0, None, None, fake, 5, None, None)
+    assert st == -1                                              # bad output dtype
+    d.softmax_scale = 0.0
+    assert call(fake, need) == -1
