@@ -249,6 +249,23 @@ skv_status skv_decode_attn(const skv_attn_desc* desc, const void* q, const void*
                            const float* lse_ext, void* o_out, int32_t out_dtype, float* lse_out,
                            void* stream);
 
+/* skv_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * The scratch is a 128 MiB array in the library's device code: each device
+ * that runs this call holds one from the first call on it until the process
+ * ends. A plan whose skv_decode_attn_scratch_bytes exceeds 128 MiB gets
+ * SKV_ERR_NO_MEMORY before anything else happens. Every call on a device
+ * shares that device's array, which keeps the last call's contents: calls
+ * that overlap in time on one device (other streams or threads) race and must
+ * be serialised by the caller. Arguments, results and errors are otherwise
+ * those of skv_decode_attn; no device memory is allocated or freed. */
+skv_status skv_decode_attn_noalloc(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                                   const void* v_pages, const int32_t* page_table,
+                                   const int32_t* seq_lens, const skv_plan* plan,
+                                   const void* workspace, int32_t n_ext, const float* o_ext,
+                                   const float* lse_ext, void* o_out, int32_t out_dtype,
+                                   float* lse_out, void* stream);
+
 /* Synchronise stream and read the workspace's device error flag (bits OR-ed
  * by every launch since the last skv_plan_upload of this workspace):
  * 0 = none;

@@ -37,6 +37,7 @@ EXPORTED = (
     "skv_plan_get_info", "skv_plan_export", "skv_plan_workspace_bytes", "skv_plan_upload",
     "skv_plan_destroy", "skv_decode_attn_partial", "skv_merge_states", "skv_read_error_flag",
     "skv_hbm_read_probe", "skv_last_error", "skv_decode_attn_scratch_bytes", "skv_decode_attn",
+    "skv_decode_attn_noalloc",
 )
 
 
@@ -96,6 +97,7 @@ def _load():
         "skv_merge_states": (I32, [pdesc, P, P, P, P, I32, P, P, P, I32, P, P]),
         "skv_decode_attn_scratch_bytes": (SZ, [P]),
         "skv_decode_attn": (I32, [pdesc, P, P, P, P, P, P, P, P, SZ, I32, P, P, P, I32, P, P]),
+        "skv_decode_attn_noalloc": (I32, [pdesc, P, P, P, P, P, P, P, I32, P, P, P, I32, P, P]),
         "skv_read_error_flag": (I32, [P, pi32, P]),
         "skv_hbm_read_probe": (I32, [P, I64, P, I32, P]),
         "skv_last_error": (ctypes.c_char_p, []),
@@ -417,6 +419,30 @@ def decode_attn(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, scale: fl
                                 scratch.data_ptr(), scratch.numel(), n_ext, _ptr(o_ext), _ptr(lse_ext),
                                 o_out.data_ptr(), _out_dtype_code(o_out), _ptr(lse_out), _stream_ptr()),
            "skv_decode_attn")
+    return o_out, lse_out
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # the library's per-device scratch array
+
+
+def decode_attn_noalloc(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, scale: float,
+                        o_ext=None, lse_ext=None, out_dtype=torch.float32, o_out=None, lse_out=None,
+                        want_lse: bool = True):
+    """decode_attn with the partial states in the library's per-device scratch
+    array (no device allocation inside the call; o_out / lse_out are
+    allocated here only when not given). Plans needing more than
+    NOALLOC_SCRATCH_BYTES raise; calls overlapping on one device race."""
+    dev = q.device
+    _check_attention_inputs(q, k_pages, v_pages, page_table, seq_lens, plan)
+    n_ext, o_out, lse_out = _merge_outputs(plan, dev, o_ext, lse_ext, out_dtype, o_out, lse_out, want_lse)
+    desc = _desc_for(plan, page_table, k_pages, scale)
+    ws = plan.workspace(dev)
+    _check(_lib.skv_decode_attn_noalloc(ctypes.byref(desc), q.data_ptr(), k_pages.data_ptr(),
+                                        v_pages.data_ptr(), page_table.data_ptr(), seq_lens.data_ptr(),
+                                        plan.handle, ws.data_ptr(), n_ext, _ptr(o_ext), _ptr(lse_ext),
+                                        o_out.data_ptr(), _out_dtype_code(o_out), _ptr(lse_out),
+                                        _stream_ptr()),
+           "skv_decode_attn_noalloc")
     return o_out, lse_out
 
 

@@ -22,6 +22,7 @@ ARCH = "gfx950"
 SOURCES = [
     "api.cpp",
     "planner.cpp",
+    "noalloc.cpp",
     "kernels/gqa_valu.hip",
     "kernels/gqa_mfma.hip",
     "kernels/mla_mfma.hip",
