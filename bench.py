@@ -7,14 +7,22 @@ plan is built on the host once per batch and reused by every layer; its own
 cost is measured separately and reported as ``plan_ms``. Inputs are resident
 in HBM before the timed region.
 
-    python bench.py [--gpus 1] [--steps 60] [--warmup 40] [--workload 2]
+    python bench.py [--gpus 1] [--steps 60] [--warmup 40] [--workload all]
 
-Prints one JSON line. ``value`` is KV bytes read by the attention (visible
-tokens x bytes per token) divided by the time of a step.
+Prints one JSON line. The headline is the decode launch of the million-token
+MLA shard (8 requests x 1,048,576 KV tokens, 128 heads, 576/512 dims): the
+largest single-GPU workload's decode part, the launch the HBM target is set
+on. ``value`` is its KV bytes (each request's KV read once) over the median
+step time. ``per_config`` holds the same measurement for the other workloads
+(Llama-405B-shaped GQA share, DeepSeek-shaped MLA batch, skewed rollout tail,
+and the whole million-token shard with its 2,048-token chunked-prefill query
+and 16 external states per row), each with its roofline and its CPU oracle
+baseline. ``--workload N`` runs one workload alone.
 """
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -30,6 +38,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, vendor figure
 METRIC = "decode attention KV GB/s (% of MI355X HBM peak) + tokens/s at 1 GPU"
+HEADLINE = "5d"
+PER_CONFIG = ("2", "3", "4", "5")
 
 KERNEL_FILES = {
     "gqa_mfma": "split_kv_partial_amd/csrc/kernels/gqa_mfma.hip",
@@ -39,27 +49,28 @@ KERNEL_FILES = {
 }
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--workload", type=str, default="2",
-                    help="1-5, or 5d for the decode-only part of workload 5")
+    ap.add_argument("--workload", type=str, default="all",
+                    help="all (headline 5d plus 2, 3, 4, 5), or one of 1-5 and 5d (the decode "
+                         "requests of workload 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true",
                     help="skip the streaming-read probe of the practical HBM read ceiling")
     ap.add_argument("--plan-param", action="append", default=[], metavar="NAME=VALUE",
                     help="override one field of the planner parameters (repeatable)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle sample")
+                    help="target CPU time of each oracle sample")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="also run one 1 GiB device-to-device copy (a plain copy of known size "
                          "that scales the FETCH_SIZE / WRITE_SIZE counters)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
-                         "`bench.py --traffic-probe` into profiles/counters.json and exit")
-    return ap.parse_args()
+                         "`bench.py --workload W --traffic-probe` into profiles/counters.json and exit")
+    return ap.parse_args(argv)
 
 
 def hbm_probe(dev, num_cu: int, gib: int = 4, reps: int = 10) -> dict:
@@ -145,6 +156,7 @@ def measured_traffic(kernel: str, workload: str):
 
 
 def visible_kv_tokens(w) -> int:
+    """Sum over query tokens of the KV tokens each one attends to."""
     tot = 0
     for L, n in zip(w.seq_lens.astype(np.int64), w.q_lens.astype(np.int64)):
         if w.causal and n > 1:
@@ -154,16 +166,35 @@ def visible_kv_tokens(w) -> int:
     return tot
 
 
+def kv_bytes(w) -> int:
+    """Algorithmic KV bytes of an attention launch: every request's KV read
+    once (a chunk's query tokens share their request's history), at the
+    storage's bytes per token (MLA rows once: the value is part of the row)."""
+    return int(w.seq_lens.astype(np.int64).sum()) * w.kv_bytes_per_token()
+
+
 def attention_flops(w) -> float:
     per_head_token = 2.0 * (w.head_dim_qk + w.head_dim_v)
     return per_head_token * w.num_q_heads * visible_kv_tokens(w)
+
+
+def step_bytes(w, state_rows: int) -> int:
+    """HBM bytes a whole step must move at the least: the KV once, queries, the
+    partial states written and read back, external states, merged outputs."""
+    el = 2 if w.dtype == "bf16" else 4
+    q = w.total_q * w.num_q_heads * w.head_dim_qk * el
+    states = state_rows * (w.head_dim_v + 1) * 4
+    ext = w.n_ext * w.total_rows * (w.head_dim_v + 1) * 4
+    out = w.total_rows * (w.head_dim_v + 1) * 4
+    return kv_bytes(w) + q + 2 * states + ext + out
 
 
 def cpu_baseline(w, target_s: float) -> dict:
     """The oracle, as it is, on requests of the same batch in order (passes over
     the batch repeat) until about target_s seconds of CPU work, with as many
     BLAS threads as the host grants this process (OMP_NUM_THREADS, at most
-    16 and at most the CPU count)."""
+    16 and at most the CPU count). Rate: KV bytes the oracle's rows attended
+    to (per query token) over its time."""
     from threadpoolctl import threadpool_limits
     from oracle import attention as A
     done_tokens, done_bytes, rows, calls = 0, 0, 0, 0
@@ -187,7 +218,7 @@ def cpu_baseline(w, target_s: float) -> dict:
                 if time.perf_counter() - t0 >= target_s:
                     break
     dt = time.perf_counter() - t0
-    return {"value": done_bytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": round(done_bytes / dt / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "seconds": round(dt, 2),
             "sample": f"float64 oracle attention, {calls} request evaluations over {len(reqs)} "
                       f"of {w.batch} requests ({rows} output rows, {done_tokens} visible KV "
@@ -236,8 +267,190 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
     print(json.dumps(db[f"{kern}:{workload}"]))
 
 
-def main():
-    args = parse()
+def decode_part(w5):
+    """The decode requests of the million-token shard (its first eight), on the
+    same KV pool and page table rows: no chunk request, no external states."""
+    nd = int(np.sum(w5.q_lens == 1))
+    assert np.all(w5.q_lens[:nd] == 1)
+    return dataclasses.replace(w5, name=w5.name + "-decode", seq_lens=w5.seq_lens[:nd].copy(),
+                               q_lens=w5.q_lens[:nd].copy(), page_table=w5.page_table[:nd].copy(),
+                               q=w5.q[:nd], n_ext=0, o_ext=None, lse_ext=None)
+
+
+def percentile(a, p) -> float:
+    return float(np.percentile(np.asarray(a, np.float64), p))
+
+
+class Runner:
+    """Uploads one workload and times steps of it on the current stream."""
+
+    def __init__(self, w, dev, num_cu, plan_params):
+        import torch
+        import split_kv_partial_amd as skv
+        self.w, self.dev = w, dev
+        bf16 = w.dtype == "bf16"
+
+        def to_dev(a):
+            if bf16:
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        self.q = to_dev(w.q)
+        self.k = to_dev(w.k_pages)
+        self.v = self.k if w.mla else to_dev(w.v_pages)
+        self.pt = torch.from_numpy(w.page_table).to(dev)
+        self.sl = torch.from_numpy(w.seq_lens).to(dev)
+        self.o_ext = None if w.o_ext is None else torch.from_numpy(w.o_ext).to(dev)
+        self.lse_ext = None if w.lse_ext is None else torch.from_numpy(w.lse_ext).to(dev)
+        self.spec = skv.AttnSpec(w.num_q_heads, w.num_kv_heads, w.head_dim_qk, w.head_dim_v, w.page_size,
+                                 dtype=torch.bfloat16 if bf16 else torch.float32, mla=w.mla,
+                                 causal=w.causal)
+        # host planner, once per batch (timed on its own, after one untimed
+        # call that starts the planner's worker threads, a once-per-process cost)
+        self.plan_times = []
+        for it in range(21):
+            t = time.perf_counter()
+            if w.chunk_tokens:
+                plan = skv.plan_fixed_chunks(w.seq_lens, self.spec, w.chunk_tokens, num_cu, q_lens=w.q_lens)
+            else:
+                plan = skv.plan_splits(w.seq_lens, self.spec, num_cu, q_lens=w.q_lens, n_ext=w.n_ext,
+                                       params=plan_params)
+            if it > 0:
+                self.plan_times.append(time.perf_counter() - t)
+        self.plan = plan
+        self.info = plan.info()
+        plan.workspace(dev)
+        self.o_part = torch.empty(self.info.state_rows, w.head_dim_v, dtype=torch.float32, device=dev)
+        self.lse_part = torch.empty(self.info.state_rows, dtype=torch.float32, device=dev)
+        self.o_out = torch.empty(self.info.total_rows, w.head_dim_v, dtype=torch.float32, device=dev)
+        self.lse_out = torch.empty(self.info.total_rows, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    def attention(self):
+        import split_kv_partial_amd as skv
+        skv.decode_attn_partial(self.q, self.k, self.v, self.pt, self.sl, self.plan, self.w.scale,
+                                o_part=self.o_part, lse_part=self.lse_part)
+
+    def merge(self):
+        import split_kv_partial_amd as skv
+        skv.merge_states(self.o_part, self.lse_part, self.plan, self.o_ext, self.lse_ext,
+                         o_out=self.o_out, lse_out=self.lse_out)
+
+    def time_steps(self, steps: int, warmup: int) -> dict:
+        """W untimed steps, then K timed ones with HIP events on the launch
+        stream (torch's current stream, which the library launches on): mark[j]
+        precedes launch j (attention and merge alternate) and also ends launch
+        j - 1, so the first and last events bracket the whole timed region."""
+        import torch
+        for _ in range(warmup):
+            self.attention()
+            self.merge()
+        torch.cuda.synchronize()
+        mark = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        for i in range(steps):
+            mark[2 * i].record()
+            self.attention()
+            mark[2 * i + 1].record()
+            self.merge()
+        mark[2 * steps].record()
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter() - t_wall
+        attn = np.array([mark[2 * i].elapsed_time(mark[2 * i + 1]) for i in range(steps)])
+        merge = np.array([mark[2 * i + 1].elapsed_time(mark[2 * i + 2]) for i in range(steps)])
+        total = mark[0].elapsed_time(mark[2 * steps])
+        return {"attn": attn, "merge": merge, "step": attn + merge, "total_ms": total, "wall_s": t_wall}
+
+    def free(self):
+        import torch
+        for name in ("q", "k", "v", "pt", "sl", "o_ext", "lse_ext", "o_part", "lse_part", "o_out", "lse_out"):
+            setattr(self, name, None)
+        self.plan = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+
+def measure(w, key: str, dev, num_cu: int, args, plan_params) -> dict:
+    """One workload's line: step times (median, p95, mean), KV GB/s, tokens/s,
+    the attention kernel's roofline and, for the chunked-prefill workload, the
+    step against max(bytes / HBM peak, flops / matrix peak)."""
+    r = Runner(w, dev, num_cu, plan_params)
+    t = r.time_steps(args.steps, args.warmup)
+    flag = r.plan.read_error_flag(dev)
+    info = r.info
+    step_med = float(np.median(t["step"]))
+    attn_avg = float(t["attn"].mean())
+    kvb = kv_bytes(w)
+    fl = attention_flops(w)
+    tokens = int(w.q_lens.sum())
+    kern = kernel_of(w)
+    mixed = bool(np.any(w.q_lens > 1)) and w.mla and fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > kvb / (
+        HBM_PEAK_GBS * 1e9)
+    if mixed:
+        ach = fl / (attn_avg * 1e-3) / 1e12
+        roof = {"kernel": kern, "bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),
+                "algorithmic_flops_per_launch": fl}
+    else:
+        ach = kvb / (attn_avg * 1e-3) / 1e9
+        roof = {"kernel": kern, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes_per_launch": int(kvb)}
+        if w.mla:
+            tf = fl / (attn_avg * 1e-3) / 1e12
+            roof["mfma_tflops"] = round(tf, 1)
+            roof["mfma_frac"] = round(tf / MFMA_BF16_PEAK_TFLOPS, 4)
+    roof["traffic"] = measured_traffic(kern, key)
+    roof["launch_ms_avg"] = round(attn_avg, 4)
+    sb = step_bytes(w, info.state_rows)
+    t_roof = max(sb / (HBM_PEAK_GBS * 1e9), fl / (MFMA_BF16_PEAK_TFLOPS * 1e12)) * 1e3
+    out = {
+        "workload": w.name, "key": key,
+        "ms_per_step": round(step_med, 4),
+        "ms_per_step_p95": round(percentile(t["step"], 95), 4),
+        "ms_per_step_mean": round(float(t["step"].mean()), 4),
+        "attn_ms": round(float(np.median(t["attn"])), 4),
+        "attn_ms_p95": round(percentile(t["attn"], 95), 4),
+        "merge_ms": round(float(np.median(t["merge"])), 4),
+        "kv_bytes": int(kvb), "kv_gbs": round(kvb / (step_med * 1e-3) / 1e9, 1),
+        "hbm_frac_of_peak": round(kvb / (step_med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "tokens_per_s": round(tokens / (step_med * 1e-3), 1),
+        "step_roofline": {"bytes": int(sb), "flops": fl, "roofline_ms": round(t_roof, 4),
+                          "frac": round(t_roof / step_med, 4)},
+        "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
+                   "num_kv_heads": w.num_kv_heads, "head_dim_qk": w.head_dim_qk,
+                   "head_dim_v": w.head_dim_v, "page_size": w.page_size,
+                   "kv_tokens": int(w.seq_lens.astype(np.int64).sum()), "query_tokens": tokens,
+                   "n_ext": w.n_ext, "splits": int(info.total_splits), "tasks": int(info.num_tasks)},
+        "plan_ms": {"p50": round(1e3 * float(np.median(r.plan_times)), 3),
+                    "p95": round(1e3 * percentile(r.plan_times, 95), 3)},
+        "device_error_flag": flag, "roofline": roof,
+        "_total_ms": t["total_ms"], "_wall_s": t["wall_s"],
+    }
+    if np.any(w.q_lens > 1):
+        dec = int(np.sum(w.q_lens[w.q_lens == 1]))
+        out["decode_tokens_per_s"] = round(dec / (step_med * 1e-3), 1)
+        out["prefill_tokens_per_s"] = round((tokens - dec) / (step_med * 1e-3), 1)
+    r.free()
+    return out
+
+
+def load(key: str, cache: dict):
+    """Workload `key` (1-5, or 5d for the decode part of 5), generated once."""
+    import workloads as wl
+    if key == "5d":
+        return decode_part(load("5", cache))
+    if key not in cache:
+        t = time.perf_counter()
+        cache[key] = wl.make(int(key))
+        print(f"[bench] workload {cache[key].name}: batch {cache[key].batch}, generated in "
+              f"{time.perf_counter() - t:.1f}s", file=sys.stderr, flush=True)
+    return cache[key]
+
+
+def main(argv=None):
+    args = parse(argv)
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1], args.workload)
         return
@@ -246,57 +459,15 @@ def main():
                           "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
-    import split_kv_partial_amd as skv
-    import workloads as wl
+    import split_kv_partial_amd as skv  # noqa: F401  (fails loudly without the built library)
 
     assert torch.cuda.is_available(), "bench needs a GPU"
     dev = torch.device("cuda:0")
-    wid = args.workload
-    cid = int(wid.rstrip("d"))
-    t_gen = time.perf_counter()
-    w = wl.make(cid, decode_only=wid.endswith("d"))
-    t_gen = time.perf_counter() - t_gen
-    print(f"[bench] workload {w.name}: batch {w.batch}, generated in {t_gen:.1f}s", file=sys.stderr,
-          flush=True)
-
-    def to_dev(a, bf16):
-        if bf16:
-            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-
-    bf16 = w.dtype == "bf16"
-    q = to_dev(w.q, bf16)
-    k = to_dev(w.k_pages, bf16)
-    v = k if w.mla else to_dev(w.v_pages, bf16)
-    pt = torch.from_numpy(w.page_table).to(dev)
-    sl = torch.from_numpy(w.seq_lens).to(dev)
-    o_ext = None if w.o_ext is None else torch.from_numpy(w.o_ext).to(dev)
-    lse_ext = None if w.lse_ext is None else torch.from_numpy(w.lse_ext).to(dev)
-    spec = skv.AttnSpec(w.num_q_heads, w.num_kv_heads, w.head_dim_qk, w.head_dim_v, w.page_size,
-                        dtype=torch.bfloat16 if bf16 else torch.float32, mla=w.mla, causal=w.causal)
     num_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-
     plan_params = plan_overrides(args.plan_param)
-
-    # host planner, once per batch (timed on its own, after one untimed call
-    # that starts the planner's worker threads, a once-per-process cost)
-    plan_times = []
-    for it in range(21):
-        t = time.perf_counter()
-        if w.chunk_tokens:
-            plan = skv.plan_fixed_chunks(w.seq_lens, spec, w.chunk_tokens, num_cu, q_lens=w.q_lens)
-        else:
-            plan = skv.plan_splits(w.seq_lens, spec, num_cu, q_lens=w.q_lens, n_ext=w.n_ext,
-                                   params=plan_params)
-        if it > 0:
-            plan_times.append(time.perf_counter() - t)
-    info = plan.info()
-    ws = plan.workspace(dev)
-    o_part = torch.empty(info.state_rows, w.head_dim_v, dtype=torch.float32, device=dev)
-    lse_part = torch.empty(info.state_rows, dtype=torch.float32, device=dev)
-    o_out = torch.empty(info.total_rows, w.head_dim_v, dtype=torch.float32, device=dev)
-    lse_out = torch.empty(info.total_rows, dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
+    head_key = HEADLINE if args.workload == "all" else args.workload
+    rest = PER_CONFIG if args.workload == "all" else ()
+    cache = {}
     if args.traffic_probe:
         src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -304,84 +475,61 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    def step():
-        skv.decode_attn_partial(q, k, v, pt, sl, plan, w.scale, o_part=o_part, lse_part=lse_part)
-        skv.merge_states(o_part, lse_part, plan, o_ext, lse_ext, o_out=o_out, lse_out=lse_out)
+    head_w = load(head_key, cache)
+    head = measure(head_w, head_key, dev, num_cu, args, plan_params)
+    print(f"[bench] {head_w.name}: {head['ms_per_step']} ms per step", file=sys.stderr, flush=True)
+    per = {}
+    for key in rest:
+        w = load(key, cache)
+        per[key] = measure(w, key, dev, num_cu, args, plan_params)
+        print(f"[bench] {w.name}: {per[key]['ms_per_step']} ms per step", file=sys.stderr, flush=True)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # per-launch events on the launch stream (torch's current stream): mark[j]
-    # precedes launch j (attention and merge alternate) and also ends launch
-    # j - 1, so a step carries two events and the first and last bracket the
-    # whole timed region
-    mark = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    for i in range(args.steps):
-        mark[2 * i].record()
-        skv.decode_attn_partial(q, k, v, pt, sl, plan, w.scale, o_part=o_part, lse_part=lse_part)
-        mark[2 * i + 1].record()
-        skv.merge_states(o_part, lse_part, plan, o_ext, lse_ext, o_out=o_out, lse_out=lse_out)
-    mark[2 * args.steps].record()
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    total_ms = mark[0].elapsed_time(mark[2 * args.steps])
-    attn_ms = np.array([mark[2 * i].elapsed_time(mark[2 * i + 1]) for i in range(args.steps)])
-    merge_ms = np.array([mark[2 * i + 1].elapsed_time(mark[2 * i + 2]) for i in range(args.steps)])
-    ms_per_step = total_ms / args.steps
-    flag = plan.read_error_flag(dev)
-
-    kv_tokens = visible_kv_tokens(w)
-    kv_bytes = kv_tokens * (w.kv_bytes_per_token() if not w.mla else w.head_dim_qk * 2)
-    gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
-    tokens = int(w.q_lens.sum())
-    kern = kernel_of(w)
-    attn_avg = float(attn_ms.mean())
-    achieved = kv_bytes / (attn_avg * 1e-3) / 1e9
-    traffic = measured_traffic(kern, wid)
-    roofline = {"kernel": kern, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic, "launch_ms_avg": round(attn_avg, 4),
-                "algorithmic_bytes_per_launch": int(kv_bytes)}
-    if w.mla:
-        fl = attention_flops(w)
-        roofline["mfma_tflops"] = round(fl / (attn_avg * 1e-3) / 1e12, 1)
-        roofline["mfma_frac"] = round(fl / (attn_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
-    out = {
-        "metric": METRIC, "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16" if bf16 else "f32", "data": "synthetic",
-        "config": {"workload": w.name, "batch": w.batch, "num_q_heads": w.num_q_heads,
-                   "num_kv_heads": w.num_kv_heads, "head_dim_qk": w.head_dim_qk,
-                   "head_dim_v": w.head_dim_v, "page_size": w.page_size,
-                   "kv_tokens": int(kv_tokens), "query_tokens": tokens, "n_ext": w.n_ext,
-                   "splits": int(info.total_splits), "tasks": int(info.num_tasks)},
-        "hbm_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-        "tokens_per_s": round(tokens / (ms_per_step * 1e-3), 1),
-        "attn_ms": round(attn_avg, 4), "merge_ms": round(float(merge_ms.mean()), 4),
-        "attn_ms_p95": round(float(np.percentile(attn_ms, 95)), 4),
-        "plan_ms": {"p50": round(1e3 * float(np.median(plan_times)), 3),
-                    "p95": round(1e3 * float(np.percentile(plan_times, 95)), 3)},
-        "ms_per_step_incl_plan": round(ms_per_step + 1e3 * float(np.median(plan_times)), 4),
-        "wall_s_timed": round(t_wall, 4), "device_error_flag": flag,
-        "roofline": roofline,
-    }
+    probe = None
     if not args.no_hbm_probe:
-        # a measurement beside the step: if its buffer cannot be had, say so
-        # and keep the step's line
+        # a measurement beside the steps: if its buffer cannot be had, say so
+        # and keep the line
         try:
-            pr = hbm_probe(dev, num_cu)
-            out["hbm_probe"] = pr
-            out["frac_of_probe"] = round(gbs / pr["gbs"], 4)
-            roofline["frac_of_probe"] = round(achieved / pr["gbs"], 4)
+            probe = hbm_probe(dev, num_cu)
         except (RuntimeError, MemoryError) as e:   # torch reports device OOM as RuntimeError
-            out["hbm_probe"] = None
             print(f"[bench] HBM probe skipped: {e}", file=sys.stderr, flush=True)
+    for m in [head, *per.values()]:
+        if probe:
+            m["frac_of_probe"] = round(m["kv_gbs"] / probe["gbs"], 4)
+            if m["roofline"]["unit"] == "GB/s":
+                m["roofline"]["frac_of_probe"] = round(m["roofline"]["achieved"] / probe["gbs"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        head["cpu_baseline"] = cpu_baseline(head_w, args.cpu_seconds)
+        for key in rest:
+            per[key]["cpu_baseline"] = cpu_baseline(load(key, cache), args.cpu_seconds)
+
+    total_ms, wall = head.pop("_total_ms"), head.pop("_wall_s")
+    for m in per.values():
+        m.pop("_total_ms"), m.pop("_wall_s")
+    out = {
+        "metric": METRIC, "value": head["kv_gbs"], "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "ms_per_step_p95": head["ms_per_step_p95"], "ms_per_step_mean": head["ms_per_step_mean"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": head_w.dtype, "data": "synthetic",
+        "config": head["config"],
+        "hbm_frac_of_peak": head["hbm_frac_of_peak"],
+        "tokens_per_s": head["tokens_per_s"],
+        "attn_ms": head["attn_ms"], "attn_ms_p95": head["attn_ms_p95"], "merge_ms": head["merge_ms"],
+        "plan_ms": head["plan_ms"],
+        "ms_per_step_incl_plan": round(head["ms_per_step"] + head["plan_ms"]["p50"], 4),
+        "timed_region_ms": round(total_ms, 3), "wall_s_timed": round(wall, 4),
+        "device_error_flag": head["device_error_flag"],
+        "roofline": head["roofline"],
+        "step_roofline": head["step_roofline"],
+    }
+    if probe:
+        out["hbm_probe"] = probe
+        out["frac_of_probe"] = head["frac_of_probe"]
+    if "cpu_baseline" in head:
+        out["cpu_baseline"] = head["cpu_baseline"]
+    if per:
+        out["per_config"] = per
     print(json.dumps(out))
 
 

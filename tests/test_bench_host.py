@@ -83,3 +83,34 @@ def test_plan_param_overrides():
     for bad in (["rho"], ["no_such=1"], ["slots_per_cu=2.5"], ["_fields_=1"]):
         with pytest.raises(ValueError):
             bench.plan_overrides(bad)
+
+
+def test_kv_bytes_count_each_request_once():
+    # a chunk of 8 query tokens shares its request's 40-token history: the KV
+    # is read once per request, whatever the number of query tokens
+    w = wl.build("t", dtype="bf16", mla=False, seq_lens=[100, 40], q_lens=[1, 8], num_q_heads=4,
+                 num_kv_heads=2, head_dim_qk=64, head_dim_v=64, page_size=16, scale=0.125, seed=1)
+    assert bench.kv_bytes(w) == 140 * 2 * (64 + 64) * 2
+    m = wl.build("m", dtype="bf16", mla=True, seq_lens=[100, 40], q_lens=[1, 8], num_q_heads=16,
+                 num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=16, scale=0.07, seed=1)
+    assert bench.kv_bytes(m) == 140 * 576 * 2          # MLA rows once: the value is part of the row
+    # step bytes: KV + queries + states written and read back + outputs
+    rows = 9 * 16
+    assert bench.step_bytes(m, state_rows=3 * rows) == (140 * 576 * 2 + 9 * 16 * 576 * 2
+                                                        + 2 * 3 * rows * 513 * 4 + rows * 513 * 4)
+
+
+def test_decode_part_of_the_shard_workload():
+    w = wl.build("shard", dtype="bf16", mla=True, seq_lens=[300, 200, 500], q_lens=[1, 1, 20],
+                 num_q_heads=16, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=64,
+                 scale=0.07, seed=3, n_ext=2)
+    d = bench.decode_part(w)
+    assert d.batch == 2 and d.n_ext == 0 and d.o_ext is None and d.total_q == 2
+    assert np.array_equal(d.page_table, w.page_table[:2]) and d.k_pages is w.k_pages
+    assert np.array_equal(d.q, w.q[:2]) and np.array_equal(d.seq_lens, [300, 200])
+
+
+def test_default_run_is_the_headline_plus_every_other_workload():
+    a = bench.parse([])
+    assert a.workload == "all" and a.steps == 60 and a.warmup == 40 and a.gpus == 1
+    assert bench.HEADLINE == "5d" and bench.PER_CONFIG == ("2", "3", "4", "5")
