@@ -103,8 +103,11 @@ typedef struct skv_plan_params {
   int32_t slots_per_cu;       /* K = num_cu * slots_per_cu; 0 = kernel default   */
   int32_t warps_per_slot;     /* merge waves per slot; 0 = kernel default        */
   int32_t max_splits;         /* upper bound on splits per request (<= 64)       */
-  int32_t overlap_reduction;  /* 0: merge runs after attention (this library's
-                                 executor); 1: fused engine of the pages         */
+  int32_t overlap_reduction;  /* 0: the merge runs after attention (two
+                                 launches); 1: the pages' fused engine, where
+                                 reduction overlaps the attention tail:
+                                 skv_decode_attn then runs attention and merge
+                                 in one launch                                   */
   int32_t use_calibration;    /* 1: take rho, delta_attn, delta_red and gamma from
                                  the library's MI355X fit for the kernel the
                                  problem selects (the fields below are ignored) */
@@ -116,7 +119,13 @@ typedef struct skv_plan_params {
                                  -1 (default): the choice measured for the
                                  kernel the problem selects (on for MLA, off
                                  for GQA)                                      */
-  int32_t reserved;
+  int32_t query_tile;         /* query tokens per attention task: 0 (default) =
+                                 the kernel's choice (one token, or a tile of
+                                 128 / G tokens for bf16 GQA groups of 8 and
+                                 16); other values plan that tile size, and the
+                                 compute calls accept such a plan only if the
+                                 kernel runs tasks of that size
+                                 (SKV_ERR_UNSUPPORTED)                         */
   double rho;                 /* per-tile time floor                             */
   double delta_attn;          /* per attention task overhead, tile-equivalents   */
   double delta_red;           /* per reduction overhead                          */
@@ -144,7 +153,9 @@ typedef struct skv_plan_info {
   double rho, delta_attn, delta_red, gamma;  /* model parameters in effect        */
   double tile_time_us;        /* microseconds per model unit (calibration)       */
   int32_t balanced_candidates; /* 0 or 1: candidate set in effect               */
-  int32_t reserved;
+  int32_t query_tile;         /* query tokens per attention task (consecutive
+                                 tokens of one request; the last tile of a
+                                 request may hold fewer)                       */
 } skv_plan_info;
 
 /* Fill p with the library defaults: use_calibration = 1,
@@ -184,7 +195,7 @@ skv_status skv_plan_get_info(const skv_plan* plan, skv_plan_info* info);
 /* Copy the plan out (host buffers; any may be NULL):
  * split_counts [batch]; split_start / split_end [total_splits] token ranges in
  * request-then-split order; state_row_offset [batch + 1];
- * task_order [num_tasks][4] = (request, kv_head, query token, split) in the
+ * task_order [num_tasks][4] = (request, kv_head, query tile, split) in the
  * launch order of the attention work-groups. */
 skv_status skv_plan_export(const skv_plan* plan, int32_t* split_counts, int32_t* split_start,
                            int32_t* split_end, int64_t* state_row_offset,
@@ -237,11 +248,17 @@ size_t skv_decode_attn_scratch_bytes(const skv_plan* plan);
 
 /* The whole path in one call: the partial attention state of every split of
  * the plan (as skv_decode_attn_partial) into `scratch`, then their exact merge
- * with n_ext external states into o_out / lse_out (as skv_merge_states).
- * Arguments are those of the two calls; scratch: device, caller-owned, at
- * least skv_decode_attn_scratch_bytes(plan) bytes (SKV_ERR_NO_MEMORY if
- * scratch_bytes is smaller), not read before it is written; the same scratch
- * must not be used by two calls that overlap in time. */
+ * with n_ext external states into o_out / lse_out (as skv_merge_states), with
+ * the same results bit for bit. A plan built with overlap_reduction = 0 runs
+ * as those two launches. One built with overlap_reduction = 1 runs as one
+ * launch (LiquidCP, section 6.2 and appendix A.3): each work-group computes
+ * one task, publishes it through a per-request counter in the scratch, and
+ * work-groups that finish after every task has started merge the requests
+ * whose tasks have all published. Arguments are those of the two calls;
+ * scratch: device, caller-owned, at least skv_decode_attn_scratch_bytes(plan)
+ * bytes (SKV_ERR_NO_MEMORY if scratch_bytes is smaller), not read before it
+ * is written; the same scratch must not be used by two calls that overlap in
+ * time. */
 skv_status skv_decode_attn(const skv_attn_desc* desc, const void* q, const void* k_pages,
                            const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
                            const skv_plan* plan, const void* workspace, void* scratch,
@@ -276,7 +293,10 @@ skv_status skv_decode_attn_noalloc(const skv_attn_desc* desc, const void* q, con
  *             tasks read no KV and write NaN states;
  * bit 2 (4) = MLA only: scores whose scaled values fp32 cannot order within
  *             the kernel's two passes (only with absurdly large scales): the
- *             affected state is NaN.
+ *             affected state is NaN;
+ * bit 3 (8) = one-launch skv_decode_attn only: a merge waited about a second
+ *             for its request's tasks and gave up: that request's merged rows
+ *             are NaN (not expected; it would mean the launch lost a task).
  * Rows of tasks that met no error are computed normally. */
 skv_status skv_read_error_flag(const void* workspace, int32_t* flag, void* stream);
 

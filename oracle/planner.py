@@ -46,8 +46,12 @@ Readings where the pages are silent:
   explicit reference plan instead.
 * A split of n tiles into s parts gives the first (n mod s) parts ceil(n/s)
   tiles and the rest floor(n/s) (Figure 8 splits 176 tiles as 59, 59, 58).
-* One attention task per (request, KV head, query token, split); the pages fix
+* One attention task per (request, KV head, query tile, split); the pages fix
   one query tile per decoding region and size the tile by the rows it holds.
+  A query tile is `query_tile` consecutive query tokens of a request (the last
+  tile may hold fewer); the executor chooses the size (one token when each
+  token's rows already fill a tile). A task's KV tiles are those its tile's
+  last query token sees (causal rows: the most of any token of the tile).
 * Events at equal times: completions first (in CTA order), then dispatches to
   the free CTAs in CTA-index order. Warps are claimed earliest-available first,
   ties by CTA then warp index. Candidate ties after the pages' keys: the earlier
@@ -96,13 +100,14 @@ class Problem:
     rows_per_token: int = 1     # output vectors per query token (query heads)
     n_ext: int = 0              # external states merged into every row
     causal: bool = True
+    query_tile: int = 1         # query tokens per attention task
 
 
 @dataclass
 class Task:
     b: int
     g: int
-    qi: int
+    qi: int       # query tile index within the request
     r: int
     lo: int       # first token of the split
     hi: int       # end token of the split (exclusive)
@@ -147,6 +152,11 @@ def is_decode(n: int) -> bool:
     return n <= 16
 
 
+def query_tiles(n: int, qt: int):
+    """(first, last) query token of each tile of a request with n tokens."""
+    return [(a, min(n, a + qt) - 1) for a in range(0, n, qt)]
+
+
 def build_tasks(pb: Problem, prm: Params, splits):
     """Attention tasks of a plan in queue order."""
     T = prm.tile_tokens
@@ -155,8 +165,8 @@ def build_tasks(pb: Problem, prm: Params, splits):
     for b in range(B):
         L, n = pb.seq_lens[b], pb.q_lens[b]
         rng = split_ranges(L, splits[b], T)
-        for qi in range(n):
-            vis = L - n + qi + 1 if pb.causal else L
+        for qi, (_, last) in enumerate(query_tiles(n, pb.query_tile)):
+            vis = L - n + last + 1 if pb.causal else L
             vis_t = n_tiles(vis, T)
             for g in range(pb.num_kv_heads):
                 for r, (lo, hi) in enumerate(rng):
@@ -282,7 +292,8 @@ def balanced_plan(pb: Problem, prm: Params, wave_tasks: int):
     max_splits) splits (at least one); None if even NoSplit has more tasks."""
     T = prm.tile_tokens
     nt = [n_tiles(L, T) for L in pb.seq_lens]
-    per_split = [n * pb.num_kv_heads for n in pb.q_lens]   # tasks of one split
+    # tasks of one split: one per query tile and KV head
+    per_split = [len(query_tiles(n, pb.query_tile)) * pb.num_kv_heads for n in pb.q_lens]
 
     def counts(t):
         return [max(1, min(-(-n // t), n, prm.max_splits)) for n in nt]

@@ -54,7 +54,7 @@ class PlanParams(ctypes.Structure):
     _fields_ = [("tile_tokens", ctypes.c_int32), ("slots_per_cu", ctypes.c_int32),
                 ("warps_per_slot", ctypes.c_int32), ("max_splits", ctypes.c_int32),
                 ("overlap_reduction", ctypes.c_int32), ("use_calibration", ctypes.c_int32),
-                ("balanced_candidates", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("balanced_candidates", ctypes.c_int32), ("query_tile", ctypes.c_int32),
                 ("rho", ctypes.c_double), ("delta_attn", ctypes.c_double),
                 ("delta_red", ctypes.c_double), ("gamma", ctypes.c_double),
                 ("min_gain", ctypes.c_double), ("tile_time_us", ctypes.c_double)]
@@ -70,7 +70,7 @@ class PlanInfo(ctypes.Structure):
                 ("nosplit_score", ctypes.c_double), ("rho", ctypes.c_double),
                 ("delta_attn", ctypes.c_double), ("delta_red", ctypes.c_double),
                 ("gamma", ctypes.c_double), ("tile_time_us", ctypes.c_double),
-                ("balanced_candidates", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("balanced_candidates", ctypes.c_int32), ("query_tile", ctypes.c_int32)]
 
 
 def _load():

@@ -33,6 +33,26 @@ namespace {
 
 bool is_pow2_page(int p) { return p == 16 || p == 32 || p == 64; }
 
+Variant pick_variant(const skv_attn_desc& d);
+
+// Query tokens per attention task for the kernel the problem selects: the
+// bf16 matrix-core GQA kernel takes tiles of consecutive tokens whose rows of
+// (token, head) fill its four waves' column blocks (64 rows for D = 128, 128
+// for D = 64); the others take one token (the MLA kernel's 128 heads already
+// fill a tile).
+int query_tile_of(const skv_attn_desc& d) {
+  const Variant v = pick_variant(d);
+  const int rows = d.head_dim_qk == 128 ? 64 : 128;
+  if (v == Variant::GqaMfma || v == Variant::GqaMfmaG8)
+    return std::max(1, rows / (d.num_q_heads / d.num_kv_heads));
+  return 1;
+}
+
+// Whether the kernel the problem selects runs tasks of qt query tokens.
+bool query_tile_runs(const skv_attn_desc& d, int qt) {
+  return qt == 1 || qt <= query_tile_of(d);
+}
+
 Variant pick_variant(const skv_attn_desc& d) {
   if (d.mla) return Variant::MlaMfma;
   const int G = d.num_q_heads / d.num_kv_heads;
@@ -141,6 +161,8 @@ skv_status check_params(const skv_plan_params* p) {
     return fail(SKV_ERR_INVALID_ARG, "balanced_candidates must be -1, 0 or 1");
   if (p->overlap_reduction != 0 && p->overlap_reduction != 1)
     return fail(SKV_ERR_INVALID_ARG, "overlap_reduction must be 0 or 1");
+  if (p->query_tile < 0 || p->query_tile > 128)
+    return fail(SKV_ERR_INVALID_ARG, "query_tile must be in [0, 128] (got %d)", p->query_tile);
   if (!(p->rho > 0) || !(p->delta_attn >= 0) || !(p->delta_red >= 0) || !(p->gamma >= 0) ||
       !(p->min_gain >= 0 && p->min_gain < 1))
     return fail(SKV_ERR_INVALID_ARG, "model parameters out of range");
@@ -161,6 +183,7 @@ struct skv_plan {
   std::vector<DevReq> reqs;
   std::vector<DevUnit> units;
   int run = 1;
+  int max_ntok = 1;                       // most query tokens of any task
   double score = NAN, t_attn = NAN, nosplit_score = NAN;
   int split_adopted = 0;
   std::vector<uint8_t> image;
@@ -183,14 +206,16 @@ void finish_plan(skv_plan* pl) {
   std::vector<int64_t> qoff(B + 1, 0);
   for (int b = 0; b < B; ++b) qoff[b + 1] = qoff[b] + pl->pb.q_lens[b];
   std::vector<DevTask> dev(pl->tasks.size());
+  const int qt = pl->pb.query_tile;
   for (size_t i = 0; i < pl->tasks.size(); ++i) {
     TaskDesc& t = pl->tasks[i];
     const int64_t L = pl->pb.seq_lens[t.b], n = pl->pb.q_lens[t.b];
     const int64_t rows = n * H;
-    t.out_row = (int32_t)(pl->state_row_offset[t.b] + (int64_t)t.r * rows + (int64_t)t.qi * H +
-                          (int64_t)t.g * G);
-    const int64_t vis = pl->pb.causal ? L - n + t.qi + 1 : L;
+    const int64_t first = (int64_t)t.qi * qt, last = std::min<int64_t>(n, first + qt) - 1;
+    t.out_row = (int32_t)(pl->state_row_offset[t.b] + (int64_t)t.r * rows + first * H + (int64_t)t.g * G);
+    const int64_t vis = pl->pb.causal ? L - n + last + 1 : L;
     DevTask& dt = dev[i];
+    std::memset(&dt, 0, sizeof dt);
     dt.b = t.b;
     dt.kvh = t.g;
     dt.lo = t.lo;
@@ -198,7 +223,11 @@ void finish_plan(skv_plan* pl) {
     dt.q_row = t.q_row;
     dt.out_row = t.out_row;
     dt.seq_len = (int32_t)L;
-    dt.pad = 0;
+    dt.ntok = (int32_t)(last - first + 1);
+    pl->max_ntok = std::max(pl->max_ntok, dt.ntok);
+    dt.hi = t.hi;
+    dt.vis_last = (int32_t)vis;
+    dt.step = pl->pb.causal ? 1 : 0;
   }
   pl->reqs.resize(B);
   for (int b = 0; b < B; ++b) {
@@ -206,7 +235,10 @@ void finish_plan(skv_plan* pl) {
     pl->reqs[b].splits = (int32_t)pl->ranges[b].size();
     pl->reqs[b].rows = (int32_t)(pl->pb.q_lens[b] * H);
     pl->reqs[b].out_row = (int32_t)(qoff[b] * H);
+    pl->reqs[b].tasks = 0;
+    pl->reqs[b].pad[0] = pl->reqs[b].pad[1] = pl->reqs[b].pad[2] = 0;
   }
+  for (const TaskDesc& t : pl->tasks) ++pl->reqs[t.b].tasks;
   pl->run = reduction_run(pl->pb, pl->prm);
   pl->units.clear();
   for (int b = 0; b < B; ++b) {
@@ -263,6 +295,13 @@ skv_status new_plan(const skv_attn_desc* desc, const int32_t* seq_lens, const in
   pl->pb.rows_per_token = desc->num_q_heads;
   pl->pb.n_ext = n_ext;
   pl->pb.causal = desc->causal != 0;
+  pl->pb.query_tile = params && params->query_tile > 0 ? params->query_tile : query_tile_of(*desc);
+  if (!query_tile_runs(*desc, pl->pb.query_tile)) {
+    const int qt = pl->pb.query_tile;
+    delete pl;
+    return fail(SKV_ERR_UNSUPPORTED, "query_tile %d exceeds the %d tokens the selected kernel runs per task",
+                qt, query_tile_of(*desc));
+  }
   pl->prm = model_params(*desc, num_cu, params);
   *pl_out = pl;
   return SKV_OK;
@@ -418,7 +457,7 @@ skv_status skv_plan_get_info(const skv_plan* pl, skv_plan_info* info) {
   info->gamma = pl->prm.gamma;
   info->tile_time_us = pl->prm.tile_time_us;
   info->balanced_candidates = pl->prm.balanced_candidates;
-  info->reserved = 0;
+  info->query_tile = pl->pb.query_tile;
   return SKV_OK;
 }
 
@@ -471,6 +510,9 @@ static skv_status check_plan_matches(const skv_attn_desc* d, const skv_plan* pl)
   for (int b = 0; b < d->batch; ++b)
     if ((pl->pb.seq_lens[b] + d->page_size - 1) / d->page_size > d->max_pages_per_seq)
       return fail(SKV_ERR_PLAN_MISMATCH, "plan's seq_lens[%d] exceeds max_pages_per_seq", b);
+  if (!query_tile_runs(*d, pl->pb.query_tile))
+    return fail(SKV_ERR_UNSUPPORTED, "the kernel for this problem does not run tasks of %d query tokens",
+                pl->pb.query_tile);
   return SKV_OK;
 }
 
@@ -511,7 +553,7 @@ skv_status launch_attention(const skv_attn_desc* desc, const void* q, const void
                             const skv_plan* plan, const void* workspace, float* o_part, float* lse_part,
                             void* stream) {
   AttnLaunch a{desc, q, k_pages, v_pages, page_table, seq_lens, workspace, o_part, lse_part,
-               (int)plan->tasks.size(), plan->tasks_off, (hipStream_t)stream};
+               (int)plan->tasks.size(), plan->tasks_off, (hipStream_t)stream, plan->max_ntok};
   hipError_t e;
   switch (pick_variant(*desc)) {
     case Variant::GqaValu: e = launch_gqa_valu(a); break;
@@ -523,17 +565,24 @@ skv_status launch_attention(const skv_attn_desc* desc, const void* q, const void
   return SKV_OK;
 }
 
-skv_status launch_merge_for(const skv_attn_desc* desc, const skv_plan* plan, const void* workspace,
-                            const float* o_part, const float* lse_part, int32_t n_ext, const float* o_ext,
-                            const float* lse_ext, void* o_out, int32_t out_dtype, float* lse_out,
-                            void* stream) {
+MergeLaunch merge_launch(const skv_attn_desc* desc, const skv_plan* plan, const void* workspace,
+                         const float* o_part, const float* lse_part, int32_t n_ext, const float* o_ext,
+                         const float* lse_ext, void* o_out, int32_t out_dtype, float* lse_out, void* stream) {
   int64_t tq = 0;
   for (int64_t n : plan->pb.q_lens) tq += n;
   int max_splits = 1;
   for (const auto& r : plan->ranges) max_splits = std::max(max_splits, (int)r.size());
-  MergeLaunch m{workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out, out_dtype == SKV_BF16, lse_out,
-                desc->head_dim_v, tq * desc->num_q_heads, (int)plan->units.size(), plan->reqs_off,
-                plan->units_off, (hipStream_t)stream, max_splits + n_ext, plan->run};
+  return MergeLaunch{workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out, out_dtype == SKV_BF16, lse_out,
+                     desc->head_dim_v, tq * desc->num_q_heads, (int)plan->units.size(), plan->reqs_off,
+                     plan->units_off, (hipStream_t)stream, max_splits + n_ext, plan->run};
+}
+
+skv_status launch_merge_for(const skv_attn_desc* desc, const skv_plan* plan, const void* workspace,
+                            const float* o_part, const float* lse_part, int32_t n_ext, const float* o_ext,
+                            const float* lse_ext, void* o_out, int32_t out_dtype, float* lse_out,
+                            void* stream) {
+  const MergeLaunch m = merge_launch(desc, plan, workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out,
+                                     out_dtype, lse_out, stream);
   hipError_t e = launch_merge(m);
   if (e != hipSuccess) return fail(SKV_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
   return SKV_OK;
@@ -547,7 +596,8 @@ ScratchLayout scratch_layout(const skv_plan* pl) {
   ScratchLayout s;
   const int64_t rows = pl->state_row_offset.back();
   s.counters_off = 0;
-  s.o_off = align256(sizeof(int32_t) * (4 + (size_t)pl->desc.batch));
+  s.o_off = align256(kFusedArgsBytes +
+                     sizeof(int32_t) * kFusedCounterLine * (kFusedCounterHead + (size_t)pl->desc.batch));
   s.lse_off = s.o_off + align256((size_t)rows * pl->desc.head_dim_v * sizeof(float));
   s.total = s.lse_off + align256((size_t)rows * sizeof(float));
   return s;
@@ -568,11 +618,33 @@ skv_status decode_attn_impl(const skv_attn_desc* desc, const void* q, const void
   uint8_t* base = static_cast<uint8_t*>(scratch);
   float* o_part = reinterpret_cast<float*>(base + lay.o_off);
   float* lse_part = reinterpret_cast<float*>(base + lay.lse_off);
-  if ((st = launch_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, o_part,
-                             lse_part, stream)))
-    return st;
-  return launch_merge_for(desc, plan, workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out, out_dtype,
-                          lse_out, stream);
+  if (!plan->prm.overlap_reduction) {
+    // the plan assumes the merge runs after attention: two launches
+    st = launch_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, o_part,
+                          lse_part, stream);
+    if (st) return st;
+    return launch_merge_for(desc, plan, workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out,
+                            out_dtype, lse_out, stream);
+  }
+  // the plan assumes the pages' fused engine: attention and merge in one
+  // launch; the setup kernel writes the merge's arguments and clears the
+  // counters in the scratch's counters block
+  const MergeLaunch m = merge_launch(desc, plan, workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out,
+                                     out_dtype, lse_out, stream);
+  uint8_t* block = base + lay.counters_off;
+  hipError_t e = launch_fused_setup(block, m, desc->batch, (int)plan->tasks.size(), (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SKV_ERR_HIP, "fused setup kernel launch: %s", hipGetErrorString(e));
+  AttnLaunch a{desc, q, k_pages, v_pages, page_table, seq_lens, workspace, o_part, lse_part,
+               (int)plan->tasks.size(), plan->tasks_off, (hipStream_t)stream, plan->max_ntok};
+  const FusedLaunch f{block};
+  switch (pick_variant(*desc)) {
+    case Variant::GqaValu: e = launch_gqa_valu_fused(a, f); break;
+    case Variant::GqaMfma:
+    case Variant::GqaMfmaG8: e = launch_gqa_mfma_fused(a, f); break;
+    default: e = launch_mla_mfma_fused(a, f); break;
+  }
+  if (e != hipSuccess) return fail(SKV_ERR_HIP, "fused attention kernel launch: %s", hipGetErrorString(e));
+  return SKV_OK;
 }
 
 }  // namespace skv

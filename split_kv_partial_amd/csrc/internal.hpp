@@ -14,9 +14,10 @@ namespace skv {
 
 constexpr int kTileTokens = 64;
 
-// One attention work-group's job: request b, KV head g, query token qi, split r,
-// KV token range [lo, hi) of the split. q_row = global query-token index;
-// out_row = state row of query head g*G of token qi in split r.
+// One attention work-group's job: request b, KV head g, query tile qi (tokens
+// qi * query_tile .. of the request), split r, KV token range [lo, hi) of the
+// split. q_row = global index of the tile's first query token; out_row = state
+// row of query head g*G of that token in split r.
 struct TaskDesc {
   int32_t b, g, qi, r;
   int32_t lo, hi, q_row, out_row;
@@ -30,13 +31,18 @@ struct DevTask {
   int32_t kvh;      // KV head
   int32_t lo;       // first KV token of the split (multiple of 64)
   int32_t end;      // one past the last KV token this task may read:
-                    // min(split end, visible end of its query token)
-  int32_t q_row;    // global query-token index
-  int32_t out_row;  // state row of the task's first query head
+                    // min(split end, visible end of its last query token)
+  int32_t q_row;    // global index of the task's first query token
+  int32_t out_row;  // state row of the first token's first query head
   int32_t seq_len;  // L_b the plan was built with (checked against seq_lens)
+  int32_t ntok;     // query tokens of the task (consecutive)
+  int32_t hi;       // end of the split's KV range
+  int32_t vis_last; // visible end of the last query token (L_b when not causal);
+                    // token j of ntok sees min(hi, vis_last - (ntok - 1 - j) * step)
+  int32_t step;     // 1 for causal rows, 0 otherwise
   int32_t pad;
 };
-static_assert(sizeof(DevTask) == 32, "device task descriptor is 32 bytes");
+static_assert(sizeof(DevTask) == 48, "device task descriptor is 48 bytes");
 
 // Per-request data the merge needs.
 struct DevReq {
@@ -44,7 +50,10 @@ struct DevReq {
   int32_t splits;      // s_b
   int32_t rows;        // rows_b = q_lens[b] * H_q
   int32_t out_row;     // first merged-output row of the request
+  int32_t tasks;       // attention tasks of the request (the fused launch waits for them)
+  int32_t pad[3];
 };
+static_assert(sizeof(DevReq) == 32, "device request descriptor is 32 bytes");
 
 // One merge unit: `count` consecutive rows of request b starting at row `row`.
 struct DevUnit {
@@ -78,6 +87,7 @@ struct Problem {
   int rows_per_token = 1;
   int n_ext = 0;
   bool causal = true;
+  int query_tile = 1;   // query tokens per attention task
 };
 
 struct Evaluation {
@@ -116,6 +126,7 @@ struct AttnLaunch {
   int num_tasks;
   int64_t tasks_off;   // byte offset of the task descriptors in the workspace
   hipStream_t stream;
+  int max_ntok;        // most query tokens of any task (1: one token per task)
 };
 hipError_t launch_gqa_valu(const AttnLaunch& a);
 hipError_t launch_gqa_mfma(const AttnLaunch& a);
@@ -140,6 +151,22 @@ struct MergeLaunch {
   int run;                       // rows per merge unit (the planner's run)
 };
 hipError_t launch_merge(const MergeLaunch& m);
+
+// Attention and merge in one launch. block: the scratch's counters block: the
+// merge's kernel arguments (kFusedArgsBytes), then kFusedCounterHead + batch
+// counters of kFusedCounterLine int32 each (one 256-byte line per counter),
+// all written by launch_fused_setup on the same stream before the launch.
+constexpr size_t kFusedArgsBytes = 128;
+constexpr int kFusedCounterHead = 3;
+constexpr int kFusedCounterLine = 64;
+struct FusedLaunch {
+  uint8_t* block;
+};
+hipError_t launch_fused_setup(uint8_t* block, const MergeLaunch& m, int batch, int num_tasks,
+                              hipStream_t stream);
+hipError_t launch_gqa_valu_fused(const AttnLaunch& a, const FusedLaunch& f);
+hipError_t launch_gqa_mfma_fused(const AttnLaunch& a, const FusedLaunch& f);
+hipError_t launch_mla_mfma_fused(const AttnLaunch& a, const FusedLaunch& f);
 hipError_t launch_hbm_probe(const void* buf, int64_t bytes, uint32_t* out, int blocks, hipStream_t stream);
 
 // Error reporting shared by the entry points: sets the thread-local message

@@ -115,6 +115,7 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 constexpr int32_t kErrPageId = 1;   // a page id outside [0, num_pages)
 constexpr int32_t kErrSeqLen = 2;   // device seq_lens differ from the plan's
 constexpr int32_t kErrRange = 4;    // scores beyond the range the softmax represents
+constexpr int32_t kErrWait = 8;     // a merge gave up waiting for its inputs
 
 // Record a device error (a vector atomic OR into the flag word).
 __device__ __forceinline__ void raise_error(int32_t* flag, int32_t bit) {

@@ -27,6 +27,7 @@
 // of one dimension are 8 contiguous bytes). No LDS is used until the final
 // merge of the four waves.
 #include "device_common.hpp"
+#include "fused.hpp"
 #include "internal.hpp"
 
 namespace skv {
@@ -191,13 +192,22 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
   }
 }
 
+// LDS of one work-group: the four waves' states for the final merge.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_mfma_kernel(MfmaArgs a) {
-  __shared__ float m_lds[kWaves][kG], l_lds[kWaves][kG];
-  __shared__ float o_lds[kWaves][kG][D + 4];
-  __shared__ int bad_lds[kWaves];
+struct MfmaShared {
+  float m_lds[kWaves][kG], l_lds[kWaves][kG];
+  float o_lds[kWaves][kG][D + 4];
+  int bad_lds[kWaves];
+};
 
-  const DevTask t = a.tasks[blockIdx.x];
+// One task: the query heads of one KV head for one query token over the KV
+// range [lo, end) of one split, written as the split's partial state.
+template <int D>
+__device__ __forceinline__ void gqa_mfma_task(const MfmaArgs& a, const DevTask& t, MfmaShared<D>& sh) {
+  auto& m_lds = sh.m_lds;
+  auto& l_lds = sh.l_lds;
+  auto& o_lds = sh.o_lds;
+  auto& bad_lds = sh.bad_lds;
   if (a.seq_lens[t.b] != t.seq_len) {
     // the device lengths are not the ones the plan was built from: no KV is
     // read and the state is NaN (uniform over the work-group: one task)
@@ -286,13 +296,288 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tasks of several query tokens (a query tile of one request: up to
+// kTileRows<D> / G consecutive tokens). The rows (row = token * G + head) are
+// columns of the products in blocks of 16: block b holds rows 16 b .. 16 b + 15.
+// Each wave owns kBPW<D> consecutive blocks (two for D = 64; one for D = 128,
+// where two would not fit the 256 registers of a wave at two waves per SIMD);
+// the waves are arranged as column groups (one per kBPW blocks) times token
+// groups (4 / column groups, which take the split's 32-token steps round-robin
+// and are merged through LDS at the end, as the one-token kernel does). A full
+// tile is four column groups of one token group: every wave streams the whole split,
+// its loads of the same keys and values as its neighbours' served by the
+// caches, so each KV byte comes from HBM once per tile instead of once per
+// token. Causal rows see their own end: lane n's column is one row, masked
+// at min(split end, the visible end of its token).
+// ---------------------------------------------------------------------------
+
+template <int D>
+constexpr int kBPW = D == 64 ? 2 : 1;               // column blocks per wave
+template <int D>
+constexpr int kTileRows = 16 * kWaves * kBPW<D>;    // rows of a full query tile
+
+template <int D>
+struct RowsShared {
+  float m_lds[kWaves][kBPW<D>][kG], l_lds[kWaves][kBPW<D>][kG];
+  float o_lds[kWaves][kBPW<D>][kG][D + 4];
+  int bad_lds[kWaves];
+};
+
+// The rows of a multi-token task written as NaN (a device error).
+template <int D>
+__device__ __forceinline__ void rows_nan(const MfmaArgs& a, const DevTask& t) {
+  for (int j = 0; j < t.ntok; ++j)
+    write_nan_state(a.o_part, a.lse_part, (int64_t)t.out_row + (int64_t)j * a.H_q, a.G, D);
+}
+
+template <int D>
+struct RowsState {
+  float m[kBPW<D>], l[kBPW<D>];
+  f32x4_t o[kBPW<D>][D / 16];
+};
+
+// One 32-token step for the wave's active blocks: scores, masked online
+// softmax (each lane's column has its own end), P*V with hi + lo weights.
+template <int D>
+__device__ __forceinline__ void rows_step(const Ctx<D>& c, int t0, StepRegs<D>& s,
+                                          const u32x4_t (&qf)[kBPW<D>][D / 32], RowsState<D>& st,
+                                          const int (&end_col)[kBPW<D>], int nblk, float scale_log2) {
+  // values past the task's last visible key hold stale or poisoned page data:
+  // zero them so that 0 * NaN cannot reach the accumulators
+  if (t0 + kStep > c.end) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int tok = t0 + 16 * blk + 4 * c.g;
+      const int nv = c.end - tok;
+      if (nv < 4) {
+        const uint32_t m0 = nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0x0000FFFFu : 0u);
+        const uint32_t m1 = nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0x0000FFFFu : 0u);
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) {
+          s.v[blk][nb][0] &= m0;
+          s.v[blk][nb][1] &= m1;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kBPW<D>; ++j) {
+    if (j >= nblk) break;   // wave-uniform
+    f32x4_t sc[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m) acc = mfma16(s.k[blk][m], qf[j][m], acc);
+      sc[blk] = acc;
+    }
+    float sv[8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int tok = t0 + 16 * blk + 4 * c.g + e;
+        sv[4 * blk + e] = tok < end_col[j] ? sc[blk][e] * scale_log2 : -INFINITY;
+      }
+    float mt = sv[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
+    mt = max_xor32(max_xor16(mt));
+    const float mn = fmaxf(st.m[j], mt);
+    // a column may see no key yet (its end precedes this step): keep a finite
+    // reference so that its weights are exp2(-inf) = 0 rather than NaN
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float alpha = fast_exp2(st.m[j] - mref);
+    st.m[j] = mn;
+    float p[8], ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = fast_exp2(sv[i] - mref);
+      ps += p[i];
+    }
+    st.l[j] = st.l[j] * alpha + ps;
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
+    const u32x4_t pf_hi = {ph[0], ph[1], ph[2], ph[3]};
+    const u32x4_t pf_lo = {pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+      st.o[j][nb] *= alpha;
+      const u32x4_t vf = {s.v[0][nb][0], s.v[0][nb][1], s.v[1][nb][0], s.v[1][nb][1]};
+      st.o[j][nb] = mfma16(vf, pf_hi, st.o[j][nb]);
+      st.o[j][nb] = mfma16(vf, pf_lo, st.o[j][nb]);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& task, RowsShared<D>& sh) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  DevTask t = task;
+  t.b = __builtin_amdgcn_readfirstlane(task.b);
+  t.kvh = __builtin_amdgcn_readfirstlane(task.kvh);
+  t.lo = __builtin_amdgcn_readfirstlane(task.lo);
+  t.end = __builtin_amdgcn_readfirstlane(task.end);
+  t.q_row = __builtin_amdgcn_readfirstlane(task.q_row);
+  t.out_row = __builtin_amdgcn_readfirstlane(task.out_row);
+  t.ntok = __builtin_amdgcn_readfirstlane(task.ntok);
+  t.hi = __builtin_amdgcn_readfirstlane(task.hi);
+  t.vis_last = __builtin_amdgcn_readfirstlane(task.vis_last);
+  t.step = __builtin_amdgcn_readfirstlane(task.step);
+  if (a.seq_lens[t.b] != task.seq_len) {
+    // the device lengths are not the ones the plan was built from: no KV is
+    // read and the state is NaN (uniform over the work-group: one task)
+    if (threadIdx.x == 0) raise_error(a.err_flag, kErrSeqLen);
+    rows_nan<D>(a, t);
+    return;
+  }
+  const int G = a.G;
+  const int R = G * t.ntok;                  // rows of the task
+  constexpr int BPW = kBPW<D>;
+  const int CB = (R + 15) >> 4;              // column blocks, at most 4 * BPW
+  const int CG = (CB + BPW - 1) / BPW;       // column groups (BPW blocks each)
+  const int TG = CG == 1 ? 4 : (CG == 2 ? 2 : 1);
+  const int cg = wave % CG, tg = wave / CG;
+  const bool active = tg < TG;
+  const int nblk = active ? min(BPW, CB - BPW * cg) : 0;
+
+  Ctx<D> c;
+  c.a = &a;
+  c.lane = lane;
+  c.g = lane >> 4;
+  c.r16 = lane & 15;
+  c.kvh = t.kvh;
+  c.end = t.end;
+  c.ptab = a.page_table + (int64_t)t.b * a.max_pages;
+
+  // Q^T operands and per-column visible ends of the wave's two blocks (rows
+  // past the task's last are computed on a copy of the last row, not written)
+  u32x4_t qf[BPW][D / 32];
+  int end_col[BPW];
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const int r = min(16 * (BPW * cg + j) + c.r16, R - 1);
+    const int tok = r / G, h = r - tok * G;
+    const uint16_t* qp = a.q + ((int64_t)(t.q_row + tok) * a.H_q + (int64_t)t.kvh * G + h) * D;
+#pragma unroll
+    for (int m = 0; m < D / 32; ++m) qf[j][m] = *reinterpret_cast<const u32x4_t*>(qp + 8 * (4 * m + c.g));
+    end_col[j] = min(t.hi, t.vis_last - (t.ntok - 1 - tok) * t.step);
+  }
+
+  RowsState<D> st;
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    st.m[j] = -INFINITY;
+    st.l[j] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.o[j][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int stride = TG * kStep;
+  int t0 = active ? t.lo + tg * kStep : t.end;
+  StepRegs<D> ra, rb;
+  bool bad = false;
+  if (t0 < c.end) bad |= load_step(c, t0, ra);
+  while (t0 < c.end) {
+    const int t1 = t0 + stride;
+    if (t1 < c.end) bad |= load_step(c, t1, rb);
+    rows_step(c, t0, ra, qf, st, end_col, nblk, a.scale_log2);
+    if (t1 >= c.end) break;
+    const int t2 = t1 + stride;
+    if (t2 < c.end) bad |= load_step(c, t2, ra);
+    rows_step(c, t1, rb, qf, st, end_col, nblk, a.scale_log2);
+    t0 = t2;
+  }
+
+  // every wave's (m, l, o) per block and column into LDS (inactive waves and
+  // blocks contribute the empty state), then each output element combines the
+  // token groups of its column group
+#pragma unroll
+  for (int j = 0; j < BPW; ++j) {
+    const float l = sum_xor32(sum_xor16(st.l[j]));
+    if (c.g == 0) {
+      sh.m_lds[wave][j][c.r16] = j < nblk ? st.m[j] : -INFINITY;
+      sh.l_lds[wave][j][c.r16] = j < nblk ? l : 0.f;
+    }
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sh.o_lds[wave][j][c.r16][16 * nb + 4 * c.g + e] = st.o[j][nb][e];
+  }
+  if (lane == 0) sh.bad_lds[wave] = bad;
+  __syncthreads();
+  if (sh.bad_lds[0] | sh.bad_lds[1] | sh.bad_lds[2] | sh.bad_lds[3]) {
+    rows_nan<D>(a, t);
+    return;
+  }
+  for (int i = threadIdx.x; i < R * D; i += 256) {
+    const int r = i / D, d = i - r * D;
+    const int bi = r >> 4, col = r & 15, gcol = bi / BPW, j = bi % BPW;
+    float M = -INFINITY;
+    for (int w = gcol; w < gcol + CG * TG; w += CG) M = fmaxf(M, sh.m_lds[w][j][col]);
+    float Z = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+      for (int w = gcol; w < gcol + CG * TG; w += CG) {
+        const float scl = fast_exp2(sh.m_lds[w][j][col] - M);
+        Z += scl * sh.l_lds[w][j][col];
+        acc += scl * sh.o_lds[w][j][col][d];
+      }
+    }
+    const int tok = r / G, h = r - tok * G;
+    const int64_t row = (int64_t)t.out_row + (int64_t)tok * a.H_q + h;
+    a.o_part[row * D + d] = M == -INFINITY ? 0.f : acc / Z;
+    if (d == 0) a.lse_part[row] = M == -INFINITY ? -INFINITY : (M + fast_log2(Z)) * kLn2;
+  }
+}
+
+// Multi-token tasks: one work-group per task, in the plan's queue order.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_rows_kernel(MfmaArgs a) {
+  __shared__ RowsShared<D> sh;
+  gqa_rows_task<D>(a, a.tasks[blockIdx.x], sh);
+}
+
+// Multi-token tasks with the merge in the same launch (fused.hpp).
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gqa_rows_fused(MfmaArgs a, FusedArgs f) {
+  __shared__ RowsShared<D> sh;
+  __shared__ int slot;
+  count_started(f);
+  const DevTask t = a.tasks[blockIdx.x];
+  gqa_rows_task<D>(a, t, sh);
+  publish_task(f, t.b);
+  if (all_started(f, &slot)) reduce_phase<D>(f, a.err_flag);
+}
+
+// One work-group per task, in the plan's queue order.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_mfma_kernel(MfmaArgs a) {
+  __shared__ MfmaShared<D> sh;
+  gqa_mfma_task<D>(a, a.tasks[blockIdx.x], sh);
+}
+
+// Attention and merge in one launch (fused.hpp): the task, then the
+// reduction role when every task has started.
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gqa_mfma_fused(MfmaArgs a, FusedArgs f) {
+  __shared__ MfmaShared<D> sh;
+  __shared__ int slot;
+  count_started(f);
+  const DevTask t = a.tasks[blockIdx.x];
+  gqa_mfma_task<D>(a, t, sh);
+  publish_task(f, t.b);
+  if (all_started(f, &slot)) reduce_phase<D>(f, a.err_flag);
+}
+
 }  // namespace
 
-hipError_t launch_gqa_mfma(const AttnLaunch& L) {
+static MfmaArgs mfma_args(const AttnLaunch& L) {
   const skv_attn_desc& d = *L.desc;
-  const int G = d.num_q_heads / d.num_kv_heads;
-  if ((G != kG && G != kG / 2) || d.dtype != SKV_BF16) return hipErrorInvalidValue;
-  if (L.num_tasks == 0) return hipSuccess;
   MfmaArgs a;
   a.q = static_cast<const uint16_t*>(L.q);
   a.k = static_cast<const uint8_t*>(L.k_pages);
@@ -305,17 +590,51 @@ hipError_t launch_gqa_mfma(const AttnLaunch& L) {
   a.lse_part = L.lse_part;
   a.H_q = d.num_q_heads;
   a.H_kv = d.num_kv_heads;
-  a.G = G;
+  a.G = d.num_q_heads / d.num_kv_heads;
   a.page_shift = __builtin_ctz((unsigned)d.page_size);
   a.max_pages = d.max_pages_per_seq;
   a.num_pages = d.num_pages;
   a.scale_log2 = d.softmax_scale * kLog2e;
-  if (d.head_dim_qk == 128)
-    hipLaunchKernelGGL(gqa_mfma_kernel<128>, dim3(L.num_tasks), dim3(256), 0, L.stream, a);
-  else if (d.head_dim_qk == 64)
-    hipLaunchKernelGGL(gqa_mfma_kernel<64>, dim3(L.num_tasks), dim3(256), 0, L.stream, a);
-  else
+  return a;
+}
+
+static bool mfma_supported(const skv_attn_desc& d) {
+  const int G = d.num_q_heads / d.num_kv_heads;
+  return (G == kG || G == kG / 2) && d.dtype == SKV_BF16 && (d.head_dim_qk == 128 || d.head_dim_qk == 64);
+}
+
+hipError_t launch_gqa_mfma(const AttnLaunch& L) {
+  const skv_attn_desc& d = *L.desc;
+  if (!mfma_supported(d)) return hipErrorInvalidValue;
+  if (L.num_tasks == 0) return hipSuccess;
+  const MfmaArgs a = mfma_args(L);
+  // plans with several query tokens per task run on the multi-token kernel
+  if (L.max_ntok > 1 && L.max_ntok * a.G > (d.head_dim_qk == 128 ? kTileRows<128> : kTileRows<64>))
     return hipErrorInvalidValue;
+  if (d.head_dim_qk == 128) {
+    if (L.max_ntok > 1) hipLaunchKernelGGL(gqa_rows_kernel<128>, dim3(L.num_tasks), dim3(256), 0, L.stream, a);
+    else hipLaunchKernelGGL(gqa_mfma_kernel<128>, dim3(L.num_tasks), dim3(256), 0, L.stream, a);
+  } else {
+    if (L.max_ntok > 1) hipLaunchKernelGGL(gqa_rows_kernel<64>, dim3(L.num_tasks), dim3(256), 0, L.stream, a);
+    else hipLaunchKernelGGL(gqa_mfma_kernel<64>, dim3(L.num_tasks), dim3(256), 0, L.stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gqa_mfma_fused(const AttnLaunch& L, const FusedLaunch& F) {
+  const skv_attn_desc& d = *L.desc;
+  if (!mfma_supported(d)) return hipErrorInvalidValue;
+  const MfmaArgs a = mfma_args(L);
+  const FusedArgs f = fused_args(F);
+  if (L.max_ntok > 1 && L.max_ntok * a.G > (d.head_dim_qk == 128 ? kTileRows<128> : kTileRows<64>))
+    return hipErrorInvalidValue;
+  if (d.head_dim_qk == 128) {
+    if (L.max_ntok > 1) hipLaunchKernelGGL(gqa_rows_fused<128>, dim3(L.num_tasks), dim3(256), 0, L.stream, a, f);
+    else hipLaunchKernelGGL(gqa_mfma_fused<128>, dim3(L.num_tasks), dim3(256), 0, L.stream, a, f);
+  } else {
+    if (L.max_ntok > 1) hipLaunchKernelGGL(gqa_rows_fused<64>, dim3(L.num_tasks), dim3(256), 0, L.stream, a, f);
+    else hipLaunchKernelGGL(gqa_mfma_fused<64>, dim3(L.num_tasks), dim3(256), 0, L.stream, a, f);
+  }
   return hipGetLastError();
 }
 

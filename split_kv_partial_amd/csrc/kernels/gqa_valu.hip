@@ -18,6 +18,7 @@
 // weights enter it as a two-term bf16 pair (hi + lo) so that P*V keeps ~16
 // significant bits of each weight.
 #include "device_common.hpp"
+#include "fused.hpp"
 #include "internal.hpp"
 
 namespace skv {
@@ -50,24 +51,38 @@ struct Elem<uint16_t> {
 constexpr int kWaves = 4;
 constexpr int kTile = 64;
 
+// LDS of one work-group.
 template <typename T, int D, int G>
-__global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
+struct ValuShared {
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int QW = kBf16 ? D / 2 : D;  // 32-bit words per query row in LDS
+  uint32_t q_lds[G * QW];
+  // Softmax weights of the current tile, private to each wave: fp32, or bf16
+  // (the bf16 path feeds them to dot2 in token pairs).
+  float p_lds[kWaves][G][kBf16 ? 1 : kTile];
+  uint16_t p16_lds[kWaves][2][G][kBf16 ? kTile : 2];   // [hi, lo]
+  float m_lds[kWaves][G], l_lds[kWaves][G];
+  float o_lds[kWaves][G][D];
+  int bad_lds[kWaves];
+};
+
+// One task: KV head g of one query token over the KV range [lo, end) of one
+// split, written as the split's partial state.
+template <typename T, int D, int G>
+__device__ __forceinline__ void gqa_valu_task(const ValuArgs& a, const DevTask& t, ValuShared<T, D, G>& sh) {
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int X = Elem<T>::X;
   constexpr int NC = D / X;          // 16-byte chunks per key row
   constexpr int DL = D / 64;         // value dimensions per lane
   constexpr int QW = kBf16 ? D / 2 : D;  // 32-bit words per query row in LDS
+  auto& q_lds = sh.q_lds;
+  auto& p_lds = sh.p_lds;
+  auto& p16_lds = sh.p16_lds;
+  auto& m_lds = sh.m_lds;
+  auto& l_lds = sh.l_lds;
+  auto& o_lds = sh.o_lds;
+  auto& bad_lds = sh.bad_lds;
 
-  __shared__ uint32_t q_lds[G * QW];
-  // Softmax weights of the current tile, private to each wave: fp32, or bf16
-  // (the bf16 path feeds them to dot2 in token pairs).
-  __shared__ float p_lds[kWaves][G][kBf16 ? 1 : kTile];
-  __shared__ uint16_t p16_lds[kWaves][2][G][kBf16 ? kTile : 2];   // [hi, lo]
-  __shared__ float m_lds[kWaves][G], l_lds[kWaves][G];
-  __shared__ float o_lds[kWaves][G][D];
-  __shared__ int bad_lds[kWaves];
-
-  const DevTask t = a.tasks[blockIdx.x];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int P = 1 << a.page_shift;
@@ -270,25 +285,49 @@ __global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
   }
 }
 
+// One work-group per task, in the plan's queue order.
 template <typename T, int D, int G>
-static hipError_t launch_t(const AttnLaunch& L, const ValuArgs& args) {
-  hipLaunchKernelGGL((gqa_valu_kernel<T, D, G>), dim3(L.num_tasks), dim3(256), 0, L.stream, args);
+__global__ __launch_bounds__(256) void gqa_valu_kernel(ValuArgs a) {
+  __shared__ ValuShared<T, D, G> sh;
+  gqa_valu_task<T, D, G>(a, a.tasks[blockIdx.x], sh);
+}
+
+// Attention and merge in one launch (fused.hpp): the task, then the
+// reduction role when every task has started.
+template <typename T, int D, int G>
+__global__ __launch_bounds__(256) void gqa_valu_fused(ValuArgs a, FusedArgs f) {
+  __shared__ ValuShared<T, D, G> sh;
+  __shared__ int slot;
+  count_started(f);
+  const DevTask t = a.tasks[blockIdx.x];
+  gqa_valu_task<T, D, G>(a, t, sh);
+  publish_task(f, t.b);
+  if (all_started(f, &slot)) reduce_phase<D>(f, a.err_flag);
+}
+
+template <typename T, int D, int G>
+static hipError_t launch_t(const AttnLaunch& L, const ValuArgs& args, const FusedLaunch* F) {
+  if (F)
+    hipLaunchKernelGGL((gqa_valu_fused<T, D, G>), dim3(L.num_tasks), dim3(256), 0, L.stream, args,
+                       fused_args(*F));
+  else
+    hipLaunchKernelGGL((gqa_valu_kernel<T, D, G>), dim3(L.num_tasks), dim3(256), 0, L.stream, args);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-static hipError_t launch_g(const AttnLaunch& L, const ValuArgs& args, int G) {
+static hipError_t launch_g(const AttnLaunch& L, const ValuArgs& args, int G, const FusedLaunch* F) {
   switch (G) {
-    case 1: return launch_t<T, D, 1>(L, args);
-    case 2: return launch_t<T, D, 2>(L, args);
-    case 4: return launch_t<T, D, 4>(L, args);
-    case 8: return launch_t<T, D, 8>(L, args);
-    case 16: return launch_t<T, D, 16>(L, args);
+    case 1: return launch_t<T, D, 1>(L, args, F);
+    case 2: return launch_t<T, D, 2>(L, args, F);
+    case 4: return launch_t<T, D, 4>(L, args, F);
+    case 8: return launch_t<T, D, 8>(L, args, F);
+    case 16: return launch_t<T, D, 16>(L, args, F);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_gqa_valu(const AttnLaunch& L) {
+static hipError_t launch_valu(const AttnLaunch& L, const FusedLaunch* F) {
   const skv_attn_desc& d = *L.desc;
   ValuArgs args;
   args.q = L.q;
@@ -309,13 +348,17 @@ hipError_t launch_gqa_valu(const AttnLaunch& L) {
   const int G = d.num_q_heads / d.num_kv_heads;
   if (L.num_tasks == 0) return hipSuccess;
   if (d.dtype == SKV_BF16) {
-    if (d.head_dim_qk == 64) return launch_g<uint16_t, 64>(L, args, G);
-    if (d.head_dim_qk == 128) return launch_g<uint16_t, 128>(L, args, G);
+    if (d.head_dim_qk == 64) return launch_g<uint16_t, 64>(L, args, G, F);
+    if (d.head_dim_qk == 128) return launch_g<uint16_t, 128>(L, args, G, F);
   } else {
-    if (d.head_dim_qk == 64) return launch_g<float, 64>(L, args, G);
-    if (d.head_dim_qk == 128) return launch_g<float, 128>(L, args, G);
+    if (d.head_dim_qk == 64) return launch_g<float, 64>(L, args, G, F);
+    if (d.head_dim_qk == 128) return launch_g<float, 128>(L, args, G, F);
   }
   return hipErrorInvalidValue;
 }
+
+hipError_t launch_gqa_valu(const AttnLaunch& L) { return launch_valu(L, nullptr); }
+
+hipError_t launch_gqa_valu_fused(const AttnLaunch& L, const FusedLaunch& F) { return launch_valu(L, &F); }
 
 }  // namespace skv

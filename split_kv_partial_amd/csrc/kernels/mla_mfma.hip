@@ -32,6 +32,7 @@
 #include <type_traits>
 
 #include "device_common.hpp"
+#include "fused.hpp"
 #include "internal.hpp"
 
 namespace skv {
@@ -266,14 +267,34 @@ constexpr int kWaitVm9 = 0x3f70 | 9;
 constexpr int kWaitVm18 = 0x3f70 | (18 & 15) | ((18 >> 4) << 14);
 static_assert(2 * kDmaPerWave == 18 && kBuf == 4, "vmcnt immediates assume 9 DMAs per tile, 4 buffers");
 
-template <bool kSinglePage>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void mla_mfma_kernel(MlaArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t ring[kBuf][kTileElems];
-  __shared__ uint32_t soff_lds[kWaves][kDmaPerWave * 64];
-  __shared__ int restart_pass;   // the last pass in which some head overflowed
+// LDS of one work-group: the tile ring, each wave's DMA offsets, and the
+// restart decision of the softmax.
+struct MlaShared {
+  __attribute__((aligned(16))) uint16_t ring[kBuf][kTileElems];
+  uint32_t soff_lds[kWaves][kDmaPerWave * 64];
+  int restart_pass;   // the last pass in which some head overflowed
+};
 
-  const DevTask t = a.tasks[blockIdx.x];
+// One task: all heads of one query token over the KV range [lo, end) of one
+// split, written as the split's partial state. Every wave of the work-group
+// runs it; it begins and ends with the ring unused.
+template <bool kSinglePage>
+__device__ __forceinline__ void mla_task(const MlaArgs& a, const DevTask& task, MlaShared& sh) {
+  // the task's fields as wave-uniform values (scalar registers), whatever the
+  // caller's code lets the compiler prove: the DMA takes its base address
+  // from scalar registers
+  DevTask t;
+  t.b = __builtin_amdgcn_readfirstlane(task.b);
+  t.kvh = 0;
+  t.lo = __builtin_amdgcn_readfirstlane(task.lo);
+  t.end = __builtin_amdgcn_readfirstlane(task.end);
+  t.q_row = __builtin_amdgcn_readfirstlane(task.q_row);
+  t.out_row = __builtin_amdgcn_readfirstlane(task.out_row);
+  t.seq_len = __builtin_amdgcn_readfirstlane(task.seq_len);
+  t.pad = 0;
+  auto& ring = sh.ring;
+  auto& soff_lds = sh.soff_lds;
+  int& restart_pass = sh.restart_pass;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, n = lane & 15;
@@ -554,11 +575,30 @@ void mla_mfma_kernel(MlaArgs a) {
   }
 }
 
-hipError_t launch_mla_mfma(const AttnLaunch& L) {
+// One work-group per task, in the plan's queue order.
+template <bool kSinglePage>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_mfma_kernel(MlaArgs a) {
+  __shared__ MlaShared sh;
+  mla_task<kSinglePage>(a, a.tasks[blockIdx.x], sh);
+}
+
+// Attention and merge in one launch (fused.hpp): the task, then the
+// reduction role when every task has started.
+template <bool kSinglePage>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_mfma_fused(MlaArgs a, FusedArgs f) {
+  __shared__ MlaShared sh;
+  __shared__ int slot;
+  count_started(f);
+  const DevTask t = a.tasks[blockIdx.x];
+  mla_task<kSinglePage>(a, t, sh);
+  publish_task(f, t.b);
+  if (all_started(f, &slot)) reduce_phase<kDv>(f, a.err_flag);
+}
+
+static MlaArgs mla_args(const AttnLaunch& L) {
   const skv_attn_desc& d = *L.desc;
-  if (d.head_dim_qk != kD || d.head_dim_v != kDv || d.num_kv_heads != 1 || d.dtype != SKV_BF16)
-    return hipErrorInvalidValue;
-  if (L.num_tasks == 0) return hipSuccess;
   MlaArgs a;
   a.q = static_cast<const uint16_t*>(L.q);
   a.kv = static_cast<const uint8_t*>(L.k_pages);
@@ -573,6 +613,28 @@ hipError_t launch_mla_mfma(const AttnLaunch& L) {
   a.max_pages = d.max_pages_per_seq;
   a.num_pages = d.num_pages;
   a.scale_log2 = d.softmax_scale * kLog2e;
+  return a;
+}
+
+hipError_t launch_mla_mfma_fused(const AttnLaunch& L, const FusedLaunch& F) {
+  const skv_attn_desc& d = *L.desc;
+  if (d.head_dim_qk != kD || d.head_dim_v != kDv || d.num_kv_heads != 1 || d.dtype != SKV_BF16)
+    return hipErrorInvalidValue;
+  const MlaArgs a = mla_args(L);
+  const FusedArgs f = fused_args(F);
+  if (d.page_size >= 32)
+    hipLaunchKernelGGL(mla_mfma_fused<true>, dim3(L.num_tasks), dim3(kThreads), 0, L.stream, a, f);
+  else
+    hipLaunchKernelGGL(mla_mfma_fused<false>, dim3(L.num_tasks), dim3(kThreads), 0, L.stream, a, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_mla_mfma(const AttnLaunch& L) {
+  const skv_attn_desc& d = *L.desc;
+  if (d.head_dim_qk != kD || d.head_dim_v != kDv || d.num_kv_heads != 1 || d.dtype != SKV_BF16)
+    return hipErrorInvalidValue;
+  if (L.num_tasks == 0) return hipSuccess;
+  const MlaArgs a = mla_args(L);
   if (d.page_size >= 32)
     hipLaunchKernelGGL(mla_mfma_kernel<true>, dim3(L.num_tasks), dim3(kThreads), 0, L.stream, a);
   else

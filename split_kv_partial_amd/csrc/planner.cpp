@@ -55,7 +55,13 @@ std::vector<std::pair<int64_t, int64_t>> split_ranges(int64_t L, int s, int T) {
 
 static bool is_decode(int64_t n) { return n <= 16; }
 
-// Tasks of a plan in queue order: FIFO enumerates (request, query token, KV head,
+// Query tiles of a request with n query tokens: qt consecutive tokens each (the
+// last may hold fewer). One attention task per (query tile, KV head, split);
+// its KV tiles are those its last token sees.
+static int64_t num_qtiles(int64_t n, int qt) { return (n + qt - 1) / qt; }
+static int64_t qtile_last(int64_t n, int qt, int64_t k) { return std::min<int64_t>(n, (k + 1) * qt) - 1; }
+
+// Tasks of a plan in queue order: FIFO enumerates (request, query tile, KV head,
 // split); split decode-only plans are reordered longest-first (stable); batches
 // with chunk requests (more than 16 query tokens) put those requests' tasks first.
 void build_tasks(const Problem& pb, const ModelParams& prm,
@@ -72,10 +78,11 @@ void build_tasks(const Problem& pb, const ModelParams& prm,
     any_split |= ranges[b].size() > 1;
     decode_only &= is_decode(pb.q_lens[b]);
   }
+  const int qt = pb.query_tile;
   for (int b = 0; b < B; ++b) {
     const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
-    for (int64_t qi = 0; qi < n; ++qi) {
-      const int64_t vis = pb.causal ? L - n + qi + 1 : L;
+    for (int64_t qi = 0; qi < num_qtiles(n, qt); ++qi) {
+      const int64_t vis = pb.causal ? L - n + qtile_last(n, qt, qi) + 1 : L;
       const int64_t vis_t = n_tiles(vis, T);
       for (int g = 0; g < pb.num_kv_heads; ++g) {
         for (int r = 0; r < (int)ranges[b].size(); ++r) {
@@ -83,7 +90,7 @@ void build_tasks(const Problem& pb, const ModelParams& prm,
           const int64_t lo_t = lo / T, hi_t = n_tiles(hi, T);
           const int64_t nt = std::max<int64_t>(0, std::min(hi_t, vis_t) - lo_t);
           TaskDesc t{b, g, (int32_t)qi, r, (int32_t)lo, (int32_t)hi,
-                     (int32_t)(qoff[b] + qi), 0};
+                     (int32_t)(qoff[b] + qi * qt), 0};
           fifo.push_back(t);
           c.push_back((double)nt + prm.delta_attn);
         }
@@ -156,15 +163,16 @@ struct Seg {
   size_t n;
 };
 
-// Request b's tasks with s splits in FIFO order (query token, KV head, split),
+// Request b's tasks with s splits in FIFO order (query tile, KV head, split),
 // consecutive equal costs merged.
 void request_fifo(const Problem& pb, const ModelParams& prm, int b, int s, std::vector<QEntry>& out) {
   out.clear();
   const int T = prm.tile_tokens;
+  const int qt = pb.query_tile;
   const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
   const int64_t total = n_tiles(L, T);
-  for (int64_t qi = 0; qi < n; ++qi) {
-    const int64_t vis = pb.causal ? L - n + qi + 1 : L;
+  for (int64_t qi = 0; qi < num_qtiles(n, qt); ++qi) {
+    const int64_t vis = pb.causal ? L - n + qtile_last(n, qt, qi) + 1 : L;
     const int64_t vis_t = n_tiles(vis, T);
     for (int g = 0; g < pb.num_kv_heads; ++g) {
       // the same tile split as split_ranges: the first total mod s parts are
@@ -552,9 +560,12 @@ static double score_lower_bound(const Problem& pb, const ModelParams& prm,
   double w = 0, r = 0;
   for (size_t b = 0; b < splits.size(); ++b) {
     const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
+    const int qt = pb.query_tile;
     int64_t vis_tiles = 0;
-    for (int64_t qi = 0; qi < n; ++qi) vis_tiles += n_tiles(pb.causal ? L - n + qi + 1 : L, T);
-    w += (double)pb.num_kv_heads * ((double)vis_tiles + prm.delta_attn * (double)n * (double)splits[b]);
+    for (int64_t qi = 0; qi < num_qtiles(n, qt); ++qi)
+      vis_tiles += n_tiles(pb.causal ? L - n + qtile_last(n, qt, qi) + 1 : L, T);
+    w += (double)pb.num_kv_heads *
+         ((double)vis_tiles + prm.delta_attn * (double)num_qtiles(n, qt) * (double)splits[b]);
     const int64_t rows = n * (int64_t)pb.rows_per_token;
     const double s_u = (double)(splits[b] + pb.n_ext);
     const int64_t full = rows / run, rem = rows % run;
@@ -618,7 +629,7 @@ std::vector<int> balanced_plan(const Problem& pb, const ModelParams& prm, int64_
   int64_t hi = 1;
   for (int b = 0; b < B; ++b) {
     nt[b] = n_tiles(pb.seq_lens[b], prm.tile_tokens);
-    per_split[b] = pb.q_lens[b] * (int64_t)pb.num_kv_heads;
+    per_split[b] = num_qtiles(pb.q_lens[b], pb.query_tile) * (int64_t)pb.num_kv_heads;
     hi = std::max(hi, nt[b]);
   }
   std::vector<int> c(B);

@@ -39,14 +39,29 @@ class DeviceInputs:
         self.lse_ext = None if w.lse_ext is None else torch.from_numpy(w.lse_ext).to(dev)
 
 
+def _bits(t: torch.Tensor) -> torch.Tensor:
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
 def run_path(w, plan, inputs: DeviceInputs | None = None, with_ext: bool = True,
-             out_dtype=torch.float32):
-    """Partial states and merged output of the HIP path, as float64 numpy arrays."""
+             out_dtype=torch.float32, fused: bool = True):
+    """Partial states and merged output of the HIP path (the two calls), as
+    float64 numpy arrays. With ``fused``, the one-call path (attention and
+    merge in one launch) also runs on the same inputs and must give the same
+    merged output and LSE bit for bit: both merges add a row's states in the
+    same order with the same operations."""
     d = inputs or DeviceInputs(w)
     o_part, lse_part = skv.decode_attn_partial(d.q, d.k, d.v, d.page_table, d.seq_lens, plan, w.scale)
     ext = with_ext and d.o_ext is not None
     o, lse = skv.merge_states(o_part, lse_part, plan, d.o_ext if ext else None,
                               d.lse_ext if ext else None, out_dtype=out_dtype)
+    if fused:
+        fo, fl = skv.decode_attn(d.q, d.k, d.v, d.page_table, d.seq_lens, plan, w.scale,
+                                 d.o_ext if ext else None, d.lse_ext if ext else None,
+                                 out_dtype=out_dtype)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(fo), _bits(o)), f"{w.name}: fused output differs from the two calls"
+        assert torch.equal(_bits(fl), _bits(lse)), f"{w.name}: fused LSE differs from the two calls"
     torch.cuda.synchronize()
     return (o_part.cpu().double().numpy(), lse_part.cpu().double().numpy(),
             o.float().cpu().double().numpy(), lse.cpu().double().numpy())

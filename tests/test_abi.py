@@ -293,9 +293,11 @@ def test_whole_path_scratch_size_and_checks():
     plan = skv.plan_splits([100, 50], SPEC, num_cu=4)
     inf = plan.info()
     need = skv.scratch_bytes(plan)
-    # counters block, then o_part and lse_part, each 256-aligned
+    # counters block (128 bytes of merge arguments, then three launch counters
+    # and one per request, each on a 256-byte line of its own), then o_part and
+    # lse_part, each 256-aligned
     up = lambda x: (x + 255) // 256 * 256
-    assert need == up(4 * (4 + 2)) + up(inf.state_rows * 128 * 4) + up(inf.state_rows * 4)
+    assert need == up(128 + 256 * (3 + 2)) + up(inf.state_rows * 128 * 4) + up(inf.state_rows * 4)
     assert skv._lib.skv_decode_attn_scratch_bytes(None) == 0
     d = SPEC.desc(2, max_pages=8, num_pages=16, scale=0.1)
     fake = ctypes.c_void_p(256)   # never dereferenced: validation fails first
@@ -310,3 +312,33 @@ def test_whole_path_scratch_size_and_checks():
     assert st == -1                                              # bad output dtype
     d.softmax_scale = 0.0
     assert call(fake, need) == -1
+
+
+def test_query_tile_defaults_and_limits():
+    # tokens per attention task: the bf16 matrix-core GQA kernel fills 64 rows
+    # of (token, head) at head dim 128 and 128 at head dim 64; every other
+    # kernel takes one token per task
+    cases = [(torch.bfloat16, 32, 2, 128, False, 4), (torch.bfloat16, 32, 2, 64, False, 8),
+             (torch.bfloat16, 16, 2, 128, False, 8), (torch.bfloat16, 16, 2, 64, False, 16),
+             (torch.bfloat16, 8, 2, 128, False, 1), (torch.float32, 32, 2, 128, False, 1),
+             (torch.bfloat16, 128, 1, 576, True, 1)]
+    seq, q = [300, 90], [20, 1]
+    for dt, hq, hkv, d, mla, qt in cases:
+        spec = skv.AttnSpec(hq, hkv, d, 512 if mla else d, 16, dtype=dt, mla=mla)
+        plan = skv.plan_splits(seq, spec, 64, q_lens=q)
+        assert plan.info().query_tile == qt, (dt, hq, hkv, d)
+        # one task per (request, KV head, query tile, split)
+        counts = plan.export()["split_counts"]
+        assert plan.info().num_tasks == sum(int(c) * hkv * -(-n // qt) for c, n in zip(counts, q))
+    spec = skv.AttnSpec(32, 2, 128, 128, 16, dtype=torch.bfloat16)
+    prm = skv.default_params()
+    for qt in (1, 2, 4):
+        prm.query_tile = qt
+        assert skv.plan_splits(seq, spec, 64, q_lens=q, params=prm).info().query_tile == qt
+    prm.query_tile = 5          # 5 tokens x 16 heads = 80 rows: more than the kernel's 64
+    with pytest.raises(skv.SplitKVError):
+        skv.plan_splits(seq, spec, 64, q_lens=q, params=prm)
+    prm.query_tile = 2          # the one-token kernels take only tiles of one
+    with pytest.raises(skv.SplitKVError):
+        skv.plan_splits(seq, skv.AttnSpec(8, 2, 128, 128, 16, dtype=torch.float32), 64, q_lens=q,
+                        params=prm)

@@ -128,3 +128,41 @@ def test_device_lengths_differ_from_plan(kind):
                                           torch.from_numpy(sl).to(dev))
     assert flag == 2, flag
     _check_rows(w, plan, o_part, lse_part, o, lse, {BAD_REQ: set(range(COUNTS[BAD_REQ]))})
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=lambda k: k if isinstance(k, str) else f"{k[0]}-G{k[1] // k[2]}")
+def test_one_launch_path_errors(kind):
+    # the fused engine's launch (a plan built with overlap_reduction = 1): a
+    # bad page id in one request and a length mismatch in another; their
+    # merged rows are NaN, the third request's match the oracle, both bits set
+    w = _workload(kind)
+    print(f"[err] one-launch case {w.name}", flush=True)
+    dev = torch.device("cuda:0")
+    N = w.num_pages
+    # as above: the bad id N names a poisoned page that exists in memory but
+    # lies outside the num_pages = N view the call is given
+    k_np = np.concatenate([w.k_pages, np.full_like(w.k_pages[:1], wl._poison_value(w.dtype))])
+    k = _dev_tensor(k_np, w.dtype, dev)[:N]
+    if w.mla:
+        v = k
+    else:
+        v_np = np.concatenate([w.v_pages, np.full_like(w.v_pages[:1], wl._poison_value(w.dtype))])
+        v = _dev_tensor(v_np, w.dtype, dev)[:N]
+    prm = skv.default_params()
+    prm.overlap_reduction = 1
+    plan = skv.plan_from_counts(w.seq_lens, spec_of(w), COUNTS, params=prm)
+    pt = w.page_table.copy()
+    pt[BAD_REQ, BAD_PAGE] = N
+    sl = w.seq_lens.copy()
+    sl[2] -= 1
+    q = _dev_tensor(w.q, w.dtype, dev)
+    o, lse = skv.decode_attn(q, k, v, torch.from_numpy(pt).to(dev), torch.from_numpy(sl).to(dev), plan,
+                             w.scale)
+    assert plan.read_error_flag(dev) == 3
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    H = w.num_q_heads
+    for b in (BAD_REQ, 2):
+        assert np.isnan(o[b * H:(b + 1) * H]).all() and np.isnan(lse[b * H:(b + 1) * H]).all()
+    ref_o, ref_l = A.attention_rows(w, 0, [0])
+    compare(o[:H].reshape(ref_o.shape), ref_o, lse[:H].reshape(ref_l.shape), ref_l, tol_for(w),
+            f"{w.name} merged b=0")

@@ -32,7 +32,7 @@ def reference_for(plan: skv.Plan, spec: skv.AttnSpec, seq, qlen, n_ext=0, params
                     balanced_candidates=inf.balanced_candidates)
     pb = PL.Problem(seq_lens=[int(x) for x in seq], q_lens=[int(x) for x in qlen],
                     num_kv_heads=spec.num_kv_heads, rows_per_token=spec.num_q_heads, n_ext=n_ext,
-                    causal=spec.causal)
+                    causal=spec.causal, query_tile=inf.query_tile)
     return pb, prm, PL.plan(pb, prm, ref=ref), PL.simulate(pb, prm, [1] * len(seq))
 
 
@@ -77,6 +77,16 @@ SPECS = [
 ]
 
 
+def kernel_tile(spec: skv.AttnSpec) -> int:
+    """Query tokens per task the library's kernel for spec takes by default:
+    the bf16 matrix-core GQA kernel fills 64 (head dim 128) or 128 (head dim
+    64) rows of (token, head); the others take one token."""
+    G = spec.num_q_heads // spec.num_kv_heads
+    if spec.dtype == torch.bfloat16 and not spec.mla and G in (8, 16):
+        return (64 if spec.head_dim_qk == 128 else 128) // G
+    return 1
+
+
 @pytest.mark.parametrize("seed", range(160))
 def test_random_batches_bit_exact(seed):
     rng = np.random.default_rng(1000 + seed)
@@ -101,9 +111,16 @@ def test_random_batches_bit_exact(seed):
         p.delta_red, p.gamma = 0.0, 0.0        # zero-cost reductions: ties between warps
     if seed % 8 in (1, 7):
         p.balanced_candidates = 1 if seed % 8 == 1 else 0   # against the kernel's default
+    if seed % 4 == 2:
+        # several query tokens per request on a bf16 GQA problem, whose kernel
+        # groups them in query tiles: its default tile, or a smaller one
+        spec = SPECS[(seed // 4) % 2]
+        q = np.minimum(seq, rng.integers(1, 40, size=B))
+        p.query_tile = int(rng.choice([0, 1, 2, kernel_tile(spec)]))
     plan = skv.plan_splits(seq, spec, num_cu=num_cu, q_lens=q, n_ext=n_ext, params=p)
     assert plan.info().balanced_candidates == (
         p.balanced_candidates if p.balanced_candidates >= 0 else int(spec.mla))
+    assert plan.info().query_tile == (p.query_tile or kernel_tile(spec))
     pb, prm, ev, ns = reference_for(plan, spec, seq, q, n_ext, p)
     assert_same(plan, pb, prm, ev, ns)
 

@@ -407,3 +407,65 @@ def test_planted_planner_mistakes_fail_a_pin(monkeypatch, name, attr, mutant, pi
     monkeypatch.setattr(PL, attr, mutant)
     with pytest.raises((AssertionError, ValueError, ZeroDivisionError, IndexError)):
         pin()
+
+
+# ---------------------------------------------------------------------------
+# Query tiles: one task per (request, KV head, tile of consecutive query
+# tokens, split), costed by the KV tiles its last token sees
+# ---------------------------------------------------------------------------
+
+def test_query_tiles_hand_example():
+    # L = 130 KV tokens, n = 5 causal query tokens, 64-token tiles: token i sees
+    # 126 + i keys, i.e. 2, 2, 2, 3, 3 KV tiles (128 keys are exactly two
+    # tiles). Tiles of 2 tokens: (0,1), (2,3), (4) -> their last tokens see
+    # 127, 129, 130 keys: 2, 3, 3 tiles.
+    prm = PL.Params(tile_tokens=64, slots=4, delta_attn=1.0)
+    assert PL.query_tiles(5, 2) == [(0, 1), (2, 3), (4, 4)]
+    assert PL.query_tiles(5, 8) == [(0, 4)]
+    pb = PL.Problem(seq_lens=[130], q_lens=[5], query_tile=1)
+    assert [t.n_t for t in PL.build_tasks(pb, prm, [1])] == [2, 2, 2, 3, 3]
+    pb = PL.Problem(seq_lens=[130], q_lens=[5], query_tile=2)
+    tasks = PL.build_tasks(pb, prm, [1])
+    assert [(t.qi, t.n_t, t.c) for t in tasks] == [(0, 2, 3.0), (1, 3, 4.0), (2, 3, 4.0)]
+    pb = PL.Problem(seq_lens=[130], q_lens=[5], query_tile=8)
+    assert [t.n_t for t in PL.build_tasks(pb, prm, [1])] == [3]
+    # two splits of 3 tiles ([0,128), [128,130)): the first split is whole for
+    # every tile, the second is empty for the tile whose last token sees 127;
+    # split decode-only plans are longest first (cost n_t + 1), stable in FIFO
+    # order (tile, KV head, split)
+    pb = PL.Problem(seq_lens=[130], q_lens=[5], query_tile=2, num_kv_heads=2)
+    tasks = PL.build_tasks(pb, prm, [2])
+    assert [(t.qi, t.g, t.r, t.n_t) for t in tasks] == [
+        (0, 0, 0, 2), (0, 1, 0, 2), (1, 0, 0, 2), (1, 1, 0, 2), (2, 0, 0, 2), (2, 1, 0, 2),
+        (1, 0, 1, 1), (1, 1, 1, 1), (2, 0, 1, 1), (2, 1, 1, 1), (0, 0, 1, 0), (0, 1, 1, 0)]
+    # non-causal rows all see the whole history
+    pb = PL.Problem(seq_lens=[130], q_lens=[5], query_tile=2, causal=False)
+    assert [t.n_t for t in PL.build_tasks(pb, prm, [1])] == [3, 3, 3]
+    # simulation: three tasks of 3, 4, 4 on four slots at tau = rho = 1 -> 4
+    pb = PL.Problem(seq_lens=[130], q_lens=[5], query_tile=2)
+    prm = PL.Params(tile_tokens=64, slots=4, rho=1.0, delta_attn=1.0, delta_red=0.0, gamma=0.0)
+    ev = PL.simulate(pb, prm, [1])
+    assert ev.n_tasks == 3 and ev.t_attn == 4.0
+
+
+def test_query_tiles_in_balanced_plan():
+    # tasks of one split = query tiles x KV heads: 5 tokens in tiles of 2 on 2
+    # KV heads = 6 tasks per split; tiles of the 10-tile request: t = 5 gives
+    # 2 splits (12 tasks), t = 4 gives 3 (18)
+    T = 64
+    pb = PL.Problem(seq_lens=[10 * T], q_lens=[5], num_kv_heads=2, query_tile=2)
+    prm = PL.Params(tile_tokens=T, slots=4)
+    assert PL.balanced_plan(pb, prm, 12) == [2]
+    assert PL.balanced_plan(pb, prm, 17) == [2]
+    assert PL.balanced_plan(pb, prm, 18) == [3]
+    assert PL.balanced_plan(pb, prm, 5) is None
+
+
+def _tiles_by_first_token(n, qt):           # planted: costs from the tile's first token
+    return [(a, a) for a in range(0, n, qt)]
+
+
+def test_planted_query_tile_mistake_fails_a_pin(monkeypatch):
+    monkeypatch.setattr(PL, "query_tiles", _tiles_by_first_token)
+    with pytest.raises(AssertionError):
+        test_query_tiles_hand_example()
