@@ -15,9 +15,10 @@ largest single-GPU workload's decode part, the launch the HBM target is set
 on. ``value`` is its KV bytes (each request's KV read once) over the median
 step time. ``per_config`` holds the same measurement for the other workloads
 (Llama-405B-shaped GQA share, DeepSeek-shaped MLA batch, skewed rollout tail,
-and the whole million-token shard with its 2,048-token chunked-prefill query
-and 16 external states per row), each with its roofline and its CPU oracle
-baseline. ``--workload N`` runs one workload alone.
+the whole million-token shard with its 2,048-token chunked-prefill query and
+16 external states per row, and a speculative-decoding step of 16 query
+tokens per request on a GQA group of 8), each with its roofline and its CPU
+oracle baseline. ``--workload N`` runs one workload alone.
 """
 from __future__ import annotations
 
@@ -39,7 +40,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, vendor figure
 METRIC = "decode attention KV GB/s (% of MI355X HBM peak) + tokens/s at 1 GPU"
 HEADLINE = "5d"
-PER_CONFIG = ("2", "3", "4", "5")
+PER_CONFIG = ("2", "3", "4", "5", "6")
 
 KERNEL_FILES = {
     "gqa_mfma": "split_kv_partial_amd/csrc/kernels/gqa_mfma.hip",
@@ -55,7 +56,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", type=str, default="all",
-                    help="all (headline 5d plus 2, 3, 4, 5), or one of 1-5 and 5d (the decode "
+                    help="all (headline 5d plus 2-6), or one of 1-6 and 5d (the decode "
                          "requests of workload 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true",
@@ -246,7 +247,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
     copy = [k for k in fetch if "copyBuffer" in k]
-    attn = [k for k in fetch if "mla_mfma_kernel" in k or "gqa_mfma_kernel" in k or "gqa_valu_kernel" in k]
+    attn = [k for k in fetch if any(n in k for n in ("mla_mfma_kernel", "gqa_mfma_kernel", "gqa_rows_kernel",
+                                                      "gqa_valu_kernel"))]
     assert copy and attn, (list(fetch), "need the copy probe and an attention kernel")
     kib = COPY_PROBE_BYTES / 1024.0
     cf = max(fetch[copy[0]]) / kib        # the probe is the largest copy
@@ -254,7 +256,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
     k = attn[0]
     f_kib = float(np.median(fetch[k]))
     w_kib = float(np.median(write[k]))
-    kern = "mla_mfma" if "mla" in k else ("gqa_mfma" if "gqa_mfma" in k else "gqa_valu")
+    kern = "mla_mfma" if "mla" in k else ("gqa_valu" if "gqa_valu" in k else "gqa_mfma")
     hbm = (f_kib / cf + w_kib / cw) * 1024.0
     path = os.path.join(ROOT, "profiles", "counters.json")
     db = json.load(open(path)) if os.path.exists(path) else {}
@@ -437,7 +439,7 @@ def measure(w, key: str, dev, num_cu: int, args, plan_params) -> dict:
 
 
 def load(key: str, cache: dict):
-    """Workload `key` (1-5, or 5d for the decode part of 5), generated once."""
+    """Workload `key` (1-6, or 5d for the decode part of 5), generated once."""
     import workloads as wl
     if key == "5d":
         return decode_part(load("5", cache))

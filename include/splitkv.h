@@ -122,10 +122,9 @@ typedef struct skv_plan_params {
   int32_t query_tile;         /* query tokens per attention task: 0 (default) =
                                  the kernel's choice (one token, or a tile of
                                  128 / G tokens for bf16 GQA groups of 8 and
-                                 16); other values plan that tile size, and the
-                                 compute calls accept such a plan only if the
-                                 kernel runs tasks of that size
-                                 (SKV_ERR_UNSUPPORTED)                         */
+                                 16); other values plan that tile size, and a
+                                 size the kernel cannot run is refused when
+                                 the plan is built (SKV_ERR_UNSUPPORTED)       */
   double rho;                 /* per-tile time floor                             */
   double delta_attn;          /* per attention task overhead, tile-equivalents   */
   double delta_red;           /* per reduction overhead                          */

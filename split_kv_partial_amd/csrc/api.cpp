@@ -37,12 +37,11 @@ Variant pick_variant(const skv_attn_desc& d);
 
 // Query tokens per attention task for the kernel the problem selects: the
 // bf16 matrix-core GQA kernel takes tiles of consecutive tokens whose rows of
-// (token, head) fill its four waves' column blocks (64 rows for D = 128, 128
-// for D = 64); the others take one token (the MLA kernel's 128 heads already
-// fill a tile).
+// (token, head) fill its four waves' column blocks (128 rows); the others take
+// one token (the MLA kernel's 128 heads already fill a tile).
 int query_tile_of(const skv_attn_desc& d) {
   const Variant v = pick_variant(d);
-  const int rows = d.head_dim_qk == 128 ? 64 : 128;
+  const int rows = 128;
   if (v == Variant::GqaMfma || v == Variant::GqaMfmaG8)
     return std::max(1, rows / (d.num_q_heads / d.num_kv_heads));
   return 1;

@@ -298,24 +298,23 @@ __device__ __forceinline__ void gqa_mfma_task(const MfmaArgs& a, const DevTask& 
 
 // ---------------------------------------------------------------------------
 // Tasks of several query tokens (a query tile of one request: up to
-// kTileRows<D> / G consecutive tokens). The rows (row = token * G + head) are
+// kTileRows / G consecutive tokens). The rows (row = token * G + head) are
 // columns of the products in blocks of 16: block b holds rows 16 b .. 16 b + 15.
-// Each wave owns kBPW<D> consecutive blocks (two for D = 64; one for D = 128,
-// where two would not fit the 256 registers of a wave at two waves per SIMD);
-// the waves are arranged as column groups (one per kBPW blocks) times token
-// groups (4 / column groups, which take the split's 32-token steps round-robin
-// and are merged through LDS at the end, as the one-token kernel does). A full
-// tile is four column groups of one token group: every wave streams the whole split,
-// its loads of the same keys and values as its neighbours' served by the
-// caches, so each KV byte comes from HBM once per tile instead of once per
-// token. Causal rows see their own end: lane n's column is one row, masked
-// at min(split end, the visible end of its token).
+// Each wave owns up to kBPW = 4 consecutive blocks (64 rows; one wave per SIMD,
+// whose 512 registers hold the four blocks' operands and accumulators); the
+// waves are arranged as column groups (one per kBPW blocks) times token groups
+// (4 / column groups, which take the split's 32-token steps round-robin and
+// are merged through LDS at the end, as the one-token kernel does). A full
+// tile of 128 rows is two column groups of two token groups: two waves stream
+// each step, the second one's loads served by the caches, and each KV byte
+// comes from HBM once per tile instead of once per token. Causal rows see
+// their own end: lane n's column is one row, masked at min(split end, the
+// visible end of its token).
 // ---------------------------------------------------------------------------
 
 template <int D>
-constexpr int kBPW = D == 64 ? 2 : 1;               // column blocks per wave
-template <int D>
-constexpr int kTileRows = 16 * kWaves * kBPW<D>;    // rows of a full query tile
+constexpr int kBPW = 4;         // column blocks per wave
+constexpr int kTileRows = 128;  // rows of a full query tile
 
 template <int D>
 struct RowsShared {
@@ -437,7 +436,7 @@ __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& 
   const int G = a.G;
   const int R = G * t.ntok;                  // rows of the task
   constexpr int BPW = kBPW<D>;
-  const int CB = (R + 15) >> 4;              // column blocks, at most 4 * BPW
+  const int CB = (R + 15) >> 4;              // column blocks, at most 8
   const int CG = (CB + BPW - 1) / BPW;       // column groups (BPW blocks each)
   const int TG = CG == 1 ? 4 : (CG == 2 ? 2 : 1);
   const int cg = wave % CG, tg = wave / CG;
@@ -535,14 +534,14 @@ __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& 
 
 // Multi-token tasks: one work-group per task, in the plan's queue order.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_rows_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gqa_rows_kernel(MfmaArgs a) {
   __shared__ RowsShared<D> sh;
   gqa_rows_task<D>(a, a.tasks[blockIdx.x], sh);
 }
 
 // Multi-token tasks with the merge in the same launch (fused.hpp).
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gqa_rows_fused(MfmaArgs a, FusedArgs f) {
   __shared__ RowsShared<D> sh;
   __shared__ int slot;
@@ -609,7 +608,7 @@ hipError_t launch_gqa_mfma(const AttnLaunch& L) {
   if (L.num_tasks == 0) return hipSuccess;
   const MfmaArgs a = mfma_args(L);
   // plans with several query tokens per task run on the multi-token kernel
-  if (L.max_ntok > 1 && L.max_ntok * a.G > (d.head_dim_qk == 128 ? kTileRows<128> : kTileRows<64>))
+  if (L.max_ntok > 1 && L.max_ntok * a.G > kTileRows)
     return hipErrorInvalidValue;
   if (d.head_dim_qk == 128) {
     if (L.max_ntok > 1) hipLaunchKernelGGL(gqa_rows_kernel<128>, dim3(L.num_tasks), dim3(256), 0, L.stream, a);
@@ -626,7 +625,7 @@ hipError_t launch_gqa_mfma_fused(const AttnLaunch& L, const FusedLaunch& F) {
   if (!mfma_supported(d)) return hipErrorInvalidValue;
   const MfmaArgs a = mfma_args(L);
   const FusedArgs f = fused_args(F);
-  if (L.max_ntok > 1 && L.max_ntok * a.G > (d.head_dim_qk == 128 ? kTileRows<128> : kTileRows<64>))
+  if (L.max_ntok > 1 && L.max_ntok * a.G > kTileRows)
     return hipErrorInvalidValue;
   if (d.head_dim_qk == 128) {
     if (L.max_ntok > 1) hipLaunchKernelGGL(gqa_rows_fused<128>, dim3(L.num_tasks), dim3(256), 0, L.stream, a, f);

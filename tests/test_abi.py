@@ -315,11 +315,10 @@ def test_whole_path_scratch_size_and_checks():
 
 
 def test_query_tile_defaults_and_limits():
-    # tokens per attention task: the bf16 matrix-core GQA kernel fills 64 rows
-    # of (token, head) at head dim 128 and 128 at head dim 64; every other
-    # kernel takes one token per task
-    cases = [(torch.bfloat16, 32, 2, 128, False, 4), (torch.bfloat16, 32, 2, 64, False, 8),
-             (torch.bfloat16, 16, 2, 128, False, 8), (torch.bfloat16, 16, 2, 64, False, 16),
+    # tokens per attention task: the bf16 matrix-core GQA kernel fills 128
+    # rows of (token, head); every other kernel takes one token per task
+    cases = [(torch.bfloat16, 32, 2, 128, False, 8), (torch.bfloat16, 32, 2, 64, False, 8),
+             (torch.bfloat16, 16, 2, 128, False, 16), (torch.bfloat16, 16, 2, 64, False, 16),
              (torch.bfloat16, 8, 2, 128, False, 1), (torch.float32, 32, 2, 128, False, 1),
              (torch.bfloat16, 128, 1, 576, True, 1)]
     seq, q = [300, 90], [20, 1]
@@ -332,10 +331,10 @@ def test_query_tile_defaults_and_limits():
         assert plan.info().num_tasks == sum(int(c) * hkv * -(-n // qt) for c, n in zip(counts, q))
     spec = skv.AttnSpec(32, 2, 128, 128, 16, dtype=torch.bfloat16)
     prm = skv.default_params()
-    for qt in (1, 2, 4):
+    for qt in (1, 2, 8):
         prm.query_tile = qt
         assert skv.plan_splits(seq, spec, 64, q_lens=q, params=prm).info().query_tile == qt
-    prm.query_tile = 5          # 5 tokens x 16 heads = 80 rows: more than the kernel's 64
+    prm.query_tile = 9          # 9 tokens x 16 heads = 144 rows: more than the kernel's 128
     with pytest.raises(skv.SplitKVError):
         skv.plan_splits(seq, spec, 64, q_lens=q, params=prm)
     prm.query_tile = 2          # the one-token kernels take only tiles of one

@@ -1,4 +1,4 @@
-"""The five benchmark workloads at full size, in the launch configuration the
+"""The benchmark workloads at full size, in the launch configuration the
 benchmark times (critical-wave plan on all CUs, partial attention, merge),
 checked against the float64 oracle on sampled output rows (all heads of the
 sampled query tokens) and, for one sampled request each, on its partial states.
@@ -112,3 +112,26 @@ def test_million_token_mla_shard_full():
     def pick(w):
         return {0: [0], 7: [0], 8: [0, 1023, 2047]}, 8
     run_full(5, pick)
+
+
+def test_skewed_rollout_gqa_sharp_full():
+    def pick(w):
+        longs = [int(b) for b in np.nonzero(w.seq_lens == 262144)[0][:1]]
+        return {b: [0] for b in longs + [int(np.argmin(w.seq_lens))]}, None
+    run_full(4, pick, sharp=True)
+
+
+def test_million_token_mla_decode_sharp_full():
+    run_full(5, lambda w: ({3: [0]}, 3), sharp=True, decode_only=True)
+
+
+def test_spec_decode_gqa_full():
+    # 16 query tokens per request (two query tiles of 8 on a group of 8):
+    # tokens at both tiles' edges, on the longest, shortest and two more
+    def pick(w):
+        return {b: [0, 7, 8, 15] for b in _spread(w, (9,))}, int(np.argmax(w.seq_lens))
+    run_full(6, pick)
+
+
+def test_spec_decode_gqa_sharp_full():
+    run_full(6, lambda w: ({b: [0, 5, 15] for b in _spread(w)[:2]}, None), sharp=True)

@@ -79,11 +79,11 @@ SPECS = [
 
 def kernel_tile(spec: skv.AttnSpec) -> int:
     """Query tokens per task the library's kernel for spec takes by default:
-    the bf16 matrix-core GQA kernel fills 64 (head dim 128) or 128 (head dim
-    64) rows of (token, head); the others take one token."""
+    the bf16 matrix-core GQA kernel fills 128 rows of (token, head); the
+    others take one token."""
     G = spec.num_q_heads // spec.num_kv_heads
     if spec.dtype == torch.bfloat16 and not spec.mla and G in (8, 16):
-        return (64 if spec.head_dim_qk == 128 else 128) // G
+        return 128 // G
     return 1
 
 
@@ -125,10 +125,10 @@ def test_random_batches_bit_exact(seed):
     assert_same(plan, pb, prm, ev, ns)
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 5])
+@pytest.mark.parametrize("cid", [1, 2, 3, 5, 6])
 def test_benchmark_workloads_bit_exact(cid):
     L, n = wl.config_lengths(cid)
-    spec = {1: SPECS[2], 2: SPECS[0], 3: SPECS[3], 5: SPECS[3]}[cid]
+    spec = {1: SPECS[2], 2: SPECS[0], 3: SPECS[3], 5: SPECS[3], 6: SPECS[1]}[cid]
     n_ext = 16 if cid == 5 else 0
     # the pure-Python reference is slow on the larger batches: they are checked
     # with a smaller split cap (same model, search and ordering code paths)

@@ -241,7 +241,11 @@ def build(name: str, *, dtype: str, mla: bool, seq_lens, q_lens=None, num_q_head
 
 
 # --------------------------------------------------------------------------------------
-# The five benchmark workloads. Lengths are drawn from the "lengths" stream.
+# The benchmark workloads. Lengths are drawn from the "lengths" stream. Workloads
+# 1-5 are the five synthetic configurations; workload 6 adds a speculative-decoding
+# step (LiquidCP section 7.1: 16 query tokens per request and iteration, one
+# target token and 15 drafts) on a GQA group of 8, where the 16 tokens' rows
+# make the products dense enough for the matrix cores.
 # --------------------------------------------------------------------------------------
 
 MLA_DQK, MLA_DV, MLA_HEADS = 576, 512, 128
@@ -275,11 +279,14 @@ def config_lengths(cid: int):
         L = np.array([1048576] * 8 + [65536 + 2048])
         n = np.array([1] * 8 + [2048])
         return L, n
+    if cid == 6:
+        L = _lengths_rng(6).integers(4096, 32768, size=32, endpoint=True)
+        return L, np.full(32, 16, np.int64)
     raise ValueError(cid)
 
 
 def make(cid: int, sharp: bool = False, decode_only: bool = False) -> Workload:
-    """Benchmark workload ``cid`` (1..5). ``sharp`` scales q so that scores have a
+    """Benchmark workload ``cid`` (1..6). ``sharp`` scales q so that scores have a
     standard deviation of about 3 (a near-uniform softmax cannot reveal a wrong
     QK^T). ``decode_only`` (workload 5) drops the chunked-prefill request and the
     external states, leaving the eight million-token decode requests."""
@@ -314,6 +321,12 @@ def make(cid: int, sharp: bool = False, decode_only: bool = False) -> Workload:
                      seed=seed, value_scale=0.1, q_scale=SHARP_MLA if sharp else 1.0,
                      n_ext=0 if decode_only else 16,
                      ext_lse_center=math.log(1048576.0))
+    if cid == 6:
+        # causal rows: draft i sees the history and the tokens before it
+        return build("spec-decode-gqa-g8", dtype="bf16", mla=False, seq_lens=L, q_lens=n,
+                     num_q_heads=64, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+                     page_size=16, scale=1.0 / math.sqrt(128.0), seed=seed,
+                     q_scale=SHARP_GQA if sharp else 1.0)
     raise ValueError(cid)
 
 
