@@ -19,6 +19,12 @@ Definitions followed
   (the chunk's own KV is the last n positions). Decode (n = 1) sees all L.
 
 Every input is upcast exactly from its stored dtype to float64 before use.
+
+FP8 KV cache (SPLASH appendix C.1 serves its MLA backend from an FP8 E4M3 KV
+cache): keys and values are stored as OCP 8-bit floating-point E4M3 codes with
+one float32 scale per (page, KV head) for keys and one for values; the value
+a code stands for is decoded from the format's definition (``e4m3_value``) and
+multiplied by its block's scale, exactly, in float64.
 """
 from __future__ import annotations
 
@@ -34,10 +40,36 @@ NEG_INF = -math.inf
 # ---------------------------------------------------------------------------------
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact upcast: bf16 bit patterns (uint16) or float32 values to float64."""
-    if dtype == "bf16":
+    """Exact upcast: bf16 bit patterns (uint16) or float32 values to float64.
+    An fp8-KV workload's queries are bf16."""
+    if dtype in ("bf16", "fp8"):
         return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
     return np.asarray(a, dtype=np.float32).astype(np.float64)
+
+
+def e4m3_value(code: int) -> float:
+    """The number an OCP E4M3 code stands for (OCP 8-bit floating point
+    specification, E4M3 format): bit 7 is the sign, bits 6-3 the exponent with
+    bias 7, bits 2-0 the mantissa. Exponent field 0 encodes subnormals
+    (mantissa / 8) * 2^-6; exponent 1..15 encodes (1 + mantissa / 8) * 2^(e - 7),
+    except exponent 15 with mantissa 7, which is NaN. There are no infinities:
+    the largest finite magnitude is 1.75 * 2^8 = 448."""
+    sign = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return math.nan
+    if e == 0:
+        return sign * math.ldexp(m / 8.0, -6)
+    return sign * math.ldexp(1.0 + m / 8.0, e - 7)
+
+
+_E4M3 = np.array([e4m3_value(c) for c in range(256)], np.float64)
+
+
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """Decode an array of E4M3 codes (uint8) to float64 values."""
+    return _E4M3[np.asarray(codes, np.uint8)]
 
 
 def gather_kv(w, b: int, upto: int | None = None):
@@ -60,6 +92,11 @@ def gather_kv(w, b: int, upto: int | None = None):
     k = np.transpose(k, (0, 3, 1, 2, 4)).reshape(npg * P, w.num_kv_heads, w.head_dim_qk)
     v = w.v_pages[pids]                                     # [npg][H][D_v][P]
     v = np.transpose(v, (0, 3, 1, 2)).reshape(npg * P, w.num_kv_heads, w.head_dim_v)
+    if w.dtype == "fp8":
+        # every token of a page takes its page's scale for its KV head
+        ks = np.repeat(w.k_scale[pids].astype(np.float64), P, axis=0)   # [npg * P][H]
+        vs = np.repeat(w.v_scale[pids].astype(np.float64), P, axis=0)
+        return (e4m3_to_f64(k[:L]) * ks[:L, :, None], e4m3_to_f64(v[:L]) * vs[:L, :, None])
     return to_f64(k[:L], w.dtype), to_f64(v[:L], w.dtype)
 
 

@@ -24,6 +24,16 @@ coalesced access in the matrix-core operand order):
 
 bf16 arrays are carried as ``numpy.uint16`` bit patterns; fp32 as ``float32``.
 
+FP8 KV (``dtype="fp8"``): queries are bf16; keys and values are OCP E4M3 codes
+(``numpy.uint8``) in the GQA layouts above with X = 16, and every (page, KV
+head) block has a float32 scale for its keys and one for its values
+(``k_scale`` / ``v_scale`` ``[num_pages][H_kv]``): the stored value is
+code_value * scale. They are drawn as the float32 normals described below,
+divided by their block's max |x| / 448 (so the block's largest value maps to
+E4M3's largest finite value) and cast to E4M3 by PyTorch's float8_e4m3fn
+conversion (round to nearest even). Unused slots hold the NaN code 0x7F and the
+spare pages' scales are NaN.
+
 Random recipe (fixed, so that every consumer sees the same bits): one
 ``SeedSequence(20260922 + config_id)`` (the base is the residency-sampler seed
 printed in SPLASH appendix B.1) spawns independent children for lengths,
@@ -97,7 +107,7 @@ def fill_normal(out: np.ndarray, seed: np.random.SeedSequence, scale: float = 1.
 class Workload:
     """One batch of decode-attention inputs in the library's storage formats."""
     name: str
-    dtype: str                      # "f32" or "bf16"
+    dtype: str                      # "f32", "bf16" or "fp8" (bf16 queries, E4M3 KV)
     mla: bool
     causal: bool
     num_q_heads: int
@@ -119,6 +129,8 @@ class Workload:
     o_ext: np.ndarray | None = None    # float32 [n_ext][total_rows][D_v]
     lse_ext: np.ndarray | None = None  # float32 [n_ext][total_rows]
     chunk_tokens: int | None = None    # explicit fixed-chunk split plan, if the config asks for one
+    k_scale: np.ndarray | None = None  # fp8: float32 [N][H_kv], key scale per page and KV head
+    v_scale: np.ndarray | None = None  # fp8: float32 [N][H_kv], value scale per page and KV head
     meta: dict = field(default_factory=dict)
 
     @property
@@ -143,17 +155,44 @@ class Workload:
 
     @property
     def x(self) -> int:
-        return 16 // (2 if self.dtype == "bf16" else 4)
+        return 16 // KV_BYTES[self.dtype]
 
-    def kv_bytes_per_token(self) -> int:
-        b = 2 if self.dtype == "bf16" else 4
+    def kv_bytes_per_token(self) -> float:
+        """KV bytes per token (fp8: plus its share of the two per-page scales)."""
+        b = KV_BYTES[self.dtype]
         if self.mla:
             return self.head_dim_qk * b
-        return self.num_kv_heads * (self.head_dim_qk + self.head_dim_v) * b
+        per = self.num_kv_heads * (self.head_dim_qk + self.head_dim_v) * b
+        if self.dtype == "fp8":
+            per += self.num_kv_heads * 8 / self.page_size
+        return per
+
+
+KV_BYTES = {"f32": 4, "bf16": 2, "fp8": 1}
+FP8_NAN = np.uint8(0x7F)
+FP8_MAX = 448.0
 
 
 def _poison_value(dtype: str):
-    return BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    return {"bf16": BF16_NAN, "fp8": FP8_NAN}.get(dtype, np.float32(np.nan))
+
+
+def _fp8_blocks(x: np.ndarray, out: np.ndarray, scale: np.ndarray, pages_per_pass: int = 4096) -> None:
+    """E4M3 codes of x [N][H][...] (float32) into out (uint8, same shape), with
+    one scale per [page][head] block: scale = max |x| / 448 (1 for an all-zero
+    block), code = E4M3(x / scale) by PyTorch's cast (nearest, ties to even)."""
+    import torch
+    N = x.shape[0]
+    for lo in range(0, N, pages_per_pass):
+        hi = min(N, lo + pages_per_pass)
+        blk = x[lo:hi]
+        amax = np.abs(blk).reshape(hi - lo, blk.shape[1], -1).max(axis=2)
+        s = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
+        scale[lo:hi] = s
+        shape = (hi - lo, blk.shape[1]) + (1,) * (blk.ndim - 2)
+        y = np.minimum(np.abs(blk / s.reshape(shape)), np.float32(FP8_MAX)) * np.sign(blk)
+        out[lo:hi] = torch.from_numpy(np.ascontiguousarray(y, np.float32)).to(
+            torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
 def build(name: str, *, dtype: str, mla: bool, seq_lens, q_lens=None, num_q_heads: int,
@@ -193,9 +232,26 @@ def build(name: str, *, dtype: str, mla: bool, seq_lens, q_lens=None, num_q_head
     el = np.uint16 if dtype == "bf16" else np.float32
     H_q, H_kv = num_q_heads, num_kv_heads
     total_q = int(q_lens.sum())
-    q = np.empty((total_q, H_q, head_dim_qk), el)
+    q = np.empty((total_q, H_q, head_dim_qk), np.uint16 if dtype == "fp8" else el)
     fill_normal(q, kids["q"], scale=value_scale * q_scale)
-    if mla:
+    k_scale = v_scale = None
+    if dtype == "fp8":
+        assert not mla and head_dim_qk % 16 == 0
+        X = 16
+        k32 = np.empty((N, H_kv, head_dim_qk // X, P, X), np.float32)
+        v32 = np.empty((N, H_kv, head_dim_v, P), np.float32)
+        fill_normal(k32, kids["k"], scale=value_scale)
+        fill_normal(v32, kids["v"], scale=value_scale)
+        k_pages = np.empty(k32.shape, np.uint8)
+        v_pages = np.empty(v32.shape, np.uint8)
+        k_scale = np.empty((N, H_kv), np.float32)
+        v_scale = np.empty((N, H_kv), np.float32)
+        _fp8_blocks(k32, k_pages, k_scale)
+        _fp8_blocks(v32, v_pages, v_scale)
+        del k32, v32
+        k_scale[spare] = np.nan
+        v_scale[spare] = np.nan
+    elif mla:
         assert H_kv == 1
         k_pages = np.empty((N, P, head_dim_qk), el)
         fill_normal(k_pages, kids["k"], scale=value_scale)
@@ -237,7 +293,8 @@ def build(name: str, *, dtype: str, mla: bool, seq_lens, q_lens=None, num_q_head
                     q_lens=q_lens.astype(np.int32), page_table=table, num_pages=N, q=q,
                     k_pages=k_pages, v_pages=v_pages, scale=float(scale),
                     logical_to_physical=l2p, page_offsets=offsets.astype(np.int32),
-                    n_ext=n_ext, o_ext=o_ext, lse_ext=lse_ext, chunk_tokens=chunk_tokens)
+                    n_ext=n_ext, o_ext=o_ext, lse_ext=lse_ext, chunk_tokens=chunk_tokens,
+                    k_scale=k_scale, v_scale=v_scale)
 
 
 # --------------------------------------------------------------------------------------
@@ -338,12 +395,15 @@ def identity_layout(w: Workload) -> Workload:
     src = np.concatenate([w.logical_to_physical, spare]).astype(np.int64)
     k = w.k_pages[src]
     v = None if w.v_pages is None else w.v_pages[src]
+    ks = None if w.k_scale is None else w.k_scale[src]
+    vs = None if w.v_scale is None else w.v_scale[src]
     pages_b = (w.seq_lens.astype(np.int64) + w.page_size - 1) // w.page_size
     table = np.full_like(w.page_table, n_used if spare.size else 0)
     for b in range(w.batch):
         table[b, : pages_b[b]] = np.arange(w.page_offsets[b], w.page_offsets[b + 1])
     out = Workload(**{**w.__dict__})
     out.k_pages, out.v_pages, out.page_table = k, v, table
+    out.k_scale, out.v_scale = ks, vs
     out.logical_to_physical = np.arange(n_used, dtype=np.int32)
     out.name = w.name + "-identity"
     return out
@@ -357,6 +417,7 @@ def physical_slot(w: Workload, b: int, j: int):
 def set_logical_values(w: Workload, b: int, values: np.ndarray) -> None:
     """Store logical values [L_b][H_kv][D_v] of request b into its pages (GQA:
     v_pages; MLA: the first D_v columns of the latent rows). Layout only."""
+    assert w.dtype != "fp8", "values of an fp8 cache are codes with scales"
     P = w.page_size
     L = int(w.seq_lens[b])
     for p in range((L + P - 1) // P):
@@ -372,7 +433,7 @@ def set_logical_values(w: Workload, b: int, values: np.ndarray) -> None:
 def zero_keys(w: Workload) -> None:
     """Set every key to zero (GQA: all of k_pages; MLA: all 576 columns), keeping
     the poison of unused slots. Layout only."""
-    zero = np.uint16(0) if w.dtype == "bf16" else np.float32(0)
+    zero = {"bf16": np.uint16(0), "fp8": np.uint8(0)}.get(w.dtype, np.float32(0))
     P = w.page_size
     for b in range(w.batch):
         L = int(w.seq_lens[b])
