@@ -16,9 +16,10 @@ on. ``value`` is its KV bytes (each request's KV read once) over the median
 step time. ``per_config`` holds the same measurement for the other workloads
 (Llama-405B-shaped GQA share, DeepSeek-shaped MLA batch, skewed rollout tail,
 the whole million-token shard with its 2,048-token chunked-prefill query and
-16 external states per row, and a speculative-decoding step of 16 query
-tokens per request on a GQA group of 8), each with its roofline and its CPU
-oracle baseline. ``--workload N`` runs one workload alone.
+16 external states per row, a speculative-decoding step of 16 query tokens
+per request on a GQA group of 8, and the Llama-405B-shaped share over an FP8
+E4M3 KV cache), each with its roofline and its CPU oracle baseline.
+``--workload N`` runs one workload alone.
 """
 from __future__ import annotations
 
@@ -40,7 +41,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, vendor figure
 METRIC = "decode attention KV GB/s (% of MI355X HBM peak) + tokens/s at 1 GPU"
 HEADLINE = "5d"
-PER_CONFIG = ("2", "3", "4", "5", "6")
+PER_CONFIG = ("2", "3", "4", "5", "6", "7")
 
 KERNEL_FILES = {
     "gqa_mfma": "split_kv_partial_amd/csrc/kernels/gqa_mfma.hip",
@@ -56,7 +57,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", type=str, default="all",
-                    help="all (headline 5d plus 2-6), or one of 1-6 and 5d (the decode "
+                    help="all (headline 5d plus 2-7), or one of 1-7 and 5d (the decode "
                          "requests of workload 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true",
@@ -129,7 +130,7 @@ def plan_overrides(items):
 def kernel_of(w) -> str:
     if w.mla:
         return "mla_mfma"
-    return "gqa_mfma" if (w.dtype == "bf16" and w.group >= 8) else "gqa_valu"
+    return "gqa_mfma" if (w.dtype in ("bf16", "fp8") and w.group >= 8) else "gqa_valu"
 
 
 def source_hash(kernel: str) -> str:
@@ -170,8 +171,9 @@ def visible_kv_tokens(w) -> int:
 def kv_bytes(w) -> int:
     """Algorithmic KV bytes of an attention launch: every request's KV read
     once (a chunk's query tokens share their request's history), at the
-    storage's bytes per token (MLA rows once: the value is part of the row)."""
-    return int(w.seq_lens.astype(np.int64).sum()) * w.kv_bytes_per_token()
+    storage's bytes per token (MLA rows once: the value is part of the row;
+    FP8: the codes plus the per-page scales)."""
+    return int(round(int(w.seq_lens.astype(np.int64).sum()) * w.kv_bytes_per_token()))
 
 
 def attention_flops(w) -> float:
@@ -182,7 +184,7 @@ def attention_flops(w) -> float:
 def step_bytes(w, state_rows: int) -> int:
     """HBM bytes a whole step must move at the least: the KV once, queries, the
     partial states written and read back, external states, merged outputs."""
-    el = 2 if w.dtype == "bf16" else 4
+    el = 4 if w.dtype == "f32" else 2   # queries are bf16 over an FP8 cache too
     q = w.total_q * w.num_q_heads * w.head_dim_qk * el
     states = state_rows * (w.head_dim_v + 1) * 4
     ext = w.n_ext * w.total_rows * (w.head_dim_v + 1) * 4
@@ -293,7 +295,8 @@ class Runner:
         bf16 = w.dtype == "bf16"
 
         def to_dev(a):
-            if bf16:
+            # bf16 bits (uint16) become bf16; float32 and FP8 codes (uint8) stay as they are
+            if a.dtype == np.uint16:
                 return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
             return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
@@ -304,9 +307,11 @@ class Runner:
         self.sl = torch.from_numpy(w.seq_lens).to(dev)
         self.o_ext = None if w.o_ext is None else torch.from_numpy(w.o_ext).to(dev)
         self.lse_ext = None if w.lse_ext is None else torch.from_numpy(w.lse_ext).to(dev)
+        self.k_scale = None if w.k_scale is None else torch.from_numpy(w.k_scale).to(dev)
+        self.v_scale = None if w.v_scale is None else torch.from_numpy(w.v_scale).to(dev)
+        dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": skv.FP8}[w.dtype]
         self.spec = skv.AttnSpec(w.num_q_heads, w.num_kv_heads, w.head_dim_qk, w.head_dim_v, w.page_size,
-                                 dtype=torch.bfloat16 if bf16 else torch.float32, mla=w.mla,
-                                 causal=w.causal)
+                                 dtype=dt, mla=w.mla, causal=w.causal)
         # host planner, once per batch (timed on its own, after one untimed
         # call that starts the planner's worker threads, a once-per-process cost)
         self.plan_times = []
@@ -330,8 +335,12 @@ class Runner:
 
     def attention(self):
         import split_kv_partial_amd as skv
-        skv.decode_attn_partial(self.q, self.k, self.v, self.pt, self.sl, self.plan, self.w.scale,
-                                o_part=self.o_part, lse_part=self.lse_part)
+        if self.k_scale is not None:
+            skv.decode_attn_partial_fp8(self.q, self.k, self.v, self.k_scale, self.v_scale, self.pt, self.sl,
+                                        self.plan, self.w.scale, o_part=self.o_part, lse_part=self.lse_part)
+        else:
+            skv.decode_attn_partial(self.q, self.k, self.v, self.pt, self.sl, self.plan, self.w.scale,
+                                    o_part=self.o_part, lse_part=self.lse_part)
 
     def merge(self):
         import split_kv_partial_amd as skv
@@ -366,7 +375,8 @@ class Runner:
 
     def free(self):
         import torch
-        for name in ("q", "k", "v", "pt", "sl", "o_ext", "lse_ext", "o_part", "lse_part", "o_out", "lse_out"):
+        for name in ("q", "k", "v", "pt", "sl", "o_ext", "lse_ext", "o_part", "lse_part", "o_out", "lse_out",
+                     "k_scale", "v_scale"):
             setattr(self, name, None)
         self.plan = None
         torch.cuda.synchronize()
@@ -439,7 +449,7 @@ def measure(w, key: str, dev, num_cu: int, args, plan_params) -> dict:
 
 
 def load(key: str, cache: dict):
-    """Workload `key` (1-6, or 5d for the decode part of 5), generated once."""
+    """Workload `key` (1-7, or 5d for the decode part of 5), generated once."""
     import workloads as wl
     if key == "5d":
         return decode_part(load("5", cache))

@@ -23,7 +23,8 @@
  *
  * Storage formats (all device, row-major, no padding)
  * ---------------------------------------------------
- * T = float (SKV_F32) or bf16 (SKV_BF16). X = 16 / sizeof(T) (4 or 8).
+ * T = float (SKV_F32) or bf16 (SKV_BF16); for SKV_FP8_E4M3, q is bf16 and the
+ * KV pages hold T = one-byte OCP E4M3 codes. X = 16 / sizeof(T) (4, 8 or 16).
  * q          [total_q][H_q][D]            T; requests concatenated in batch order,
  *                                         request b owning q_lens[b] tokens.
  * GQA keys   [num_pages][H_kv][D/X][P][X] T; 16-byte chunks of X dimensions,
@@ -43,6 +44,11 @@
  *                                         page are never consumed.
  * seq_lens   [batch]                      int32; L_b = KV tokens of request b,
  *                                         including its own q_lens[b] new tokens.
+ * FP8 scales k_scales, v_scales [num_pages][H_kv] float32 (SKV_FP8_E4M3 only):
+ *                                         a stored key is its code's E4M3 value
+ *                                         times k_scales[page][kv_head], a value
+ *                                         likewise with v_scales (SPLASH,
+ *                                         appendix C.1: an FP8 E4M3 KV cache).
  * Query token i of request b with n_b tokens sees KV positions
  * [0, L_b - n_b + i] when causal (bottom-right aligned), [0, L_b) otherwise.
  * KV head of query head h is h / (H_q / H_kv).
@@ -73,7 +79,9 @@ typedef int32_t skv_status;
 #define SKV_ERR_NO_MEMORY     -4   /* host allocation failed, or workspace too small */
 #define SKV_ERR_PLAN_MISMATCH -5   /* plan built for a different problem description */
 
-typedef enum { SKV_F32 = 0, SKV_BF16 = 1 } skv_dtype;
+/* SKV_FP8_E4M3: bf16 queries; GQA keys and values stored as OCP E4M3 bytes
+ * with float32 scales per (page, KV head) (skv_decode_attn_partial_fp8). */
+typedef enum { SKV_F32 = 0, SKV_BF16 = 1, SKV_FP8_E4M3 = 2 } skv_dtype;
 
 /* Problem description, passed by value in host memory. */
 typedef struct skv_attn_desc {
@@ -90,7 +98,9 @@ typedef struct skv_attn_desc {
                                  writes a NaN state (see skv_read_error_flag) */
   int32_t mla;                /* 1: MLA rows (v_pages == k_pages)                 */
   int32_t causal;             /* 1: bottom-right causal rows when q_len > 1      */
-  int32_t dtype;              /* skv_dtype of q and the KV pages                 */
+  int32_t dtype;              /* skv_dtype of q and the KV pages; SKV_FP8_E4M3
+                                 needs a GQA group of 8 or 16 and runs one
+                                 query token per task                          */
   float softmax_scale;        /* scores are softmax_scale * <q, k>; must be
                                  positive and finite (SKV_ERR_INVALID_ARG)     */
 } skv_attn_desc;
@@ -234,6 +244,20 @@ skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q,
  * nearest even); lse_out: device float32 [total_rows] or NULL.
  * Rows whose states are all empty produce o = 0, lse = -inf; a row with a
  * NaN LSE among its states (a task that met a device error) produces NaN. */
+/* FP8 KV cache (SPLASH, appendix C.1, serves an FP8 E4M3 KV cache): as
+ * skv_decode_attn_partial for desc->dtype = SKV_FP8_E4M3, with the key and
+ * value scales [num_pages][H_kv] float32 (device). Each code is decoded
+ * exactly (E4M3 values are bf16 values) and the products run on bf16 matrix
+ * cores with fp32 accumulation; the key scale multiplies the block's scores,
+ * the value scale its softmax weights. The other compute entry points reject
+ * FP8 descriptions (SKV_ERR_INVALID_ARG); skv_merge_states merges the states
+ * as any others. A NaN code yields NaN in the states that read it. */
+skv_status skv_decode_attn_partial_fp8(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                                       const void* v_pages, const float* k_scales, const float* v_scales,
+                                       const int32_t* page_table, const int32_t* seq_lens,
+                                       const skv_plan* plan, const void* workspace, float* o_part,
+                                       float* lse_part, void* stream);
+
 skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan,
                             const void* workspace, const float* o_part,
                             const float* lse_part, int32_t n_ext, const float* o_ext,

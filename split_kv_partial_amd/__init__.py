@@ -27,7 +27,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 # build of the CPU tests); by default the in-tree build is loaded.
 LIB_PATH = os.environ.get("SKV_LIBRARY") or os.path.join(_HERE, "libsplitkv.so")
 
-SKV_F32, SKV_BF16 = 0, 1
+SKV_F32, SKV_BF16, SKV_FP8_E4M3 = 0, 1, 2
+# AttnSpec dtype of an FP8 KV cache: bf16 queries, E4M3 keys and values
+FP8 = torch.float8_e4m3fn
 STATUS = {0: "SKV_OK", -1: "SKV_ERR_INVALID_ARG", -2: "SKV_ERR_UNSUPPORTED", -3: "SKV_ERR_HIP",
           -4: "SKV_ERR_NO_MEMORY", -5: "SKV_ERR_PLAN_MISMATCH"}
 
@@ -37,7 +39,7 @@ EXPORTED = (
     "skv_plan_get_info", "skv_plan_export", "skv_plan_workspace_bytes", "skv_plan_upload",
     "skv_plan_destroy", "skv_decode_attn_partial", "skv_merge_states", "skv_read_error_flag",
     "skv_hbm_read_probe", "skv_last_error", "skv_decode_attn_scratch_bytes", "skv_decode_attn",
-    "skv_decode_attn_noalloc",
+    "skv_decode_attn_noalloc", "skv_decode_attn_partial_fp8",
 )
 
 
@@ -94,6 +96,7 @@ def _load():
         "skv_plan_upload": (I32, [P, P, SZ, P]),
         "skv_plan_destroy": (None, [P]),
         "skv_decode_attn_partial": (I32, [pdesc, P, P, P, P, P, P, P, P, P, P]),
+        "skv_decode_attn_partial_fp8": (I32, [pdesc, P, P, P, P, P, P, P, P, P, P, P, P]),
         "skv_merge_states": (I32, [pdesc, P, P, P, P, I32, P, P, P, I32, P, P]),
         "skv_decode_attn_scratch_bytes": (SZ, [P]),
         "skv_decode_attn": (I32, [pdesc, P, P, P, P, P, P, P, P, SZ, I32, P, P, P, I32, P, P]),
@@ -151,9 +154,18 @@ class AttnSpec:
     causal: bool = True
 
     def desc(self, batch: int, max_pages: int = 1, num_pages: int = 1, scale: float = 1.0) -> AttnDesc:
+        code = {torch.bfloat16: SKV_BF16, torch.float32: SKV_F32, FP8: SKV_FP8_E4M3}[self.dtype]
         return AttnDesc(batch, self.num_q_heads, self.num_kv_heads, self.head_dim_qk, self.head_dim_v,
-                        self.page_size, max_pages, num_pages, int(self.mla), int(self.causal),
-                        SKV_BF16 if self.dtype == torch.bfloat16 else SKV_F32, float(scale))
+                        self.page_size, max_pages, num_pages, int(self.mla), int(self.causal), code,
+                        float(scale))
+
+    @property
+    def q_dtype(self) -> torch.dtype:
+        return torch.bfloat16 if self.dtype == FP8 else self.dtype
+
+    @property
+    def kv_dtypes(self) -> tuple:
+        return (torch.uint8, FP8) if self.dtype == FP8 else (self.dtype,)
 
 
 def default_params() -> PlanParams:
@@ -299,9 +311,9 @@ def _check_attention_inputs(q, k_pages, v_pages, page_table, seq_lens, plan: Pla
     sp = plan.spec
     dev = q.device
     B = len(plan.seq_lens)
-    _check_tensor(q, "q", dev, (sp.dtype,),
+    _check_tensor(q, "q", dev, (sp.q_dtype,),
                   shape=(int(plan.q_lens.sum()), sp.num_q_heads, sp.head_dim_qk))
-    _check_tensor(k_pages, "k_pages", dev, (sp.dtype,))
+    _check_tensor(k_pages, "k_pages", dev, sp.kv_dtypes)
     if k_pages.dim() < 1 or k_pages.shape[0] < 1:
         raise ValueError("k_pages must hold at least one page")
     n_pages = int(k_pages.shape[0])
@@ -315,7 +327,7 @@ def _check_attention_inputs(q, k_pages, v_pages, page_table, seq_lens, plan: Pla
         per_page_v = sp.num_kv_heads * sp.head_dim_v * sp.page_size
         if k_pages.numel() != n_pages * per_page_k:
             raise ValueError(f"k_pages must hold {per_page_k} elements per page")
-        _check_tensor(v_pages, "v_pages", dev, (sp.dtype,), numel=n_pages * per_page_v)
+        _check_tensor(v_pages, "v_pages", dev, sp.kv_dtypes, numel=n_pages * per_page_v)
     _check_tensor(page_table, "page_table", dev, (torch.int32,))
     if page_table.dim() != 2 or page_table.shape[0] != B or page_table.shape[1] < plan.max_pages:
         raise ValueError(f"page_table must be [{B}][>= {plan.max_pages}] int32, "
@@ -356,6 +368,8 @@ def decode_attn_partial(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, s
     inf = plan.info()
     sp = plan.spec
     dev = q.device
+    if sp.dtype == FP8:
+        raise ValueError("an FP8 KV cache needs its scales: use decode_attn_partial_fp8")
     if o_part is None:
         o_part = torch.empty(inf.state_rows, sp.head_dim_v, dtype=torch.float32, device=dev)
     if lse_part is None:
@@ -370,6 +384,39 @@ def decode_attn_partial(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, s
                                         plan.handle, ws.data_ptr(), o_part.data_ptr(),
                                         lse_part.data_ptr(), _stream_ptr()),
            "skv_decode_attn_partial")
+    return o_part, lse_part
+
+
+
+def decode_attn_partial_fp8(q, k_pages, v_pages, k_scales, v_scales, page_table, seq_lens, plan: Plan,
+                            scale: float, o_part=None, lse_part=None):
+    """decode_attn_partial over an FP8 (OCP E4M3) KV cache: k_pages / v_pages
+    hold codes (uint8 or float8_e4m3fn) in the GQA layouts with X = 16, and
+    k_scales / v_scales [num_pages][H_kv] float32 the per-page, per-KV-head
+    factors of the decoded keys and values. The plan's spec has dtype FP8."""
+    inf = plan.info()
+    sp = plan.spec
+    dev = q.device
+    if sp.dtype != FP8:
+        raise ValueError("decode_attn_partial_fp8 needs a plan built for dtype FP8")
+    if o_part is None:
+        o_part = torch.empty(inf.state_rows, sp.head_dim_v, dtype=torch.float32, device=dev)
+    if lse_part is None:
+        lse_part = torch.empty(inf.state_rows, dtype=torch.float32, device=dev)
+    _check_attention_inputs(q, k_pages, v_pages, page_table, seq_lens, plan)
+    n_pages = int(k_pages.shape[0])
+    _check_tensor(k_scales, "k_scales", dev, (torch.float32,), shape=(n_pages, sp.num_kv_heads))
+    _check_tensor(v_scales, "v_scales", dev, (torch.float32,), shape=(n_pages, sp.num_kv_heads))
+    _check_tensor(o_part, "o_part", dev, (torch.float32,), numel=inf.state_rows * sp.head_dim_v)
+    _check_tensor(lse_part, "lse_part", dev, (torch.float32,), numel=inf.state_rows)
+    desc = _desc_for(plan, page_table, k_pages, scale)
+    ws = plan.workspace(dev)
+    _check(_lib.skv_decode_attn_partial_fp8(ctypes.byref(desc), q.data_ptr(), k_pages.data_ptr(),
+                                            v_pages.data_ptr(), k_scales.data_ptr(), v_scales.data_ptr(),
+                                            page_table.data_ptr(), seq_lens.data_ptr(), plan.handle,
+                                            ws.data_ptr(), o_part.data_ptr(), lse_part.data_ptr(),
+                                            _stream_ptr()),
+           "skv_decode_attn_partial_fp8")
     return o_part, lse_part
 
 

@@ -42,6 +42,7 @@ Variant pick_variant(const skv_attn_desc& d);
 int query_tile_of(const skv_attn_desc& d) {
   const Variant v = pick_variant(d);
   const int rows = 128;
+  if (d.dtype == SKV_FP8_E4M3) return 1;   // FP8 KV runs on the one-token kernel
   if (v == Variant::GqaMfma || v == Variant::GqaMfmaG8)
     return std::max(1, rows / (d.num_q_heads / d.num_kv_heads));
   return 1;
@@ -55,8 +56,9 @@ bool query_tile_runs(const skv_attn_desc& d, int qt) {
 Variant pick_variant(const skv_attn_desc& d) {
   if (d.mla) return Variant::MlaMfma;
   const int G = d.num_q_heads / d.num_kv_heads;
-  if (d.dtype == SKV_BF16 && G >= 16) return Variant::GqaMfma;
-  if (d.dtype == SKV_BF16 && G == 8) return Variant::GqaMfmaG8;
+  const bool bf16_q = d.dtype == SKV_BF16 || d.dtype == SKV_FP8_E4M3;
+  if (bf16_q && G >= 16) return Variant::GqaMfma;
+  if (bf16_q && G == 8) return Variant::GqaMfmaG8;
   return Variant::GqaValu;
 }
 
@@ -71,8 +73,8 @@ skv_status check_desc(const skv_attn_desc* d) {
     return fail(SKV_ERR_UNSUPPORTED, "page_size must be 16, 32 or 64 (got %d)", d->page_size);
   if (d->max_pages_per_seq < 1) return fail(SKV_ERR_INVALID_ARG, "max_pages_per_seq must be >= 1");
   if (d->num_pages < 1) return fail(SKV_ERR_INVALID_ARG, "num_pages must be >= 1");
-  if (d->dtype != SKV_F32 && d->dtype != SKV_BF16)
-    return fail(SKV_ERR_INVALID_ARG, "dtype must be SKV_F32 or SKV_BF16 (got %d)", d->dtype);
+  if (d->dtype != SKV_F32 && d->dtype != SKV_BF16 && d->dtype != SKV_FP8_E4M3)
+    return fail(SKV_ERR_INVALID_ARG, "dtype must be SKV_F32, SKV_BF16 or SKV_FP8_E4M3 (got %d)", d->dtype);
   // a positive finite scale (the MLA kernel's overflow threshold divides by it)
   if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f))
     return fail(SKV_ERR_INVALID_ARG, "softmax_scale must be positive and finite (got %g)",
@@ -92,6 +94,8 @@ skv_status check_desc(const skv_attn_desc* d) {
     return fail(SKV_ERR_UNSUPPORTED, "GQA needs head_dim_qk = head_dim_v in {64, 128} (got %d, %d)",
                 d->head_dim_qk, d->head_dim_v);
   const int G = d->num_q_heads / d->num_kv_heads;
+  if (d->dtype == SKV_FP8_E4M3 && G != 8 && G != 16)
+    return fail(SKV_ERR_UNSUPPORTED, "FP8 KV needs GQA groups of 8 or 16 query heads (got %d)", G);
   if (pick_variant(*d) == Variant::GqaMfma) {
     if (G != 16)
       return fail(SKV_ERR_UNSUPPORTED, "bf16 GQA groups of 16 or more query heads must be exactly 16 (got %d)", G);
@@ -519,15 +523,21 @@ static skv_status check_plan_matches(const skv_attn_desc* d, const skv_plan* pl)
 
 namespace {
 
-// Argument checks of the attention launch (no launch).
+// Argument checks of the attention launch (no launch). FP8 KV takes its
+// scales; other storage takes none.
 skv_status check_attention(const skv_attn_desc* desc, const void* q, const void* k_pages,
                            const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
-                           const skv_plan* plan, const void* workspace) {
+                           const skv_plan* plan, const void* workspace, const float* k_scales = nullptr,
+                           const float* v_scales = nullptr) {
   skv_status st = check_desc(desc);
   if (st) return st;
   if ((st = check_plan_matches(desc, plan))) return st;
   if (!q || !k_pages || !v_pages || !page_table || !seq_lens || !workspace)
     return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
+  if (desc->dtype == SKV_FP8_E4M3 && (!k_scales || !v_scales))
+    return fail(SKV_ERR_INVALID_ARG, "FP8 KV needs its key and value scales (skv_decode_attn_partial_fp8)");
+  if (desc->dtype != SKV_FP8_E4M3 && (k_scales || v_scales))
+    return fail(SKV_ERR_INVALID_ARG, "scales go with FP8 KV only");
   if (desc->mla && v_pages != k_pages)
     return fail(SKV_ERR_INVALID_ARG, "MLA reads values from the key rows: v_pages must equal k_pages");
   return SKV_OK;
@@ -550,9 +560,10 @@ skv_status check_merge(const skv_attn_desc* desc, const skv_plan* plan, const vo
 skv_status launch_attention(const skv_attn_desc* desc, const void* q, const void* k_pages,
                             const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
                             const skv_plan* plan, const void* workspace, float* o_part, float* lse_part,
-                            void* stream) {
+                            void* stream, const float* k_scales = nullptr, const float* v_scales = nullptr) {
   AttnLaunch a{desc, q, k_pages, v_pages, page_table, seq_lens, workspace, o_part, lse_part,
-               (int)plan->tasks.size(), plan->tasks_off, (hipStream_t)stream, plan->max_ntok};
+               (int)plan->tasks.size(), plan->tasks_off, (hipStream_t)stream, plan->max_ntok,
+               k_scales, v_scales};
   hipError_t e;
   switch (pick_variant(*desc)) {
     case Variant::GqaValu: e = launch_gqa_valu(a); break;
@@ -659,6 +670,21 @@ skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q, con
   if (!o_part || !lse_part) return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
   return launch_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, o_part,
                           lse_part, stream);
+}
+
+skv_status skv_decode_attn_partial_fp8(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                                       const void* v_pages, const float* k_scales, const float* v_scales,
+                                       const int32_t* page_table, const int32_t* seq_lens,
+                                       const skv_plan* plan, const void* workspace, float* o_part,
+                                       float* lse_part, void* stream) {
+  if (desc && desc->dtype != SKV_FP8_E4M3)
+    return fail(SKV_ERR_INVALID_ARG, "skv_decode_attn_partial_fp8 needs desc->dtype = SKV_FP8_E4M3");
+  skv_status st = check_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace,
+                                  k_scales, v_scales);
+  if (st) return st;
+  if (!o_part || !lse_part) return fail(SKV_ERR_INVALID_ARG, "a device pointer is NULL");
+  return launch_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, o_part,
+                          lse_part, stream, k_scales, v_scales);
 }
 
 skv_status skv_merge_states(const skv_attn_desc* desc, const skv_plan* plan, const void* workspace,

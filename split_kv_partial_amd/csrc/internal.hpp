@@ -127,6 +127,8 @@ struct AttnLaunch {
   int64_t tasks_off;   // byte offset of the task descriptors in the workspace
   hipStream_t stream;
   int max_ntok;        // most query tokens of any task (1: one token per task)
+  const float* k_scales = nullptr;   // FP8 KV: [num_pages][H_kv] key scales
+  const float* v_scales = nullptr;   // FP8 KV: [num_pages][H_kv] value scales
 };
 hipError_t launch_gqa_valu(const AttnLaunch& a);
 hipError_t launch_gqa_mfma(const AttnLaunch& a);

@@ -26,6 +26,19 @@
 // contiguous bytes), values dimension-major [D][P] per page (a lane's 4 tokens
 // of one dimension are 8 contiguous bytes). No LDS is used until the final
 // merge of the four waves.
+//
+// FP8 KV (OCP E4M3 codes with a float32 scale per page and KV head; SPLASH
+// appendix C.1 serves an FP8 E4M3 KV cache): the same layouts at one byte per
+// element, so a lane's key load is one 16-byte chunk of 16 dimensions (the
+// operands of two consecutive products; the query operand takes the same
+// dimension order) and its value load 4 bytes (4 tokens of one dimension).
+// v_cvt_scalef32_pk_bf16_fp8 turns two codes into two bf16 in one instruction,
+// exactly (every E4M3 value is a bf16 value), and the products run as for bf16
+// storage. A block of 16 tokens lies in one page (P >= 16), so its key scale
+// multiplies its scores and its value scale its softmax weights before the
+// P*V product (the normaliser sums the unscaled weights). The matrix cores'
+// own FP8 products would need the queries and weights in FP8 as well, which
+// costs far more accuracy than this stream has to spend time.
 #include "device_common.hpp"
 #include "fused.hpp"
 #include "internal.hpp"
@@ -42,6 +55,8 @@ struct MfmaArgs {
   int32_t* err_flag;
   float* o_part;
   float* lse_part;
+  const float* k_scale;   // FP8 KV: [num_pages][H_kv]
+  const float* v_scale;
   int32_t H_q, H_kv, G, page_shift, max_pages, num_pages;
   float scale_log2;
 };
@@ -63,10 +78,17 @@ struct StepRegs {
   u32x2_t v[2][D / 16];   // 4 tokens x 1 dimension per block, per 16-dim group
 };
 
+// Read-only inputs addressed through the constant address space: wave-uniform
+// loads from it become scalar loads (lgkmcnt), so a page id or scale the wave
+// waits for does not drain the vector loads already in flight (vmcnt counts
+// in issue order).
+typedef const __attribute__((address_space(4))) int32_t const_i32_t;
+typedef const __attribute__((address_space(4))) float const_f32_t;
+
 template <int D>
 struct Ctx {
   const MfmaArgs* a;
-  const int32_t* ptab;
+  const_i32_t* ptab;
   int64_t kvh;
   int end;
   int lane, g, r16;  // g = lane / 16 (k-group), r16 = lane % 16
@@ -113,16 +135,95 @@ __device__ __forceinline__ bool load_step(const Ctx<D>& c, int t0, StepRegs<D>& 
   return bad;
 }
 
+// FP8 KV: one step's raw codes and the two blocks' scales.
+template <int D>
+struct StepRegs8 {
+  u32x4_t k[2][D / 64];   // 16 codes (dims 16 (4j + g) .. + 15) of token r16
+  uint32_t v[2][D / 16];  // 4 codes: tokens 4g .. 4g + 3 of dimension 16 nb + r16
+  float ks[2], vs[2];
+};
+
+template <int D>
+__device__ __forceinline__ bool load_step8(const Ctx<D>& c, int t0, StepRegs8<D>& s) {
+  const MfmaArgs& a = *c.a;
+  const int P = 1 << a.page_shift;
+  bool bad = false;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int tb = t0 + 16 * blk;
+    int pid = -1;
+    if (tb < c.end) {
+      pid = c.ptab[tb >> a.page_shift];
+      if (pid < 0 || pid >= a.num_pages) {
+        if (c.lane == 0) raise_error(a.err_flag, kErrPageId);
+        bad = true;
+        pid = -1;
+      }
+    }
+    if (pid >= 0) {
+      const int slot = tb & (P - 1);
+      const int64_t ph = (int64_t)pid * a.H_kv + c.kvh;
+      const uint8_t* kp = a.k + (ph * (D / 16) * P + slot + c.r16) * 16;
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j)
+        s.k[blk][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + (int64_t)(4 * j + c.g) * P * 16));
+      const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v) + (ph * D + c.r16) * P + slot + 4 * c.g;
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb)
+        s.v[blk][nb] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp + (int64_t)16 * nb * P));
+      s.ks[blk] = ((const_f32_t*)a.k_scale)[ph];
+      s.vs[blk] = ((const_f32_t*)a.v_scale)[ph];
+    } else {
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) s.k[blk][j] = u32x4_t{0, 0, 0, 0};
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) s.v[blk][nb] = 0;
+      s.ks[blk] = 0.f;
+      s.vs[blk] = 0.f;
+    }
+  }
+  return bad;
+}
+
+// Two E4M3 codes (byte pair kHi of w) as two bf16 in one word.
+template <bool kHi>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
+// Codes to the bf16 operand registers of compute_step (product 2j takes the
+// low 8 codes of chunk j, product 2j + 1 the high 8).
+template <int D>
+__device__ __forceinline__ void decode_step(const StepRegs8<D>& r, StepRegs<D>& s) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) {
+      const u32x4_t w = r.k[blk][j];
+      s.k[blk][2 * j] = u32x4_t{e4m3x2_to_bf16x2<false>(w[0]), e4m3x2_to_bf16x2<true>(w[0]),
+                                e4m3x2_to_bf16x2<false>(w[1]), e4m3x2_to_bf16x2<true>(w[1])};
+      s.k[blk][2 * j + 1] = u32x4_t{e4m3x2_to_bf16x2<false>(w[2]), e4m3x2_to_bf16x2<true>(w[2]),
+                                    e4m3x2_to_bf16x2<false>(w[3]), e4m3x2_to_bf16x2<true>(w[3])};
+    }
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb)
+      s.v[blk][nb] = u32x2_t{e4m3x2_to_bf16x2<false>(r.v[blk][nb]), e4m3x2_to_bf16x2<true>(r.v[blk][nb])};
+  }
+}
+
 template <int D>
 struct State {
   float m, l;
   f32x4_t o[D / 16];
 };
 
-template <int D>
+// kmul / vmul (FP8 KV): per token block, the factor of its scores (softmax
+// scale in log2 units times the key scale) and of its weights (value scale).
+template <int D, bool kF8 = false>
 __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D>& s,
                                              const u32x4_t (&qf)[D / 32], State<D>& st,
-                                             float scale_log2) {
+                                             float scale_log2, const float* kmul = nullptr,
+                                             const float* vmul = nullptr) {
   // scores S^T for both token blocks
   f32x4_t sc[2];
 #pragma unroll
@@ -140,7 +241,7 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int tok = t0 + 16 * blk + 4 * c.g + e;
-      const float x = sc[blk][e] * scale_log2;
+      const float x = sc[blk][e] * (kF8 ? kmul[blk] : scale_log2);
       sv[4 * blk + e] = (!tail || tok < c.end) ? x : -INFINITY;
     }
   float mt = sv[0];
@@ -161,8 +262,13 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
   // throughput that this HBM-bound kernel has to spare, and keeps ~16 bits of
   // each weight instead of 8.
   uint32_t ph[4], pl[4];
+  if constexpr (kF8) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
+    for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i] * vmul[i >> 1], p[2 * i + 1] * vmul[i >> 1], ph[i], pl[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
+  }
   const u32x4_t pf_hi = {ph[0], ph[1], ph[2], ph[3]};
   const u32x4_t pf_lo = {pl[0], pl[1], pl[2], pl[3]};
   // values past `end` (the split's end, or poisoned slots of the last page)
@@ -202,7 +308,7 @@ struct MfmaShared {
 
 // One task: the query heads of one KV head for one query token over the KV
 // range [lo, end) of one split, written as the split's partial state.
-template <int D>
+template <int D, bool kF8 = false>
 __device__ __forceinline__ void gqa_mfma_task(const MfmaArgs& a, const DevTask& t, MfmaShared<D>& sh) {
   auto& m_lds = sh.m_lds;
   auto& l_lds = sh.l_lds;
@@ -222,17 +328,23 @@ __device__ __forceinline__ void gqa_mfma_task(const MfmaArgs& a, const DevTask& 
   c.r16 = c.lane & 15;
   c.kvh = t.kvh;
   c.end = t.end;
-  c.ptab = a.page_table + (int64_t)t.b * a.max_pages;
-  const int wave = threadIdx.x >> 6;
+  c.ptab = (const_i32_t*)(a.page_table + (int64_t)t.b * a.max_pages);
+  // wave-uniform (readfirstlane): the step positions, page ids and scales
+  // derived from it stay scalar, so page ids come by scalar loads and waiting
+  // for one does not drain the vector loads already in flight
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
-  // Q^T operand: lane owns head r16; its k-slots of product m are dims 8(4m+g)..+7
+  // Q^T operand: lane owns head r16; its k-slots of product m are dims
+  // 8(4m+g)..+7 (FP8 KV: 16(4(m/2)+g) + 8(m%2)..+7, the key chunk order)
   u32x4_t qf[D / 32];
   {
     // groups of G < 16 heads: lanes past G compute copies of the group's heads
     const uint16_t* qp = a.q + ((int64_t)t.q_row * a.H_q + (int64_t)t.kvh * a.G + (c.r16 & (a.G - 1))) * D;
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m)
-      qf[m] = *reinterpret_cast<const u32x4_t*>(qp + 8 * (4 * m + c.g));
+    for (int m = 0; m < D / 32; ++m) {
+      const int dim0 = kF8 ? 16 * (4 * (m >> 1) + c.g) + 8 * (m & 1) : 8 * (4 * m + c.g);
+      qf[m] = *reinterpret_cast<const u32x4_t*>(qp + dim0);
+    }
   }
 
   State<D> st;
@@ -245,18 +357,45 @@ __device__ __forceinline__ void gqa_mfma_task(const MfmaArgs& a, const DevTask& 
   // the previous step is computed.
   constexpr int kStride = kWaves * kStep;
   int t0 = t.lo + wave * kStep;
-  StepRegs<D> ra, rb;
   bool bad = false;   // wave-uniform: the page ids are per 16-token block
-  if (t0 < c.end) bad |= load_step(c, t0, ra);
-  while (t0 < c.end) {
-    const int t1 = t0 + kStride;
-    if (t1 < c.end) bad |= load_step(c, t1, rb);
-    compute_step(c, t0, ra, qf, st, a.scale_log2);
-    if (t1 >= c.end) break;
-    const int t2 = t1 + kStride;
-    if (t2 < c.end) bad |= load_step(c, t2, ra);
-    compute_step(c, t1, rb, qf, st, a.scale_log2);
-    t0 = t2;
+  if constexpr (kF8) {
+    // a ring of kRing raw steps: loads run kRing - 1 steps ahead (a step of
+    // codes is half a bf16 step's bytes, so more of them stay in flight)
+    constexpr int kRing = 3;
+    StepRegs8<D> r[kRing];
+    StepRegs<D> s;
+    // one step's codes decoded, with its blocks' score and weight factors
+    auto step = [&](int ts, const StepRegs8<D>& rr) {
+      decode_step(rr, s);
+      const float km[2] = {a.scale_log2 * rr.ks[0], a.scale_log2 * rr.ks[1]};
+      compute_step<D, true>(c, ts, s, qf, st, a.scale_log2, km, rr.vs);
+    };
+#pragma unroll
+    for (int i = 0; i < kRing - 1; ++i)
+      if (t0 + i * kStride < c.end) bad |= load_step8(c, t0 + i * kStride, r[i]);
+    while (t0 < c.end) {
+#pragma unroll
+      for (int i = 0; i < kRing; ++i) {
+        const int tl = t0 + (kRing - 1) * kStride;
+        if (tl < c.end) bad |= load_step8(c, tl, r[(i + kRing - 1) % kRing]);
+        step(t0, r[i]);
+        t0 += kStride;
+        if (t0 >= c.end) break;
+      }
+    }
+  } else {
+    StepRegs<D> ra, rb;
+    if (t0 < c.end) bad |= load_step(c, t0, ra);
+    while (t0 < c.end) {
+      const int t1 = t0 + kStride;
+      if (t1 < c.end) bad |= load_step(c, t1, rb);
+      compute_step(c, t0, ra, qf, st, a.scale_log2);
+      if (t1 >= c.end) break;
+      const int t2 = t1 + kStride;
+      if (t2 < c.end) bad |= load_step(c, t2, ra);
+      compute_step(c, t1, rb, qf, st, a.scale_log2);
+      t0 = t2;
+    }
   }
 
   // Merge the four waves' states: sum l over the 4 lanes of each head first.
@@ -450,7 +589,7 @@ __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& 
   c.r16 = lane & 15;
   c.kvh = t.kvh;
   c.end = t.end;
-  c.ptab = a.page_table + (int64_t)t.b * a.max_pages;
+  c.ptab = (const_i32_t*)(a.page_table + (int64_t)t.b * a.max_pages);
 
   // Q^T operands and per-column visible ends of the wave's two blocks (rows
   // past the task's last are computed on a copy of the last row, not written)
@@ -553,10 +692,10 @@ void gqa_rows_fused(MfmaArgs a, FusedArgs f) {
 }
 
 // One work-group per task, in the plan's queue order.
-template <int D>
+template <int D, bool kF8 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_mfma_kernel(MfmaArgs a) {
   __shared__ MfmaShared<D> sh;
-  gqa_mfma_task<D>(a, a.tasks[blockIdx.x], sh);
+  gqa_mfma_task<D, kF8>(a, a.tasks[blockIdx.x], sh);
 }
 
 // Attention and merge in one launch (fused.hpp): the task, then the
@@ -587,6 +726,8 @@ static MfmaArgs mfma_args(const AttnLaunch& L) {
   a.err_flag = reinterpret_cast<int32_t*>(const_cast<void*>(L.workspace));
   a.o_part = L.o_part;
   a.lse_part = L.lse_part;
+  a.k_scale = L.k_scales;
+  a.v_scale = L.v_scales;
   a.H_q = d.num_q_heads;
   a.H_kv = d.num_kv_heads;
   a.G = d.num_q_heads / d.num_kv_heads;
@@ -602,8 +743,25 @@ static bool mfma_supported(const skv_attn_desc& d) {
   return (G == kG || G == kG / 2) && d.dtype == SKV_BF16 && (d.head_dim_qk == 128 || d.head_dim_qk == 64);
 }
 
+static bool fp8_supported(const AttnLaunch& L) {
+  const skv_attn_desc& d = *L.desc;
+  const int G = d.num_q_heads / d.num_kv_heads;
+  return (G == kG || G == kG / 2) && d.dtype == SKV_FP8_E4M3 && (d.head_dim_qk == 128 || d.head_dim_qk == 64) &&
+         L.max_ntok == 1 && L.k_scales && L.v_scales;
+}
+
 hipError_t launch_gqa_mfma(const AttnLaunch& L) {
   const skv_attn_desc& d = *L.desc;
+  if (d.dtype == SKV_FP8_E4M3) {
+    if (!fp8_supported(L)) return hipErrorInvalidValue;
+    if (L.num_tasks == 0) return hipSuccess;
+    const MfmaArgs a = mfma_args(L);
+    if (d.head_dim_qk == 128)
+      hipLaunchKernelGGL((gqa_mfma_kernel<128, true>), dim3(L.num_tasks), dim3(256), 0, L.stream, a);
+    else
+      hipLaunchKernelGGL((gqa_mfma_kernel<64, true>), dim3(L.num_tasks), dim3(256), 0, L.stream, a);
+    return hipGetLastError();
+  }
   if (!mfma_supported(d)) return hipErrorInvalidValue;
   if (L.num_tasks == 0) return hipSuccess;
   const MfmaArgs a = mfma_args(L);

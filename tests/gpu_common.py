@@ -13,17 +13,21 @@ TOL_BF16 = dict(abs=2e-3, rel=1e-2, lse=2e-3)
 
 
 def tol_for(w):
+    """fp32 storage: 1e-5; bf16 storage and FP8 KV (bf16 queries, codes decoded
+    exactly to bf16, the same bf16 products with fp32 accumulation): the bf16
+    bound."""
     return TOL_F32 if w.dtype == "f32" else TOL_BF16
 
 
 def spec_of(w) -> skv.AttnSpec:
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": skv.FP8}[w.dtype]
     return skv.AttnSpec(w.num_q_heads, w.num_kv_heads, w.head_dim_qk, w.head_dim_v, w.page_size,
-                        dtype=torch.float32 if w.dtype == "f32" else torch.bfloat16, mla=w.mla,
-                        causal=w.causal)
+                        dtype=dt, mla=w.mla, causal=w.causal)
 
 
 def _dev_tensor(a: np.ndarray, dtype: str, dev):
-    if dtype == "bf16":
+    """bf16 bits (uint16) as a bf16 tensor; float32 and fp8 codes (uint8) as they are."""
+    if dtype == "bf16" or (dtype == "fp8" and a.dtype == np.uint16):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
     return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
@@ -33,6 +37,8 @@ class DeviceInputs:
         self.q = _dev_tensor(w.q, w.dtype, dev)
         self.k = _dev_tensor(w.k_pages, w.dtype, dev)
         self.v = self.k if w.mla else _dev_tensor(w.v_pages, w.dtype, dev)
+        self.k_scale = None if w.k_scale is None else torch.from_numpy(w.k_scale).to(dev)
+        self.v_scale = None if w.v_scale is None else torch.from_numpy(w.v_scale).to(dev)
         self.page_table = torch.from_numpy(w.page_table).to(dev)
         self.seq_lens = torch.from_numpy(w.seq_lens).to(dev)
         self.o_ext = None if w.o_ext is None else torch.from_numpy(w.o_ext).to(dev)
@@ -51,7 +57,13 @@ def run_path(w, plan, inputs: DeviceInputs | None = None, with_ext: bool = True,
     merged output and LSE bit for bit: both merges add a row's states in the
     same order with the same operations."""
     d = inputs or DeviceInputs(w)
-    o_part, lse_part = skv.decode_attn_partial(d.q, d.k, d.v, d.page_table, d.seq_lens, plan, w.scale)
+    if w.dtype == "fp8":
+        # FP8 KV has its own attention entry point; the one-call path takes none
+        o_part, lse_part = skv.decode_attn_partial_fp8(d.q, d.k, d.v, d.k_scale, d.v_scale, d.page_table,
+                                                       d.seq_lens, plan, w.scale)
+        fused = False
+    else:
+        o_part, lse_part = skv.decode_attn_partial(d.q, d.k, d.v, d.page_table, d.seq_lens, plan, w.scale)
     ext = with_ext and d.o_ext is not None
     o, lse = skv.merge_states(o_part, lse_part, plan, d.o_ext if ext else None,
                               d.lse_ext if ext else None, out_dtype=out_dtype)

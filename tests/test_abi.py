@@ -20,7 +20,7 @@ HEADER = os.path.join(ROOT, "include", "splitkv.h")
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(skv_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(skv_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -341,3 +341,43 @@ def test_query_tile_defaults_and_limits():
     with pytest.raises(skv.SplitKVError):
         skv.plan_splits(seq, skv.AttnSpec(8, 2, 128, 128, 16, dtype=torch.float32), 64, q_lens=q,
                         params=prm)
+
+
+def test_fp8_descriptions_and_entry_point_checks():
+    f8 = skv.AttnSpec(num_q_heads=32, num_kv_heads=2, head_dim_qk=128, head_dim_v=128, page_size=16,
+                      dtype=skv.FP8)
+    assert _plan_call(f8.desc(1, max_pages=8, num_pages=8), [100]) == 0
+    for hq, hkv, d in ((8, 2, 128), (4, 4, 64), (64, 2, 128)):      # groups of 4, 1, 32
+        g = skv.AttnSpec(hq, hkv, d, d, 16, dtype=skv.FP8)
+        assert _plan_call(g.desc(1, max_pages=8, num_pages=8), [100]) == -2
+    mla = skv.AttnSpec(128, 1, 576, 512, 64, dtype=skv.FP8, mla=True)
+    assert _plan_call(mla.desc(1, max_pages=4, num_pages=4), [100]) == -2
+    bad = f8.desc(1, max_pages=8, num_pages=8)
+    bad.dtype = 3
+    assert _plan_call(bad, [100]) == -1
+    # FP8 plans run one query token per task
+    prm = skv.default_params()
+    prm.query_tile = 2
+    with pytest.raises(skv.SplitKVError):
+        skv.plan_splits([100], f8, 64, q_lens=[5], params=prm)
+    plan = skv.plan_splits([100, 50], f8, num_cu=4, q_lens=[3, 1])
+    assert plan.info().query_tile == 1
+    d = f8.desc(2, max_pages=8, num_pages=16, scale=0.1)
+    fake = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    call = lambda desc, ks, vs: skv._lib.skv_decode_attn_partial_fp8(
+        ctypes.byref(desc), fake, fake, fake, ks, vs, fake, fake, plan.handle, fake, fake, fake, None)
+    assert call(d, None, fake) == -1 and "scales" in skv._lib.skv_last_error().decode()
+    assert call(d, fake, None) == -1
+    bf = SPEC.desc(2, max_pages=8, num_pages=16, scale=0.1)     # a bf16 description
+    assert call(bf, fake, fake) == -1
+    # the bf16 entry points refuse FP8 descriptions (no scales to pass)
+    st = skv._lib.skv_decode_attn_partial(ctypes.byref(d), fake, fake, fake, fake, fake, plan.handle, fake,
+                                          fake, fake, None)
+    assert st == -1 and "scales" in skv._lib.skv_last_error().decode()
+    need = skv.scratch_bytes(plan)
+    st = skv._lib.skv_decode_attn(ctypes.byref(d), fake, fake, fake, fake, fake, plan.handle, fake, fake, need,
+                                  0, None, None, fake, 0, None, None)
+    assert st == -1
+    # the Python face: FP8 specs go through decode_attn_partial_fp8 only
+    with pytest.raises(ValueError):
+        skv.decode_attn_partial(torch.empty(0), None, None, None, None, plan, 0.1)

@@ -135,3 +135,12 @@ def test_spec_decode_gqa_full():
 
 def test_spec_decode_gqa_sharp_full():
     run_full(6, lambda w: ({b: [0, 5, 15] for b in _spread(w)[:2]}, None), sharp=True)
+
+
+def test_llama405b_gqa_share_fp8_full():
+    # workload 2's shape and lengths over an FP8 E4M3 KV cache
+    run_full(7, lambda w: ({b: [0] for b in _spread(w, (17,))}, int(np.argmax(w.seq_lens))))
+
+
+def test_llama405b_gqa_share_fp8_sharp_full():
+    run_full(7, lambda w: ({b: [0] for b in _spread(w)[:2]}, None), sharp=True)

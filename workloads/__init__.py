@@ -190,7 +190,8 @@ def _fp8_blocks(x: np.ndarray, out: np.ndarray, scale: np.ndarray, pages_per_pas
         s = np.where(amax > 0, amax / np.float32(FP8_MAX), np.float32(1.0)).astype(np.float32)
         scale[lo:hi] = s
         shape = (hi - lo, blk.shape[1]) + (1,) * (blk.ndim - 2)
-        y = np.minimum(np.abs(blk / s.reshape(shape)), np.float32(FP8_MAX)) * np.sign(blk)
+        # |x / scale| <= 448 up to one float32 rounding, which the cast takes to 448
+        y = blk / s.reshape(shape)
         out[lo:hi] = torch.from_numpy(np.ascontiguousarray(y, np.float32)).to(
             torch.float8_e4m3fn).view(torch.uint8).numpy()
 
@@ -302,7 +303,8 @@ def build(name: str, *, dtype: str, mla: bool, seq_lens, q_lens=None, num_q_head
 # 1-5 are the five synthetic configurations; workload 6 adds a speculative-decoding
 # step (LiquidCP section 7.1: 16 query tokens per request and iteration, one
 # target token and 15 drafts) on a GQA group of 8, where the 16 tokens' rows
-# make the products dense enough for the matrix cores.
+# make the products dense enough for the matrix cores; workload 7 is workload
+# 2 over an FP8 E4M3 KV cache.
 # --------------------------------------------------------------------------------------
 
 MLA_DQK, MLA_DV, MLA_HEADS = 576, 512, 128
@@ -339,11 +341,13 @@ def config_lengths(cid: int):
     if cid == 6:
         L = _lengths_rng(6).integers(4096, 32768, size=32, endpoint=True)
         return L, np.full(32, 16, np.int64)
+    if cid == 7:
+        return config_lengths(2)
     raise ValueError(cid)
 
 
 def make(cid: int, sharp: bool = False, decode_only: bool = False) -> Workload:
-    """Benchmark workload ``cid`` (1..6). ``sharp`` scales q so that scores have a
+    """Benchmark workload ``cid`` (1..7). ``sharp`` scales q so that scores have a
     standard deviation of about 3 (a near-uniform softmax cannot reveal a wrong
     QK^T). ``decode_only`` (workload 5) drops the chunked-prefill request and the
     external states, leaving the eight million-token decode requests."""
@@ -378,6 +382,12 @@ def make(cid: int, sharp: bool = False, decode_only: bool = False) -> Workload:
                      seed=seed, value_scale=0.1, q_scale=SHARP_MLA if sharp else 1.0,
                      n_ext=0 if decode_only else 16,
                      ext_lse_center=math.log(1048576.0))
+    if cid == 7:
+        # workload 2's shape and lengths over an FP8 E4M3 KV cache
+        return build("llama405b-gqa-share-fp8", dtype="fp8", mla=False, seq_lens=L, q_lens=n,
+                     num_q_heads=128, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
+                     page_size=16, scale=1.0 / math.sqrt(128.0), seed=seed,
+                     q_scale=SHARP_GQA if sharp else 1.0)
     if cid == 6:
         # causal rows: draft i sees the history and the tokens before it
         return build("spec-decode-gqa-g8", dtype="bf16", mla=False, seq_lens=L, q_lens=n,
