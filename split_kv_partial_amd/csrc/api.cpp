@@ -744,46 +744,23 @@ VariantShape variant_shape(Variant v) {
   }
 }
 
-// Critical-wave parameters for each kernel on MI355X (the pages' appendix A.2
-// fits them per platform; here they are fitted per kernel to whole-kernel
-// times of plans with 1 to 64 splits per request).
-//  - GQA matrix-core kernel: least-squares fit over the 32-request,
-//    4K-32K-token shape (time unit = one 64-token tile per slot with all
-//    slots busy).
-//  - GQA vector kernel: four work-groups share a CU (128 registers per lane
-//    for a group of 8 heads). A work-group alone on a CU is bound by its own
-//    load-then-compute chain and runs only about twice as fast as in a full
-//    wave. Measured on the skewed 256-request batch (8 requests of 262,144
-//    tokens), kernel time is lowest when the long requests give at least one
-//    full wave of equal long tasks on every CU (16 splits or more) and rises
-//    when a CU ends up with one long task more than its neighbours, which the
-//    model (identical slots, one global rate) does not see. Eight slots per
-//    CU with rho 0.8 and delta_attn 1 make the search split those requests
-//    24 ways, inside the measured optimum; four slots per CU (the occupancy)
-//    stopped at 13 (10% slower).
-//  - MLA: a work-group's tile rate is set by its own matrix and LDS work, not
-//    by shared HBM, so a lone work-group is no faster than one in a full wave
-//    (rho = 1), and the per-task overhead is small (Q load, epilogue).
-//  - GQA matrix-core kernel on groups of 8 (the skewed 256-request batch: 8
-//    requests of 262,144 tokens among 248 of 512-2,048): with the fit above
-//    the search split the long requests too little (281 splits, 1.68 ms per
-//    step); four slots per CU, rho 0.5 and delta_attn 3 give 313 splits and
-//    1.47 ms, the best of the six parameter sets measured (the vector kernel's
-//    set gives 440 splits and 1.51 ms). On the 32-request group-16 shape the
-//    same four-slot set would cost 5%, so the two group sizes keep separate
-//    fits.
-// The last field turns on the proportional candidates by default. On the MLA
-// 64-request DeepSeek shape the one-task-per-slot proportional plan the model
-// prefers ran 0.6-3.6% faster than the search result in alternating runs
-// (within the spread of separate runs); on the GQA 32-request
-// shape the model's one-wave proportional plan (512 tasks) ran 1% slower than
+// Critical-wave parameters for each kernel on MI355X, from the table the
+// calibration tool writes (split_kv_partial_amd/calibrate.py): the model of
+// LiquidCP section 5.2 fitted to timed plans per kernel as in appendix A.2,
+// then validated on the planner's own plans for the workloads the kernel
+// serves (the model's identical slots at one rate cannot see how tasks spread
+// over CUs, so the fit of least error is not always the fastest). The last
+// field turns on the proportional candidates by default: on the MLA 64-request
+// DeepSeek shape the one-task-per-slot proportional plan the model prefers ran
+// 0.6-3.6% faster than the search result in alternating runs; on the GQA
+// 32-request shape the model's one-wave proportional plan ran 1% slower than
 // the two-wave search result, so GQA keeps the pages' candidates.
 Calibration calibration(Variant v) {
-  switch (v) {
-    case Variant::GqaMfma: return {0.50, 3.0, 1.0, 0.47, 2.66, 0};
-    case Variant::GqaMfmaG8: return {0.50, 3.0, 1.0, 0.47, 5.2, 0};
-    case Variant::GqaValu: return {0.80, 1.0, 1.0, 0.47, 11.2, 0};
-    default: return {1.00, 2.0, 1.0, 0.47, 7.4, 1};
-  }
+  // the table written by the calibration tool (split_kv_partial_amd/calibrate.py)
+#define CAL(V, rho, delta_attn, delta_red, gamma, tile_time_us, balanced) \
+  if (v == Variant::V) return {rho, delta_attn, delta_red, gamma, tile_time_us, balanced};
+#include "calibration_mi355x.inc"
+#undef CAL
+  return {1.0, 2.0, 1.0, 0.47, 1.0, 0};   // not reached: every variant has a row
 }
 }  // namespace skv

@@ -381,3 +381,21 @@ def test_fp8_descriptions_and_entry_point_checks():
     # the Python face: FP8 specs go through decode_attn_partial_fp8 only
     with pytest.raises(ValueError):
         skv.decode_attn_partial(torch.empty(0), None, None, None, None, plan, 0.1)
+
+
+def test_library_defaults_are_the_calibration_tools_fit():
+    # the table the library compiles in is the one the calibration tool wrote
+    # beside profiles/mi355x.json: every kernel's default parameters equal it
+    import json
+    fit = json.load(open(os.path.join(ROOT, "profiles", "mi355x.json")))["kernels"]
+    specs = {"gqa_mfma": skv.AttnSpec(128, 8, 128, 128, 16),
+             "gqa_mfma_g8": skv.AttnSpec(64, 8, 128, 128, 16),
+             "gqa_valu": skv.AttnSpec(32, 8, 128, 128, 16, dtype=torch.float32),
+             "mla_mfma": skv.AttnSpec(128, 1, 576, 512, 64, mla=True)}
+    for kernel, spec in specs.items():
+        inf = skv.plan_splits([5000, 7000], spec, 64).info()
+        c = fit[kernel]
+        assert (inf.rho, inf.delta_attn, inf.delta_red, inf.gamma) == (c["rho"], c["delta_attn"], c["delta_red"],
+                                                                      c["gamma"]), kernel
+        assert inf.tile_time_us == c["tile_time_us"] and inf.balanced_candidates == c["balanced"], kernel
+        assert c["rmse_attn_us"] > 0 and len(c["points"]) >= 10
