@@ -43,6 +43,10 @@
 #include "fused.hpp"
 #include "internal.hpp"
 
+#ifndef RING_STEPS
+#define RING_STEPS 4
+#endif
+
 namespace skv {
 
 struct MfmaArgs {
@@ -438,28 +442,49 @@ __device__ __forceinline__ void gqa_mfma_task(const MfmaArgs& a, const DevTask& 
 // ---------------------------------------------------------------------------
 // Tasks of several query tokens (a query tile of one request: up to
 // kTileRows / G consecutive tokens). The rows (row = token * G + head) are
-// columns of the products in blocks of 16: block b holds rows 16 b .. 16 b + 15.
-// Each wave owns up to kBPW = 4 consecutive blocks (64 rows; one wave per SIMD,
-// whose 512 registers hold the four blocks' operands and accumulators); the
-// waves are arranged as column groups (one per kBPW blocks) times token groups
-// (4 / column groups, which take the split's 32-token steps round-robin and
-// are merged through LDS at the end, as the one-token kernel does). A full
-// tile of 128 rows is two column groups of two token groups: two waves stream
-// each step, the second one's loads served by the caches, and each KV byte
-// comes from HBM once per tile instead of once per token. Causal rows see
-// their own end: lane n's column is one row, masked at min(split end, the
-// visible end of its token).
+// columns of the products in blocks of 16; wave w owns blocks 2w and 2w + 1
+// (rows 32w .. 32w + 31) for the whole split, so a wave's state needs no
+// merge with the others'. The split's keys and values pass through LDS once
+// per work-group: each 32-token step is copied by the LDS DMA
+// (global_load_lds_dwordx4: lane i's 16 bytes land at the instruction's LDS
+// base + 16 i) into a ring of kRing steps, issued kRing - 1 steps ahead of
+// its use, and every wave reads its operands from there, each key and value
+// fragment once for both of its blocks. Step layout in LDS:
+//   keys   [D/8 chunks][32 tokens][16 bytes]: the page's own chunk-major order,
+//          so a 16-lane read of one chunk is 256 contiguous bytes; the lanes
+//          a 16-byte read serves together (8 of one 16-lane group with the
+//          other half of the neighbouring group) then read tokens 0-7 of one
+//          chunk and 8-15 of the next, different banks;
+//   values [D dims][32 tokens] (64 bytes per dimension) in 8-byte slots of 4
+//          tokens, slot (token / 4) ^ (2 ((dim / 4) % 4)): the 32 lanes one
+//          8-byte read serves (16 dimensions x two token groups) then cover
+//          all 64 banks. A 16-byte DMA chunk (8 tokens of one dimension) keeps
+//          its two slots adjacent, the XOR being even. The reads stay single
+//          8-byte reads: paired into two-address reads (ds_read2_b64, which
+//          the compiler forms from reads a fixed distance apart) they measured
+//          8 bank-conflict cycles each with the bank-conflict counter, single
+//          reads and the key reads none.
+// Causal rows see their own end: lane n's column is one row, masked at
+// min(split end, the visible end of its token).
 // ---------------------------------------------------------------------------
 
-template <int D>
-constexpr int kBPW = 4;         // column blocks per wave
 constexpr int kTileRows = 128;  // rows of a full query tile
+constexpr int kRing = RING_STEPS;        // LDS steps in the ring
+constexpr int kRowsBPW = 2;     // column blocks per wave
+
+constexpr int kVGroupBytes = 1024;                // 16 dimensions of values
+template <int D>
+constexpr int kKeyBytes = kStep * D * 2;          // keys of one step
+template <int D>
+constexpr int kStepBytes = kKeyBytes<D> + (D / 16) * kVGroupBytes;
+template <int D>
+constexpr int kStepBlocks = 2 * kKeyBytes<D> / 1024;   // 1 KB DMA blocks per step (keys, then values)
+template <int D>
+constexpr int kDmaPerWaveStep = kStepBlocks<D> / kWaves;
 
 template <int D>
 struct RowsShared {
-  float m_lds[kWaves][kBPW<D>][kG], l_lds[kWaves][kBPW<D>][kG];
-  float o_lds[kWaves][kBPW<D>][kG][D + 4];
-  int bad_lds[kWaves];
+  __attribute__((aligned(16))) uint8_t ring[kRing][kStepBytes<D>];
 };
 
 // The rows of a multi-token task written as NaN (a device error).
@@ -469,91 +494,105 @@ __device__ __forceinline__ void rows_nan(const MfmaArgs& a, const DevTask& t) {
     write_nan_state(a.o_part, a.lse_part, (int64_t)t.out_row + (int64_t)j * a.H_q, a.G, D);
 }
 
-template <int D>
-struct RowsState {
-  float m[kBPW<D>], l[kBPW<D>];
-  f32x4_t o[kBPW<D>][D / 16];
-};
+typedef __attribute__((address_space(3))) void rows_lds_void_t;
 
-// One 32-token step for the wave's active blocks: scores, masked online
-// softmax (each lane's column has its own end), P*V with hi + lo weights.
-template <int D>
-__device__ __forceinline__ void rows_step(const Ctx<D>& c, int t0, StepRegs<D>& s,
-                                          const u32x4_t (&qf)[kBPW<D>][D / 32], RowsState<D>& st,
-                                          const int (&end_col)[kBPW<D>], int nblk, float scale_log2) {
-  // values past the task's last visible key hold stale or poisoned page data:
-  // zero them so that 0 * NaN cannot reach the accumulators
-  if (t0 + kStep > c.end) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      const int tok = t0 + 16 * blk + 4 * c.g;
-      const int nv = c.end - tok;
-      if (nv < 4) {
-        const uint32_t m0 = nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0x0000FFFFu : 0u);
-        const uint32_t m1 = nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0x0000FFFFu : 0u);
-#pragma unroll
-        for (int nb = 0; nb < D / 16; ++nb) {
-          s.v[blk][nb][0] &= m0;
-          s.v[blk][nb][1] &= m1;
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < kBPW<D>; ++j) {
-    if (j >= nblk) break;   // wave-uniform
-    f32x4_t sc[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int m = 0; m < D / 32; ++m) acc = mfma16(s.k[blk][m], qf[j][m], acc);
-      sc[blk] = acc;
-    }
-    float sv[8];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = t0 + 16 * blk + 4 * c.g + e;
-        sv[4 * blk + e] = tok < end_col[j] ? sc[blk][e] * scale_log2 : -INFINITY;
-      }
-    float mt = sv[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
-    mt = max_xor32(max_xor16(mt));
-    const float mn = fmaxf(st.m[j], mt);
-    // a column may see no key yet (its end precedes this step): keep a finite
-    // reference so that its weights are exp2(-inf) = 0 rather than NaN
-    const float mref = mn == -INFINITY ? 0.f : mn;
-    const float alpha = fast_exp2(st.m[j] - mref);
-    st.m[j] = mn;
-    float p[8], ps = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = fast_exp2(sv[i] - mref);
-      ps += p[i];
-    }
-    st.l[j] = st.l[j] * alpha + ps;
-    uint32_t ph[4], pl[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
-    const u32x4_t pf_hi = {ph[0], ph[1], ph[2], ph[3]};
-    const u32x4_t pf_lo = {pl[0], pl[1], pl[2], pl[3]};
-#pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) {
-      st.o[j][nb] *= alpha;
-      const u32x4_t vf = {s.v[0][nb][0], s.v[0][nb][1], s.v[1][nb][0], s.v[1][nb][1]};
-      st.o[j][nb] = mfma16(vf, pf_hi, st.o[j][nb]);
-      st.o[j][nb] = mfma16(vf, pf_lo, st.o[j][nb]);
-    }
+// One DMA instruction: each lane's 16 bytes at `src` to LDS byte
+// lds + 16 lane (M0 carries the LDS base; one wait state separates its write
+// from the DMA). Inline assembly, so that the compiler does not track these
+// loads: the loop orders them with its own vmcnt waits (the vector-memory
+// counter retires in order).
+__device__ __forceinline__ void rows_dma(const uint8_t* src, uint32_t lds) {
+  __asm__ __volatile__("s_mov_b32 m0, %[l]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[p], off nt"
+                       :
+                       : [l] "s"(lds), [p] "v"(src)
+                       : "memory", "m0");
+}
+
+// s_waitcnt immediates for the vector-memory counter only (gfx9 encoding).
+template <int N>
+constexpr int kRowsWaitVm = 0x3f70 | (N & 15) | ((N >> 4) << 14);
+
+// Wait until at most `ahead` steps of this wave's DMAs are in flight.
+template <int D, int N = kRing - 2>
+__device__ __forceinline__ void rows_wait_ahead(int ahead) {
+  if constexpr (N == 0) {
+    __builtin_amdgcn_s_waitcnt(kRowsWaitVm<0>);
+  } else {
+    if (ahead >= N) __builtin_amdgcn_s_waitcnt(kRowsWaitVm<N * kDmaPerWaveStep<D>>);
+    else rows_wait_ahead<D, N - 1>(ahead);
   }
 }
+
+__device__ __forceinline__ void rows_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
+
+// Page ids of the step at t0 (its two 16-token halves), wave-uniform scalars
+// read one step before they are used, so the scalar-load latency is not paid
+// at every step. Indices past the request's last page are clamped to it (those
+// tokens are masked where they are used).
+struct StepPages {
+  int p0, p1;
+};
+__device__ __forceinline__ StepPages step_pages(const MfmaArgs& a, const_i32_t* ptab, int t0, int end) {
+  const int last = (end - 1) >> a.page_shift;
+  return StepPages{ptab[min(t0 >> a.page_shift, last)], ptab[min((t0 + 16) >> a.page_shift, last)]};
+}
+
+// Sources of this wave's DMA blocks of the step at t0 (kDmaPerWaveStep<D>
+// blocks: wave, wave + 4, ...). A block below kStepBlocks / 2 holds keys, the
+// rest values. An id outside the pool is never dereferenced: page 0 stands in
+// and the task's state is written as NaN.
+template <int D>
+struct RowsDma {
+  const uint8_t* src[kDmaPerWaveStep<D>];
+
+  __device__ __forceinline__ bool prepare(const MfmaArgs& a, StepPages pg, int kvh, int t0, int wave,
+                                          int lane) {
+    const int P = 1 << a.page_shift;
+    int p0 = pg.p0, p1 = pg.p1;
+    const bool ok0 = p0 >= 0 && p0 < a.num_pages, ok1 = p1 >= 0 && p1 < a.num_pages;
+    if (!ok0) p0 = 0;
+    if (!ok1) p1 = 0;
+    const int64_t ph0 = (int64_t)p0 * a.H_kv + kvh, ph1 = (int64_t)p1 * a.H_kv + kvh;
+#pragma unroll
+    for (int j = 0; j < kDmaPerWaveStep<D>; ++j) {
+      const int blk = wave + kWaves * j;
+      if (blk < kStepBlocks<D> / 2) {       // keys: chunk c of token t
+        const int sl = 64 * blk + lane;
+        const int c = sl >> 5, t = sl & 31;
+        const int64_t ph = t < 16 ? ph0 : ph1;
+        const int slot = (t0 + t) & (P - 1);
+        src[j] = a.k + ((ph * (D / 8) + c) * P + slot) * 16;
+      } else {                               // values: dimension d, 8 tokens
+        const int sl = 64 * (blk - kStepBlocks<D> / 2) + lane;
+        const int d = sl >> 2, pair = sl & 3;
+        const int t = 4 * ((2 * pair) ^ (2 * ((d >> 2) & 3)));
+        const int64_t ph = t < 16 ? ph0 : ph1;
+        const int slot = (t0 + t) & (P - 1);
+        src[j] = reinterpret_cast<const uint8_t*>(a.v) + ((ph * D + d) * P + slot) * 2;
+      }
+    }
+    return !ok0 || !ok1;
+  }
+  __device__ __forceinline__ void issue(uint32_t lds_step, int wave) const {
+#pragma unroll
+    for (int j = 0; j < kDmaPerWaveStep<D>; ++j) {
+      const int blk = wave + kWaves * j;
+      const int off = blk < kStepBlocks<D> / 2 ? 1024 * blk
+                                               : kKeyBytes<D> + (blk - kStepBlocks<D> / 2) * kVGroupBytes;
+      rows_dma(src[j], lds_step + (uint32_t)off);
+    }
+  }
+};
 
 template <int D>
 __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& task, RowsShared<D>& sh) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, r16 = lane & 15;
   DevTask t = task;
   t.b = __builtin_amdgcn_readfirstlane(task.b);
   t.kvh = __builtin_amdgcn_readfirstlane(task.kvh);
@@ -573,114 +612,201 @@ __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& 
     return;
   }
   const int G = a.G;
-  const int R = G * t.ntok;                  // rows of the task
-  constexpr int BPW = kBPW<D>;
-  const int CB = (R + 15) >> 4;              // column blocks, at most 8
-  const int CG = (CB + BPW - 1) / BPW;       // column groups (BPW blocks each)
-  const int TG = CG == 1 ? 4 : (CG == 2 ? 2 : 1);
-  const int cg = wave % CG, tg = wave / CG;
-  const bool active = tg < TG;
-  const int nblk = active ? min(BPW, CB - BPW * cg) : 0;
+  const int R = G * t.ntok;                       // rows of the task
+  const int CB = (R + 15) >> 4;                   // column blocks in use
+  const int nblk = max(0, min(kRowsBPW, CB - kRowsBPW * wave));   // this wave's (uniform)
+  const int end = t.end;
+  const_i32_t* ptab = (const_i32_t*)(a.page_table + (int64_t)t.b * a.max_pages);
 
-  Ctx<D> c;
-  c.a = &a;
-  c.lane = lane;
-  c.g = lane >> 4;
-  c.r16 = lane & 15;
-  c.kvh = t.kvh;
-  c.end = t.end;
-  c.ptab = (const_i32_t*)(a.page_table + (int64_t)t.b * a.max_pages);
-
-  // Q^T operands and per-column visible ends of the wave's two blocks (rows
-  // past the task's last are computed on a copy of the last row, not written)
-  u32x4_t qf[BPW][D / 32];
-  int end_col[BPW];
+  // Q^T operands and per-column visible ends of the wave's blocks (rows past
+  // the task's last are computed on a copy of the last row, not written)
+  u32x4_t qf[kRowsBPW][D / 32];
+  int end_col[kRowsBPW];
 #pragma unroll
-  for (int j = 0; j < BPW; ++j) {
-    const int r = min(16 * (BPW * cg + j) + c.r16, R - 1);
+  for (int j = 0; j < kRowsBPW; ++j) {
+    const int r = min(16 * (kRowsBPW * wave + j) + r16, R - 1);
     const int tok = r / G, h = r - tok * G;
     const uint16_t* qp = a.q + ((int64_t)(t.q_row + tok) * a.H_q + (int64_t)t.kvh * G + h) * D;
 #pragma unroll
-    for (int m = 0; m < D / 32; ++m) qf[j][m] = *reinterpret_cast<const u32x4_t*>(qp + 8 * (4 * m + c.g));
+    for (int m = 0; m < D / 32; ++m) qf[j][m] = *reinterpret_cast<const u32x4_t*>(qp + 8 * (4 * m + g));
     end_col[j] = min(t.hi, t.vis_last - (t.ntok - 1 - tok) * t.step);
   }
+  // Q has landed before the first DMA (otherwise the compiler's wait for it
+  // would sit inside the loop and drain the ring)
+  __builtin_amdgcn_s_waitcnt(kRowsWaitVm<0>);
 
-  RowsState<D> st;
+  float mrow[kRowsBPW], lrow[kRowsBPW];
+  f32x4_t o[kRowsBPW][D / 16];
 #pragma unroll
-  for (int j = 0; j < BPW; ++j) {
-    st.m[j] = -INFINITY;
-    st.l[j] = 0.f;
+  for (int j = 0; j < kRowsBPW; ++j) {
+    mrow[j] = -INFINITY;
+    lrow[j] = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb) st.o[j][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < D / 16; ++nb) o[j][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int stride = TG * kStep;
-  int t0 = active ? t.lo + tg * kStep : t.end;
-  StepRegs<D> ra, rb;
-  bool bad = false;
-  if (t0 < c.end) bad |= load_step(c, t0, ra);
-  while (t0 < c.end) {
-    const int t1 = t0 + stride;
-    if (t1 < c.end) bad |= load_step(c, t1, rb);
-    rows_step(c, t0, ra, qf, st, end_col, nblk, a.scale_log2);
-    if (t1 >= c.end) break;
-    const int t2 = t1 + stride;
-    if (t2 < c.end) bad |= load_step(c, t2, ra);
-    rows_step(c, t1, rb, qf, st, end_col, nblk, a.scale_log2);
-    t0 = t2;
-  }
-
-  // every wave's (m, l, o) per block and column into LDS (inactive waves and
-  // blocks contribute the empty state), then each output element combines the
-  // token groups of its column group
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(rows_lds_void_t*)&sh.ring[0][0]);
+  // per-lane LDS byte offsets of the operand reads within a step
+  uint32_t koff[2];
 #pragma unroll
-  for (int j = 0; j < BPW; ++j) {
-    const float l = sum_xor32(sum_xor16(st.l[j]));
-    if (c.g == 0) {
-      sh.m_lds[wave][j][c.r16] = j < nblk ? st.m[j] : -INFINITY;
-      sh.l_lds[wave][j][c.r16] = j < nblk ? l : 0.f;
+  for (int blk = 0; blk < 2; ++blk) koff[blk] = (uint32_t)((g * 32 + 16 * blk + r16) * 16);
+  uint32_t voff[2][D / 16];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) {
+      const int d = 16 * nb + r16, tg = 4 * blk + g;
+      voff[blk][nb] = (uint32_t)(kKeyBytes<D> + nb * kVGroupBytes + r16 * 64 + ((tg ^ (2 * ((d >> 2) & 3))) * 8));
+      // opaque to the compiler, so that it does not pair two of these reads
+      __asm__ __volatile__("" : "+v"(voff[blk][nb]));
     }
+
+  const int nsteps = end > t.lo ? (end - t.lo + kStep - 1) / kStep : 0;
+  bool bad = false;
+  StepPages pg{0, 0};   // page ids of the next step to send
+  if (nsteps > 0) pg = step_pages(a, ptab, t.lo, end);
 #pragma unroll
-    for (int nb = 0; nb < D / 16; ++nb)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sh.o_lds[wave][j][c.r16][16 * nb + 4 * c.g + e] = st.o[j][nb][e];
+  for (int i = 0; i < kRing - 1; ++i) {
+    if (i < nsteps) {
+      RowsDma<D> dm;
+      bad |= dm.prepare(a, pg, t.kvh, t.lo + i * kStep, wave, lane);
+      dm.issue(ring_lds + (uint32_t)(i * kStepBytes<D>), wave);
+      pg = step_pages(a, ptab, t.lo + (i + 1) * kStep, end);   // clamped: always a valid entry
+    }
   }
-  if (lane == 0) sh.bad_lds[wave] = bad;
-  __syncthreads();
-  if (sh.bad_lds[0] | sh.bad_lds[1] | sh.bad_lds[2] | sh.bad_lds[3]) {
+  for (int k = 0; k < nsteps; ++k) {
+    // step k has landed for this wave (its DMAs retire in order), then for all
+    rows_wait_ahead<D>(min(kRing - 2, nsteps - 1 - k));
+    rows_barrier();
+    // the DMA of step k + kRing - 1, into the buffer step k - 1 left (every
+    // wave has passed this barrier, so its reads of that step are done)
+    if (k + kRing - 1 < nsteps) {
+      RowsDma<D> dm;
+      bad |= dm.prepare(a, pg, t.kvh, t.lo + (k + kRing - 1) * kStep, wave, lane);
+      dm.issue(ring_lds + (uint32_t)(((k + kRing - 1) % kRing) * kStepBytes<D>), wave);
+      pg = step_pages(a, ptab, t.lo + (k + kRing) * kStep, end);
+    }
+    if (nblk == 0) continue;   // wave-uniform: this wave's rows are past the task's
+    const uint8_t* st = sh.ring[k % kRing];
+    const int t0 = t.lo + k * kStep;
+    // key fragments of both token blocks and value fragments
+    u32x4_t kf[2][D / 32];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int m = 0; m < D / 32; ++m)
+        kf[blk][m] = *reinterpret_cast<const u32x4_t*>(st + koff[blk] + 4 * 32 * 16 * m);
+    u32x2_t vf[2][D / 16];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) vf[blk][nb] = *reinterpret_cast<const u32x2_t*>(st + voff[blk][nb]);
+    // values past `end` hold stale or poisoned page data: zero them, so that
+    // 0 * NaN cannot reach the accumulators
+    if (t0 + kStep > end) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int nv = end - (t0 + 16 * blk + 4 * g);   // valid tokens among the lane's 4
+        if (nv < 4) {
+          const uint32_t m0 = nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0x0000FFFFu : 0u);
+          const uint32_t m1 = nv >= 4 ? 0xFFFFFFFFu : (nv == 3 ? 0x0000FFFFu : 0u);
+#pragma unroll
+          for (int nb = 0; nb < D / 16; ++nb) {
+            vf[blk][nb][0] &= m0;
+            vf[blk][nb][1] &= m1;
+          }
+        }
+      }
+    }
+    // both blocks always (a block past the task's rows computes on copies of
+    // its last row and is not written): one straight-line body, in which the
+    // compiler can overlap one block's softmax with the other's products
+#pragma unroll
+    for (int j = 0; j < kRowsBPW; ++j) {
+      f32x4_t sc[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < D / 32; ++m) acc = mfma16(kf[blk][m], qf[j][m], acc);
+        sc[blk] = acc;
+      }
+      float sv[8];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tok = t0 + 16 * blk + 4 * g + e;
+          sv[4 * blk + e] = tok < end_col[j] ? sc[blk][e] * a.scale_log2 : -INFINITY;
+        }
+      float mt = sv[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
+      mt = max_xor32(max_xor16(mt));
+      const float mn = fmaxf(mrow[j], mt);
+      // a column may see no key yet (its end precedes this step): keep a
+      // finite reference so that its weights are exp2(-inf) = 0, not NaN
+      const float mref = mn == -INFINITY ? 0.f : mn;
+      const float alpha = fast_exp2(mrow[j] - mref);
+      mrow[j] = mn;
+      float p[8], ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        p[i] = fast_exp2(sv[i] - mref);
+        ps += p[i];
+      }
+      lrow[j] = lrow[j] * alpha + ps;
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
+      const u32x4_t pf_hi = {ph[0], ph[1], ph[2], ph[3]};
+      const u32x4_t pf_lo = {pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+      for (int nb = 0; nb < D / 16; ++nb) {
+        o[j][nb] *= alpha;
+        const u32x4_t vv = {vf[0][nb][0], vf[0][nb][1], vf[1][nb][0], vf[1][nb][1]};
+        o[j][nb] = mfma16(vv, pf_hi, o[j][nb]);
+        o[j][nb] = mfma16(vv, pf_lo, o[j][nb]);
+      }
+    }
+  }
+  // every wave's DMAs have landed before the work-group leaves its LDS
+  __builtin_amdgcn_s_waitcnt(kRowsWaitVm<0>);
+  // a bad page id is seen by every wave that prepared a DMA of it; any wave
+  // that saw one makes the whole task NaN
+  const bool any_bad = __syncthreads_or(bad);
+  if (any_bad) {
+    if (threadIdx.x == 0) raise_error(a.err_flag, kErrPageId);
     rows_nan<D>(a, t);
     return;
   }
-  for (int i = threadIdx.x; i < R * D; i += 256) {
-    const int r = i / D, d = i - r * D;
-    const int bi = r >> 4, col = r & 15, gcol = bi / BPW, j = bi % BPW;
-    float M = -INFINITY;
-    for (int w = gcol; w < gcol + CG * TG; w += CG) M = fmaxf(M, sh.m_lds[w][j][col]);
-    float Z = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-      for (int w = gcol; w < gcol + CG * TG; w += CG) {
-        const float scl = fast_exp2(sh.m_lds[w][j][col] - M);
-        Z += scl * sh.l_lds[w][j][col];
-        acc += scl * sh.o_lds[w][j][col][d];
-      }
-    }
+#pragma unroll
+  for (int j = 0; j < kRowsBPW; ++j) {
+    if (j >= nblk) break;
+    const int r = 16 * (kRowsBPW * wave + j) + r16;
+    const float l = sum_xor32(sum_xor16(lrow[j]));
+    if (r >= R) continue;
     const int tok = r / G, h = r - tok * G;
     const int64_t row = (int64_t)t.out_row + (int64_t)tok * a.H_q + h;
-    a.o_part[row * D + d] = M == -INFINITY ? 0.f : acc / Z;
-    if (d == 0) a.lse_part[row] = M == -INFINITY ? -INFINITY : (M + fast_log2(Z)) * kLn2;
+    const bool empty = mrow[j] == -INFINITY;
+    const float inv = empty ? 0.f : 1.f / l;
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb)
+      *reinterpret_cast<f32x4_t*>(a.o_part + row * D + 16 * nb + 4 * g) = o[j][nb] * inv;
+    if (g == 0) a.lse_part[row] = empty ? -INFINITY : (mrow[j] + fast_log2(l)) * kLn2;
   }
 }
 
 // Multi-token tasks: one work-group per task, in the plan's queue order.
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gqa_rows_kernel(MfmaArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void gqa_rows_kernel(MfmaArgs a) {
   __shared__ RowsShared<D> sh;
   gqa_rows_task<D>(a, a.tasks[blockIdx.x], sh);
 }
 
 // Multi-token tasks with the merge in the same launch (fused.hpp).
 template <int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gqa_rows_fused(MfmaArgs a, FusedArgs f) {
   __shared__ RowsShared<D> sh;
   __shared__ int slot;
