@@ -129,6 +129,52 @@ def test_coverage_probe_recovers_split_ranges(dtype, G, P):
             assert np.array_equal(got, np.broadcast_to(want, got.shape)), (b, r)
 
 
+@pytest.mark.parametrize("q_lens", [None, [1, 5, 3, 1, 17]], ids=["decode", "chunk-rows"])
+def test_coverage_probe_token_index_values(q_lens):
+    # fp32, q = 0: every visible key gets weight 1. Values V[j, 0] = j and
+    # V[j, 1] = j^2 (exact in fp32 for these lengths), the rest 1: a split over
+    # [a, e) must give O[0] = mean(j), O[1] = mean(j^2), LSE = ln(e - a), and
+    # the merged row of query token i (visible end v) mean(j) and mean(j^2)
+    # over [0, v) - a skipped, repeated or shifted token changes both.
+    seq = [1000, 2049, 65, 129, 4000]
+    w = small("f32", 8, 2, 64, 16, seq, q_lens=q_lens, seed=19)
+    w.q[...] = 0
+    for b, L in enumerate(seq):
+        j = np.arange(L, dtype=np.float64)
+        vals = np.ones((L, w.num_kv_heads, w.head_dim_v), np.float32)
+        vals[:, :, 0] = j[:, None]
+        vals[:, :, 1] = (j * j)[:, None]
+        wl.set_logical_values(w, b, vals)
+    plan = skv.plan_from_counts(w.seq_lens, spec_of(w), [3, 7, 2, 1, 13], q_lens=w.q_lens)
+    o_part, lse_part, o, lse = run_path(w, plan)
+    e = plan.export()
+    H = w.num_q_heads
+    qoff = np.concatenate([[0], np.cumsum(w.q_lens)])
+    for b, L in enumerate(seq):
+        n = int(w.q_lens[b])
+        off = int(e["state_row_offset"][b])
+        for r, (a, en) in enumerate(plan.ranges()[b]):
+            for i in range(n):
+                vis = L - n + i + 1
+                lo, hi = a, min(en, vis)
+                rows = slice(off + (r * n + i) * H, off + (r * n + i + 1) * H)
+                if hi <= lo:
+                    assert np.all(np.isneginf(lse_part[rows])) and np.all(o_part[rows] == 0)
+                    continue
+                jj = np.arange(lo, hi, dtype=np.float64)
+                assert np.allclose(lse_part[rows], np.log(hi - lo), rtol=0, atol=1e-5), (b, r, i)
+                assert np.allclose(o_part[rows, 0], jj.mean(), rtol=1e-5, atol=0), (b, r, i)
+                assert np.allclose(o_part[rows, 1], (jj * jj).mean(), rtol=1e-5, atol=0), (b, r, i)
+                assert np.all(o_part[rows, 2:] == 1.0)
+        for i in range(n):
+            vis = L - n + i + 1
+            jj = np.arange(vis, dtype=np.float64)
+            rows = slice((int(qoff[b]) + i) * H, (int(qoff[b]) + i + 1) * H)
+            assert np.allclose(lse[rows], np.log(vis), rtol=0, atol=1e-5)
+            assert np.allclose(o[rows, 0], jj.mean(), rtol=1e-5, atol=0), (b, i)
+            assert np.allclose(o[rows, 1], (jj * jj).mean(), rtol=1e-5, atol=0), (b, i)
+
+
 def test_merge_external_states():
     w = small("f32", 8, 2, 64, 16, [300, 1000, 17], seed=4, n_ext=5)
     check_all(w, skv.plan_from_counts(w.seq_lens, spec_of(w), [2, 4, 1], n_ext=5))

@@ -125,6 +125,38 @@ def test_random_batches_bit_exact(seed):
     assert_same(plan, pb, prm, ev, ns)
 
 
+@pytest.mark.parametrize("chunk", range(10))
+def test_small_random_batches_bit_exact(chunk):
+    # 1,000 small batches in all (100 per case), C++ = Python bit for bit:
+    # 1-6 requests of 1-3,000 tokens, some with several query tokens, every
+    # kernel's shape, 1-8 CUs (so that K is small and the search takes many
+    # steps), both reduction models, random caps, calibrated or random model
+    # parameters, forced query tiles where the kernel runs them
+    for seed in range(100 * chunk, 100 * (chunk + 1)):
+        rng = np.random.default_rng(50000 + seed)
+        spec = SPECS[int(rng.integers(0, len(SPECS)))]
+        B = int(rng.integers(1, 7))
+        seq = rng.integers(1, 3001, size=B)
+        q = np.ones(B, np.int64)
+        if rng.random() < 0.3:
+            k = int(rng.integers(0, B))
+            q[k] = min(int(seq[k]), int(rng.integers(2, 40)))
+        p = skv.default_params()
+        p.overlap_reduction = int(rng.integers(0, 2))
+        p.max_splits = int(rng.choice([2, 4, 8, 16, 64]))
+        if rng.random() < 0.5:
+            p.use_calibration = 0
+            p.rho, p.delta_attn = float(rng.uniform(0.1, 1.0)), float(rng.integers(0, 8))
+            p.delta_red, p.gamma = float(rng.uniform(0, 3)), float(rng.uniform(0, 1))
+        if kernel_tile(spec) > 1 and rng.random() < 0.3:
+            p.query_tile = int(rng.integers(1, kernel_tile(spec) + 1))
+        num_cu = int(rng.choice([1, 2, 4, 8]))
+        n_ext = int(rng.integers(0, 3))
+        plan = skv.plan_splits(seq, spec, num_cu=num_cu, q_lens=q, n_ext=n_ext, params=p)
+        pb, prm, ev, ns = reference_for(plan, spec, seq, q, n_ext, p)
+        assert_same(plan, pb, prm, ev, ns)
+
+
 @pytest.mark.parametrize("cid", [1, 2, 5])
 def test_benchmark_workloads_bit_exact(cid):
     # (workloads 3-6 at the default split cap: test_default_cap_large_workloads_bit_exact)
