@@ -226,7 +226,8 @@ QOrder queue_order(const Problem& pb, const std::vector<int>& splits) {
 }
 
 struct SimScratch {
-  std::vector<double> done_fw, ev_fw, ev_t, done;
+  std::vector<double> done_fw, ev_fw, ev_t, done, sufmax;
+  std::vector<size_t> seg_base;
   std::vector<Group> heap;
   std::vector<std::pair<double, int64_t>> warps;   // min-heap of (free time, warps)
   std::vector<QEntry> tmp;
@@ -237,6 +238,7 @@ struct SimScratch {
 struct SimResult {
   double score = 0, t_attn = 0;
   int64_t n_tasks = 0;
+  bool cut = false;   // abandoned: its score exceeds the cutoff
 };
 
 bool warp_later(const std::pair<double, int64_t>& x, const std::pair<double, int64_t>& y) {
@@ -270,15 +272,59 @@ struct Recording {
 // receives the requests whose attention ends at the attention completion.
 // With `from`, the run continues from a snapshot of the recording `base`; with
 // `rec` (non-overlapped model only), it records snapshots for rec->thresholds.
+// With `cutoff` (non-overlapped model only), the run is abandoned (cut) as
+// soon as a lower bound on its score exceeds *cutoff (a score that some other
+// run has reached): the time so far; plus the remaining attention time, at
+// least the remaining task cost (unstarted, and the rest of the running ones)
+// over K, since attention advances by at most K tile units per time unit, and
+// at least rho times the largest remaining cost of one task (an unstarted one,
+// or the rest of the last running one), since a task advances by at most
+// 1 / rho per time unit; plus the reduction phase's lower bound (the largest
+// unit cost, and the summed unit cost over K x W warps: every unit starts
+// after attention).
 SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits,
                          const Seg* segs, size_t nseg, SimScratch& sc, std::vector<int>* tail,
                          const Snapshot* from = nullptr, const Recording* base = nullptr,
-                         Recording* rec = nullptr, int run_hint = 0) {
+                         Recording* rec = nullptr, int run_hint = 0,
+                         const std::atomic<double>* cutoff = nullptr) {
   const int B = (int)pb.seq_lens.size();
   const int64_t K = prm.slots;
   int64_t nt = 0;
   for (size_t i = 0; i < nseg; ++i)
     for (size_t j = 0; j < segs[i].n; ++j) nt += segs[i].p[j].count;
+  const int run = run_hint > 0 ? run_hint : reduction_run(pb, prm);
+  double w_left = 0, red_lb = 0;   // unstarted task cost; reduction-phase bound
+  double w_end = 0, fw_max = 0;    // running groups: sum of count x finish, latest finish
+  std::vector<size_t>& seg_base = sc.seg_base;
+  std::vector<double>& sufmax = sc.sufmax;   // largest cost from each queue position on
+  if (cutoff) {
+    seg_base.assign(nseg + 1, 0);
+    for (size_t i = 0; i < nseg; ++i) seg_base[i + 1] = seg_base[i] + segs[i].n;
+    sufmax.assign(seg_base[nseg] + 1, 0.0);
+    for (size_t i = nseg; i-- > 0;)
+      for (size_t j = segs[i].n; j-- > 0;)
+        sufmax[seg_base[i] + j] = std::max(sufmax[seg_base[i] + j + 1], segs[i].p[j].cost);
+    const size_t s0 = from ? from->si : 0, e0 = from ? from->ei : 0;
+    for (size_t i = s0; i < nseg; ++i)
+      for (size_t j = i == s0 ? e0 : 0; j < segs[i].n; ++j)
+        w_left += segs[i].p[j].cost * (double)segs[i].p[j].count;
+    if (from && s0 < nseg && e0 < segs[s0].n) w_left -= segs[s0].p[e0].cost * (double)from->off;
+    if (from)
+      for (const Group& gr : from->heap) {
+        w_end += gr.fw * (double)gr.n;
+        fw_max = std::max(fw_max, gr.fw);
+      }
+    double rmax = 0, rsum = 0;
+    for (int b = 0; b < B; ++b) {
+      const int64_t rows = pb.q_lens[b] * (int64_t)pb.rows_per_token;
+      const double s_u = (double)(splits[b] + pb.n_ext);
+      const int64_t full = rows / run, rem = rows % run;
+      rsum += (double)full * (prm.delta_red + prm.gamma * (double)run * s_u);
+      if (rem > 0) rsum += prm.delta_red + prm.gamma * (double)rem * s_u;
+      rmax = std::max(rmax, prm.delta_red + prm.gamma * (double)(rows >= run ? run : rows) * s_u);
+    }
+    red_lb = std::max(rmax, rsum / ((double)K * (double)prm.warps_per_slot));
+  }
 
   // ---- attention phase ----
   sc.ev_fw.clear();
@@ -287,6 +333,10 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
   auto heap_push = [&](double fw, int64_t n) {
     sc.heap.push_back({fw, n});
     std::push_heap(sc.heap.begin(), sc.heap.end(), std::greater<Group>());
+    if (cutoff) {
+      w_end += fw * (double)n;
+      fw_max = std::max(fw_max, fw);
+    }
   };
   double t = 0.0, vw = 0.0;
   int64_t running = 0, started_total = 0;
@@ -350,6 +400,7 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
         }
       }
       heap_push(fw, taken);
+      if (cutoff) w_left -= c * (double)taken;
       started += taken;
       started_total += taken;
     }
@@ -394,7 +445,21 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
     step(K);
     if (prm.overlap_reduction && K > nt) release[0.0] += (K - nt) * prm.warps_per_slot;
   }
+  uint32_t n_events = 0;
   while (!sc.heap.empty()) {
+    if (cutoff && (++n_events & 15) == 0) {
+      const double bst = cutoff->load(std::memory_order_relaxed);
+      const double c_next = si < nseg ? sufmax[seg_base[si] + ei] : 0.0;
+      const double rest = std::max((w_left + (w_end - (double)running * vw)) / (double)K,
+                                   prm.rho * std::max(c_next, fw_max - vw));
+      if (t + rest + red_lb > bst + 1e-9 * std::fabs(bst)) {
+        SimResult cut;
+        cut.score = cut.t_attn = INFINITY;
+        cut.n_tasks = nt;
+        cut.cut = true;
+        return cut;
+      }
+    }
     const double tau = std::max(prm.rho, (double)running / (double)K);
     const double fw = sc.heap.front().fw;
     t = t + (fw - vw) * tau;
@@ -402,6 +467,7 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
     int64_t m = 0;
     while (!sc.heap.empty() && sc.heap.front().fw == fw) {
       m += sc.heap.front().n;
+      if (cutoff) w_end -= fw * (double)sc.heap.front().n;
       std::pop_heap(sc.heap.begin(), sc.heap.end(), std::greater<Group>());
       sc.heap.pop_back();
     }
@@ -435,7 +501,6 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
   // ---- reduction phase: units in request order, each on the earliest-free warp ----
   // (a heap of (free time, count) groups; equal times need not be merged, since
   // every unit still starts at the earliest free time)
-  const int run = run_hint > 0 ? run_hint : reduction_run(pb, prm);
   const int64_t nwarps = K * prm.warps_per_slot;
   auto& wh = sc.warps;
   wh.clear();
@@ -528,6 +593,18 @@ Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector
   return to_eval(splits, r, std::move(tail));
 }
 
+// The same with a cutoff (non-overlapped model): false if the run was cut.
+static bool simulate_below(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits,
+                           const std::atomic<double>& cutoff, Evaluation& out) {
+  thread_local SimScratch sc;
+  build_queue(pb, prm, splits, sc);
+  const SimResult r = simulate_queue(pb, prm, splits, sc.segs.data(), sc.segs.size(), sc, nullptr, nullptr,
+                                     nullptr, nullptr, 0, &cutoff);
+  if (r.cut) return false;
+  out = to_eval(splits, r, {});
+  return true;
+}
+
 static bool key_less(const Evaluation& a, const Evaluation& b) {
   return std::tie(a.score, a.t_attn, a.n_tasks, a.total_splits) <
          std::tie(b.score, b.t_attn, b.n_tasks, b.total_splits);
@@ -550,14 +627,17 @@ static SimPool& sim_pool() {
 // A lower bound on a plan's score in the non-overlapped model. However many
 // slots run, attention advances by at most K tile units per time unit
 // (k / tau(k) <= K), so the attention completion is at least the summed task
-// cost over K; every reduction starts after it, on K x W warps. A query
-// token's splits cover its visible tiles once, so the task cost sums to
-// heads x visible tiles + delta_attn per task.
+// cost over K; and a task of cost c runs at least rho c (tau >= rho), so it is
+// at least rho times the largest task cost (a request's first split, which
+// its last query token sees whole). Every reduction starts after it, on K x W
+// warps: the score adds at least the summed unit cost over K x W and the
+// largest unit cost. A query token's splits cover its visible tiles once, so
+// the task cost sums to heads x visible tiles + delta_attn per task.
 static double score_lower_bound(const Problem& pb, const ModelParams& prm,
                                 const std::vector<int>& splits) {
   const int T = prm.tile_tokens;
   const int run = reduction_run(pb, prm);
-  double w = 0, r = 0;
+  double w = 0, r = 0, tmax = 0, rmax = 0;
   for (size_t b = 0; b < splits.size(); ++b) {
     const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
     const int qt = pb.query_tile;
@@ -566,13 +646,16 @@ static double score_lower_bound(const Problem& pb, const ModelParams& prm,
       vis_tiles += n_tiles(pb.causal ? L - n + qtile_last(n, qt, qi) + 1 : L, T);
     w += (double)pb.num_kv_heads *
          ((double)vis_tiles + prm.delta_attn * (double)num_qtiles(n, qt) * (double)splits[b]);
+    tmax = std::max(tmax, (double)((n_tiles(L, T) + splits[b] - 1) / splits[b]) + prm.delta_attn);
     const int64_t rows = n * (int64_t)pb.rows_per_token;
     const double s_u = (double)(splits[b] + pb.n_ext);
     const int64_t full = rows / run, rem = rows % run;
     r += (double)full * (prm.delta_red + prm.gamma * (double)run * s_u);
     if (rem > 0) r += prm.delta_red + prm.gamma * (double)rem * s_u;
+    rmax = std::max(rmax, prm.delta_red + prm.gamma * (double)(rows >= run ? run : rows) * s_u);
   }
-  return w / (double)prm.slots + r / ((double)prm.slots * (double)prm.warps_per_slot);
+  const double K = (double)prm.slots;
+  return std::max(prm.rho * tmax, w / K) + std::max(rmax, r / (K * (double)prm.warps_per_slot));
 }
 
 // Stand-in for the pages' FA3-derived reference plan (FA3's heuristic is not
@@ -605,7 +688,7 @@ std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
       const int u = order[i] + 1;
       const double bst = best.load();
       if (lb[u - 1] > bst + 1e-9 * std::fabs(bst)) return;
-      evs[u - 1] = simulate(pb, prm, uniform_plan(pb, prm, u));
+      if (!simulate_below(pb, prm, uniform_plan(pb, prm, u), best, evs[u - 1])) return;
       done[u - 1] = 1;
       double cur = best.load();
       while (evs[u - 1].score < cur && !best.compare_exchange_weak(cur, evs[u - 1].score)) {
@@ -800,8 +883,61 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
     }
     return p;
   };
-  auto eval_cand = [&](const std::vector<int>& clist, CandScratch& cs, bool use_snapshot) {
+  // A chunk request's candidate (chunk-first order) changes the queue's first
+  // segments, so the current plan's recording cannot shorten its run. It keeps
+  // a recording of its own last full run instead, with snapshots before the
+  // first run of every later segment: while the request's own count stays,
+  // a later run agrees with the recorded queue up to the first segment whose
+  // request has changed since, and resumes there (or repeats the recorded
+  // result when none has). Each candidate touches only its own entry.
+  struct OwnRecording {
+    bool valid = false;
+    std::vector<int> splits;   // the candidate's split counts when recorded
+    Recording rec;
+    SimResult res;
+  };
+  std::vector<OwnRecording> own(resume && !decode_only ? B : 0);
+  auto eval_own = [&](int c, CandScratch& cs, const std::atomic<double>* cutoff) {
+    OwnRecording& o = own[c];
+    if (o.valid && o.splits[c] == cs.splits[c]) {
+      int64_t pos = 0, p = -1;
+      for (const Seg& sg : cs.segs) {
+        const int r = sg.p[0].req;
+        if (r != c && o.splits[r] != cs.splits[r]) {
+          p = pos;
+          break;
+        }
+        pos += (int64_t)sg.n;
+      }
+      if (p < 0) return o.res;
+      const size_t k = std::lower_bound(o.rec.thresholds.begin(), o.rec.thresholds.end(), p) -
+                       o.rec.thresholds.begin();
+      if (k < o.rec.thresholds.size() && o.rec.thresholds[k] == p)
+        return simulate_queue(pb, prm, cs.splits, cs.segs.data(), cs.segs.size(), cs.sim, nullptr,
+                              &o.rec.snaps[o.rec.snap_of[k]], &o.rec, nullptr, red_run, cutoff);
+    }
+    // record a full run: thresholds at the segments after c's own
+    o.rec.thresholds.clear();
+    int64_t pos = 0;
+    bool after = false;
+    for (const Seg& sg : cs.segs) {
+      if (after) o.rec.thresholds.push_back(pos);
+      after |= sg.p[0].req == c;
+      pos += (int64_t)sg.n;
+    }
+    o.res = simulate_queue(pb, prm, cs.splits, cs.segs.data(), cs.segs.size(), cs.sim, nullptr, nullptr,
+                           nullptr, &o.rec, red_run);
+    o.splits = cs.splits;
+    o.valid = true;
+    return o.res;
+  };
+  // cutoff (non-overlapped model): the best score found so far among this
+  // round's candidates; a run that cannot beat it is cut (and not picked)
+  auto eval_cand = [&](const std::vector<int>& clist, CandScratch& cs, bool use_snapshot,
+                       const std::atomic<double>* cutoff) {
     const int64_t p = build_cand(clist, cs);
+    if (use_snapshot && !own.empty() && clist.size() == 1 && !is_decode(pb.q_lens[clist[0]]))
+      return eval_own(clist[0], cs, cutoff);
     const Snapshot* from = nullptr;
     if (use_snapshot) {
       const size_t k = std::lower_bound(rec.thresholds.begin(), rec.thresholds.end(), p) -
@@ -809,33 +945,104 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
       from = &rec.snaps[rec.snap_of[k]];
     }
     return simulate_queue(pb, prm, cs.splits, cs.segs.data(), cs.segs.size(), cs.sim, nullptr, from,
-                          from ? &rec : nullptr, nullptr, red_run);
+                          from ? &rec : nullptr, nullptr, red_run, cutoff);
   };
   CandScratch adopt;
 
-  // Lower bound on a candidate's score in the non-overlapped model: a task of
-  // cost c takes at least rho c (tau >= rho), so attention ends no earlier
-  // than rho times the largest task cost (a request's first split, which its
-  // last query token sees whole: ceil(tiles / s) + delta_attn); every
-  // reduction unit starts after attention, so the score is at least that
-  // plus the largest unit cost.
+  // Lower bound on a candidate's score in the non-overlapped model.
+  // Attention: a task of cost c takes at least rho c (tau >= rho), so it ends
+  // no earlier than rho times the largest task cost (a request's first split,
+  // which its last query token sees whole: ceil(tiles / s) + delta_attn); and
+  // attention advances by at most K tile units per time unit (k / tau(k) <= K),
+  // so it ends no earlier than the summed task cost over K. Reduction: every
+  // unit starts after attention (the warps are released at its end), so the
+  // score adds at least the largest unit cost and the summed unit cost over
+  // K x W warps. A query tile's splits cover its visible tiles once, so a
+  // request's task cost sums to KV heads x (visible tiles + delta_attn x
+  // query tiles x splits).
   const bool bound = !prm.overlap_reduction;
-  std::vector<int64_t> tiles_of(B);
-  for (int b = 0; b < B; ++b) tiles_of[b] = n_tiles(pb.seq_lens[b], prm.tile_tokens);
+  std::vector<int64_t> tiles_of(B), vis_of(B), qtiles_of(B);
+  for (int b = 0; b < B; ++b) {
+    tiles_of[b] = n_tiles(pb.seq_lens[b], prm.tile_tokens);
+    const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
+    qtiles_of[b] = num_qtiles(n, pb.query_tile);
+    vis_of[b] = 0;
+    for (int64_t qi = 0; qi < qtiles_of[b]; ++qi)
+      vis_of[b] += n_tiles(pb.causal ? L - n + qtile_last(n, pb.query_tile, qi) + 1 : L, prm.tile_tokens);
+  }
   auto task_max = [&](int b, int s) { return (double)((tiles_of[b] + s - 1) / s) + prm.delta_attn; };
   auto red_max = [&](int b, int s) {
     const int64_t rows = pb.q_lens[b] * (int64_t)pb.rows_per_token;
     const int64_t unit = rows >= red_run ? red_run : rows;
     return prm.delta_red + prm.gamma * (double)unit * (double)(s + pb.n_ext);
   };
-  auto cand_bound = [&](const std::vector<int>& clist) {
-    double tm = 0, rm = 0;
-    for (int b = 0; b < B; ++b) {
-      const int s = cur.splits[b] + (std::find(clist.begin(), clist.end(), b) != clist.end() ? 1 : 0);
-      tm = std::max(tm, task_max(b, s));
-      rm = std::max(rm, red_max(b, s));
+  auto work_of = [&](int b, int s) {
+    return (double)pb.num_kv_heads *
+           ((double)vis_of[b] + prm.delta_attn * (double)qtiles_of[b] * (double)s);
+  };
+  auto red_of = [&](int b, int s) {
+    const int64_t rows = pb.q_lens[b] * (int64_t)pb.rows_per_token;
+    const double s_u = (double)(s + pb.n_ext);
+    const int64_t full = rows / red_run, rem = rows % red_run;
+    double r = (double)full * (prm.delta_red + prm.gamma * (double)red_run * s_u);
+    if (rem > 0) r += prm.delta_red + prm.gamma * (double)rem * s_u;
+    return r;
+  };
+  // the current plan's terms: totals, and the two largest per-request maxima
+  // (a one-request candidate's maximum over the other requests is the
+  // largest one not its own)
+  struct Top2 {
+    double v1 = -INFINITY, v2 = -INFINITY;
+    int i1 = -1;
+    void add(double v, int i) {
+      if (v > v1) {
+        v2 = v1;
+        v1 = v;
+        i1 = i;
+      } else if (v > v2) {
+        v2 = v;
+      }
     }
-    return prm.rho * tm + rm;
+    double without(int i) const { return i == i1 ? v2 : v1; }
+  };
+  Top2 t_top, r_top;
+  double w_tot = 0, r_tot = 0;
+  auto bound_terms = [&] {
+    t_top = Top2{};
+    r_top = Top2{};
+    w_tot = r_tot = 0;
+    for (int b = 0; b < B; ++b) {
+      t_top.add(task_max(b, cur.splits[b]), b);
+      r_top.add(red_max(b, cur.splits[b]), b);
+      w_tot += work_of(b, cur.splits[b]);
+      r_tot += red_of(b, cur.splits[b]);
+    }
+  };
+  std::vector<uint8_t> in_cand(B, 0);
+  auto cand_bound = [&](const std::vector<int>& clist) {
+    double tm, rm, w = w_tot, r = r_tot;
+    if (clist.size() == 1) {
+      const int c = clist[0], s = cur.splits[c];
+      tm = std::max(t_top.without(c), task_max(c, s + 1));
+      rm = std::max(r_top.without(c), red_max(c, s + 1));
+      w += work_of(c, s + 1) - work_of(c, s);
+      r += red_of(c, s + 1) - red_of(c, s);
+    } else {
+      for (int b : clist) in_cand[b] = 1;
+      tm = rm = -INFINITY;
+      for (int b = 0; b < B; ++b) {
+        const int s = cur.splits[b] + in_cand[b];
+        tm = std::max(tm, task_max(b, s));
+        rm = std::max(rm, red_max(b, s));
+      }
+      for (int b : clist) {
+        w += work_of(b, cur.splits[b] + 1) - work_of(b, cur.splits[b]);
+        r += red_of(b, cur.splits[b] + 1) - red_of(b, cur.splits[b]);
+        in_cand[b] = 0;
+      }
+    }
+    const double K = (double)prm.slots;
+    return std::max(prm.rho * tm, w / K) + std::max(rm, r / (K * (double)prm.warps_per_slot));
   };
 
   for (;;) {
@@ -860,6 +1067,7 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
     if (bound) {
       std::vector<double> lb(nc);
       std::vector<uint32_t> order(nc);
+      bound_terms();
       for (size_t i = 0; i < nc; ++i) {
         lb[i] = cand_bound(cands[i]);
         order[i] = (uint32_t)i;
@@ -872,7 +1080,8 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
         const double bs = best_score.load();
         if (lb[i] > bs + 1e-9 * std::fabs(bs)) return;
         thread_local CandScratch cs;
-        res[i] = eval_cand(cands[i], cs, resume);
+        res[i] = eval_cand(cands[i], cs, resume, &best_score);
+        if (res[i].cut) return;
         done[i] = 1;
         double c = best_score.load();
         while (res[i].score < c && !best_score.compare_exchange_weak(c, res[i].score)) {
@@ -881,7 +1090,7 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
     } else {
       pool.run(nc, [&](size_t i) {
         thread_local CandScratch cs;
-        res[i] = eval_cand(cands[i], cs, resume);
+        res[i] = eval_cand(cands[i], cs, resume, nullptr);
       });
     }
     const int64_t tot = cur.total_splits;

@@ -157,6 +157,34 @@ def test_small_random_batches_bit_exact(chunk):
         assert_same(plan, pb, prm, ev, ns)
 
 
+@pytest.mark.parametrize("seed", range(24))
+def test_several_chunk_requests_bit_exact(seed):
+    # batches with 2-4 chunk requests (more than 16 query tokens) among decode
+    # requests, on few CUs so that the search takes many steps: a chunk
+    # request's candidate resumes from its own earlier run after other
+    # requests (before or after it in the chunk-first queue) have changed
+    rng = np.random.default_rng(7000 + seed)
+    spec = SPECS[[0, 2, 3][seed % 3]]
+    n_chunk = int(rng.integers(2, 5))
+    B = n_chunk + int(rng.integers(1, 6))
+    seq = rng.integers(200, 6000, size=B)
+    q = np.ones(B, np.int64)
+    for k in rng.choice(B, size=n_chunk, replace=False):
+        q[k] = min(int(seq[k]), int(rng.integers(17, 48)))
+    p = skv.default_params()
+    p.overlap_reduction = 0
+    p.max_splits = int(rng.choice([4, 8, 16]))
+    if seed % 2:
+        p.use_calibration = 0
+        p.rho, p.delta_attn = float(rng.uniform(0.2, 1.0)), float(rng.integers(0, 6))
+        p.delta_red, p.gamma = float(rng.uniform(0, 2)), float(rng.uniform(0, 0.5))
+    num_cu = int(rng.choice([2, 4, 8, 16]))
+    n_ext = int(rng.integers(0, 3))
+    plan = skv.plan_splits(seq, spec, num_cu=num_cu, q_lens=q, n_ext=n_ext, params=p)
+    pb, prm, ev, ns = reference_for(plan, spec, seq, q, n_ext, p)
+    assert_same(plan, pb, prm, ev, ns)
+
+
 @pytest.mark.parametrize("cid", [1, 2, 5])
 def test_benchmark_workloads_bit_exact(cid):
     # (workloads 3-6 at the default split cap: test_default_cap_large_workloads_bit_exact)
