@@ -341,6 +341,7 @@ skv_status skv_plan_splits(const skv_attn_desc* desc, const int32_t* seq_lens, c
   try {
     const int B = desc->batch;
     std::vector<int> ref;
+    Evaluation ref_ev;
     if (ref_splits) {
       ref.assign(ref_splits, ref_splits + B);
       for (int b = 0; b < B; ++b) {
@@ -351,10 +352,10 @@ skv_status skv_plan_splits(const skv_attn_desc* desc, const int32_t* seq_lens, c
         }
       }
     } else {
-      ref = reference_plan(pl->pb, pl->prm);
+      ref = reference_plan(pl->pb, pl->prm, &ref_ev);
     }
     Evaluation ns;
-    Evaluation ev = plan_search(pl->pb, pl->prm, ref, &ns);
+    Evaluation ev = plan_search(pl->pb, pl->prm, ref, &ns, ref_splits ? nullptr : &ref_ev);
     pl->score = ev.score;
     pl->t_attn = ev.t_attn;
     pl->nosplit_score = ns.score;

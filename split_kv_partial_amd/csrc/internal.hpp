@@ -106,11 +106,13 @@ void build_tasks(const Problem& pb, const ModelParams& prm,
 int reduction_run(const Problem& pb, const ModelParams& prm);
 Evaluation simulate(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits);
 std::vector<int> balanced_plan(const Problem& pb, const ModelParams& prm, int64_t wave_tasks);
-std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm);
+// ev_out (optional) receives the evaluation of the returned plan.
+std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm, Evaluation* ev_out = nullptr);
 std::vector<int> split_limits(const Problem& pb, const ModelParams& prm,
                               const std::vector<int>& ref);
+// ref_ev (optional): the evaluation of ref, when the caller has it.
 Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vector<int>& ref,
-                       Evaluation* nosplit_out);
+                       Evaluation* nosplit_out, const Evaluation* ref_ev = nullptr);
 
 // Kernel launchers (one per kernel file). Return hipSuccess or the launch error.
 struct AttnLaunch {

@@ -226,6 +226,7 @@ QOrder queue_order(const Problem& pb, const std::vector<int>& splits) {
 }
 
 struct SimScratch {
+  std::vector<Group> step_groups;
   std::vector<double> done_fw, ev_fw, ev_t, done, sufmax;
   std::vector<size_t> seg_base;
   std::vector<Group> heap;
@@ -293,6 +294,11 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
   for (size_t i = 0; i < nseg; ++i)
     for (size_t j = 0; j < segs[i].n; ++j) nt += segs[i].p[j].count;
   const int run = run_hint > 0 ? run_hint : reduction_run(pb, prm);
+  // Per-request attention ends are needed for the overlapped model's
+  // reductions and for `tail`. Otherwise every reduction starts at the
+  // attention completion or later (the warps are released there), whatever
+  // its request's end, so the events need not be kept.
+  const bool track = prm.overlap_reduction || tail != nullptr;
   double w_left = 0, red_lb = 0;   // unstarted task cost; reduction-phase bound
   double w_end = 0, fw_max = 0;    // running groups: sum of count x finish, latest finish
   std::vector<size_t>& seg_base = sc.seg_base;
@@ -378,10 +384,14 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
     if (rec) max_read = std::max<int64_t>(max_read, (int64_t)(seg_start[si] + ei));
     return segs[si].p[ei];
   };
-  // start up to free_slots queued tasks at work clock vw, one group per maximal
-  // stretch of equal cost; returns how many started
+  // start up to free_slots queued tasks at work clock vw, one group per cost
+  // (stretches of equal cost started in the same step finish together, and
+  // the event loop takes every group of one finish time at once, so they are
+  // one group); returns how many started
+  auto& step_groups = sc.step_groups;
   auto start_tasks = [&](int64_t free_slots) {
     int64_t started = 0;
+    step_groups.clear();
     while (started < free_slots && started_total < nt) {
       const double c = entry().cost;
       const double fw = vw + c;
@@ -399,11 +409,19 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
           skip_empty();
         }
       }
-      heap_push(fw, taken);
+      size_t g = 0;
+      while (g < step_groups.size() && step_groups[g].fw != fw) ++g;
+      if (g < step_groups.size())
+        step_groups[g].n += taken;
+      else if (step_groups.size() < 16)
+        step_groups.push_back({fw, taken});
+      else
+        heap_push(fw, taken);
       if (cutoff) w_left -= c * (double)taken;
       started += taken;
       started_total += taken;
     }
+    for (const Group& gr : step_groups) heap_push(gr.fw, gr.n);
     running += started;
     return started;
   };
@@ -472,8 +490,10 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
       sc.heap.pop_back();
     }
     running -= m;
-    sc.ev_fw.push_back(fw);
-    sc.ev_t.push_back(t);
+    if (track) {
+      sc.ev_fw.push_back(fw);
+      sc.ev_t.push_back(t);
+    }
     const int64_t started = step(m);
     if (prm.overlap_reduction && m > started) release[t] += (m - started) * prm.warps_per_slot;
   }
@@ -483,7 +503,7 @@ SimResult simulate_queue(const Problem& pb, const ModelParams& prm, const std::v
   sc.done.assign(B, 0.0);
   const double* pfw = base ? base->ev_fw.data() : nullptr;
   const double* pt = base ? base->ev_t.data() : nullptr;
-  for (int b = 0; b < B; ++b) {
+  for (int b = 0; track && b < B; ++b) {
     const double f = sc.done_fw[b];
     if (f == 0.0) continue;  // no task started (cannot happen: every request has one)
     if (n_prefix > 0 && f <= pfw[n_prefix - 1]) {
@@ -633,19 +653,26 @@ static SimPool& sim_pool() {
 // warps: the score adds at least the summed unit cost over K x W and the
 // largest unit cost. A query token's splits cover its visible tiles once, so
 // the task cost sums to heads x visible tiles + delta_attn per task.
-static double score_lower_bound(const Problem& pb, const ModelParams& prm,
-                                const std::vector<int>& splits) {
+// vis[b]: request b's visible tiles summed over its query tiles.
+static std::vector<int64_t> visible_tiles(const Problem& pb, const ModelParams& prm) {
+  std::vector<int64_t> vis(pb.seq_lens.size(), 0);
+  for (size_t b = 0; b < vis.size(); ++b) {
+    const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
+    for (int64_t qi = 0; qi < num_qtiles(n, pb.query_tile); ++qi)
+      vis[b] += n_tiles(pb.causal ? L - n + qtile_last(n, pb.query_tile, qi) + 1 : L, prm.tile_tokens);
+  }
+  return vis;
+}
+
+static double score_lower_bound(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits,
+                                const std::vector<int64_t>& vis, int run) {
   const int T = prm.tile_tokens;
-  const int run = reduction_run(pb, prm);
   double w = 0, r = 0, tmax = 0, rmax = 0;
   for (size_t b = 0; b < splits.size(); ++b) {
     const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
     const int qt = pb.query_tile;
-    int64_t vis_tiles = 0;
-    for (int64_t qi = 0; qi < num_qtiles(n, qt); ++qi)
-      vis_tiles += n_tiles(pb.causal ? L - n + qtile_last(n, qt, qi) + 1 : L, T);
     w += (double)pb.num_kv_heads *
-         ((double)vis_tiles + prm.delta_attn * (double)num_qtiles(n, qt) * (double)splits[b]);
+         ((double)vis[b] + prm.delta_attn * (double)num_qtiles(n, qt) * (double)splits[b]);
     tmax = std::max(tmax, (double)((n_tiles(L, T) + splits[b] - 1) / splits[b]) + prm.delta_attn);
     const int64_t rows = n * (int64_t)pb.rows_per_token;
     const double s_u = (double)(splits[b] + pb.n_ext);
@@ -665,7 +692,7 @@ static double score_lower_bound(const Problem& pb, const ModelParams& prm,
 // a count whose bound exceeds the best score found so far cannot win and is
 // not simulated (non-overlapped model; the margin covers rounding in the
 // bound). The pick among simulated counts is sequential.
-std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
+std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm, Evaluation* ev_out) {
   const int U = prm.max_splits;
   std::vector<Evaluation> evs(U);
   std::vector<char> done(U, 0);
@@ -676,8 +703,10 @@ std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
   } else {
     std::vector<double> lb(U);
     std::vector<int> order(U);
+    const std::vector<int64_t> vis = visible_tiles(pb, prm);
+    const int run = reduction_run(pb, prm);
     for (int u = 1; u <= U; ++u) {
-      lb[u - 1] = score_lower_bound(pb, prm, uniform_plan(pb, prm, u));
+      lb[u - 1] = score_lower_bound(pb, prm, uniform_plan(pb, prm, u), vis, run);
       order[u - 1] = u - 1;
     }
     std::stable_sort(order.begin(), order.end(), [&](int x, int y) { return lb[x] < lb[y]; });
@@ -698,6 +727,7 @@ std::vector<int> reference_plan(const Problem& pb, const ModelParams& prm) {
   int best_u = 0;
   for (int u = 1; u <= U; ++u)
     if (done[u - 1] && (best_u == 0 || key_less(evs[u - 1], evs[best_u - 1]))) best_u = u;
+  if (ev_out) *ev_out = evs[best_u - 1];
   return uniform_plan(pb, prm, best_u);
 }
 
@@ -797,7 +827,7 @@ struct CandScratch {
 }  // namespace
 
 Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vector<int>& ref,
-                       Evaluation* nosplit_out) {
+                       Evaluation* nosplit_out, const Evaluation* ref_ev) {
   const int B = (int)pb.seq_lens.size();
   const std::vector<int> lim = split_limits(pb, prm, ref);
   const Evaluation nosplit = simulate(pb, prm, std::vector<int>(B, 1));
@@ -961,14 +991,11 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
   // request's task cost sums to KV heads x (visible tiles + delta_attn x
   // query tiles x splits).
   const bool bound = !prm.overlap_reduction;
-  std::vector<int64_t> tiles_of(B), vis_of(B), qtiles_of(B);
+  const std::vector<int64_t> vis_of = visible_tiles(pb, prm);
+  std::vector<int64_t> tiles_of(B), qtiles_of(B);
   for (int b = 0; b < B; ++b) {
     tiles_of[b] = n_tiles(pb.seq_lens[b], prm.tile_tokens);
-    const int64_t L = pb.seq_lens[b], n = pb.q_lens[b];
-    qtiles_of[b] = num_qtiles(n, pb.query_tile);
-    vis_of[b] = 0;
-    for (int64_t qi = 0; qi < qtiles_of[b]; ++qi)
-      vis_of[b] += n_tiles(pb.causal ? L - n + qtile_last(n, pb.query_tile, qi) + 1 : L, prm.tile_tokens);
+    qtiles_of[b] = num_qtiles(pb.q_lens[b], pb.query_tile);
   }
   auto task_max = [&](int b, int s) { return (double)((tiles_of[b] + s - 1) / s) + prm.delta_attn; };
   auto red_max = [&](int b, int s) {
@@ -1129,16 +1156,30 @@ Evaluation plan_search(const Problem& pb, const ModelParams& prm, const std::vec
       std::vector<int> c = balanced_plan(pb, prm, (int64_t)m * prm.slots);
       if (!c.empty()) finals.push_back(std::move(c));
     }
-  std::vector<Evaluation> fevs(finals.size());
-  pool.run(finals.size(), [&](size_t i) { fevs[i] = simulate(pb, prm, finals[i]); });
   Evaluation chosen = nosplit;
   bool chose_nosplit = true;
   if (key_less(cur, chosen)) {
     chosen = cur;
     chose_nosplit = false;
   }
-  for (auto& ev : fevs) {
-    if (key_less(ev, chosen)) {
+  // a final candidate can only replace `chosen` with a score no larger than
+  // its score: in the non-overlapped model a run that cannot is cut (and
+  // skipped); the reference plan's evaluation is reused when given
+  std::vector<Evaluation> fevs(finals.size());
+  std::vector<char> fdone(finals.size(), 1);
+  const std::atomic<double> fcut{chosen.score};
+  pool.run(finals.size(), [&](size_t i) {
+    if (i == 0 && ref_ev) {
+      fevs[0] = *ref_ev;
+    } else if (bound) {
+      fdone[i] = simulate_below(pb, prm, finals[i], fcut, fevs[i]);
+    } else {
+      fevs[i] = simulate(pb, prm, finals[i]);
+    }
+  });
+  for (size_t i = 0; i < fevs.size(); ++i) {
+    Evaluation& ev = fevs[i];
+    if (fdone[i] && key_less(ev, chosen)) {
       chosen = std::move(ev);
       chose_nosplit = false;
     }
