@@ -31,14 +31,17 @@
 // appendix C.1 serves an FP8 E4M3 KV cache): the same layouts at one byte per
 // element, so a lane's key load is one 16-byte chunk of 16 dimensions (the
 // operands of two consecutive products; the query operand takes the same
-// dimension order) and its value load 4 bytes (4 tokens of one dimension).
-// v_cvt_scalef32_pk_bf16_fp8 turns two codes into two bf16 in one instruction,
-// exactly (every E4M3 value is a bf16 value), and the products run as for bf16
-// storage. A block of 16 tokens lies in one page (P >= 16), so its key scale
-// multiplies its scores and its value scale its softmax weights before the
-// P*V product (the normaliser sums the unscaled weights). The matrix cores'
-// own FP8 products would need the queries and weights in FP8 as well, which
-// costs far more accuracy than this stream has to spend time.
+// dimension order). The step's tokens are ordered so that a lane's value load
+// is 8 bytes (8 consecutive tokens of one dimension, within one page) rather
+// than two 4-byte loads: the score rows of each product are taken in runs of
+// 4 tokens (StepRegs8). v_cvt_scalef32_pk_bf16_fp8 turns two codes into two
+// bf16 in one instruction, exactly (every E4M3 value is a bf16 value), and the
+// products run as for bf16 storage. Each 16-token half of a step lies in one
+// page (P >= 16) and a lane's tokens lie in one half, so the half's key scale
+// multiplies the lane's scores and its value scale the lane's softmax weights
+// before the P*V product (the normaliser sums the unscaled weights). The
+// matrix cores' own FP8 products would need the queries and weights in FP8 as
+// well, which costs far more accuracy than this stream has to spend time.
 #include "device_common.hpp"
 #include "fused.hpp"
 #include "internal.hpp"
@@ -139,12 +142,17 @@ __device__ __forceinline__ bool load_step(const Ctx<D>& c, int t0, StepRegs<D>& 
   return bad;
 }
 
-// FP8 KV: one step's raw codes and the two blocks' scales.
+// FP8 KV: one step's raw codes and the scales of its two 16-token halves
+// (each half lies in one page). The step's tokens are ordered so that a lane
+// holds 8 consecutive tokens of one dimension in the value operand (one 8-byte
+// load): score block blk row r is token 8 (r / 4) + 4 blk + r % 4, so lane
+// (g, r16) gets the scores of tokens 8 g + 4 blk + e, and the k-index 8 g + i
+// of the P*V product is token 8 g + i.
 template <int D>
 struct StepRegs8 {
-  u32x4_t k[2][D / 64];   // 16 codes (dims 16 (4j + g) .. + 15) of token r16
-  uint32_t v[2][D / 16];  // 4 codes: tokens 4g .. 4g + 3 of dimension 16 nb + r16
-  float ks[2], vs[2];
+  u32x4_t k[2][D / 64];   // block blk: 16 codes (dims 16 (4j + g) .. + 15) of its row r16's token
+  uint32_t v[2][D / 16];  // dimension 16 nb + r16: tokens 8g .. 8g + 3 (v[0]) and 8g + 4 .. + 7 (v[1])
+  float ks[2], vs[2];     // per half
 };
 
 template <int D>
@@ -152,39 +160,53 @@ __device__ __forceinline__ bool load_step8(const Ctx<D>& c, int t0, StepRegs8<D>
   const MfmaArgs& a = *c.a;
   const int P = 1 << a.page_shift;
   bool bad = false;
+  int64_t ph[2] = {0, 0};   // page-head block of each half
+  int slot[2] = {0, 0};
+  bool ok[2] = {false, false};
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const int tb = t0 + 16 * blk;
-    int pid = -1;
-    if (tb < c.end) {
-      pid = c.ptab[tb >> a.page_shift];
+  for (int h = 0; h < 2; ++h) {
+    const int th = t0 + 16 * h;
+    s.ks[h] = 0.f;
+    s.vs[h] = 0.f;
+    if (th < c.end) {
+      const int pid = c.ptab[th >> a.page_shift];
       if (pid < 0 || pid >= a.num_pages) {
         if (c.lane == 0) raise_error(a.err_flag, kErrPageId);
         bad = true;
-        pid = -1;
+      } else {
+        ok[h] = true;
+        slot[h] = th & (P - 1);
+        ph[h] = (int64_t)pid * a.H_kv + c.kvh;
+        s.ks[h] = ((const_f32_t*)a.k_scale)[ph[h]];
+        s.vs[h] = ((const_f32_t*)a.v_scale)[ph[h]];
       }
     }
-    if (pid >= 0) {
-      const int slot = tb & (P - 1);
-      const int64_t ph = (int64_t)pid * a.H_kv + c.kvh;
-      const uint8_t* kp = a.k + (ph * (D / 16) * P + slot + c.r16) * 16;
+  }
+  // keys: row r16 of block blk is token 8 (r16 / 4) + 4 blk + r16 % 4, in
+  // half r16 / 8
+  const int kh = c.r16 >> 3;
 #pragma unroll
-      for (int j = 0; j < D / 64; ++j)
-        s.k[blk][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + (int64_t)(4 * j + c.g) * P * 16));
-      const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v) + (ph * D + c.r16) * P + slot + 4 * c.g;
+  for (int blk = 0; blk < 2; ++blk) {
+    const int tok = 8 * ((c.r16 >> 2) & 1) + 4 * blk + (c.r16 & 3);   // within the half
+    const uint8_t* kp = a.k + ((kh ? ph[1] : ph[0]) * (D / 16) * P + (kh ? slot[1] : slot[0]) + tok) * 16;
 #pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb)
-        s.v[blk][nb] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vp + (int64_t)16 * nb * P));
-      s.ks[blk] = ((const_f32_t*)a.k_scale)[ph];
-      s.vs[blk] = ((const_f32_t*)a.v_scale)[ph];
-    } else {
-#pragma unroll
-      for (int j = 0; j < D / 64; ++j) s.k[blk][j] = u32x4_t{0, 0, 0, 0};
-#pragma unroll
-      for (int nb = 0; nb < D / 16; ++nb) s.v[blk][nb] = 0;
-      s.ks[blk] = 0.f;
-      s.vs[blk] = 0.f;
+    for (int j = 0; j < D / 64; ++j) {
+      u32x4_t w = {0, 0, 0, 0};
+      if (kh ? ok[1] : ok[0])
+        w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(kp + (int64_t)(4 * j + c.g) * P * 16));
+      s.k[blk][j] = w;
     }
+  }
+  // values: tokens 8 (g % 2) .. + 7 of half g / 2, 8 bytes
+  const int vh = c.g >> 1;
+  const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v) + ((vh ? ph[1] : ph[0]) * D + c.r16) * P +
+                      (vh ? slot[1] : slot[0]) + 8 * (c.g & 1);
+#pragma unroll
+  for (int nb = 0; nb < D / 16; ++nb) {
+    u32x2_t w = {0u, 0u};
+    if (vh ? ok[1] : ok[0]) w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(vp + (int64_t)16 * nb * P));
+    s.v[0][nb] = w[0];
+    s.v[1][nb] = w[1];
   }
   return bad;
 }
@@ -221,8 +243,10 @@ struct State {
   f32x4_t o[D / 16];
 };
 
-// kmul / vmul (FP8 KV): per token block, the factor of its scores (softmax
-// scale in log2 units times the key scale) and of its weights (value scale).
+// kmul / vmul (FP8 KV): the factor of the lane's scores (softmax scale in
+// log2 units times the key scale) and of its weights (value scale). With kF8
+// the step's tokens take the FP8 order (StepRegs8): lane (g, r16)'s scores
+// of block blk are tokens 8 g + 4 blk + e; otherwise 16 blk + 4 g + e.
 template <int D, bool kF8 = false>
 __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D>& s,
                                              const u32x4_t (&qf)[D / 32], State<D>& st,
@@ -244,8 +268,8 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
   for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int tok = t0 + 16 * blk + 4 * c.g + e;
-      const float x = sc[blk][e] * (kF8 ? kmul[blk] : scale_log2);
+      const int tok = t0 + (kF8 ? 8 * c.g + 4 * blk : 16 * blk + 4 * c.g) + e;
+      const float x = sc[blk][e] * (kF8 ? *kmul : scale_log2);
       sv[4 * blk + e] = (!tail || tok < c.end) ? x : -INFINITY;
     }
   float mt = sv[0];
@@ -268,7 +292,7 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
   uint32_t ph[4], pl[4];
   if constexpr (kF8) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i] * vmul[i >> 1], p[2 * i + 1] * vmul[i >> 1], ph[i], pl[i]);
+    for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i] * *vmul, p[2 * i + 1] * *vmul, ph[i], pl[i]);
   } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
@@ -280,7 +304,7 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
   if (tail) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int tok = t0 + 16 * blk + 4 * c.g;
+      const int tok = t0 + (kF8 ? 8 * c.g + 4 * blk : 16 * blk + 4 * c.g);
       const int nv = c.end - tok;  // valid tokens among this lane's 4
       if (nv < 4) {
         const uint32_t m0 = nv >= 2 ? 0xFFFFFFFFu : (nv == 1 ? 0x0000FFFFu : 0u);
@@ -371,8 +395,10 @@ __device__ __forceinline__ void gqa_mfma_task(const MfmaArgs& a, const DevTask& 
     // one step's codes decoded, with its blocks' score and weight factors
     auto step = [&](int ts, const StepRegs8<D>& rr) {
       decode_step(rr, s);
-      const float km[2] = {a.scale_log2 * rr.ks[0], a.scale_log2 * rr.ks[1]};
-      compute_step<D, true>(c, ts, s, qf, st, a.scale_log2, km, rr.vs);
+      // the lane's tokens all lie in half g / 2
+      const float km = a.scale_log2 * (c.g >> 1 ? rr.ks[1] : rr.ks[0]);
+      const float vm = c.g >> 1 ? rr.vs[1] : rr.vs[0];
+      compute_step<D, true>(c, ts, s, qf, st, a.scale_log2, &km, &vm);
     };
 #pragma unroll
     for (int i = 0; i < kRing - 1; ++i)
