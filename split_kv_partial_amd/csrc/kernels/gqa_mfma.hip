@@ -278,6 +278,9 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
   mt = max_xor32(max_xor16(mt));
   const float mn = fmaxf(st.m, mt);
   const float alpha = fast_exp2(st.m - mn);
+  // the accumulators need rescaling only where a head's maximum rose
+  // (elsewhere alpha is exactly 1; at the first step they are zero)
+  const bool rescale = __builtin_amdgcn_ballot_w64(mn != st.m) != 0;
   st.m = mn;
   float p[8], ps = 0.f;
 #pragma unroll
@@ -317,9 +320,12 @@ __device__ __forceinline__ void compute_step(const Ctx<D>& c, int t0, StepRegs<D
       }
     }
   }
+  if (rescale) {
+#pragma unroll
+    for (int nb = 0; nb < D / 16; ++nb) st.o[nb] *= alpha;
+  }
 #pragma unroll
   for (int nb = 0; nb < D / 16; ++nb) {
-    st.o[nb] *= alpha;
     const u32x4_t vf = {s.v[0][nb][0], s.v[0][nb][1], s.v[1][nb][0], s.v[1][nb][1]};
     st.o[nb] = mfma16(vf, pf_hi, st.o[nb]);
     st.o[nb] = mfma16(vf, pf_lo, st.o[nb]);
@@ -774,6 +780,10 @@ __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& 
       // finite reference so that its weights are exp2(-inf) = 0, not NaN
       const float mref = mn == -INFINITY ? 0.f : mn;
       const float alpha = fast_exp2(mrow[j] - mref);
+      // the accumulators need rescaling only where a column's maximum rose
+      // (elsewhere alpha is exactly 1, or the column has no weight yet and
+      // its accumulators are zero): usually no column after the first steps
+      const bool rescale = __builtin_amdgcn_ballot_w64(mn != mrow[j]) != 0;
       mrow[j] = mn;
       float p[8], ps = 0.f;
 #pragma unroll
@@ -787,9 +797,12 @@ __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& 
       for (int i = 0; i < 4; ++i) split_bf16x2(p[2 * i], p[2 * i + 1], ph[i], pl[i]);
       const u32x4_t pf_hi = {ph[0], ph[1], ph[2], ph[3]};
       const u32x4_t pf_lo = {pl[0], pl[1], pl[2], pl[3]};
+      if (rescale) {
+#pragma unroll
+        for (int nb = 0; nb < D / 16; ++nb) o[j][nb] *= alpha;
+      }
 #pragma unroll
       for (int nb = 0; nb < D / 16; ++nb) {
-        o[j][nb] *= alpha;
         const u32x4_t vv = {vf[0][nb][0], vf[0][nb][1], vf[1][nb][0], vf[1][nb][1]};
         o[j][nb] = mfma16(vv, pf_hi, o[j][nb]);
         o[j][nb] = mfma16(vv, pf_lo, o[j][nb]);
