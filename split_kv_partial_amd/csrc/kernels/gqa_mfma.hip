@@ -573,50 +573,66 @@ __device__ __forceinline__ StepPages step_pages(const MfmaArgs& a, const_i32_t* 
   return StepPages{ptab[min(t0 >> a.page_shift, last)], ptab[min((t0 + 16) >> a.page_shift, last)]};
 }
 
-// Sources of this wave's DMA blocks of the step at t0 (kDmaPerWaveStep<D>
-// blocks: wave, wave + 4, ...). A block below kStepBlocks / 2 holds keys, the
-// rest values. An id outside the pool is never dereferenced: page 0 stands in
-// and the task's state is written as NaN.
+// This wave's DMA blocks of a step (kDmaPerWaveStep<D> blocks: wave, wave +
+// 4, ...; a block below kStepBlocks / 2 holds keys, the rest values). Each
+// lane's source is a per-step base of the page half it reads (keys: the
+// lane's token, values: its 4-token group) plus a lane offset fixed for the
+// task plus a per-block step, so a step costs a few scalar operations and one
+// select and 64-bit add per block. An id outside the pool is never
+// dereferenced: page 0 stands in and the task's state is written as NaN.
 template <int D>
 struct RowsDma {
-  const uint8_t* src[kDmaPerWaveStep<D>];
+  static constexpr int kHalf = kDmaPerWaveStep<D> / 2;   // key blocks per wave
+  uint32_t koff, voff;    // lane offsets (bytes) from the half's base
+  bool khi, vhi;          // the lane's token lies in the step's second half
+  uint32_t ldsoff[kDmaPerWaveStep<D>];   // wave-uniform LDS offsets within a step
 
-  __device__ __forceinline__ bool prepare(const MfmaArgs& a, StepPages pg, int kvh, int t0, int wave,
-                                          int lane) {
+  // once per task
+  __device__ __forceinline__ void setup(const MfmaArgs& a, int wave, int lane) {
+    const int P = 1 << a.page_shift;
+    // keys: block wave + 4 j holds chunks 2 blk, 2 blk + 1 of the 32 tokens
+    // (slot 64 blk + lane: chunk (64 blk + lane) / 32, token lane % 32)
+    const int tk = lane & 31;
+    khi = tk >= 16;
+    const int tkp = P >= 32 ? tk : (tk & 15);           // token within its page row run
+    koff = (uint32_t)(((2 * wave + (lane >> 5)) * P + tkp) * 16);
+    // values: block 8 + wave + 4 jv holds dims 16 (wave + 4 jv) .. + 15, lane
+    // (d, 8-token pair): dimension lane / 4 of the block, tokens of its slot
+    const int d = lane >> 2, pair = lane & 3;
+    const int tv = 4 * ((2 * pair) ^ (2 * ((d >> 2) & 3)));
+    vhi = tv >= 16;
+    const int tvp = P >= 32 ? tv : (tv & 15);
+    voff = (uint32_t)(((16 * wave + d) * P + tvp) * 2);
+#pragma unroll
+    for (int j = 0; j < kDmaPerWaveStep<D>; ++j) {
+      const int blk = wave + kWaves * j;
+      ldsoff[j] = j < kHalf ? 1024u * blk : (uint32_t)(kKeyBytes<D> + (blk - kStepBlocks<D> / 2) * kVGroupBytes);
+    }
+  }
+  // Issue the step at t0 into the LDS step buffer lds_step; returns true if
+  // a page id of the step is outside the pool.
+  __device__ __forceinline__ bool issue(const MfmaArgs& a, StepPages pg, int kvh, int t0, uint32_t lds_step) const {
     const int P = 1 << a.page_shift;
     int p0 = pg.p0, p1 = pg.p1;
     const bool ok0 = p0 >= 0 && p0 < a.num_pages, ok1 = p1 >= 0 && p1 < a.num_pages;
     if (!ok0) p0 = 0;
     if (!ok1) p1 = 0;
     const int64_t ph0 = (int64_t)p0 * a.H_kv + kvh, ph1 = (int64_t)p1 * a.H_kv + kvh;
+    const int64_t sl = P >= 32 ? (t0 & (P - 1)) : 0;   // the step's first slot in its page
+    const uint8_t* kb0 = a.k + (ph0 * (D / 8) * P + sl) * 16;
+    const uint8_t* kb1 = a.k + (ph1 * (D / 8) * P + sl) * 16;
+    const uint8_t* vb0 = reinterpret_cast<const uint8_t*>(a.v) + (ph0 * D * P + sl) * 2;
+    const uint8_t* vb1 = reinterpret_cast<const uint8_t*>(a.v) + (ph1 * D * P + sl) * 2;
+    const uint8_t* kb = (khi ? kb1 : kb0) + koff;
+    const uint8_t* vb = (vhi ? vb1 : vb0) + voff;
 #pragma unroll
     for (int j = 0; j < kDmaPerWaveStep<D>; ++j) {
-      const int blk = wave + kWaves * j;
-      if (blk < kStepBlocks<D> / 2) {       // keys: chunk c of token t
-        const int sl = 64 * blk + lane;
-        const int c = sl >> 5, t = sl & 31;
-        const int64_t ph = t < 16 ? ph0 : ph1;
-        const int slot = (t0 + t) & (P - 1);
-        src[j] = a.k + ((ph * (D / 8) + c) * P + slot) * 16;
-      } else {                               // values: dimension d, 8 tokens
-        const int sl = 64 * (blk - kStepBlocks<D> / 2) + lane;
-        const int d = sl >> 2, pair = sl & 3;
-        const int t = 4 * ((2 * pair) ^ (2 * ((d >> 2) & 3)));
-        const int64_t ph = t < 16 ? ph0 : ph1;
-        const int slot = (t0 + t) & (P - 1);
-        src[j] = reinterpret_cast<const uint8_t*>(a.v) + ((ph * D + d) * P + slot) * 2;
-      }
+      // key block j: chunks 8 j further (4 blocks of 2 chunks); value block
+      // j - kHalf: 64 dimensions further
+      const uint8_t* src = j < kHalf ? kb + (int64_t)(8 * j) * P * 16 : vb + (int64_t)(64 * (j - kHalf)) * P * 2;
+      rows_dma(src, lds_step + ldsoff[j]);
     }
     return !ok0 || !ok1;
-  }
-  __device__ __forceinline__ void issue(uint32_t lds_step, int wave) const {
-#pragma unroll
-    for (int j = 0; j < kDmaPerWaveStep<D>; ++j) {
-      const int blk = wave + kWaves * j;
-      const int off = blk < kStepBlocks<D> / 2 ? 1024 * blk
-                                               : kKeyBytes<D> + (blk - kStepBlocks<D> / 2) * kVGroupBytes;
-      rows_dma(src[j], lds_step + (uint32_t)off);
-    }
   }
 };
 
@@ -663,6 +679,11 @@ __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& 
     for (int m = 0; m < D / 32; ++m) qf[j][m] = *reinterpret_cast<const u32x4_t*>(qp + 8 * (4 * m + g));
     end_col[j] = min(t.hi, t.vis_last - (t.ntok - 1 - tok) * t.step);
   }
+  // the least visible end among the wave's columns (that of its first row's
+  // token: a column's end grows with its token): steps wholly before it need
+  // no mask
+  const int end_min = __builtin_amdgcn_readfirstlane(
+      min(t.hi, t.vis_last - (t.ntok - 1 - min(16 * kRowsBPW * wave, R - 1) / G) * t.step));
   // Q has landed before the first DMA (otherwise the compiler's wait for it
   // would sit inside the loop and drain the ring)
   __builtin_amdgcn_s_waitcnt(kRowsWaitVm<0>);
@@ -695,31 +716,36 @@ __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& 
 
   const int nsteps = end > t.lo ? (end - t.lo + kStep - 1) / kStep : 0;
   bool bad = false;
+  RowsDma<D> dm;
+  dm.setup(a, wave, lane);
   StepPages pg{0, 0};   // page ids of the next step to send
   if (nsteps > 0) pg = step_pages(a, ptab, t.lo, end);
 #pragma unroll
   for (int i = 0; i < kRing - 1; ++i) {
     if (i < nsteps) {
-      RowsDma<D> dm;
-      bad |= dm.prepare(a, pg, t.kvh, t.lo + i * kStep, wave, lane);
-      dm.issue(ring_lds + (uint32_t)(i * kStepBytes<D>), wave);
+      bad |= dm.issue(a, pg, t.kvh, t.lo + i * kStep, ring_lds + (uint32_t)(i * kStepBytes<D>));
       pg = step_pages(a, ptab, t.lo + (i + 1) * kStep, end);   // clamped: always a valid entry
     }
   }
-  for (int k = 0; k < nsteps; ++k) {
+  // the loop runs the ring's buffers in order, unrolled once around the ring
+  // so that every buffer offset is a constant of the LDS instructions
+  for (int k0 = 0; k0 < nsteps; k0 += kRing)
+#pragma unroll
+  for (int u = 0; u < kRing; ++u) {
+    const int k = k0 + u;
+    if (k >= nsteps) break;
     // step k has landed for this wave (its DMAs retire in order), then for all
     rows_wait_ahead<D>(min(kRing - 2, nsteps - 1 - k));
     rows_barrier();
     // the DMA of step k + kRing - 1, into the buffer step k - 1 left (every
     // wave has passed this barrier, so its reads of that step are done)
     if (k + kRing - 1 < nsteps) {
-      RowsDma<D> dm;
-      bad |= dm.prepare(a, pg, t.kvh, t.lo + (k + kRing - 1) * kStep, wave, lane);
-      dm.issue(ring_lds + (uint32_t)(((k + kRing - 1) % kRing) * kStepBytes<D>), wave);
+      bad |= dm.issue(a, pg, t.kvh, t.lo + (k + kRing - 1) * kStep,
+                      ring_lds + (uint32_t)(((u + kRing - 1) % kRing) * kStepBytes<D>));
       pg = step_pages(a, ptab, t.lo + (k + kRing) * kStep, end);
     }
     if (nblk == 0) continue;   // wave-uniform: this wave's rows are past the task's
-    const uint8_t* st = sh.ring[k % kRing];
+    const uint8_t* st = sh.ring[u];
     const int t0 = t.lo + k * kStep;
     // key fragments of both token blocks and value fragments
     u32x4_t kf[2][D / 32];
@@ -764,13 +790,20 @@ __device__ __forceinline__ void gqa_rows_task(const MfmaArgs& a, const DevTask& 
         sc[blk] = acc;
       }
       float sv[8];
+      if (t0 + kStep > end_min) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = t0 + 16 * blk + 4 * g + e;
-          sv[4 * blk + e] = tok < end_col[j] ? sc[blk][e] * a.scale_log2 : -INFINITY;
-        }
+          for (int e = 0; e < 4; ++e) {
+            const int tok = t0 + 16 * blk + 4 * g + e;
+            sv[4 * blk + e] = tok < end_col[j] ? sc[blk][e] * a.scale_log2 : -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sv[4 * blk + e] = sc[blk][e] * a.scale_log2;
+      }
       float mt = sv[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
