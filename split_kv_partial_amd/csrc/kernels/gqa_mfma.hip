@@ -596,8 +596,9 @@ struct RowsDma {
     khi = tk >= 16;
     const int tkp = P >= 32 ? tk : (tk & 15);           // token within its page row run
     koff = (uint32_t)(((2 * wave + (lane >> 5)) * P + tkp) * 16);
-    // values: block 8 + wave + 4 jv holds dims 16 (wave + 4 jv) .. + 15, lane
-    // (d, 8-token pair): dimension lane / 4 of the block, tokens of its slot
+    // values: block kStepBlocks / 2 + wave + 4 jv holds dims 16 (wave + 4 jv)
+    // .. + 15; lane (d, pair): dimension lane / 4 of the block, the 4 tokens of
+    // its 8-byte slot
     const int d = lane >> 2, pair = lane & 3;
     const int tv = 4 * ((2 * pair) ^ (2 * ((d >> 2) & 3)));
     vhi = tv >= 16;
@@ -618,7 +619,10 @@ struct RowsDma {
     if (!ok0) p0 = 0;
     if (!ok1) p1 = 0;
     const int64_t ph0 = (int64_t)p0 * a.H_kv + kvh, ph1 = (int64_t)p1 * a.H_kv + kvh;
-    const int64_t sl = P >= 32 ? (t0 & (P - 1)) : 0;   // the step's first slot in its page
+    // the step's first slot in its page (steps start at multiples of 32
+    // tokens, splits at multiples of the 64-token KV tile: with P >= 32 the
+    // step lies in one page, with P = 16 its halves are whole pages)
+    const int64_t sl = P >= 32 ? (t0 & (P - 1)) : 0;
     const uint8_t* kb0 = a.k + (ph0 * (D / 8) * P + sl) * 16;
     const uint8_t* kb1 = a.k + (ph1 * (D / 8) * P + sl) * 16;
     const uint8_t* vb0 = reinterpret_cast<const uint8_t*>(a.v) + (ph0 * D * P + sl) * 2;

@@ -644,15 +644,6 @@ static SimPool& sim_pool() {
   return pool;
 }
 
-// A lower bound on a plan's score in the non-overlapped model. However many
-// slots run, attention advances by at most K tile units per time unit
-// (k / tau(k) <= K), so the attention completion is at least the summed task
-// cost over K; and a task of cost c runs at least rho c (tau >= rho), so it is
-// at least rho times the largest task cost (a request's first split, which
-// its last query token sees whole). Every reduction starts after it, on K x W
-// warps: the score adds at least the summed unit cost over K x W and the
-// largest unit cost. A query token's splits cover its visible tiles once, so
-// the task cost sums to heads x visible tiles + delta_attn per task.
 // vis[b]: request b's visible tiles summed over its query tiles.
 static std::vector<int64_t> visible_tiles(const Problem& pb, const ModelParams& prm) {
   std::vector<int64_t> vis(pb.seq_lens.size(), 0);
@@ -664,6 +655,15 @@ static std::vector<int64_t> visible_tiles(const Problem& pb, const ModelParams& 
   return vis;
 }
 
+// A lower bound on a plan's score in the non-overlapped model. However many
+// slots run, attention advances by at most K tile units per time unit
+// (k / tau(k) <= K), so the attention completion is at least the summed task
+// cost over K; and a task of cost c runs at least rho c (tau >= rho), so it is
+// at least rho times the largest task cost (a request's first split, which
+// its last query token sees whole). Every reduction starts after it, on K x W
+// warps: the score adds at least the summed unit cost over K x W and the
+// largest unit cost. A query token's splits cover its visible tiles once, so
+// the task cost sums to heads x visible tiles + delta_attn per task.
 static double score_lower_bound(const Problem& pb, const ModelParams& prm, const std::vector<int>& splits,
                                 const std::vector<int64_t>& vis, int run) {
   const int T = prm.tile_tokens;
