@@ -165,6 +165,9 @@ typedef struct skv_plan_info {
   int32_t query_tile;         /* query tokens per attention task (consecutive
                                  tokens of one request; the last tile of a
                                  request may hold fewer)                       */
+  double reference_score;     /* skv_plan_splits: model completion time of the
+                                 reference plan the search started from (its
+                                 own or ref_splits); NaN for the other plans   */
 } skv_plan_info;
 
 /* Fill p with the library defaults: use_calibration = 1,

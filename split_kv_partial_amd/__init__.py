@@ -72,7 +72,8 @@ class PlanInfo(ctypes.Structure):
                 ("nosplit_score", ctypes.c_double), ("rho", ctypes.c_double),
                 ("delta_attn", ctypes.c_double), ("delta_red", ctypes.c_double),
                 ("gamma", ctypes.c_double), ("tile_time_us", ctypes.c_double),
-                ("balanced_candidates", ctypes.c_int32), ("query_tile", ctypes.c_int32)]
+                ("balanced_candidates", ctypes.c_int32), ("query_tile", ctypes.c_int32),
+                ("reference_score", ctypes.c_double)]
 
 
 def _load():

@@ -187,7 +187,7 @@ struct skv_plan {
   std::vector<DevUnit> units;
   int run = 1;
   int max_ntok = 1;                       // most query tokens of any task
-  double score = NAN, t_attn = NAN, nosplit_score = NAN;
+  double score = NAN, t_attn = NAN, nosplit_score = NAN, reference_score = NAN;
   int split_adopted = 0;
   std::vector<uint8_t> image;
   int64_t tasks_off = 0, reqs_off = 0, units_off = 0;
@@ -354,6 +354,7 @@ skv_status skv_plan_splits(const skv_attn_desc* desc, const int32_t* seq_lens, c
     } else {
       ref = reference_plan(pl->pb, pl->prm, &ref_ev);
     }
+    pl->reference_score = ref_splits ? simulate(pl->pb, pl->prm, ref).score : ref_ev.score;
     Evaluation ns;
     Evaluation ev = plan_search(pl->pb, pl->prm, ref, &ns, ref_splits ? nullptr : &ref_ev);
     pl->score = ev.score;
@@ -462,6 +463,7 @@ skv_status skv_plan_get_info(const skv_plan* pl, skv_plan_info* info) {
   info->tile_time_us = pl->prm.tile_time_us;
   info->balanced_candidates = pl->prm.balanced_candidates;
   info->query_tile = pl->pb.query_tile;
+  info->reference_score = pl->reference_score;
   return SKV_OK;
 }
 

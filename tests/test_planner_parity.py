@@ -185,6 +185,40 @@ def test_several_chunk_requests_bit_exact(seed):
     assert_same(plan, pb, prm, ev, ns)
 
 
+@pytest.mark.parametrize("seed", range(40))
+def test_library_reference_plan_is_the_oracles(seed):
+    # The library evaluates the uniform split counts of its reference plan
+    # lowest score bound first and cuts a run as soon as it cannot beat the
+    # best count found so far. Handing it the oracle's reference plan must
+    # then change nothing: the same plan, bit for bit, as the one it builds
+    # on its own.
+    rng = np.random.default_rng(9000 + seed)
+    spec = SPECS[seed % len(SPECS)]
+    B = int(rng.integers(1, 24))
+    seq = rng.integers(1, 40000, size=B)
+    q = np.ones(B, np.int64)
+    if seed % 3 == 1:
+        k = int(rng.integers(0, B))
+        q[k] = min(int(seq[k]), int(rng.integers(17, 64)))
+    p = skv.default_params()
+    p.overlap_reduction = int(seed % 4 == 3)
+    p.max_splits = int(rng.choice([8, 16, 64]))
+    num_cu = int(rng.choice([8, 64, 256]))
+    n_ext = int(rng.integers(0, 3))
+    own = skv.plan_splits(seq, spec, num_cu=num_cu, q_lens=q, n_ext=n_ext, params=p)
+    pb, prm, _, _ = reference_for(own, spec, seq, q, n_ext, p)
+    ref = PL.reference_plan(pb, prm)
+    given = skv.plan_splits(seq, spec, num_cu=num_cu, q_lens=q, n_ext=n_ext, params=p, ref_splits=ref)
+    a, b = own.export(), given.export()
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+    ia, ib = own.info(), given.info()
+    assert bits(ia.score) == bits(ib.score) and bits(ia.t_attn) == bits(ib.t_attn)
+    # and the reference plan itself scores as the oracle's does
+    assert bits(ia.reference_score) == bits(PL.simulate(pb, prm, ref).score)
+    assert bits(ib.reference_score) == bits(ia.reference_score)
+
+
 @pytest.mark.parametrize("cid", [1, 2, 5])
 def test_benchmark_workloads_bit_exact(cid):
     # (workloads 3-6 at the default split cap: test_default_cap_large_workloads_bit_exact)
