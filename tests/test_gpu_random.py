@@ -1,4 +1,4 @@
-"""Randomised GPU parity: seeded random shapes (dtype, group size, head dim,
+"""Randomised GPU parity: seeded random shapes (dtype (fp32, bf16, FP8 KV), group size, head dim,
 page size, batch, ragged lengths, chunk rows, external states, planner or
 random split counts) for the GQA and MLA paths, each checked element-wise
 against the float64 oracle (partial states and merged outputs)."""
@@ -73,4 +73,24 @@ def test_random_mla(seed):
                  scale=wl.MLA_SCALE, seed=seed, value_scale=0.1,
                  q_scale=float(rng.choice([1.0, wl.SHARP_MLA])), causal=True, n_ext=n_ext,
                  ext_lse_center=5.0)
+    check_all(w, _plan(rng, w))
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_fp8(seed):
+    # FP8 (OCP E4M3) KV with per-(page, KV head) scales: groups of 8 and 16,
+    # head dims 64 and 128, page sizes 16-64, ragged lengths, a few chunk rows
+    rng = np.random.default_rng(3000 + seed)
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([16, 32, 64]))
+    G = int(rng.choice([8, 16]))
+    H_kv = int(rng.choice([1, 2, 4]))
+    batch = int(rng.integers(1, 6))
+    q_lens = [int(rng.integers(2, 24)) if rng.random() < 0.2 else 1 for _ in range(batch)]
+    seq = _lengths(rng, batch, q_lens, 2500)
+    n_ext = int(rng.choice([0, 0, 1, 3, 12]))
+    w = wl.build(f"rand-fp8-{seed}", dtype="fp8", mla=False, seq_lens=seq, q_lens=q_lens,
+                 num_q_heads=G * H_kv, num_kv_heads=H_kv, head_dim_qk=D, head_dim_v=D, page_size=P,
+                 scale=1.0 / math.sqrt(D), seed=seed, q_scale=float(rng.choice([1.0, 3.0])),
+                 causal=True, n_ext=n_ext, ext_lse_center=4.0)
     check_all(w, _plan(rng, w))
