@@ -62,6 +62,8 @@ def parse(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true",
                     help="skip the streaming-read probe of the practical HBM read ceiling")
+    ap.add_argument("--no-mfma-probe", action="store_true",
+                    help="skip the probe of the sustained dense bf16 matrix rate")
     ap.add_argument("--plan-param", action="append", default=[], metavar="NAME=VALUE",
                     help="override one field of the planner parameters (repeatable)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -104,6 +106,39 @@ def hbm_probe(dev, num_cu: int, gib: int = 4, reps: int = 10) -> dict:
     del buf
     torch.cuda.synchronize()
     return best
+
+
+def mfma_probe(dev, num_cu: int, iters: int = 32768, seconds: float = 1.0) -> dict:
+    """Sustained dense bf16 matrix rate: the library's matrix-core probe (one
+    work-group of four waves per CU, so one wave per SIMD, each keeping eight
+    independent 16x16x32 product chains busy on pseudo-random operands),
+    launched back to back for about `seconds` so that the clock settles
+    under the load; HIP events on the launch stream. The per-wave cycle
+    counts over the launch time give the clock the chip ran at."""
+    import time
+    import torch
+    import split_kv_partial_amd as skv
+    waves = 4
+    out = torch.empty(num_cu * waves, 2, dtype=torch.int32, device=dev)
+    flops = num_cu * waves * iters * 8 * 16384
+    for _ in range(3):
+        skv.mfma_probe(num_cu, waves, iters, dev, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 0
+    t_end = time.time() + seconds
+    e0.record()
+    while time.time() < t_end:
+        for _ in range(10):
+            skv.mfma_probe(num_cu, waves, iters, dev, out)
+        n += 10
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    cycles = float(np.median(out[:, 1].cpu().numpy().astype(np.uint32)))
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "launch_ms": round(ms, 4), "launches": n,
+            "cycles_per_product": round(cycles / (8 * iters), 3), "est_ghz": round(cycles / (ms * 1e6), 3)}
 
 
 def plan_overrides(items):
@@ -504,11 +539,19 @@ def main(argv=None):
             probe = hbm_probe(dev, num_cu)
         except (RuntimeError, MemoryError) as e:   # torch reports device OOM as RuntimeError
             print(f"[bench] HBM probe skipped: {e}", file=sys.stderr, flush=True)
+    mprobe = None
+    if not args.no_mfma_probe:
+        mprobe = mfma_probe(dev, num_cu)
     for m in [head, *per.values()]:
         if probe:
             m["frac_of_probe"] = round(m["kv_gbs"] / probe["gbs"], 4)
             if m["roofline"]["unit"] == "GB/s":
                 m["roofline"]["frac_of_probe"] = round(m["roofline"]["achieved"] / probe["gbs"], 4)
+        if mprobe:
+            r = m["roofline"]
+            tf = r["achieved"] if r["unit"] == "TFLOP/s" else r.get("mfma_tflops")
+            if tf is not None:
+                r["mfma_frac_of_probe"] = round(tf / mprobe["tflops"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         head["cpu_baseline"] = cpu_baseline(head_w, args.cpu_seconds)
@@ -538,6 +581,8 @@ def main(argv=None):
     if probe:
         out["hbm_probe"] = probe
         out["frac_of_probe"] = head["frac_of_probe"]
+    if mprobe:
+        out["mfma_probe"] = mprobe
     if "cpu_baseline" in head:
         out["cpu_baseline"] = head["cpu_baseline"]
     if per:

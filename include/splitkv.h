@@ -336,6 +336,17 @@ skv_status skv_read_error_flag(const void* workspace, int32_t* flag, void* strea
 skv_status skv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,
                               void* stream);
 
+/* Measurement utility (not a step of the method): `blocks` work-groups of
+ * `waves` waves (1..8 waves, blocks 1..65536, iters 1..2^24) each run
+ * `iters` trips of eight independent bf16 v_mfma_f32_16x16x32 products on
+ * pseudo-random register operands: 16384 * 8 * iters flop per wave. out:
+ * device uint32[2 * blocks * waves]; for wave w (block-major) out[2w] holds
+ * the bits of a float sum of its results and out[2w + 1] the shader-clock
+ * cycles (s_memtime) its product loop took. Asynchronous on `stream`; the
+ * caller times it. Used to state the bf16 matrix rate the chip sustains under
+ * a dense load, the ceiling of matrix-bound attention launches. */
+skv_status skv_mfma_probe(uint32_t* out, int32_t blocks, int32_t waves, int32_t iters, void* stream);
+
 /* Thread-local message for the last non-OK status of this thread. */
 const char* skv_last_error(void);
 

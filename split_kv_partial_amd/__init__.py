@@ -39,7 +39,7 @@ EXPORTED = (
     "skv_plan_get_info", "skv_plan_export", "skv_plan_workspace_bytes", "skv_plan_upload",
     "skv_plan_destroy", "skv_decode_attn_partial", "skv_merge_states", "skv_read_error_flag",
     "skv_hbm_read_probe", "skv_last_error", "skv_decode_attn_scratch_bytes", "skv_decode_attn",
-    "skv_decode_attn_noalloc", "skv_decode_attn_partial_fp8",
+    "skv_decode_attn_noalloc", "skv_decode_attn_partial_fp8", "skv_mfma_probe",
 )
 
 
@@ -104,6 +104,7 @@ def _load():
         "skv_decode_attn_noalloc": (I32, [pdesc, P, P, P, P, P, P, P, I32, P, P, P, I32, P, P]),
         "skv_read_error_flag": (I32, [P, pi32, P]),
         "skv_hbm_read_probe": (I32, [P, I64, P, I32, P]),
+        "skv_mfma_probe": (I32, [P, I32, I32, I32, P]),
         "skv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -505,4 +506,19 @@ def hbm_read_probe(buf: torch.Tensor, blocks: int, out: torch.Tensor | None = No
     _check(_lib.skv_hbm_read_probe(buf.data_ptr(), buf.numel() * buf.element_size(), out.data_ptr(),
                                    int(blocks), _stream_ptr()),
            "skv_hbm_read_probe")
+    return out
+
+
+def mfma_probe(blocks: int, waves: int, iters: int, device, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Dense bf16 matrix-core load (a measurement utility for the sustained
+    matrix rate, not a step of the method): `blocks` work-groups of `waves`
+    waves, each wave 8 * iters products of 16x16x32. Returns out
+    [blocks * waves, 2] int32: per wave the bits of a float sum of its results
+    and the shader-clock cycles of its product loop."""
+    if out is None:
+        out = torch.empty(blocks * waves, 2, dtype=torch.int32, device=device)
+    if not out.is_contiguous() or out.numel() < 2 * blocks * waves:
+        raise ValueError("out must be a contiguous device tensor of 2 * blocks * waves int32")
+    _check(_lib.skv_mfma_probe(out.data_ptr(), int(blocks), int(waves), int(iters), _stream_ptr()),
+           "skv_mfma_probe")
     return out

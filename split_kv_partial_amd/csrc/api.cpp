@@ -725,6 +725,16 @@ skv_status skv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* out, int
   return SKV_OK;
 }
 
+skv_status skv_mfma_probe(uint32_t* out, int32_t blocks, int32_t waves, int32_t iters, void* stream) {
+  if (!out) return fail(SKV_ERR_INVALID_ARG, "out is NULL");
+  if (blocks < 1 || blocks > 65536) return fail(SKV_ERR_INVALID_ARG, "blocks must be in [1, 65536]");
+  if (waves < 1 || waves > 8) return fail(SKV_ERR_INVALID_ARG, "waves must be in [1, 8]");
+  if (iters < 1 || iters > (1 << 24)) return fail(SKV_ERR_INVALID_ARG, "iters must be in [1, 2^24]");
+  hipError_t e = launch_mfma_probe(blocks, waves, iters, out, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(SKV_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+  return SKV_OK;
+}
+
 skv_status skv_read_error_flag(const void* workspace, int32_t* flag, void* stream) {
   if (!workspace || !flag) return fail(SKV_ERR_INVALID_ARG, "workspace or flag is NULL");
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);

@@ -41,4 +41,69 @@ hipError_t launch_hbm_probe(const void* buf, int64_t bytes, uint32_t* out, int b
   return hipGetLastError();
 }
 
+
+// Matrix-core throughput probe: a measurement utility beside the attention
+// path, like the read probe above. Each wave keeps eight independent bf16
+// v_mfma_f32_16x16x32 accumulation chains busy for `iters` trips; the eight
+// A operands differ from one product to the next and hold pseudo-random bf16
+// values (signs, exponents 2^-3..2^0, full mantissas), so the multipliers see
+// changing data as they do under attention. It states the bf16 product rate
+// the chip sustains under a dense matrix load (power and clock included), the
+// ceiling beside which a matrix-bound attention kernel is read. Per wave it
+// writes the sum of its lane-0 accumulators (so no product is dropped) and
+// the shader-clock cycles the loop took.
+namespace {
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {   // a 32-bit integer hash (xorshift-multiply)
+  x ^= x >> 16; x *= 0x7feb352du;
+  x ^= x >> 15; x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+// Two bf16 values from a hash: sign, exponent 124..127, seven mantissa bits.
+__device__ __forceinline__ uint32_t rand_bf16x2(uint32_t h) {
+  const uint32_t lo = (h & 0x807Fu) | ((124u + ((h >> 7) & 3u)) << 7);
+  const uint32_t hi = ((h >> 16) & 0x807Fu) | ((124u + ((h >> 23) & 3u)) << 7);
+  return lo | (hi << 16);
+}
+
+__global__ __launch_bounds__(512) void mfma_probe_kernel(int iters, uint32_t* out) {
+  const uint32_t lane = threadIdx.x & 63;
+  const uint32_t wid = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  u32x4_t a[8], b[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a[j][e] = rand_bf16x2(mix32((wid * 64 + lane) * 64 + 4 * j + e));
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) b[j][e] = rand_bf16x2(mix32(0x9e3779b9u ^ ((wid * 64 + lane) * 8 + 4 * j + e)));
+  f32x4_t c[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
+                                                     __builtin_bit_cast(bf16x8_t, b[j & 1]), c[j], 0, 0, 0);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  if (lane == 0) {
+    out[2 * wid] = __float_as_uint(s);
+    out[2 * wid + 1] = (uint32_t)(t1 - t0);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_probe(int blocks, int waves, int iters, uint32_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(64 * waves), 0, stream, iters, out);
+  return hipGetLastError();
+}
+
 }  // namespace skv

@@ -191,6 +191,17 @@ def test_hbm_probe_argument_errors():
     assert lib.skv_hbm_read_probe(4096, 1024, None, 8, None) == -1
 
 
+def test_mfma_probe_argument_errors():
+    # checked before any launch (the output address is never dereferenced)
+    lib = skv._lib
+    out = ctypes.c_void_p(4096)
+    for blocks, waves, iters in [(0, 4, 8), (70000, 4, 8), (8, 0, 8), (8, 9, 8), (8, 4, 0),
+                                 (8, 4, (1 << 24) + 1)]:
+        st = lib.skv_mfma_probe(out, blocks, waves, iters, None)
+        assert st == -1, (blocks, waves, iters, st)
+    assert lib.skv_mfma_probe(None, 8, 4, 8, None) == -1
+
+
 def test_softmax_scale_must_be_positive_and_finite():
     # the MLA kernel's overflow threshold divides by the scale: zero, -0.0,
     # negative and non-finite scales are refused before any launch, by the

@@ -245,3 +245,48 @@ def test_hbm_read_probe_reads_every_word():
     for blocks in (1, 7, 512):
         out = skv.hbm_read_probe(buf, blocks).cpu().numpy().view(np.uint32)
         assert np.bitwise_xor.reduce(out) == np.bitwise_xor.reduce(words)
+
+
+def _mix32(x):
+    x = np.uint64(x) & np.uint64(0xFFFFFFFF)
+    x ^= x >> np.uint64(16); x = (x * np.uint64(0x7feb352d)) & np.uint64(0xFFFFFFFF)
+    x ^= x >> np.uint64(15); x = (x * np.uint64(0x846ca68b)) & np.uint64(0xFFFFFFFF)
+    x ^= x >> np.uint64(16)
+    return int(x)
+
+
+def _bf16_pair(h):
+    # two bf16 values (sign, exponent 124..127, seven mantissa bits) from a hash
+    out = []
+    for half in (h & 0xFFFF, h >> 16):
+        bits = (half & 0x807F) | ((124 + ((half >> 7) & 3)) << 7)
+        out.append(np.array([bits << 16], dtype=np.uint32).view(np.float32)[0])
+    return out
+
+
+def test_mfma_probe_products_and_cycles():
+    # The probe's first wave recomputed on the host: operand lane layout of the
+    # 16x16x32 bf16 product (lane L holds row/column L % 16 and k = 8 (L / 16)
+    # .. + 7 of A and B; lane 0's results are rows 0-3 of column 0). With the
+    # operands fixed over the trips, each chain is iters * (A_j B_(j%2)).
+    iters, blocks, waves = 3, 2, 4
+    out = skv.mfma_probe(blocks, waves, iters, "cuda").cpu().numpy()
+    assert out.shape == (blocks * waves, 2)
+    A = np.zeros((8, 16, 32)); B = np.zeros((2, 32, 16))
+    for L in range(64):
+        for j in range(8):
+            for e in range(4):
+                lo, hi = _bf16_pair(_mix32(L * 64 + 4 * j + e))
+                A[j, L % 16, 8 * (L // 16) + 2 * e] = lo
+                A[j, L % 16, 8 * (L // 16) + 2 * e + 1] = hi
+        for j in range(2):
+            for e in range(4):
+                lo, hi = _bf16_pair(_mix32(0x9E3779B9 ^ (L * 8 + 4 * j + e)))
+                B[j, 8 * (L // 16) + 2 * e, L % 16] = lo
+                B[j, 8 * (L // 16) + 2 * e + 1, L % 16] = hi
+    want = sum(iters * (A[j] @ B[j % 2])[0:4, 0].sum() for j in range(8))
+    got = float(out[0, 0:1].view(np.float32)[0])
+    assert abs(got - want) <= 1e-4 * max(1.0, abs(want)), (got, want)
+    # every wave ran its loop: at least 16 cycles per product
+    cycles = out[:, 1].astype(np.uint32)
+    assert np.all(cycles >= 16 * 8 * iters), cycles
