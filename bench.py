@@ -64,6 +64,9 @@ def parse(argv=None):
                     help="skip the streaming-read probe of the practical HBM read ceiling")
     ap.add_argument("--no-mfma-probe", action="store_true",
                     help="skip the probe of the sustained dense bf16 matrix rate")
+    ap.add_argument("--probe-sweep", action="store_true",
+                    help="print the mixed product + HBM stream probe over a range of flop-per-byte "
+                         "ratios (one JSON line each) and exit")
     ap.add_argument("--plan-param", action="append", default=[], metavar="NAME=VALUE",
                     help="override one field of the planner parameters (repeatable)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -108,37 +111,74 @@ def hbm_probe(dev, num_cu: int, gib: int = 4, reps: int = 10) -> dict:
     return best
 
 
-def mfma_probe(dev, num_cu: int, iters: int = 32768, seconds: float = 1.0) -> dict:
-    """Sustained dense bf16 matrix rate: the library's matrix-core probe (one
-    work-group of four waves per CU, so one wave per SIMD, each keeping eight
-    independent 16x16x32 product chains busy on pseudo-random operands),
-    launched back to back for about `seconds` so that the clock settles
-    under the load; HIP events on the launch stream. The per-wave cycle
-    counts over the launch time give the clock the chip ran at."""
+def _timed_probe_runs(launch, seconds: float) -> float:
+    """Average launch time (ms) of `launch` run back to back for about
+    `seconds`, so that the clock settles under the load; HIP events on the
+    launch stream."""
     import time
     import torch
-    import split_kv_partial_amd as skv
-    waves = 4
-    out = torch.empty(num_cu * waves, 2, dtype=torch.int32, device=dev)
-    flops = num_cu * waves * iters * 8 * 16384
     for _ in range(3):
-        skv.mfma_probe(num_cu, waves, iters, dev, out)
+        launch()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     n = 0
     t_end = time.time() + seconds
     e0.record()
     while time.time() < t_end:
-        for _ in range(10):
-            skv.mfma_probe(num_cu, waves, iters, dev, out)
-        n += 10
+        for _ in range(5):
+            launch()
+        n += 5
         torch.cuda.synchronize()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / n
+    return e0.elapsed_time(e1) / n
+
+
+def mfma_probe(dev, num_cu: int, iters: int = 32768, seconds: float = 1.0) -> dict:
+    """Sustained dense bf16 matrix rate: the library's matrix-core probe (one
+    work-group of four waves per CU, so one wave per SIMD, each keeping eight
+    independent 16x16x32 product chains busy on pseudo-random operands). The
+    per-wave cycle counts over the launch time give the clock the chip ran
+    at."""
+    import torch
+    import split_kv_partial_amd as skv
+    waves = 4
+    out = torch.empty(num_cu * waves, 2, dtype=torch.int32, device=dev)
+    flops = num_cu * waves * iters * 8 * 16384
+    ms = _timed_probe_runs(lambda: skv.mfma_probe(num_cu, waves, iters, dev, out), seconds)
     cycles = float(np.median(out[:, 1].cpu().numpy().astype(np.uint32)))
-    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "launch_ms": round(ms, 4), "launches": n,
+    return {"tflops": round(flops / (ms * 1e-3) / 1e12, 1), "launch_ms": round(ms, 4),
             "cycles_per_product": round(cycles / (8 * iters), 3), "est_ghz": round(cycles / (ms * 1e6), 3)}
+
+
+def mixed_probe(dev, num_cu: int, flop_per_byte: float, gib: int = 4, passes: int = 2,
+                seconds: float = 1.0) -> dict:
+    """What a launch that does nothing but bf16 products and an HBM stream
+    reaches at the given flop-per-byte ratio: the matrix-core probe with four
+    product waves and four streaming waves per CU (one of each per SIMD),
+    `passes` non-temporal passes over a `gib` GiB buffer of random words and
+    as many products as the ratio asks. Both parts run at once, under the
+    chip's power and clock management, with no other work."""
+    import torch
+    import split_kv_partial_amd as skv
+    nbytes = gib << 30
+    buf = torch.empty(nbytes // 4, dtype=torch.int32, device=dev)
+    buf.random_()
+    waves, mw = 8, 4
+    B = passes * nbytes
+    iters = max(1, int(round(flop_per_byte * B / (num_cu * mw * 8 * 16384))))
+    F = num_cu * mw * iters * 8 * 16384
+    out = torch.empty(num_cu * waves, 2, dtype=torch.int32, device=dev)
+    ms = _timed_probe_runs(lambda: skv.mfma_probe(num_cu, waves, iters, dev, out, mfma_waves=mw, buf=buf,
+                                                  passes=passes), seconds)
+    cyc = out[:, 1].cpu().numpy().astype(np.uint32).reshape(num_cu, waves).astype(np.float64)
+    c_mfma, c_stream = float(np.median(cyc[:, :mw])), float(np.median(cyc[:, mw:]))
+    del buf
+    torch.cuda.synchronize()
+    return {"flop_per_byte": round(F / B, 1), "gbs": round(B / (ms * 1e-3) / 1e9, 1),
+            "tflops": round(F / (ms * 1e-3) / 1e12, 1), "launch_ms": round(ms, 4), "bytes": B, "flops": F,
+            "est_ghz": round(max(c_mfma, c_stream) / (ms * 1e6), 3),
+            "longer_part": "products" if c_mfma >= c_stream else "stream"}
 
 
 def plan_overrides(items):
@@ -511,6 +551,12 @@ def main(argv=None):
     assert torch.cuda.is_available(), "bench needs a GPU"
     dev = torch.device("cuda:0")
     num_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    if args.probe_sweep:
+        print(json.dumps({"probe": "hbm", **hbm_probe(dev, num_cu)}), flush=True)
+        print(json.dumps({"probe": "mfma", **mfma_probe(dev, num_cu)}), flush=True)
+        for r in (32, 64, 128, 192, 242, 320, 512, 1024):
+            print(json.dumps({"probe": "mixed", **mixed_probe(dev, num_cu, float(r))}), flush=True)
+        return
     plan_params = plan_overrides(args.plan_param)
     head_key = HEADLINE if args.workload == "all" else args.workload
     rest = PER_CONFIG if args.workload == "all" else ()
@@ -539,9 +585,18 @@ def main(argv=None):
             probe = hbm_probe(dev, num_cu)
         except (RuntimeError, MemoryError) as e:   # torch reports device OOM as RuntimeError
             print(f"[bench] HBM probe skipped: {e}", file=sys.stderr, flush=True)
-    mprobe = None
+    mprobe = xprobe = None
     if not args.no_mfma_probe:
         mprobe = mfma_probe(dev, num_cu)
+        if head_w.mla:
+            # the products and the KV stream of the headline launch, in its
+            # proportion, with nothing else
+            try:
+                xprobe = mixed_probe(dev, num_cu, attention_flops(head_w) / kv_bytes(head_w))
+            except (RuntimeError, MemoryError) as e:
+                print(f"[bench] mixed probe skipped: {e}", file=sys.stderr, flush=True)
+        if xprobe and head["roofline"]["unit"] == "GB/s":
+            head["roofline"]["frac_of_mixed_probe"] = round(head["roofline"]["achieved"] / xprobe["gbs"], 4)
     for m in [head, *per.values()]:
         if probe:
             m["frac_of_probe"] = round(m["kv_gbs"] / probe["gbs"], 4)
@@ -583,6 +638,8 @@ def main(argv=None):
         out["frac_of_probe"] = head["frac_of_probe"]
     if mprobe:
         out["mfma_probe"] = mprobe
+    if xprobe:
+        out["mixed_probe"] = xprobe
     if "cpu_baseline" in head:
         out["cpu_baseline"] = head["cpu_baseline"]
     if per:

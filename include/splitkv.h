@@ -336,16 +336,23 @@ skv_status skv_read_error_flag(const void* workspace, int32_t* flag, void* strea
 skv_status skv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,
                               void* stream);
 
-/* Measurement utility (not a step of the method): `blocks` work-groups of
- * `waves` waves (1..8 waves, blocks 1..65536, iters 1..2^24) each run
- * `iters` trips of eight independent bf16 v_mfma_f32_16x16x32 products on
- * pseudo-random register operands: 16384 * 8 * iters flop per wave. out:
- * device uint32[2 * blocks * waves]; for wave w (block-major) out[2w] holds
- * the bits of a float sum of its results and out[2w + 1] the shader-clock
- * cycles (s_memtime) its product loop took. Asynchronous on `stream`; the
- * caller times it. Used to state the bf16 matrix rate the chip sustains under
- * a dense load, the ceiling of matrix-bound attention launches. */
-skv_status skv_mfma_probe(uint32_t* out, int32_t blocks, int32_t waves, int32_t iters, void* stream);
+/* Measurement utility (not a step of the method): `blocks` work-groups
+ * (1..65536) of `waves` waves (1..8). The first `mfma_waves` (0..waves) of
+ * each run `iters` (0..2^24) trips of eight independent bf16
+ * v_mfma_f32_16x16x32 products on pseudo-random register operands (16384 * 8
+ * * iters flop per wave); the others together read the `bytes` bytes at
+ * device address `buf` `passes` times (0..1024) with the non-temporal hint
+ * (buf 16-byte aligned, bytes a positive multiple of 16; not read, and may be
+ * NULL, when mfma_waves == waves). out: device uint32[2 * blocks * waves];
+ * for wave w (block-major) out[2w] holds a word folded from its results (the
+ * bits of a float sum of its products for a product wave) and out[2w + 1]
+ * the shader-clock cycles (s_memtime) of its loop. Asynchronous on `stream`;
+ * the caller times it. Used to state the bf16 matrix rate the chip sustains
+ * under a dense load, and the rate of a launch that runs nothing but products
+ * and an HBM stream in a given proportion: the ceilings of matrix-side
+ * attention launches. */
+skv_status skv_mfma_probe(const void* buf, int64_t bytes, int32_t passes, uint32_t* out, int32_t blocks,
+                          int32_t waves, int32_t mfma_waves, int32_t iters, void* stream);
 
 /* Thread-local message for the last non-OK status of this thread. */
 const char* skv_last_error(void);

@@ -104,7 +104,7 @@ def _load():
         "skv_decode_attn_noalloc": (I32, [pdesc, P, P, P, P, P, P, P, I32, P, P, P, I32, P, P]),
         "skv_read_error_flag": (I32, [P, pi32, P]),
         "skv_hbm_read_probe": (I32, [P, I64, P, I32, P]),
-        "skv_mfma_probe": (I32, [P, I32, I32, I32, P]),
+        "skv_mfma_probe": (I32, [P, I64, I32, P, I32, I32, I32, I32, P]),
         "skv_last_error": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -509,16 +509,24 @@ def hbm_read_probe(buf: torch.Tensor, blocks: int, out: torch.Tensor | None = No
     return out
 
 
-def mfma_probe(blocks: int, waves: int, iters: int, device, out: torch.Tensor | None = None) -> torch.Tensor:
-    """Dense bf16 matrix-core load (a measurement utility for the sustained
-    matrix rate, not a step of the method): `blocks` work-groups of `waves`
-    waves, each wave 8 * iters products of 16x16x32. Returns out
-    [blocks * waves, 2] int32: per wave the bits of a float sum of its results
-    and the shader-clock cycles of its product loop."""
+def mfma_probe(blocks: int, waves: int, iters: int, device, out: torch.Tensor | None = None,
+               mfma_waves: int | None = None, buf: torch.Tensor | None = None, passes: int = 0) -> torch.Tensor:
+    """Dense bf16 matrix-core load, optionally beside an HBM stream (a
+    measurement utility for the sustained matrix rate, not a step of the
+    method): `blocks` work-groups of `waves` waves; the first `mfma_waves`
+    (default: all) run 8 * iters products of 16x16x32 each, the others read
+    the contiguous device tensor `buf` `passes` times. Returns out
+    [blocks * waves, 2] int32: per wave a word folded from its results and the
+    shader-clock cycles of its loop."""
+    mw = waves if mfma_waves is None else mfma_waves
     if out is None:
         out = torch.empty(blocks * waves, 2, dtype=torch.int32, device=device)
     if not out.is_contiguous() or out.numel() < 2 * blocks * waves:
         raise ValueError("out must be a contiguous device tensor of 2 * blocks * waves int32")
-    _check(_lib.skv_mfma_probe(out.data_ptr(), int(blocks), int(waves), int(iters), _stream_ptr()),
+    if mw < waves and (buf is None or not buf.is_contiguous() or buf.device.type != "cuda"):
+        raise ValueError("streaming waves need buf, a contiguous device tensor")
+    ptr, nbytes = (buf.data_ptr(), buf.numel() * buf.element_size()) if buf is not None else (None, 0)
+    _check(_lib.skv_mfma_probe(ptr, nbytes, int(passes), out.data_ptr(), int(blocks), int(waves), int(mw),
+                               int(iters), _stream_ptr()),
            "skv_mfma_probe")
     return out

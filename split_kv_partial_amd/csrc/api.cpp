@@ -725,12 +725,21 @@ skv_status skv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* out, int
   return SKV_OK;
 }
 
-skv_status skv_mfma_probe(uint32_t* out, int32_t blocks, int32_t waves, int32_t iters, void* stream) {
+skv_status skv_mfma_probe(const void* buf, int64_t bytes, int32_t passes, uint32_t* out, int32_t blocks,
+                          int32_t waves, int32_t mfma_waves, int32_t iters, void* stream) {
   if (!out) return fail(SKV_ERR_INVALID_ARG, "out is NULL");
   if (blocks < 1 || blocks > 65536) return fail(SKV_ERR_INVALID_ARG, "blocks must be in [1, 65536]");
   if (waves < 1 || waves > 8) return fail(SKV_ERR_INVALID_ARG, "waves must be in [1, 8]");
-  if (iters < 1 || iters > (1 << 24)) return fail(SKV_ERR_INVALID_ARG, "iters must be in [1, 2^24]");
-  hipError_t e = launch_mfma_probe(blocks, waves, iters, out, (hipStream_t)stream);
+  if (mfma_waves < 0 || mfma_waves > waves) return fail(SKV_ERR_INVALID_ARG, "mfma_waves must be in [0, waves]");
+  if (iters < 0 || iters > (1 << 24)) return fail(SKV_ERR_INVALID_ARG, "iters must be in [0, 2^24]");
+  if (mfma_waves < waves) {   // streaming waves read the buffer
+    if (!buf) return fail(SKV_ERR_INVALID_ARG, "buf is NULL but the launch has streaming waves");
+    if ((uintptr_t)buf % 16 != 0) return fail(SKV_ERR_INVALID_ARG, "buf must be 16-byte aligned");
+    if (bytes <= 0 || bytes % 16 != 0) return fail(SKV_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+    if (passes < 0 || passes > 1024) return fail(SKV_ERR_INVALID_ARG, "passes must be in [0, 1024]");
+  }
+  hipError_t e = launch_mfma_probe(buf, mfma_waves < waves ? bytes : 0, mfma_waves < waves ? passes : 0, blocks,
+                                   waves, mfma_waves, iters, out, (hipStream_t)stream);
   if (e != hipSuccess) return fail(SKV_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
   return SKV_OK;
 }

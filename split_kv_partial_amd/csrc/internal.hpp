@@ -172,7 +172,8 @@ hipError_t launch_gqa_valu_fused(const AttnLaunch& a, const FusedLaunch& f);
 hipError_t launch_gqa_mfma_fused(const AttnLaunch& a, const FusedLaunch& f);
 hipError_t launch_mla_mfma_fused(const AttnLaunch& a, const FusedLaunch& f);
 hipError_t launch_hbm_probe(const void* buf, int64_t bytes, uint32_t* out, int blocks, hipStream_t stream);
-hipError_t launch_mfma_probe(int blocks, int waves, int iters, uint32_t* out, hipStream_t stream);
+hipError_t launch_mfma_probe(const void* buf, int64_t bytes, int passes, int blocks, int waves, int mfma_waves,
+                             int iters, uint32_t* out, hipStream_t stream);
 
 // Error reporting shared by the entry points: sets the thread-local message
 // that skv_last_error returns and gives back st.

@@ -42,16 +42,21 @@ hipError_t launch_hbm_probe(const void* buf, int64_t bytes, uint32_t* out, int b
 }
 
 
-// Matrix-core throughput probe: a measurement utility beside the attention
-// path, like the read probe above. Each wave keeps eight independent bf16
-// v_mfma_f32_16x16x32 accumulation chains busy for `iters` trips; the eight
-// A operands differ from one product to the next and hold pseudo-random bf16
-// values (signs, exponents 2^-3..2^0, full mantissas), so the multipliers see
-// changing data as they do under attention. It states the bf16 product rate
-// the chip sustains under a dense matrix load (power and clock included), the
-// ceiling beside which a matrix-bound attention kernel is read. Per wave it
-// writes the sum of its lane-0 accumulators (so no product is dropped) and
-// the shader-clock cycles the loop took.
+// Matrix-core and mixed-load probe: a measurement utility beside the
+// attention path, like the read probe above. The first `mfma_waves` waves of
+// each work-group keep eight independent bf16 v_mfma_f32_16x16x32 chains busy
+// for `iters` trips; their eight A operands differ from one product to the
+// next and hold pseudo-random bf16 values (signs, exponents 2^-3..2^0, full
+// mantissas), so the multipliers see changing data as they do under
+// attention. The other waves of the work-group stream `passes` passes over a
+// buffer with the non-temporal hint (16 loads of 16 bytes in flight per lane),
+// so that a launch can put the products and an HBM stream on the chip at the
+// same time, in any proportion. It states the bf16 product rate the chip
+// sustains under a dense matrix load alone, and what a launch that does
+// nothing but products and a stream reaches at a given flop-per-byte ratio
+// (power and clock included): the ceilings beside which a matrix-side
+// attention launch is read. Per wave it writes a word folded from its results
+// (so no product or load is dropped) and the shader-clock cycles it took.
 namespace {
 
 __device__ __forceinline__ uint32_t mix32(uint32_t x) {   // a 32-bit integer hash (xorshift-multiply)
@@ -67,42 +72,77 @@ __device__ __forceinline__ uint32_t rand_bf16x2(uint32_t h) {
   return lo | (hi << 16);
 }
 
-__global__ __launch_bounds__(512) void mfma_probe_kernel(int iters, uint32_t* out) {
-  const uint32_t lane = threadIdx.x & 63;
-  const uint32_t wid = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-  u32x4_t a[8], b[2];
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a[j][e] = rand_bf16x2(mix32((wid * 64 + lane) * 64 + 4 * j + e));
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) b[j][e] = rand_bf16x2(mix32(0x9e3779b9u ^ ((wid * 64 + lane) * 8 + 4 * j + e)));
-  f32x4_t c[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) c[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint64_t t0 = __builtin_amdgcn_s_memtime();
-  for (int i = 0; i < iters; ++i) {
+__global__ __launch_bounds__(512) void mfma_probe_kernel(const u32x4_t* buf, int64_t n16, int passes, int iters,
+                                                         int mfma_waves, uint32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wpb = blockDim.x >> 6;
+  const uint32_t wid = blockIdx.x * wpb + wave;
+  uint32_t res;
+  uint64_t t0, t1;
+  if (wave < mfma_waves) {
+    u32x4_t a[8], b[2];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
-                                                     __builtin_bit_cast(bf16x8_t, b[j & 1]), c[j], 0, 0, 0);
-  }
-  float s = 0.f;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
-  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+      for (int e = 0; e < 4; ++e) a[j][e] = rand_bf16x2(mix32((wid * 64 + lane) * 64 + 4 * j + e));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) b[j][e] = rand_bf16x2(mix32(0x9e3779b9u ^ ((wid * 64 + lane) * 8 + 4 * j + e)));
+    f32x4_t c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    t0 = __builtin_amdgcn_s_memtime();
+    for (int i = 0; i < iters; ++i) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[j]),
+                                                       __builtin_bit_cast(bf16x8_t, b[j & 1]), c[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+    t1 = __builtin_amdgcn_s_memtime();
+    res = __float_as_uint(s);   // lane 0's value is the one written
+  } else {
+    // the streaming waves of the grid read the buffer grid-stride, lane by lane
+    const int sw = wpb - mfma_waves;
+    const int64_t nthreads = (int64_t)gridDim.x * sw * 64;
+    const int64_t tid = ((int64_t)blockIdx.x * sw + (wave - mfma_waves)) * 64 + lane;
+    uint32_t acc = 0;
+    t0 = __builtin_amdgcn_s_memtime();
+    for (int p = 0; p < passes; ++p) {
+      int64_t i = tid;
+      constexpr int kU = 16;
+      for (; i + (kU - 1) * nthreads < n16; i += kU * nthreads) {
+        u32x4_t v[kU];
+#pragma unroll
+        for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * nthreads);
+#pragma unroll
+        for (int u = 0; u < kU; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+      }
+      for (; i < n16; i += nthreads) {
+        const u32x4_t v = __builtin_nontemporal_load(buf + i);
+        acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      }
+    }
+    t1 = __builtin_amdgcn_s_memtime();
+    for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m, 64);
+    res = acc;
+  }
   if (lane == 0) {
-    out[2 * wid] = __float_as_uint(s);
+    out[2 * wid] = res;
     out[2 * wid + 1] = (uint32_t)(t1 - t0);
   }
 }
 
 }  // namespace
 
-hipError_t launch_mfma_probe(int blocks, int waves, int iters, uint32_t* out, hipStream_t stream) {
-  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(64 * waves), 0, stream, iters, out);
+hipError_t launch_mfma_probe(const void* buf, int64_t bytes, int passes, int blocks, int waves, int mfma_waves,
+                             int iters, uint32_t* out, hipStream_t stream) {
+  hipLaunchKernelGGL(mfma_probe_kernel, dim3(blocks), dim3(64 * waves), 0, stream,
+                     static_cast<const u32x4_t*>(buf), bytes / 16, passes, iters, mfma_waves, out);
   return hipGetLastError();
 }
 

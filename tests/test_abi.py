@@ -192,14 +192,19 @@ def test_hbm_probe_argument_errors():
 
 
 def test_mfma_probe_argument_errors():
-    # checked before any launch (the output address is never dereferenced)
+    # checked before any launch (no address here is dereferenced)
     lib = skv._lib
     out = ctypes.c_void_p(4096)
-    for blocks, waves, iters in [(0, 4, 8), (70000, 4, 8), (8, 0, 8), (8, 9, 8), (8, 4, 0),
-                                 (8, 4, (1 << 24) + 1)]:
-        st = lib.skv_mfma_probe(out, blocks, waves, iters, None)
-        assert st == -1, (blocks, waves, iters, st)
-    assert lib.skv_mfma_probe(None, 8, 4, 8, None) == -1
+    for blocks, waves, mw, iters in [(0, 4, 4, 8), (70000, 4, 4, 8), (8, 0, 0, 8), (8, 9, 9, 8),
+                                     (8, 4, 5, 8), (8, 4, -1, 8), (8, 4, 4, -1), (8, 4, 4, (1 << 24) + 1)]:
+        st = lib.skv_mfma_probe(None, 0, 0, out, blocks, waves, mw, iters, None)
+        assert st == -1, (blocks, waves, mw, iters, st)
+    assert lib.skv_mfma_probe(None, 0, 0, None, 8, 4, 4, 8, None) == -1
+    # streaming waves need a readable, aligned buffer of whole 16-byte chunks
+    for buf, nbytes, passes in [(None, 1024, 1), (4096 + 8, 1024, 1), (4096, 1000, 1), (4096, 0, 1),
+                                (4096, 1024, -1), (4096, 1024, 2000)]:
+        st = lib.skv_mfma_probe(buf, nbytes, passes, out, 8, 8, 4, 8, None)
+        assert st == -1, (buf, nbytes, passes, st)
 
 
 def test_softmax_scale_must_be_positive_and_finite():

@@ -290,3 +290,17 @@ def test_mfma_probe_products_and_cycles():
     # every wave ran its loop: at least 16 cycles per product
     cycles = out[:, 1].astype(np.uint32)
     assert np.all(cycles >= 16 * 8 * iters), cycles
+
+
+def test_mfma_probe_streaming_waves_read_every_word():
+    # with product and streaming waves together, the streaming waves' words
+    # combine to the XOR of the buffer over one pass and cancel over two
+    n = (16 << 20) // 4 + 4 * 21   # words; not a multiple of the grid stride
+    words = np.random.default_rng(2).integers(0, 2**32, size=n, dtype=np.uint64).astype(np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    blocks, waves, mw = 5, 8, 3
+    for passes, want in ((1, np.bitwise_xor.reduce(words)), (2, np.uint32(0))):
+        out = skv.mfma_probe(blocks, waves, 4, "cuda", mfma_waves=mw, buf=buf, passes=passes)
+        got = out.cpu().numpy().view(np.uint32).reshape(blocks, waves, 2)
+        assert np.bitwise_xor.reduce(got[:, mw:, 0].ravel()) == want, passes
+        assert np.all(got[:, :, 1] > 0)
