@@ -86,7 +86,12 @@ def gather_kv(w, b: int, upto: int | None = None):
     pids = w.page_table[b, :npg].astype(np.int64)
     if w.mla:
         rows = w.k_pages[pids]                              # [npg][P][576]
-        rows = to_f64(rows, w.dtype).reshape(npg * P, 1, w.head_dim_qk)[:L]
+        if w.dtype == "fp8":
+            # every row of a page takes the page's scale
+            rows = e4m3_to_f64(rows) * w.k_scale[pids].astype(np.float64)[:, :, None]
+        else:
+            rows = to_f64(rows, w.dtype)
+        rows = rows.reshape(npg * P, 1, w.head_dim_qk)[:L]
         return rows, rows[:, :, : w.head_dim_v]
     k = w.k_pages[pids]                                     # [npg][H][D/X][P][X]
     k = np.transpose(k, (0, 3, 1, 2, 4)).reshape(npg * P, w.num_kv_heads, w.head_dim_qk)

@@ -8,7 +8,9 @@ binade, sign symmetry), to an independent implementation (PyTorch's
 float8_e4m3fn conversion, all 256 codes), and each planted mistake below fails
 at least one pin. The paged gather of an FP8 workload is checked by brute force
 against a per-element loop, and attention over it equals attention over an fp32
-workload that stores the decoded values."""
+workload that stores the decoded values; the same for FP8 MLA latent rows, whose
+one scale per page covers both the keys and the values (the rows' first 512
+codes)."""
 import math
 
 import numpy as np
@@ -151,3 +153,75 @@ def test_fp8_attention_equals_fp32_on_decoded_values():
         of, lf = A.attention_rows(wf, b, ids)
         # the only difference is the float32 rounding of code * scale
         assert np.allclose(o8, of, rtol=1e-6, atol=1e-6) and np.allclose(l8, lf, rtol=1e-6, atol=1e-6)
+
+
+def _fp8_mla_case(seed=4, P=16, heads=16):
+    return wl.build("fp8-mla-small", dtype="fp8", mla=True, seq_lens=[37, 16, 90], q_lens=[1, 2, 1],
+                    num_q_heads=heads, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=P,
+                    scale=1.0 / math.sqrt(192.0), seed=seed, value_scale=0.1)
+
+
+def test_mla_generator_codes_and_scales():
+    w = _fp8_mla_case()
+    assert w.k_pages.dtype == np.uint8 and w.k_pages.shape == (w.num_pages, 16, 576)
+    assert w.v_pages is None and w.k_scale.shape == (w.num_pages, 1) and w.v_scale is w.k_scale
+    used = w.logical_to_physical
+    assert np.all(w.k_scale[used] > 0)
+    # one scale per page: the largest magnitude of each fully used page maps to
+    # 448 (the tail slots of a request's last page are poisoned after scaling)
+    P = w.page_size
+    full = [int(w.page_table[b, p]) for b in range(w.batch) for p in range(int(w.seq_lens[b]) // P)]
+    vals = A.e4m3_to_f64(w.k_pages[full]).reshape(len(full), -1)
+    assert len(full) >= 4 and np.all(np.max(np.abs(vals), axis=1) == 448.0)
+    spare = np.setdiff1d(np.arange(w.num_pages), used)
+    assert np.all(np.isnan(w.k_scale[spare]))
+
+
+def test_mla_gather_fp8_brute_force():
+    # a latent row is its codes' E4M3 values times its page's scale; the value
+    # is the row's first 512 entries
+    w = _fp8_mla_case()
+    P = w.page_size
+    for b in range(w.batch):
+        K, V = A.gather_kv(w, b)
+        L = int(w.seq_lens[b])
+        assert K.shape == (L, 1, 576) and V.shape == (L, 1, 512)
+        for j in range(L):
+            pid = int(w.page_table[b, j // P])
+            for d in (0, 7, 300, 511, 512, 575):
+                want = A.e4m3_value(int(w.k_pages[pid, j % P, d])) * float(w.k_scale[pid, 0])
+                assert K[j, 0, d] == want
+                if d < 512:
+                    assert V[j, 0, d] == want
+
+
+def test_mla_fp8_attention_equals_fp32_on_decoded_values():
+    # an fp32 MLA workload storing the decoded rows (code value times scale,
+    # rounded to float32) agrees with the FP8 one to that rounding
+    w = _fp8_mla_case(seed=10)
+    kd = A.e4m3_to_f64(w.k_pages) * w.k_scale.astype(np.float64)[:, :, None]
+    wf = wl.Workload(**{**w.__dict__})
+    wf.dtype = "f32"
+    wf.q = A.to_f64(w.q, "fp8").astype(np.float32)
+    wf.k_pages = kd.astype(np.float32)
+    wf.k_scale = wf.v_scale = None
+    for b in range(w.batch):
+        ids = list(range(int(w.q_lens[b])))
+        o8, l8 = A.attention_rows(w, b, ids)
+        of, lf = A.attention_rows(wf, b, ids)
+        assert np.allclose(o8, of, rtol=1e-6, atol=1e-7) and np.allclose(l8, lf, rtol=1e-6, atol=1e-6)
+
+
+def test_mla_fp8_scale_is_per_page():
+    # doubling one page's scale doubles exactly the rows of that page
+    w = _fp8_mla_case(seed=11)
+    b = 2
+    K0, _ = A.gather_kv(w, b)
+    pid = int(w.page_table[b, 1])
+    w.k_scale = w.k_scale.copy()
+    w.k_scale[pid, 0] *= 2
+    w.v_scale = w.k_scale
+    K1, _ = A.gather_kv(w, b)
+    P = w.page_size
+    assert np.array_equal(K1[P:2 * P], 2 * K0[P:2 * P])
+    assert np.array_equal(K1[:P], K0[:P]) and np.array_equal(K1[2 * P:], K0[2 * P:])

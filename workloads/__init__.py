@@ -28,7 +28,9 @@ FP8 KV (``dtype="fp8"``): queries are bf16; keys and values are OCP E4M3 codes
 (``numpy.uint8``) in the GQA layouts above with X = 16, and every (page, KV
 head) block has a float32 scale for its keys and one for its values
 (``k_scale`` / ``v_scale`` ``[num_pages][H_kv]``): the stored value is
-code_value * scale. They are drawn as the float32 normals described below,
+code_value * scale. MLA latent rows in FP8 keep the ``[num_pages][P][576]``
+layout with one scale per page (``k_scale [num_pages][1]``; ``v_scale`` is the
+same array, the values being the rows' first 512 codes). They are drawn as the float32 normals described below,
 divided by their block's max |x| / 448 (so the block's largest value maps to
 E4M3's largest finite value) and cast to E4M3 by PyTorch's float8_e4m3fn
 conversion (round to nearest even). Unused slots hold the NaN code 0x7F and the
@@ -130,7 +132,7 @@ class Workload:
     lse_ext: np.ndarray | None = None  # float32 [n_ext][total_rows]
     chunk_tokens: int | None = None    # explicit fixed-chunk split plan, if the config asks for one
     k_scale: np.ndarray | None = None  # fp8: float32 [N][H_kv], key scale per page and KV head
-    v_scale: np.ndarray | None = None  # fp8: float32 [N][H_kv], value scale per page and KV head
+    v_scale: np.ndarray | None = None  # fp8: float32 [N][H_kv], value scale (MLA: k_scale itself)
     meta: dict = field(default_factory=dict)
 
     @property
@@ -158,10 +160,10 @@ class Workload:
         return 16 // KV_BYTES[self.dtype]
 
     def kv_bytes_per_token(self) -> float:
-        """KV bytes per token (fp8: plus its share of the two per-page scales)."""
+        """KV bytes per token (fp8: plus its share of the per-page scales)."""
         b = KV_BYTES[self.dtype]
         if self.mla:
-            return self.head_dim_qk * b
+            return self.head_dim_qk * b + (4 / self.page_size if self.dtype == "fp8" else 0)
         per = self.num_kv_heads * (self.head_dim_qk + self.head_dim_v) * b
         if self.dtype == "fp8":
             per += self.num_kv_heads * 8 / self.page_size
@@ -236,8 +238,22 @@ def build(name: str, *, dtype: str, mla: bool, seq_lens, q_lens=None, num_q_head
     q = np.empty((total_q, H_q, head_dim_qk), np.uint16 if dtype == "fp8" else el)
     fill_normal(q, kids["q"], scale=value_scale * q_scale)
     k_scale = v_scale = None
-    if dtype == "fp8":
-        assert not mla and head_dim_qk % 16 == 0
+    if dtype == "fp8" and mla:
+        # one block (and one scale) per page: the page's 576-wide rows, whose
+        # first 512 entries are also the values
+        assert H_kv == 1
+        k32 = np.empty((N, 1, P, head_dim_qk), np.float32)
+        fill_normal(k32, kids["k"], scale=value_scale)
+        codes = np.empty(k32.shape, np.uint8)
+        k_scale = np.empty((N, 1), np.float32)
+        _fp8_blocks(k32, codes, k_scale)
+        del k32
+        k_pages = codes.reshape(N, P, head_dim_qk)
+        v_pages = None
+        k_scale[spare] = np.nan
+        v_scale = k_scale
+    elif dtype == "fp8":
+        assert head_dim_qk % 16 == 0
         X = 16
         k32 = np.empty((N, H_kv, head_dim_qk // X, P, X), np.float32)
         v32 = np.empty((N, H_kv, head_dim_v, P), np.float32)
@@ -304,7 +320,8 @@ def build(name: str, *, dtype: str, mla: bool, seq_lens, q_lens=None, num_q_head
 # step (LiquidCP section 7.1: 16 query tokens per request and iteration, one
 # target token and 15 drafts) on a GQA group of 8, where the 16 tokens' rows
 # make the products dense enough for the matrix cores; workload 7 is workload
-# 2 over an FP8 E4M3 KV cache.
+# 2 over an FP8 E4M3 KV cache, workload 8 workload 3 over an FP8 E4M3 latent
+# cache.
 # --------------------------------------------------------------------------------------
 
 MLA_DQK, MLA_DV, MLA_HEADS = 576, 512, 128
@@ -343,11 +360,13 @@ def config_lengths(cid: int):
         return L, np.full(32, 16, np.int64)
     if cid == 7:
         return config_lengths(2)
+    if cid == 8:
+        return config_lengths(3)
     raise ValueError(cid)
 
 
 def make(cid: int, sharp: bool = False, decode_only: bool = False) -> Workload:
-    """Benchmark workload ``cid`` (1..7). ``sharp`` scales q so that scores have a
+    """Benchmark workload ``cid`` (1..8). ``sharp`` scales q so that scores have a
     standard deviation of about 3 (a near-uniform softmax cannot reveal a wrong
     QK^T). ``decode_only`` (workload 5) drops the chunked-prefill request and the
     external states, leaving the eight million-token decode requests."""
@@ -388,6 +407,13 @@ def make(cid: int, sharp: bool = False, decode_only: bool = False) -> Workload:
                      num_q_heads=128, num_kv_heads=8, head_dim_qk=128, head_dim_v=128,
                      page_size=16, scale=1.0 / math.sqrt(128.0), seed=seed,
                      q_scale=SHARP_GQA if sharp else 1.0)
+    if cid == 8:
+        # workload 3's shape and lengths over an FP8 E4M3 latent cache (SPLASH
+        # appendix C.1 serves its MLA backend from an FP8 E4M3 KV cache)
+        return build("deepseek-mla-fp8", dtype="fp8", mla=True, seq_lens=L, q_lens=n,
+                     num_q_heads=MLA_HEADS, num_kv_heads=1, head_dim_qk=MLA_DQK,
+                     head_dim_v=MLA_DV, page_size=64, scale=MLA_SCALE, seed=seed,
+                     value_scale=0.1, q_scale=SHARP_MLA if sharp else 1.0)
     if cid == 6:
         # causal rows: draft i sees the history and the tokens before it
         return build("spec-decode-gqa-g8", dtype="bf16", mla=False, seq_lens=L, q_lens=n,
