@@ -17,8 +17,9 @@ step time. ``per_config`` holds the same measurement for the other workloads
 (Llama-405B-shaped GQA share, DeepSeek-shaped MLA batch, skewed rollout tail,
 the whole million-token shard with its 2,048-token chunked-prefill query and
 16 external states per row, a speculative-decoding step of 16 query tokens
-per request on a GQA group of 8, and the Llama-405B-shaped share over an FP8
-E4M3 KV cache), each with its roofline and its CPU oracle baseline.
+per request on a GQA group of 8, the Llama-405B-shaped share over an FP8
+E4M3 KV cache, and the DeepSeek-shaped MLA batch over an FP8 E4M3 latent
+cache), each with its roofline and its CPU oracle baseline.
 ``--workload N`` runs one workload alone.
 """
 from __future__ import annotations
@@ -41,7 +42,7 @@ HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, vendor figure
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16 matrix cores, vendor figure
 METRIC = "decode attention KV GB/s (% of MI355X HBM peak) + tokens/s at 1 GPU"
 HEADLINE = "5d"
-PER_CONFIG = ("2", "3", "4", "5", "6", "7")
+PER_CONFIG = ("2", "3", "4", "5", "6", "7", "8")
 
 KERNEL_FILES = {
     "gqa_mfma": "split_kv_partial_amd/csrc/kernels/gqa_mfma.hip",
@@ -57,7 +58,7 @@ def parse(argv=None):
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", type=str, default="all",
-                    help="all (headline 5d plus 2-7), or one of 1-7 and 5d (the decode "
+                    help="all (headline 5d plus 2-8), or one of 1-8 and 5d (the decode "
                          "requests of workload 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-hbm-probe", action="store_true",
@@ -383,7 +384,9 @@ class Runner:
         self.o_ext = None if w.o_ext is None else torch.from_numpy(w.o_ext).to(dev)
         self.lse_ext = None if w.lse_ext is None else torch.from_numpy(w.lse_ext).to(dev)
         self.k_scale = None if w.k_scale is None else torch.from_numpy(w.k_scale).to(dev)
-        self.v_scale = None if w.v_scale is None else torch.from_numpy(w.v_scale).to(dev)
+        # FP8 MLA rows: one scale per page for keys and values (the same tensor)
+        self.v_scale = (self.k_scale if w.mla else
+                        None if w.v_scale is None else torch.from_numpy(w.v_scale).to(dev))
         dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": skv.FP8}[w.dtype]
         self.spec = skv.AttnSpec(w.num_q_heads, w.num_kv_heads, w.head_dim_qk, w.head_dim_v, w.page_size,
                                  dtype=dt, mla=w.mla, causal=w.causal)
@@ -472,9 +475,11 @@ def measure(w, key: str, dev, num_cu: int, args, plan_params) -> dict:
     fl = attention_flops(w)
     tokens = int(w.q_lens.sum())
     kern = kernel_of(w)
-    mixed = bool(np.any(w.q_lens > 1)) and w.mla and fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > kvb / (
-        HBM_PEAK_GBS * 1e9)
-    if mixed:
+    # the launch's bound: the matrix side when its products take longer at the
+    # bf16 peak than its KV bytes at the HBM peak (MLA chunk rows, and MLA
+    # over an FP8 cache at 484 flop/B)
+    mfma_bound = w.mla and fl / (MFMA_BF16_PEAK_TFLOPS * 1e12) > kvb / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
         ach = fl / (attn_avg * 1e-3) / 1e12
         roof = {"kernel": kern, "bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4),

@@ -30,7 +30,7 @@
  * GQA keys   [num_pages][H_kv][D/X][P][X] T; 16-byte chunks of X dimensions,
  *                                         tokens of a page adjacent per chunk.
  * GQA values [num_pages][H_kv][D_v][P]    T; per page and head, dimension-major.
- * MLA rows   [num_pages][P][D]            bf16, D = 576 (512 latent + 64 rope).
+ * MLA rows   [num_pages][P][D]            T = bf16 or E4M3, D = 576 (512 latent + 64 rope).
  *                                         The value of a token is the first
  *                                         D_v = 512 entries of its own row, so
  *                                         v_pages must equal k_pages (SPLASH,
@@ -49,6 +49,9 @@
  *                                         times k_scales[page][kv_head], a value
  *                                         likewise with v_scales (SPLASH,
  *                                         appendix C.1: an FP8 E4M3 KV cache).
+ *                                         MLA: one scale per page for the whole
+ *                                         row, keys and values alike, so
+ *                                         v_scales must equal k_scales.
  * Query token i of request b with n_b tokens sees KV positions
  * [0, L_b - n_b + i] when causal (bottom-right aligned), [0, L_b) otherwise.
  * KV head of query head h is h / (H_q / H_kv).
@@ -79,8 +82,8 @@ typedef int32_t skv_status;
 #define SKV_ERR_NO_MEMORY     -4   /* host allocation failed, or workspace too small */
 #define SKV_ERR_PLAN_MISMATCH -5   /* plan built for a different problem description */
 
-/* SKV_FP8_E4M3: bf16 queries; GQA keys and values stored as OCP E4M3 bytes
- * with float32 scales per (page, KV head) (skv_decode_attn_partial_fp8). */
+/* SKV_FP8_E4M3: bf16 queries; GQA keys and values, or MLA rows, stored as OCP
+ * E4M3 bytes with float32 scales per (page, KV head) (skv_decode_attn_partial_fp8). */
 typedef enum { SKV_F32 = 0, SKV_BF16 = 1, SKV_FP8_E4M3 = 2 } skv_dtype;
 
 /* Problem description, passed by value in host memory. */
@@ -252,9 +255,11 @@ skv_status skv_decode_attn_partial(const skv_attn_desc* desc, const void* q,
  * value scales [num_pages][H_kv] float32 (device). Each code is decoded
  * exactly (E4M3 values are bf16 values) and the products run on bf16 matrix
  * cores with fp32 accumulation; the key scale multiplies the block's scores,
- * the value scale its softmax weights. The other compute entry points reject
- * FP8 descriptions (SKV_ERR_INVALID_ARG); skv_merge_states merges the states
- * as any others. A NaN code yields NaN in the states that read it. */
+ * the value scale its softmax weights. GQA groups of 8 or 16, or MLA rows
+ * (v_pages == k_pages and v_scales == k_scales, one scale per page). The other
+ * compute entry points reject FP8 descriptions (SKV_ERR_INVALID_ARG);
+ * skv_merge_states merges the states as any others. A NaN code yields NaN in
+ * the states that read it. */
 skv_status skv_decode_attn_partial_fp8(const skv_attn_desc* desc, const void* q, const void* k_pages,
                                        const void* v_pages, const float* k_scales, const float* v_scales,
                                        const int32_t* page_table, const int32_t* seq_lens,

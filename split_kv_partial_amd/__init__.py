@@ -393,9 +393,11 @@ def decode_attn_partial(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, s
 def decode_attn_partial_fp8(q, k_pages, v_pages, k_scales, v_scales, page_table, seq_lens, plan: Plan,
                             scale: float, o_part=None, lse_part=None):
     """decode_attn_partial over an FP8 (OCP E4M3) KV cache: k_pages / v_pages
-    hold codes (uint8 or float8_e4m3fn) in the GQA layouts with X = 16, and
-    k_scales / v_scales [num_pages][H_kv] float32 the per-page, per-KV-head
-    factors of the decoded keys and values. The plan's spec has dtype FP8."""
+    hold codes (uint8 or float8_e4m3fn) in the GQA layouts with X = 16, or MLA
+    rows [num_pages][P][576] (v_pages is k_pages), and k_scales / v_scales
+    [num_pages][H_kv] float32 the per-page, per-KV-head factors of the decoded
+    keys and values (MLA: one scale per page, v_scales is k_scales). The plan's
+    spec has dtype FP8."""
     inf = plan.info()
     sp = plan.spec
     dev = q.device
@@ -409,6 +411,8 @@ def decode_attn_partial_fp8(q, k_pages, v_pages, k_scales, v_scales, page_table,
     n_pages = int(k_pages.shape[0])
     _check_tensor(k_scales, "k_scales", dev, (torch.float32,), shape=(n_pages, sp.num_kv_heads))
     _check_tensor(v_scales, "v_scales", dev, (torch.float32,), shape=(n_pages, sp.num_kv_heads))
+    if sp.mla and v_scales.data_ptr() != k_scales.data_ptr():
+        raise ValueError("FP8 MLA rows have one scale per page: v_scales must be k_scales")
     _check_tensor(o_part, "o_part", dev, (torch.float32,), numel=inf.state_rows * sp.head_dim_v)
     _check_tensor(lse_part, "lse_part", dev, (torch.float32,), numel=inf.state_rows)
     desc = _desc_for(plan, page_table, k_pages, scale)

@@ -82,9 +82,10 @@ skv_status check_desc(const skv_attn_desc* d) {
   if (d->causal != 0 && d->causal != 1) return fail(SKV_ERR_INVALID_ARG, "causal must be 0 or 1");
   if (d->mla) {
     if (d->mla != 1) return fail(SKV_ERR_INVALID_ARG, "mla must be 0 or 1");
-    if (d->num_kv_heads != 1 || d->head_dim_qk != 576 || d->head_dim_v != 512 || d->dtype != SKV_BF16)
+    if (d->num_kv_heads != 1 || d->head_dim_qk != 576 || d->head_dim_v != 512 ||
+        (d->dtype != SKV_BF16 && d->dtype != SKV_FP8_E4M3))
       return fail(SKV_ERR_UNSUPPORTED,
-                  "MLA needs bf16, num_kv_heads 1, head_dim_qk 576, head_dim_v 512");
+                  "MLA needs bf16 or FP8 E4M3 rows, num_kv_heads 1, head_dim_qk 576, head_dim_v 512");
     if (d->num_q_heads % 16 || d->num_q_heads > 128)
       return fail(SKV_ERR_UNSUPPORTED, "MLA needs num_q_heads a multiple of 16, at most 128 (got %d)",
                   d->num_q_heads);
@@ -543,6 +544,8 @@ skv_status check_attention(const skv_attn_desc* desc, const void* q, const void*
     return fail(SKV_ERR_INVALID_ARG, "scales go with FP8 KV only");
   if (desc->mla && v_pages != k_pages)
     return fail(SKV_ERR_INVALID_ARG, "MLA reads values from the key rows: v_pages must equal k_pages");
+  if (desc->mla && desc->dtype == SKV_FP8_E4M3 && v_scales != k_scales)
+    return fail(SKV_ERR_INVALID_ARG, "FP8 MLA rows have one scale per page: v_scales must equal k_scales");
   return SKV_OK;
 }
 

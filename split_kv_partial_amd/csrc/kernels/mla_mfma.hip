@@ -46,6 +46,7 @@ struct MlaArgs {
   int32_t* err_flag;
   float* o_part;
   float* lse_part;
+  const float* kv_scale;   // FP8 rows: float32 scale per page (NULL for bf16 rows)
   int32_t H_q, page_shift, max_pages, num_pages;
   float scale_log2;
 };
@@ -575,6 +576,378 @@ __device__ __forceinline__ void mla_task(const MlaArgs& a, const DevTask& task, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// FP8 (OCP E4M3) latent rows: [num_pages][P][576] one-byte codes with one
+// float32 scale per page (SPLASH appendix C.1 serves its MLA backend from an
+// FP8 E4M3 KV cache). A stored entry is its code's E4M3 value times the page's
+// scale; the value of a token is the first 512 entries of its row, under the
+// same scale. The tile loop is the bf16 one: each 32-token tile is read by the
+// products from a bf16 tile in the same swizzled LDS layout. The codes stream
+// HBM -> LDS in 64-token tiles (36 KB: the same nine 1 KB DMAs per wave as a
+// bf16 tile, so two compute tiles per DMA tile) into a ring of two, and the
+// work-group converts each 32-token half once into one of two bf16 tiles
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1: every E4M3 value is a bf16
+// value, so the codes are decoded exactly) one tile ahead of its products.
+// The page scale multiplies the tile's scores (folded into the exponent's
+// multiplier, and into the running maximum) and the softmax weights before
+// they are packed for P*V, while the normaliser sums the unscaled weights:
+// o = sum_j p_j (s_j c_j) / sum_j p_j with c_j the decoded codes.
+// Schedule: FP8 tile F (F >= 2) is sent at iteration 2F - 3 into the ring slot
+// that FP8 tile F - 2 left (both its halves converted by then), and is
+// converted from iteration 2F - 1 on; iteration k converts tile k + 1 and
+// computes tile k.
+// ---------------------------------------------------------------------------
+constexpr int kF8Tokens = 64;                      // tokens per FP8 DMA tile
+constexpr int kF8TileBytes = kF8Tokens * kD;       // 36,864: 36 DMA blocks of 1 KB
+constexpr int kF8HalfBytes = kT * kD;              // 18,432: the codes of one 32-token tile
+constexpr int kCvt = kT * kRowSlots / kThreads;    // 8-code chunks per lane per tile (9)
+static_assert(kF8TileBytes == kDmaPerTile * 1024 && kCvt == kDmaPerWave, "FP8 tiles reuse the DMA shape");
+
+typedef const __attribute__((address_space(4))) float const_f32_t;
+
+struct MlaShared8 {
+  __attribute__((aligned(16))) uint8_t f8[2][kF8TileBytes];
+  __attribute__((aligned(16))) uint16_t bf[2][kTileElems];
+  // per lane, its nine chunks of a tile: byte offset of the codes within the
+  // 32-token half (low 16 bits) and of the bf16 slot within the tile (high)
+  uint32_t cvt_lds[kWaves][kCvt * 64];
+  int restart_pass;
+};
+
+// Chunk i of lane `lane` of wave `wave`: wave w converts rows 8w..8w+7 of a
+// tile, its lanes taking the 576 chunks of 8 codes in order.
+__device__ __forceinline__ uint32_t cvt_entry(int wave, int i, int lane) {
+  const int idx = 64 * i + lane;
+  const int r = 8 * wave + idx / kRowSlots, c = idx % kRowSlots;
+  const uint32_t src = (uint32_t)(r * kD + 8 * c);
+  const uint32_t dst = (uint32_t)(16 * (kRowSlots * r + (c ^ swz(r))));
+  return src | (dst << 16);
+}
+
+// Two E4M3 codes (byte pair kHi of w) as two bf16 in one word, exactly.
+template <bool kHi>
+__device__ __forceinline__ uint32_t f8x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, kHi));
+}
+
+// Decode this lane's nine chunks of one 32-token half of an FP8 tile (codes
+// at `half`) into a bf16 tile (`tile`), both in LDS.
+__device__ __forceinline__ void convert_tile(const uint8_t* half, uint8_t* tile, const uint32_t* tab, int lane) {
+  uint32_t e[kCvt];
+#pragma unroll
+  for (int i = 0; i < kCvt; ++i) e[i] = tab[64 * i + lane];
+  u32x2_t c[kCvt];
+#pragma unroll
+  for (int i = 0; i < kCvt; ++i) c[i] = *reinterpret_cast<const u32x2_t*>(half + (e[i] & 0xFFFFu));
+#pragma unroll
+  for (int i = 0; i < kCvt; ++i) {
+    const u32x4_t v = {f8x2_to_bf16x2<false>(c[i][0]), f8x2_to_bf16x2<true>(c[i][0]),
+                       f8x2_to_bf16x2<false>(c[i][1]), f8x2_to_bf16x2<true>(c[i][1])};
+    *reinterpret_cast<u32x4_t*>(tile + (e[i] >> 16)) = v;
+  }
+}
+
+// This wave's nine DMAs of the 64-token FP8 tile at t0 (a multiple of 64, so
+// the tile covers 64 / P whole pages): block b = 4j + wave lies in page
+// b / (9P / 16) of the tile at byte (b mod 9P / 16) * 1 KB. Page indices past
+// the request's last page are clamped to it (rows past `end` are masked where
+// they are used). Returns true if a page id is outside the pool: it is not
+// dereferenced (page 0 stands in) and the state is written as NaN.
+template <int kP>
+__device__ __forceinline__ bool f8_dma(const MlaArgs& a, const_i32_t* ptab, int end, int t0, uint32_t lds,
+                                       int wave, uint32_t voff) {
+  constexpr int kPages = kF8Tokens / kP;
+  constexpr int kBpp = 9 * kP / 16;   // 1 KB blocks per page
+  const int last = (end - 1) / kP;
+  const uint8_t* base[kPages];
+  bool bad = false;
+#pragma unroll
+  for (int pg = 0; pg < kPages; ++pg) {
+    const int pid = ptab[min(t0 / kP + pg, last)];
+    const bool ok = pid >= 0 && pid < a.num_pages;
+    bad |= !ok;
+    base[pg] = a.kv + (ok ? (int64_t)pid * (kP * kD) : 0);
+  }
+  if (bad && (threadIdx.x & 63) == 0) raise_error(a.err_flag, kErrPageId);
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int b = 4 * j + wave;
+    const int pg = kPages == 1 ? 0 : b / kBpp;
+    const uint8_t* src = base[0];
+#pragma unroll
+    for (int q = 1; q < kPages; ++q)
+      if (pg == q) src = base[q];
+    src += (b - pg * kBpp) * 1024;
+    switch (j) {
+      case 0: dma_sbase<0>(src, voff, lds); break;
+      case 1: dma_sbase<1>(src, voff, lds); break;
+      case 2: dma_sbase<2>(src, voff, lds); break;
+      case 3: dma_sbase<3>(src, voff, lds); break;
+      case 4: dma_sbase<4>(src, voff, lds); break;
+      case 5: dma_sbase<5>(src, voff, lds); break;
+      case 6: dma_sbase<6>(src, voff, lds); break;
+      case 7: dma_sbase<7>(src, voff, lds); break;
+      default: dma_sbase<8>(src, voff, lds); break;
+    }
+  }
+  return bad;
+}
+
+template <int kP>
+__device__ __forceinline__ void mla_task_f8(const MlaArgs& a, const DevTask& task, MlaShared8& sh) {
+  DevTask t;
+  t.b = __builtin_amdgcn_readfirstlane(task.b);
+  t.kvh = 0;
+  t.lo = __builtin_amdgcn_readfirstlane(task.lo);
+  t.end = __builtin_amdgcn_readfirstlane(task.end);
+  t.q_row = __builtin_amdgcn_readfirstlane(task.q_row);
+  t.out_row = __builtin_amdgcn_readfirstlane(task.out_row);
+  t.seq_len = __builtin_amdgcn_readfirstlane(task.seq_len);
+  t.pad = 0;
+  int& restart_pass = sh.restart_pass;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, n = lane & 15;
+  if (a.seq_lens[t.b] != t.seq_len) {
+    if (threadIdx.x == 0) raise_error(a.err_flag, kErrSeqLen);
+    write_nan_state(a.o_part, a.lse_part, t.out_row, a.H_q, kDv);
+    return;
+  }
+  const int end = t.end;
+  const_i32_t* ptab = (const_i32_t*)(a.page_table + (int64_t)t.b * a.max_pages);
+  const_f32_t* pscale = (const_f32_t*)a.kv_scale;
+
+  u32x4_t qf[2][kKs];
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    const int head = min(32 * wave + 16 * hb + n, a.H_q - 1);
+    const uint16_t* qp = a.q + ((int64_t)t.q_row * a.H_q + head) * kD + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) qf[hb][ks] = *reinterpret_cast<const u32x4_t*>(qp + 32 * ks);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+
+  const int ntiles = end > t.lo ? (end - t.lo + kT - 1) / kT : 0;
+  const int nf = (ntiles + 1) / 2;   // FP8 DMA tiles
+  uint32_t* tab = sh.cvt_lds[wave];
+#pragma unroll
+  for (int i = 0; i < kCvt; ++i) tab[64 * i + lane] = cvt_entry(wave, i, lane);
+  if (threadIdx.x == 0) restart_pass = 0;
+  const uint32_t f8_lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)&sh.f8[0][0]);
+  const uint32_t dma_lds = f8_lds + 1024u * wave;   // this wave's first DMA block in slot 0
+  const uint32_t voff = 16u * lane;
+
+  // operand read offsets: those of the bf16 kernel
+  uint32_t ke[2], ko[2];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int r = 8 * (n >> 2) + 4 * blk + (n & 3);
+    const int h = swz(r);
+    const int base = kRowSlots * r + (g ^ (h & 3));
+    ke[blk] = 16u * (uint32_t)(base + 4 * (h >> 2));
+    ko[blk] = 16u * (uint32_t)(base - 4 * (h >> 2));
+  }
+  uint32_t va4[4];
+  {
+    const int r = 8 * g + (n >> 2);
+    const int h = swz(r);
+    const int vb = kRowSlots * r + (((n & 3) >> 1) ^ (h & 1));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) va4[j] = 16u * (uint32_t)(vb + 2 * (j ^ (h >> 1))) + 8u * (n & 1);
+  }
+
+  float m[2] = {0.f, 0.f};
+  float thr[2] = {INFINITY, INFINITY};
+  float mr[2] = {-INFINITY, -INFINITY};   // the lane's running maximum of scaled raw scores
+  auto set_reference = [&](int hb) {
+    m[hb] = max_xor32(max_xor16(mr[hb])) * a.scale_log2;
+    thr[hb] = (m[hb] + 64.f) / a.scale_log2;
+  };
+  float l[2];
+  f32x4_t o[kNb][2];
+  bool bad_page = false;
+  bool range_err = false;
+  for (int pass = 1;; ++pass) {
+    bool over = false;
+    l[0] = l[1] = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < kNb; ++nb) o[nb][0] = o[nb][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    // FP8 tiles 0 and 1, then tile 0's first half converted
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+      if (f < nf) bad_page |= f8_dma<kP>(a, ptab, end, t.lo + f * kF8Tokens, dma_lds + f * kF8TileBytes, wave, voff);
+    if (ntiles > 0) {
+      if (nf > 1) __builtin_amdgcn_s_waitcnt(kWaitVm9);
+      else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      bare_barrier();
+      convert_tile(&sh.f8[0][0], reinterpret_cast<uint8_t*>(&sh.bf[0][0]), tab, lane);
+    }
+
+    for (int k = 0; k < ntiles; ++k) {
+      // odd k: FP8 tile (k + 1) / 2, which tile k + 1 is converted from, has
+      // landed for this wave (no later DMA is in flight); every k: tile k's
+      // conversion is written (LDS counter) before the barrier
+      if (k & 1) __builtin_amdgcn_s_waitcnt(kWaitVm0 & 0xc07f);
+      else __builtin_amdgcn_s_waitcnt(0xc07f);
+      bare_barrier();
+      const int F = (k + 3) / 2;   // the FP8 tile sent at this (odd) iteration
+      if ((k & 1) && F < nf)
+        bad_page |= f8_dma<kP>(a, ptab, end, t.lo + F * kF8Tokens, dma_lds + (F & 1) * kF8TileBytes, wave, voff);
+      // page scale(s) of tile k: one page (P >= 32) or two (P = 16; a lane's
+      // eight tokens lie in one 16-token half); ids outside the pool read page
+      // 0's scale (the state is NaN anyway)
+      const int t0 = t.lo + k * kT;
+      float sc;
+      {
+        const int last = (end - 1) / kP;
+        const int p0 = ptab[min(t0 / kP, last)];
+        const float s0 = pscale[(p0 >= 0 && p0 < a.num_pages) ? p0 : 0];
+        if (kP == 16) {
+          const int p1 = ptab[min(t0 / kP + 1, last)];
+          const float s1 = pscale[(p1 >= 0 && p1 < a.num_pages) ? p1 : 0];
+          sc = g < 2 ? s0 : s1;
+        } else {
+          sc = s0;
+        }
+      }
+      uint16_t* tile = sh.bf[k & 1];
+      const uint8_t* lb = reinterpret_cast<const uint8_t*>(tile);
+      const bool tail = t0 + kT > end;
+      if (tail) {
+        const int r0 = end - t0;
+        for (int sl = kRowSlots * r0 + threadIdx.x; sl < kTileSlots; sl += kThreads)
+          reinterpret_cast<u32x4_t*>(tile)[sl] = u32x4_t{0u, 0u, 0u, 0u};
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        bare_barrier();
+      }
+      // tile k + 1's codes into the other bf16 tile (its last reader, tile
+      // k - 1, finished before this iteration's barrier)
+      if (k + 1 < ntiles)
+        convert_tile(&sh.f8[(k + 1) / 2 & 1][((k + 1) & 1) * kF8HalfBytes],
+                     reinterpret_cast<uint8_t*>(&sh.bf[(k + 1) & 1][0]), tab, lane);
+
+      // ---- scores S^T of tile k over all 576 dims ----
+      f32x4_t s[2][2];
+      {
+        u32x4_t kb[kKd][2];
+        auto kread = [&](int ks, u32x4_t (&dst)[2]) {
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+            dst[blk] = *reinterpret_cast<const u32x4_t*>(lb + ((ks & 1) ? ko[blk] : ke[blk]) + 64 * ks);
+        };
+#pragma unroll
+        for (int i = 0; i < kKd - 1; ++i) {
+          kread(i, kb[i]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int ks = 0; ks < kKs; ++ks) {
+          if (ks + kKd - 1 < kKs) kread(ks + kKd - 1, kb[(ks + kKd - 1) % kKd]);
+          if (ks == 0) qk_step<true>(s, kb[0], qf[0][0], qf[1][0]);
+          else qk_step<false>(s, kb[ks % kKd], qf[0][ks], qf[1][ks]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      scores_ready(s);
+
+      if (tail) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (t0 + 8 * g + 4 * blk + e >= end) s[blk][hb][e] = -INFINITY;
+      }
+      u32x4_t pf[2];
+      const bool first = k == 0 && pass == 1;
+      const float mul = a.scale_log2 * sc;   // raw score -> log2 domain, page scale included
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const float tmax = max3f(max3f(s[0][hb][0], s[0][hb][1], s[0][hb][2]),
+                                 max3f(s[0][hb][3], s[1][hb][0], s[1][hb][1]),
+                                 max3f(s[1][hb][2], s[1][hb][3], s[1][hb][3]));
+        mr[hb] = max3f(tmax * sc, mr[hb], mr[hb]);   // scaled raw scores (sc > 0 keeps the order)
+        if (first) set_reference(hb);
+        over = over || mr[hb] > thr[hb];
+        float ps = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            s[blk][hb][e] = fast_exp2(fmaf(s[blk][hb][e], mul, -m[hb]));
+            ps += s[blk][hb][e];
+          }
+        l[hb] += ps;
+        // the weights times the page scale meet the decoded codes in P*V
+        pf[hb] = u32x4_t{pack_bf16x2(s[0][hb][0] * sc, s[0][hb][1] * sc), pack_bf16x2(s[0][hb][2] * sc, s[0][hb][3] * sc),
+                         pack_bf16x2(s[1][hb][0] * sc, s[1][hb][1] * sc), pack_bf16x2(s[1][hb][2] * sc, s[1][hb][3] * sc)};
+      }
+
+      // ---- O^T += V^T P^T over all 512 value dims, tile k ----
+      {
+        u32x4_t vb[kVd];
+        auto vread = [&](int nb, u32x4_t& dst) {
+          const uint8_t* p = lb + va4[nb & 3] + 128 * (nb >> 2);
+          const u32x2_t lo = tr_read(p);
+          const u32x2_t hi = tr_read(p + 4 * kRowSlots * 16);
+          dst = u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+        };
+#pragma unroll
+        for (int i = 0; i < kVd - 1; ++i) {
+          vread(i, vb[i]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int nb = 0; nb < kNb; ++nb) {
+          if (nb + kVd - 1 < kNb) vread(nb + kVd - 1, vb[(nb + kVd - 1) % kVd]);
+          o[nb][0] = mfma16(vb[nb % kVd], pf[0], o[nb][0]);
+          o[nb][1] = mfma16(vb[nb % kVd], pf[1], o[nb][1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    if (__builtin_amdgcn_ballot_w64(over) != 0 && lane == 0) restart_pass = pass;
+    __builtin_amdgcn_s_waitcnt(kWaitVm0 & 0xc07f);
+    bare_barrier();
+    if (restart_pass != pass) break;
+    if (pass == 2) {
+      range_err = true;
+      if (threadIdx.x == 0) raise_error(a.err_flag, kErrRange);
+      break;
+    }
+    set_reference(0);
+    set_reference(1);
+  }
+  if (bad_page || range_err) {
+    write_nan_state(a.o_part, a.lse_part, t.out_row, a.H_q, kDv);
+    return;
+  }
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    float lt = l[hb];
+    lt = sum_xor32(sum_xor16(lt));
+    const int head = 32 * wave + 16 * hb + n;
+    if (head >= a.H_q) continue;
+    const bool empty = ntiles == 0;
+    const float inv = empty ? 0.f : 1.f / lt;
+    const int64_t row = (int64_t)t.out_row + head;
+    float* orow = a.o_part + row * kDv + 4 * g;
+#pragma unroll
+    for (int nb = 0; nb < kNb; ++nb)
+      *reinterpret_cast<f32x4_t*>(orow + 16 * nb) = o[nb][hb] * inv;
+    if (g == 0) a.lse_part[row] = empty ? -INFINITY : (m[hb] + fast_log2(lt)) * kLn2;
+  }
+}
+
+template <int kP>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void mla_mfma_f8_kernel(MlaArgs a) {
+  __shared__ MlaShared8 sh;
+  mla_task_f8<kP>(a, a.tasks[blockIdx.x], sh);
+}
+
 // One work-group per task, in the plan's queue order.
 template <bool kSinglePage>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -604,6 +977,7 @@ static MlaArgs mla_args(const AttnLaunch& L) {
   a.kv = static_cast<const uint8_t*>(L.k_pages);
   a.page_table = L.page_table;
   a.seq_lens = L.seq_lens;
+  a.kv_scale = L.k_scales;
   a.tasks = reinterpret_cast<const DevTask*>(static_cast<const uint8_t*>(L.workspace) + L.tasks_off);
   a.err_flag = reinterpret_cast<int32_t*>(const_cast<void*>(L.workspace));
   a.o_part = L.o_part;
@@ -631,8 +1005,20 @@ hipError_t launch_mla_mfma_fused(const AttnLaunch& L, const FusedLaunch& F) {
 
 hipError_t launch_mla_mfma(const AttnLaunch& L) {
   const skv_attn_desc& d = *L.desc;
-  if (d.head_dim_qk != kD || d.head_dim_v != kDv || d.num_kv_heads != 1 || d.dtype != SKV_BF16)
-    return hipErrorInvalidValue;
+  if (d.head_dim_qk != kD || d.head_dim_v != kDv || d.num_kv_heads != 1) return hipErrorInvalidValue;
+  if (d.dtype == SKV_FP8_E4M3) {
+    if (!L.k_scales || L.v_scales != L.k_scales) return hipErrorInvalidValue;
+    if (L.num_tasks == 0) return hipSuccess;
+    const MlaArgs a = mla_args(L);
+    if (d.page_size == 64)
+      hipLaunchKernelGGL(mla_mfma_f8_kernel<64>, dim3(L.num_tasks), dim3(kThreads), 0, L.stream, a);
+    else if (d.page_size == 32)
+      hipLaunchKernelGGL(mla_mfma_f8_kernel<32>, dim3(L.num_tasks), dim3(kThreads), 0, L.stream, a);
+    else
+      hipLaunchKernelGGL(mla_mfma_f8_kernel<16>, dim3(L.num_tasks), dim3(kThreads), 0, L.stream, a);
+    return hipGetLastError();
+  }
+  if (d.dtype != SKV_BF16) return hipErrorInvalidValue;
   if (L.num_tasks == 0) return hipSuccess;
   const MlaArgs a = mla_args(L);
   if (d.page_size >= 32)

@@ -38,7 +38,9 @@ class DeviceInputs:
         self.k = _dev_tensor(w.k_pages, w.dtype, dev)
         self.v = self.k if w.mla else _dev_tensor(w.v_pages, w.dtype, dev)
         self.k_scale = None if w.k_scale is None else torch.from_numpy(w.k_scale).to(dev)
-        self.v_scale = None if w.v_scale is None else torch.from_numpy(w.v_scale).to(dev)
+        # FP8 MLA rows: one scale per page for keys and values (the same tensor)
+        self.v_scale = (self.k_scale if w.mla else
+                        None if w.v_scale is None else torch.from_numpy(w.v_scale).to(dev))
         self.page_table = torch.from_numpy(w.page_table).to(dev)
         self.seq_lens = torch.from_numpy(w.seq_lens).to(dev)
         self.o_ext = None if w.o_ext is None else torch.from_numpy(w.o_ext).to(dev)

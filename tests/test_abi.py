@@ -366,8 +366,17 @@ def test_fp8_descriptions_and_entry_point_checks():
     for hq, hkv, d in ((8, 2, 128), (4, 4, 64), (64, 2, 128)):      # groups of 4, 1, 32
         g = skv.AttnSpec(hq, hkv, d, d, 16, dtype=skv.FP8)
         assert _plan_call(g.desc(1, max_pages=8, num_pages=8), [100]) == -2
+    # FP8 MLA rows: planned like bf16 rows; one scale per page, so the value
+    # scales must be the key scales (checked before any launch)
     mla = skv.AttnSpec(128, 1, 576, 512, 64, dtype=skv.FP8, mla=True)
-    assert _plan_call(mla.desc(1, max_pages=4, num_pages=4), [100]) == -2
+    assert _plan_call(mla.desc(1, max_pages=4, num_pages=4), [100]) == 0
+    mplan = skv.plan_splits([100, 300], mla, num_cu=4)
+    md = mla.desc(2, max_pages=8, num_pages=16, scale=0.1)
+    fk = ctypes.c_void_p(256)
+    mcall = lambda ks, vs, vp: skv._lib.skv_decode_attn_partial_fp8(
+        ctypes.byref(md), fk, fk, vp, ks, vs, fk, fk, mplan.handle, fk, fk, fk, None)
+    assert mcall(fk, ctypes.c_void_p(512), fk) == -1 and "v_scales" in skv._lib.skv_last_error().decode()
+    assert mcall(fk, fk, ctypes.c_void_p(512)) == -1 and "v_pages" in skv._lib.skv_last_error().decode()
     bad = f8.desc(1, max_pages=8, num_pages=8)
     bad.dtype = 3
     assert _plan_call(bad, [100]) == -1

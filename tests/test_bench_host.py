@@ -113,4 +113,4 @@ def test_decode_part_of_the_shard_workload():
 def test_default_run_is_the_headline_plus_every_other_workload():
     a = bench.parse([])
     assert a.workload == "all" and a.steps == 60 and a.warmup == 40 and a.gpus == 1
-    assert bench.HEADLINE == "5d" and bench.PER_CONFIG == ("2", "3", "4", "5", "6", "7")
+    assert bench.HEADLINE == "5d" and bench.PER_CONFIG == ("2", "3", "4", "5", "6", "7", "8")
