@@ -325,8 +325,8 @@ def summarize_pmc(fetch_dir: str, write_dir: str, workload: str) -> None:
 
     fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
     copy = [k for k in fetch if "copyBuffer" in k]
-    attn = [k for k in fetch if any(n in k for n in ("mla_mfma_kernel", "gqa_mfma_kernel", "gqa_rows_kernel",
-                                                      "gqa_valu_kernel"))]
+    attn = [k for k in fetch if any(n in k for n in ("mla_mfma_kernel", "mla_mfma_f8_kernel", "gqa_mfma_kernel",
+                                                      "gqa_rows_kernel", "gqa_valu_kernel"))]
     assert copy and attn, (list(fetch), "need the copy probe and an attention kernel")
     kib = COPY_PROBE_BYTES / 1024.0
     cf = max(fetch[copy[0]]) / kib        # the probe is the largest copy

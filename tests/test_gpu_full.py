@@ -144,3 +144,12 @@ def test_llama405b_gqa_share_fp8_full():
 
 def test_llama405b_gqa_share_fp8_sharp_full():
     run_full(7, lambda w: ({b: [0] for b in _spread(w)[:2]}, None), sharp=True)
+
+
+def test_deepseek_mla_fp8_full():
+    # workload 3's shape and lengths over FP8 E4M3 latent rows
+    run_full(8, lambda w: ({b: [0] for b in _spread(w, (40,))}, int(np.argmax(w.seq_lens))))
+
+
+def test_deepseek_mla_fp8_sharp_full():
+    run_full(8, lambda w: ({b: [0] for b in _spread(w)[:2]}, None), sharp=True)
