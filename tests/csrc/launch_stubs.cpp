@@ -15,6 +15,9 @@ hipError_t launch_gqa_valu_fused(const AttnLaunch&, const FusedLaunch&) { return
 hipError_t launch_gqa_mfma_fused(const AttnLaunch&, const FusedLaunch&) { return hipErrorNoDevice; }
 hipError_t launch_mla_mfma_fused(const AttnLaunch&, const FusedLaunch&) { return hipErrorNoDevice; }
 hipError_t launch_hbm_probe(const void*, int64_t, uint32_t*, int, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_mfma_probe(const void*, int64_t, int, int, int, int, int, uint32_t*, hipStream_t) {
+  return hipErrorNoDevice;
+}
 }  // namespace skv
 
 // The no-allocation entry point lives beside its device array (built with the
