@@ -56,6 +56,45 @@ def check_rows(w, plan, res, samples, partial_req=None):
             f"in {time.time() - t:.1f}s")
 
 
+def value_bound(w) -> float:
+    """Largest magnitude any attention output can take: every output is a
+    convex combination of value vectors (and, merged, of external outputs),
+    so no entry exceeds the largest stored value's magnitude."""
+    if w.dtype == "fp8":
+        codes = np.abs(A.e4m3_to_f64(np.arange(256, dtype=np.uint8)))
+        top = float(np.nanmax(codes))      # 448
+        vb = top * float(np.nanmax(w.k_scale if w.v_scale is None else w.v_scale))
+    else:
+        vals = w.k_pages if w.mla else w.v_pages
+        vb = 0.0
+        for lo in range(0, vals.shape[0], 2048):   # a few pages at a time (the pool is large)
+            blk = vals[lo:lo + 2048]
+            if w.mla:
+                blk = blk[..., : w.head_dim_v]
+            if w.dtype == "bf16":
+                # magnitudes of finite bf16 values order like their bit patterns
+                mag = blk.view(np.uint16) & np.uint16(0x7FFF)
+                mag = mag[mag <= 0x7F80]
+                if mag.size:
+                    vb = max(vb, float(A.to_f64(np.array([mag.max()], np.uint16), "bf16")[0]))
+            else:
+                vb = max(vb, float(np.nanmax(np.abs(blk))))
+    if w.n_ext:
+        vb = max(vb, float(np.abs(w.o_ext).max()))
+    return vb
+
+
+def check_every_row(w, res):
+    """Properties of all rows (not only the sampled ones): finite outputs and
+    LSEs, and no output entry beyond the largest stored value (a row is a
+    convex combination of values)."""
+    o_part, lse_part, o, lse = res
+    assert np.isfinite(o).all() and np.isfinite(lse).all(), f"{w.name}: non-finite merged rows"
+    vb = value_bound(w)
+    assert float(np.abs(o).max()) <= vb * (1 + 1e-2), f"{w.name}: an output exceeds the values' bound {vb}"
+    log(f"{w.name}: all {lse.shape[0]} rows finite and within the values' bound")
+
+
 def run_full(cid, samples_fn, sharp=False, decode_only=False):
     t = time.time()
     w = wl.make(cid, sharp=sharp, decode_only=decode_only)
@@ -66,6 +105,7 @@ def run_full(cid, samples_fn, sharp=False, decode_only=False):
     inf = plan.info()
     log(f"{w.name}: GPU done, {inf.num_tasks} tasks, {inf.total_splits} splits")
     assert plan.read_error_flag() == 0
+    check_every_row(w, res)
     samples, partial_req = samples_fn(w)
     check_rows(w, plan, res, samples, partial_req)
     del d
@@ -110,7 +150,7 @@ def test_million_token_mla_shard_full():
     # 8 decode requests of 1,048,576 tokens plus one 2,048-token chunk over a
     # 65,536-token history, 16 external states merged into every row
     def pick(w):
-        return {0: [0], 7: [0], 8: [0, 1023, 2047]}, 8
+        return {0: [0], 7: [0], 8: [0, 1, 511, 1023, 1024, 1535, 2046, 2047]}, 8
     run_full(5, pick)
 
 
