@@ -593,15 +593,31 @@ def main(argv=None):
     mprobe = xprobe = None
     if not args.no_mfma_probe:
         mprobe = mfma_probe(dev, num_cu)
-        if head_w.mla:
-            # the products and the KV stream of the headline launch, in its
-            # proportion, with nothing else
-            try:
-                xprobe = mixed_probe(dev, num_cu, attention_flops(head_w) / kv_bytes(head_w))
-            except (RuntimeError, MemoryError) as e:
-                print(f"[bench] mixed probe skipped: {e}", file=sys.stderr, flush=True)
-        if xprobe and head["roofline"]["unit"] == "GB/s":
-            head["roofline"]["frac_of_mixed_probe"] = round(head["roofline"]["achieved"] / xprobe["gbs"], 4)
+        # For launches with matrix-side work (MLA rows, query tiles: 64 flop
+        # per KV byte or more), the probe with products and a KV stream in the
+        # launch's own proportion and nothing else: what the chip reaches there.
+        probes = {}
+        for key, m in [(head_key, head), *per.items()]:
+            w = load(key, cache)
+            r = attention_flops(w) / kv_bytes(w)
+            if r < 64:
+                continue
+            rk = round(r)
+            if rk not in probes:
+                try:
+                    probes[rk] = mixed_probe(dev, num_cu, r)
+                except (RuntimeError, MemoryError) as e:
+                    print(f"[bench] mixed probe skipped: {e}", file=sys.stderr, flush=True)
+                    probes[rk] = None
+            x = probes[rk]
+            if not x:
+                continue
+            roof = m["roofline"]
+            roof["mixed_probe"] = {k: x[k] for k in ("flop_per_byte", "gbs", "tflops", "est_ghz")}
+            ref = x["gbs"] if roof["unit"] == "GB/s" else x["tflops"]
+            roof["frac_of_mixed_probe"] = round(roof["achieved"] / ref, 4)
+            if key == head_key:
+                xprobe = x
     for m in [head, *per.values()]:
         if probe:
             m["frac_of_probe"] = round(m["kv_gbs"] / probe["gbs"], 4)
