@@ -297,6 +297,18 @@ skv_status skv_decode_attn(const skv_attn_desc* desc, const void* q, const void*
                            const float* lse_ext, void* o_out, int32_t out_dtype, float* lse_out,
                            void* stream);
 
+/* skv_decode_attn over an FP8 E4M3 KV cache (desc->dtype = SKV_FP8_E4M3):
+ * the attention as skv_decode_attn_partial_fp8 with its scales, then the
+ * merge, through `scratch` as skv_decode_attn. The plan must be built with
+ * overlap_reduction = 0 (the two launches; SKV_ERR_UNSUPPORTED otherwise).
+ * Arguments, results and errors are otherwise those of the two calls. */
+skv_status skv_decode_attn_fp8(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                               const void* v_pages, const float* k_scales, const float* v_scales,
+                               const int32_t* page_table, const int32_t* seq_lens, const skv_plan* plan,
+                               const void* workspace, void* scratch, size_t scratch_bytes, int32_t n_ext,
+                               const float* o_ext, const float* lse_ext, void* o_out, int32_t out_dtype,
+                               float* lse_out, void* stream);
+
 /* skv_decode_attn for callers that cannot allocate device memory (code under
  * HIP graph capture, tight serving loops, harnesses that forbid allocation).
  * The scratch is a 128 MiB array in the library's device code: each device

@@ -39,7 +39,7 @@ EXPORTED = (
     "skv_plan_get_info", "skv_plan_export", "skv_plan_workspace_bytes", "skv_plan_upload",
     "skv_plan_destroy", "skv_decode_attn_partial", "skv_merge_states", "skv_read_error_flag",
     "skv_hbm_read_probe", "skv_last_error", "skv_decode_attn_scratch_bytes", "skv_decode_attn",
-    "skv_decode_attn_noalloc", "skv_decode_attn_partial_fp8", "skv_mfma_probe",
+    "skv_decode_attn_noalloc", "skv_decode_attn_partial_fp8", "skv_mfma_probe", "skv_decode_attn_fp8",
 )
 
 
@@ -102,6 +102,7 @@ def _load():
         "skv_decode_attn_scratch_bytes": (SZ, [P]),
         "skv_decode_attn": (I32, [pdesc, P, P, P, P, P, P, P, P, SZ, I32, P, P, P, I32, P, P]),
         "skv_decode_attn_noalloc": (I32, [pdesc, P, P, P, P, P, P, P, I32, P, P, P, I32, P, P]),
+        "skv_decode_attn_fp8": (I32, [pdesc, P, P, P, P, P, P, P, P, P, P, SZ, I32, P, P, P, I32, P, P]),
         "skv_read_error_flag": (I32, [P, pi32, P]),
         "skv_hbm_read_probe": (I32, [P, I64, P, I32, P]),
         "skv_mfma_probe": (I32, [P, I64, I32, P, I32, I32, I32, I32, P]),
@@ -472,6 +473,38 @@ def decode_attn(q, k_pages, v_pages, page_table, seq_lens, plan: Plan, scale: fl
                                 scratch.data_ptr(), scratch.numel(), n_ext, _ptr(o_ext), _ptr(lse_ext),
                                 o_out.data_ptr(), _out_dtype_code(o_out), _ptr(lse_out), _stream_ptr()),
            "skv_decode_attn")
+    return o_out, lse_out
+
+
+def decode_attn_fp8(q, k_pages, v_pages, k_scales, v_scales, page_table, seq_lens, plan: Plan, scale: float,
+                    o_ext=None, lse_ext=None, out_dtype=torch.float32, o_out=None, lse_out=None,
+                    want_lse: bool = True, scratch=None):
+    """decode_attn over an FP8 (OCP E4M3) KV cache, with the scales of
+    decode_attn_partial_fp8; the plan is built for dtype FP8 with
+    overlap_reduction = 0 (the two launches)."""
+    dev = q.device
+    sp = plan.spec
+    if sp.dtype != FP8:
+        raise ValueError("decode_attn_fp8 needs a plan built for dtype FP8")
+    _check_attention_inputs(q, k_pages, v_pages, page_table, seq_lens, plan)
+    n_pages = int(k_pages.shape[0])
+    _check_tensor(k_scales, "k_scales", dev, (torch.float32,), shape=(n_pages, sp.num_kv_heads))
+    _check_tensor(v_scales, "v_scales", dev, (torch.float32,), shape=(n_pages, sp.num_kv_heads))
+    if sp.mla and v_scales.data_ptr() != k_scales.data_ptr():
+        raise ValueError("FP8 MLA rows have one scale per page: v_scales must be k_scales")
+    n_ext, o_out, lse_out = _merge_outputs(plan, dev, o_ext, lse_ext, out_dtype, o_out, lse_out, want_lse)
+    need = scratch_bytes(plan)
+    if scratch is None:
+        scratch = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check_tensor(scratch, "scratch", dev, (torch.uint8,), numel=need)
+    desc = _desc_for(plan, page_table, k_pages, scale)
+    ws = plan.workspace(dev)
+    _check(_lib.skv_decode_attn_fp8(ctypes.byref(desc), q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                                    k_scales.data_ptr(), v_scales.data_ptr(), page_table.data_ptr(),
+                                    seq_lens.data_ptr(), plan.handle, ws.data_ptr(), scratch.data_ptr(),
+                                    scratch.numel(), n_ext, _ptr(o_ext), _ptr(lse_ext), o_out.data_ptr(),
+                                    _out_dtype_code(o_out), _ptr(lse_out), _stream_ptr()),
+           "skv_decode_attn_fp8")
     return o_out, lse_out
 
 

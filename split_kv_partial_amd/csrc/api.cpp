@@ -623,10 +623,14 @@ skv_status decode_attn_impl(const skv_attn_desc* desc, const void* q, const void
                             const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
                             const skv_plan* plan, const void* workspace, void* scratch,
                             size_t scratch_bytes, int32_t n_ext, const float* o_ext, const float* lse_ext,
-                            void* o_out, int32_t out_dtype, float* lse_out, void* stream) {
-  skv_status st = check_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace);
+                            void* o_out, int32_t out_dtype, float* lse_out, void* stream,
+                            const float* k_scales, const float* v_scales) {
+  skv_status st = check_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, k_scales,
+                                  v_scales);
   if (st) return st;
   if ((st = check_merge(desc, plan, workspace, n_ext, o_ext, lse_ext, o_out, out_dtype))) return st;
+  if (desc->dtype == SKV_FP8_E4M3 && plan->prm.overlap_reduction)
+    return fail(SKV_ERR_UNSUPPORTED, "FP8 KV runs the two launches: build its plan with overlap_reduction = 0");
   if (!scratch) return fail(SKV_ERR_INVALID_ARG, "scratch is NULL");
   const ScratchLayout lay = scratch_layout(plan);
   if (scratch_bytes < lay.total)
@@ -637,7 +641,7 @@ skv_status decode_attn_impl(const skv_attn_desc* desc, const void* q, const void
   if (!plan->prm.overlap_reduction) {
     // the plan assumes the merge runs after attention: two launches
     st = launch_attention(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, o_part,
-                          lse_part, stream);
+                          lse_part, stream, k_scales, v_scales);
     if (st) return st;
     return launch_merge_for(desc, plan, workspace, o_part, lse_part, n_ext, o_ext, lse_ext, o_out,
                             out_dtype, lse_out, stream);
@@ -715,6 +719,19 @@ skv_status skv_decode_attn(const skv_attn_desc* desc, const void* q, const void*
                            void* o_out, int32_t out_dtype, float* lse_out, void* stream) {
   return decode_attn_impl(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, scratch,
                           scratch_bytes, n_ext, o_ext, lse_ext, o_out, out_dtype, lse_out, stream);
+}
+
+skv_status skv_decode_attn_fp8(const skv_attn_desc* desc, const void* q, const void* k_pages,
+                               const void* v_pages, const float* k_scales, const float* v_scales,
+                               const int32_t* page_table, const int32_t* seq_lens, const skv_plan* plan,
+                               const void* workspace, void* scratch, size_t scratch_bytes, int32_t n_ext,
+                               const float* o_ext, const float* lse_ext, void* o_out, int32_t out_dtype,
+                               float* lse_out, void* stream) {
+  if (desc && desc->dtype != SKV_FP8_E4M3)
+    return fail(SKV_ERR_INVALID_ARG, "skv_decode_attn_fp8 needs desc->dtype = SKV_FP8_E4M3");
+  return decode_attn_impl(desc, q, k_pages, v_pages, page_table, seq_lens, plan, workspace, scratch,
+                          scratch_bytes, n_ext, o_ext, lse_ext, o_out, out_dtype, lse_out, stream, k_scales,
+                          v_scales);
 }
 
 skv_status skv_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* out, int32_t blocks,

@@ -193,7 +193,8 @@ skv_status decode_attn_impl(const skv_attn_desc* desc, const void* q, const void
                             const void* v_pages, const int32_t* page_table, const int32_t* seq_lens,
                             const skv_plan* plan, const void* workspace, void* scratch,
                             size_t scratch_bytes, int32_t n_ext, const float* o_ext, const float* lse_ext,
-                            void* o_out, int32_t out_dtype, float* lse_out, void* stream);
+                            void* o_out, int32_t out_dtype, float* lse_out, void* stream,
+                            const float* k_scales = nullptr, const float* v_scales = nullptr);
 
 // Default executor shape of each attention kernel (used by the planner).
 // GqaMfmaG8: the matrix-core GQA kernel on groups of 8 (the same kernel, with

@@ -595,10 +595,7 @@ __device__ __forceinline__ void mla_task(const MlaArgs& a, const DevTask& task, 
 // Schedule: FP8 tile F (F >= 2) is sent at iteration 2F - 3 into the ring slot
 // that FP8 tile F - 2 left (both its halves converted by then), and is
 // converted from iteration 2F - 1 on; iteration k converts tile k + 1 and
-// computes tile k. The conversion and the DMA are spread over the score
-// products (as the bf16 kernel spreads its DMA): 1.3% faster than converting
-// the whole tile between the barrier and the products, in an alternating
-// A/B on the DeepSeek-shaped FP8 batch.
+// computes tile k.
 // ---------------------------------------------------------------------------
 constexpr int kF8Tokens = 64;                      // tokens per FP8 DMA tile
 constexpr int kF8TileBytes = kF8Tokens * kD;       // 36,864: 36 DMA blocks of 1 KB
@@ -650,51 +647,51 @@ __device__ __forceinline__ void convert_tile(const uint8_t* half, uint8_t* tile,
   }
 }
 
-// The DMA of one 64-token FP8 tile at t0 (a multiple of 64, so the tile
-// covers 64 / P whole pages): 36 blocks of 1 KB; this wave sends blocks
-// b = 4j + wave (j = 0..8), block b from page b / (9P / 16) of the tile at byte
-// (b mod 9P / 16) * 1 KB. prepare() reads the tile's page ids (wave-uniform
-// scalars; indices past the request's last page are clamped to it, rows past
-// `end` being masked where they are used) and returns true if one is outside
-// the pool: it is reported, not dereferenced (page 0 stands in), and the state
-// is written as NaN. issue<J>() sends instruction J.
+// This wave's nine DMAs of the 64-token FP8 tile at t0 (a multiple of 64, so
+// the tile covers 64 / P whole pages): block b = 4j + wave lies in page
+// b / (9P / 16) of the tile at byte (b mod 9P / 16) * 1 KB. Page indices past
+// the request's last page are clamped to it (rows past `end` are masked where
+// they are used). Returns true if a page id is outside the pool: it is not
+// dereferenced (page 0 stands in) and the state is written as NaN.
 template <int kP>
-struct F8Dma {
-  static constexpr int kPages = kF8Tokens / kP;
-  static constexpr int kBpp = 9 * kP / 16;   // 1 KB blocks per page
+__device__ __forceinline__ bool f8_dma(const MlaArgs& a, const_i32_t* ptab, int end, int t0, uint32_t lds,
+                                       int wave, uint32_t voff) {
+  constexpr int kPages = kF8Tokens / kP;
+  constexpr int kBpp = 9 * kP / 16;   // 1 KB blocks per page
+  const int last = (end - 1) / kP;
   const uint8_t* base[kPages];
-  uint32_t lds;
-  __device__ __forceinline__ bool prepare(const MlaArgs& a, const_i32_t* ptab, int end, int t0,
-                                          uint32_t lds_addr) {
-    const int last = (end - 1) / kP;
-    bool bad = false;
+  bool bad = false;
 #pragma unroll
-    for (int pg = 0; pg < kPages; ++pg) {
-      const int pid = ptab[min(t0 / kP + pg, last)];
-      const bool ok = pid >= 0 && pid < a.num_pages;
-      bad |= !ok;
-      base[pg] = a.kv + (ok ? (int64_t)pid * (kP * kD) : 0);
-    }
-    lds = lds_addr;
-    if (bad && (threadIdx.x & 63) == 0) raise_error(a.err_flag, kErrPageId);
-    return bad;
+  for (int pg = 0; pg < kPages; ++pg) {
+    const int pid = ptab[min(t0 / kP + pg, last)];
+    const bool ok = pid >= 0 && pid < a.num_pages;
+    bad |= !ok;
+    base[pg] = a.kv + (ok ? (int64_t)pid * (kP * kD) : 0);
   }
-  template <int J>
-  __device__ __forceinline__ void issue(int wave, uint32_t voff) const {
-    const int b = 4 * J + wave;
+  if (bad && (threadIdx.x & 63) == 0) raise_error(a.err_flag, kErrPageId);
+#pragma unroll
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int b = 4 * j + wave;
     const int pg = kPages == 1 ? 0 : b / kBpp;
     const uint8_t* src = base[0];
 #pragma unroll
     for (int q = 1; q < kPages; ++q)
       if (pg == q) src = base[q];
-    dma_sbase<J>(src + (b - pg * kBpp) * 1024, voff, lds);
+    src += (b - pg * kBpp) * 1024;
+    switch (j) {
+      case 0: dma_sbase<0>(src, voff, lds); break;
+      case 1: dma_sbase<1>(src, voff, lds); break;
+      case 2: dma_sbase<2>(src, voff, lds); break;
+      case 3: dma_sbase<3>(src, voff, lds); break;
+      case 4: dma_sbase<4>(src, voff, lds); break;
+      case 5: dma_sbase<5>(src, voff, lds); break;
+      case 6: dma_sbase<6>(src, voff, lds); break;
+      case 7: dma_sbase<7>(src, voff, lds); break;
+      default: dma_sbase<8>(src, voff, lds); break;
+    }
   }
-  __device__ __forceinline__ void issue_all(int wave, uint32_t voff) const {
-    issue<0>(wave, voff); issue<1>(wave, voff); issue<2>(wave, voff); issue<3>(wave, voff);
-    issue<4>(wave, voff); issue<5>(wave, voff); issue<6>(wave, voff); issue<7>(wave, voff);
-    issue<8>(wave, voff);
-  }
-};
+  return bad;
+}
 
 template <int kP>
 __device__ __forceinline__ void mla_task_f8(const MlaArgs& a, const DevTask& task, MlaShared8& sh) {
@@ -779,12 +776,7 @@ __device__ __forceinline__ void mla_task_f8(const MlaArgs& a, const DevTask& tas
     // FP8 tiles 0 and 1, then tile 0's first half converted
 #pragma unroll
     for (int f = 0; f < 2; ++f)
-      if (f < nf) {
-        F8Dma<kP> d;
-        bad_page |= d.prepare(a, ptab, end, t.lo + f * kF8Tokens, dma_lds + f * kF8TileBytes);
-        d.issue_all(wave, voff);
-      }
-    F8Dma<kP> dn{};   // the next FP8 tile to send, its page ids read an iteration ahead
+      if (f < nf) bad_page |= f8_dma<kP>(a, ptab, end, t.lo + f * kF8Tokens, dma_lds + f * kF8TileBytes, wave, voff);
     if (ntiles > 0) {
       if (nf > 1) __builtin_amdgcn_s_waitcnt(kWaitVm9);
       else __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -799,15 +791,9 @@ __device__ __forceinline__ void mla_task_f8(const MlaArgs& a, const DevTask& tas
       if (k & 1) __builtin_amdgcn_s_waitcnt(kWaitVm0 & 0xc07f);
       else __builtin_amdgcn_s_waitcnt(0xc07f);
       bare_barrier();
-      // odd k: FP8 tile F = (k + 3) / 2 goes out during the score products
-      // (its page ids were read at iteration k - 1); even k: read the ids of
-      // the tile the next iteration sends
-      const int F = (k + 3) / 2;
-      const bool send = (k & 1) && F < nf;
-      if (send) dn.lds = dma_lds + (F & 1) * kF8TileBytes;
-      const F8Dma<kP> d = dn;
-      if (!(k & 1) && (k + 4) / 2 < nf)
-        bad_page |= dn.prepare(a, ptab, end, t.lo + ((k + 4) / 2) * kF8Tokens, dma_lds);
+      const int F = (k + 3) / 2;   // the FP8 tile sent at this (odd) iteration
+      if ((k & 1) && F < nf)
+        bad_page |= f8_dma<kP>(a, ptab, end, t.lo + F * kF8Tokens, dma_lds + (F & 1) * kF8TileBytes, wave, voff);
       // page scale(s) of tile k: one page (P >= 32) or two (P = 16; a lane's
       // eight tokens lie in one 16-token half); ids outside the pool read page
       // 0's scale (the state is NaN anyway)
@@ -835,29 +821,15 @@ __device__ __forceinline__ void mla_task_f8(const MlaArgs& a, const DevTask& tas
         __builtin_amdgcn_s_waitcnt(0xc07f);
         bare_barrier();
       }
-      // ---- scores S^T of tile k over all 576 dims, with tile k + 1's codes
-      // decoded into the other bf16 tile (its last reader, tile k - 1,
-      // finished before this iteration's barrier) and the DMA of an odd
-      // iteration spread over the products: chunk i's table entry is read at
-      // k-step 2i - 2, its codes at 2i, its bf16 slot written at 2i + 2 ----
+      // tile k + 1's codes into the other bf16 tile (its last reader, tile
+      // k - 1, finished before this iteration's barrier)
+      if (k + 1 < ntiles)
+        convert_tile(&sh.f8[(k + 1) / 2 & 1][((k + 1) & 1) * kF8HalfBytes],
+                     reinterpret_cast<uint8_t*>(&sh.bf[(k + 1) & 1][0]), tab, lane);
+
+      // ---- scores S^T of tile k over all 576 dims ----
       f32x4_t s[2][2];
-      const uint8_t* half = &sh.f8[(k + 1) / 2 & 1][((k + 1) & 1) * kF8HalfBytes];
-      uint8_t* next = reinterpret_cast<uint8_t*>(&sh.bf[(k + 1) & 1][0]);
-      auto qk = [&](auto send_tag, auto cvt_tag) {
-        constexpr bool kSend = decltype(send_tag)::value;
-        constexpr bool kDecode = decltype(cvt_tag)::value;
-        uint32_t e[3];
-        u32x2_t c[2];
-        auto write_chunk = [&](int i) {
-          const u32x2_t w = c[i & 1];
-          *reinterpret_cast<u32x4_t*>(next + (e[i % 3] >> 16)) =
-              u32x4_t{f8x2_to_bf16x2<false>(w[0]), f8x2_to_bf16x2<true>(w[0]),
-                      f8x2_to_bf16x2<false>(w[1]), f8x2_to_bf16x2<true>(w[1])};
-        };
-        if (kDecode) {
-          e[0] = tab[lane];
-          e[1] = tab[64 + lane];
-        }
+      {
         u32x4_t kb[kKd][2];
         auto kread = [&](int ks, u32x4_t (&dst)[2]) {
 #pragma unroll
@@ -874,36 +846,8 @@ __device__ __forceinline__ void mla_task_f8(const MlaArgs& a, const DevTask& tas
           if (ks + kKd - 1 < kKs) kread(ks + kKd - 1, kb[(ks + kKd - 1) % kKd]);
           if (ks == 0) qk_step<true>(s, kb[0], qf[0][0], qf[1][0]);
           else qk_step<false>(s, kb[ks % kKd], qf[0][ks], qf[1][ks]);
-          if (kDecode && ks % 2 == 0) {
-            const int i = ks / 2;            // 0..8
-            if (i >= 1) write_chunk(i - 1);
-            c[i & 1] = *reinterpret_cast<const u32x2_t*>(half + (e[i % 3] & 0xFFFFu));
-            if (i + 2 < kCvt) e[(i + 2) % 3] = tab[64 * (i + 2) + lane];
-          }
-          if (kSend && ks % 2 == 1) {
-            switch (ks / 2) {
-              case 0: d.template issue<0>(wave, voff); break;
-              case 1: d.template issue<1>(wave, voff); break;
-              case 2: d.template issue<2>(wave, voff); break;
-              case 3: d.template issue<3>(wave, voff); break;
-              case 4: d.template issue<4>(wave, voff); break;
-              case 5: d.template issue<5>(wave, voff); break;
-              case 6: d.template issue<6>(wave, voff); break;
-              case 7: d.template issue<7>(wave, voff); break;
-              default: d.template issue<8>(wave, voff); break;
-            }
-          }
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (kDecode) write_chunk(kCvt - 1);
-      };
-      const bool decode = k + 1 < ntiles;
-      if (send) {
-        if (decode) qk(std::true_type{}, std::true_type{});
-        else qk(std::true_type{}, std::false_type{});
-      } else {
-        if (decode) qk(std::false_type{}, std::true_type{});
-        else qk(std::false_type{}, std::false_type{});
       }
       scores_ready(s);
 

@@ -55,24 +55,31 @@ def run_path(w, plan, inputs: DeviceInputs | None = None, with_ext: bool = True,
              out_dtype=torch.float32, fused: bool = True):
     """Partial states and merged output of the HIP path (the two calls), as
     float64 numpy arrays. With ``fused``, the one-call path (attention and
-    merge in one launch) also runs on the same inputs and must give the same
-    merged output and LSE bit for bit: both merges add a row's states in the
-    same order with the same operations."""
+    merge in one launch for plans built for it, else the two launches; FP8 KV
+    through its own one-call entry point) also runs on the same inputs and
+    must give the same merged output and LSE bit for bit: both merges add a
+    row's states in the same order with the same operations."""
     d = inputs or DeviceInputs(w)
-    if w.dtype == "fp8":
-        # FP8 KV has its own attention entry point; the one-call path takes none
+    fp8 = w.dtype == "fp8"
+    if fp8:
+        # FP8 KV has its own entry points (with the scales); its one-call path
+        # runs the two launches
         o_part, lse_part = skv.decode_attn_partial_fp8(d.q, d.k, d.v, d.k_scale, d.v_scale, d.page_table,
                                                        d.seq_lens, plan, w.scale)
-        fused = False
     else:
         o_part, lse_part = skv.decode_attn_partial(d.q, d.k, d.v, d.page_table, d.seq_lens, plan, w.scale)
     ext = with_ext and d.o_ext is not None
     o, lse = skv.merge_states(o_part, lse_part, plan, d.o_ext if ext else None,
                               d.lse_ext if ext else None, out_dtype=out_dtype)
-    if fused:
+    if fused and fp8:
+        fo, fl = skv.decode_attn_fp8(d.q, d.k, d.v, d.k_scale, d.v_scale, d.page_table, d.seq_lens, plan,
+                                     w.scale, d.o_ext if ext else None, d.lse_ext if ext else None,
+                                     out_dtype=out_dtype)
+    elif fused:
         fo, fl = skv.decode_attn(d.q, d.k, d.v, d.page_table, d.seq_lens, plan, w.scale,
                                  d.o_ext if ext else None, d.lse_ext if ext else None,
                                  out_dtype=out_dtype)
+    if fused:
         torch.cuda.synchronize()
         assert torch.equal(_bits(fo), _bits(o)), f"{w.name}: fused output differs from the two calls"
         assert torch.equal(_bits(fl), _bits(lse)), f"{w.name}: fused LSE differs from the two calls"

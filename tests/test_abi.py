@@ -403,6 +403,17 @@ def test_fp8_descriptions_and_entry_point_checks():
     st = skv._lib.skv_decode_attn(ctypes.byref(d), fake, fake, fake, fake, fake, plan.handle, fake, fake, need,
                                   0, None, None, fake, 0, None, None)
     assert st == -1
+    # the FP8 one-call entry point: an FP8 description, its scales, and a plan
+    # for the two launches (the one-launch engine has no FP8 kernels)
+    fcall = lambda desc, ks, vs, pl: skv._lib.skv_decode_attn_fp8(
+        ctypes.byref(desc), fake, fake, fake, ks, vs, fake, fake, pl.handle, fake, fake,
+        skv.scratch_bytes(pl), 0, None, None, fake, 0, None, None)
+    assert fcall(bf, fake, fake, plan) == -1 and "SKV_FP8_E4M3" in skv._lib.skv_last_error().decode()
+    assert fcall(d, None, fake, plan) == -1 and "scales" in skv._lib.skv_last_error().decode()
+    prm1 = skv.default_params()
+    prm1.overlap_reduction = 1
+    plan1 = skv.plan_splits([100, 50], f8, num_cu=4, q_lens=[3, 1], params=prm1)
+    assert fcall(d, fake, fake, plan1) == -2 and "overlap_reduction" in skv._lib.skv_last_error().decode()
     # the Python face: FP8 specs go through decode_attn_partial_fp8 only
     with pytest.raises(ValueError):
         skv.decode_attn_partial(torch.empty(0), None, None, None, None, plan, 0.1)
