@@ -558,7 +558,8 @@ def mfma_probe(blocks: int, waves: int, iters: int, device, out: torch.Tensor | 
     mw = waves if mfma_waves is None else mfma_waves
     if out is None:
         out = torch.empty(blocks * waves, 2, dtype=torch.int32, device=device)
-    if not out.is_contiguous() or out.numel() < 2 * blocks * waves:
+    if (out.dtype != torch.int32 or out.device.type != "cuda" or not out.is_contiguous()
+            or out.numel() < 2 * blocks * waves):
         raise ValueError("out must be a contiguous device tensor of 2 * blocks * waves int32")
     if mw < waves and (buf is None or not buf.is_contiguous() or buf.device.type != "cuda"):
         raise ValueError("streaming waves need buf, a contiguous device tensor")
