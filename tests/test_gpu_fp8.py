@@ -185,3 +185,27 @@ def test_fp8_mla_out_of_range_page_and_flag():
         ro, rl = A.attention_rows(w, b, [0])
         compare(o[b * H:(b + 1) * H].reshape(ro.shape), ro, lse[b * H:(b + 1) * H].reshape(rl.shape), rl,
                 tol_for(w), f"{w.name} b={b}")
+
+
+@pytest.mark.parametrize("mla", [False, True], ids=["gqa", "mla"])
+def test_fp8_device_lengths_differ_from_plan(mla):
+    # a request's device length one short of the plan's: its tasks read no KV
+    # and write NaN states (flag bit 1, value 2); the other requests are exact
+    w = fp8_mla([300, 1000, 777], seed=72) if mla else fp8_case(32, 2, 128, 16, [300, 1000, 777], seed=72)
+    print(f"[fp8] {w.name} device lengths", flush=True)
+    dev = torch.device("cuda:0")
+    d = DeviceInputs(w)
+    sl = w.seq_lens.copy()
+    sl[1] -= 1
+    plan = skv.plan_from_counts(w.seq_lens, spec_of(w), [2, 3, 2])
+    o_part, lse_part = skv.decode_attn_partial_fp8(d.q, d.k, d.v, d.k_scale, d.v_scale, d.page_table,
+                                                   torch.from_numpy(sl).to(dev), plan, w.scale)
+    o, lse = skv.merge_states(o_part, lse_part, plan)
+    assert plan.read_error_flag(dev) == 2
+    o, lse = o.cpu().double().numpy(), lse.cpu().double().numpy()
+    H = w.num_q_heads
+    assert np.isnan(o[H:2 * H]).all() and np.isnan(lse[H:2 * H]).all()
+    for b in (0, 2):
+        ro, rl = A.attention_rows(w, b, [0])
+        compare(o[b * H:(b + 1) * H].reshape(ro.shape), ro, lse[b * H:(b + 1) * H].reshape(rl.shape), rl,
+                tol_for(w), f"{w.name} b={b}")
