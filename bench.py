@@ -529,7 +529,7 @@ def measure(w, key: str, dev, num_cu: int, args, plan_params) -> dict:
 
 
 def load(key: str, cache: dict):
-    """Workload `key` (1-7, or 5d for the decode part of 5), generated once."""
+    """Workload `key` (1-8, or 5d for the decode part of 5), generated once."""
     import workloads as wl
     if key == "5d":
         return decode_part(load("5", cache))
