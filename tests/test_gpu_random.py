@@ -1,4 +1,4 @@
-"""Randomised GPU parity: seeded random shapes (dtype (fp32, bf16, FP8 KV), group size, head dim,
+"""Randomised GPU parity: seeded random shapes (dtype (fp32, bf16, FP8 KV; FP8 MLA rows), group size, head dim,
 page size, batch, ragged lengths, chunk rows, external states, planner or
 random split counts) for the GQA and MLA paths, each checked element-wise
 against the float64 oracle (partial states and merged outputs)."""
@@ -93,4 +93,24 @@ def test_random_fp8(seed):
                  num_q_heads=G * H_kv, num_kv_heads=H_kv, head_dim_qk=D, head_dim_v=D, page_size=P,
                  scale=1.0 / math.sqrt(D), seed=seed, q_scale=float(rng.choice([1.0, 3.0])),
                  causal=True, n_ext=n_ext, ext_lse_center=4.0)
+    check_all(w, _plan(rng, w))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_fp8_mla(seed):
+    # FP8 (OCP E4M3) MLA rows with one scale per page: 16-128 heads, page sizes
+    # 16-64, ragged lengths around the 32- and 64-token tiles, chunk rows,
+    # external states, planner or random split counts
+    rng = np.random.default_rng(4000 + seed)
+    H = int(rng.choice([16, 32, 64, 96, 128]))
+    P = int(rng.choice([16, 32, 64]))
+    batch = int(rng.integers(1, 5))
+    q_lens = [int(rng.integers(2, 12)) if rng.random() < 0.2 else 1 for _ in range(batch)]
+    seq = _lengths(rng, batch, q_lens, 2200)
+    n_ext = int(rng.choice([0, 0, 2, 16, 64]))
+    w = wl.build(f"rand-fp8-mla-{seed}", dtype="fp8", mla=True, seq_lens=seq, q_lens=q_lens,
+                 num_q_heads=H, num_kv_heads=1, head_dim_qk=576, head_dim_v=512, page_size=P,
+                 scale=wl.MLA_SCALE, seed=seed, value_scale=0.1,
+                 q_scale=float(rng.choice([1.0, wl.SHARP_MLA])), causal=True, n_ext=n_ext,
+                 ext_lse_center=5.0)
     check_all(w, _plan(rng, w))
